@@ -1,0 +1,234 @@
+/*
+ * tq.h -- C ABI of the TurboQuant hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The library quantizes key/value vectors online and estimates attention
+ * logits (and vector-search scores) straight from the packed codes.  Every
+ * call returns a tq_status (TQ_OK == 0); nothing throws across the ABI.  On
+ * failure tq_last_error() returns a thread-local message for the last failed
+ * call made by this thread.
+ *
+ * Method (sources are web pages on TurboQuant; section names are given so a
+ * reader can find the passage):
+ *  - turboquant.net, "PolarQuant" section: after a random rotation the
+ *    coordinates of a unit vector follow
+ *      f_d(x) = Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)) (1 - x^2)^((d-3)/2)
+ *    on [-1, 1], so a scalar Lloyd-Max quantizer per coordinate needs no
+ *    per-block constants.
+ *  - turboquant.net, "pseudo-code implementation steps": Lloyd-Max centroids
+ *    precomputed once; Pi = Q factor of a Gaussian d x d matrix, generated
+ *    once and reused ("potential challenges" section); quant: rotate, nearest
+ *    centroid; dequant: centroids[idx] rotated back; attention estimates inner
+ *    products with QJL.
+ *  - admirer.cn article on Google Research's TurboQuant: (b-1) bits of scalar
+ *    codes plus one QJL sign bit of the residual make b bits per coordinate;
+ *    the QJL sign sketch gives unbiased inner products.
+ *  - turboquant.net, "potential challenges": the residual norm is kept as one
+ *    fp16 scalar per vector.
+ *
+ * Readings of what the pages leave open (the library and its test oracle
+ * share them):
+ *  - vectors are normalised first; nu = ||x|| is stored as fp16 next to the
+ *    residual norm gamma = ||r|| (fp16, round to nearest even);
+ *  - S is a d x d matrix of iid N(0,1) (m = d sketch rows); the QJL scale is
+ *    alpha = sqrt(pi/2) / d, which makes the estimate unbiased over S;
+ *  - sign(0) = +1; nearest-centroid ties go to the lower index;
+ *  - a zero vector stores nu = gamma = 0, the codes of y = 0, all signs +1.
+ *
+ * Estimator (used by tq_attn_logits, tq_search_topk and, with q = e_j, by
+ * tq_dequantize):
+ *   est(q, rec) = nu * ( <Pi q, c[idx]> + alpha * gamma * <S q, s> )
+ *
+ * Packed record layout ("canonical layout", caller-owned device memory):
+ *  W = ceil(d/32).  planes: uint32 [n_records][W][b]; for word group w the b
+ *  words are: words 0..b-2 = bit p of the code index of coordinates
+ *  32w..32w+31 (bit j%32 <-> coordinate j), word b-1 = QJL signs (1 <-> +1).
+ *  Bits of coordinates >= d are 0.  norms: uint16 [n_records][2] holding the
+ *  fp16 bit patterns of (nu, gamma).  A record is b*d bits + 4 bytes.
+ *
+ * Device pointers must come from the HIP device the context was created on;
+ * `stream` is a hipStream_t (NULL = default stream).  Calls are asynchronous:
+ * outputs are valid once the stream has been synchronised.  The context is
+ * immutable after creation, so concurrent calls on different streams may share
+ * it.  No call on the hot path allocates memory.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(_WIN32)
+#define TQ_API
+#else
+#define TQ_API __attribute__((visibility("default")))
+#endif
+
+typedef int32_t tq_status;
+#define TQ_OK 0
+#define TQ_ERR_INVALID_ARG (-1)   /* bad pointer, size, stride or alignment */
+#define TQ_ERR_UNSUPPORTED (-2)   /* d or b outside the supported set */
+#define TQ_ERR_NOT_CONVERGED (-3) /* tq_lloyd_max hit max_iter */
+#define TQ_ERR_HIP (-4)           /* a HIP runtime call or launch failed */
+#define TQ_ERR_ALLOC (-5)         /* device allocation failed (context creation) */
+
+/* Input element types of tq_quantize_kv. */
+#define TQ_F32 0
+#define TQ_BF16 1
+
+/* Supported shapes on the device: d a multiple of 8 in 8..2048, b in {2, 3, 4}
+ * (b-1 code bits + 1 sign bit).  The host set-up calls accept 3 <= d <= 2048. */
+#define TQ_MAX_D 2048
+
+/* Human-readable name of a status code (static string, never NULL). */
+TQ_API const char* tq_status_string(tq_status s);
+
+/* Message of the last failure on the calling thread ("" if none). */
+TQ_API const char* tq_last_error(void);
+
+/* W = ceil(d/32): 32-bit words per bit plane; 0 if d < 1. */
+TQ_API int32_t tq_words_per_plane(int32_t d);
+
+/* Words of one packed record: W * b (the record also has 2 fp16 norms). */
+TQ_API int32_t tq_record_words(int32_t d, int32_t b);
+
+/* ---- offline set-up (host memory, deterministic, no device needed) ------ */
+
+/* Rotation and sketch (turboquant.net pseudo-code, "generate random rotation
+ * matrix"; reuse per "potential challenges"; QJL sketch per the admirer.cn
+ * QJL paragraph).  Gaussians come from SplitMix64 (key = output `stream` of
+ * state `seed`, value i = output i of state key) and Box-Muller (pair j uses
+ * uniforms 2j, 2j+1, giving r cos, r sin); G uses stream 0 and S stream 1,
+ * both filled row-major.  pi receives the Q factor of G with column signs
+ * fixed so that diag(R) > 0 (computed in double, rounded to fp32); y = pi x.
+ * s receives S (m = d rows).
+ *   pi, s: host float[d*d], row-major, caller-owned.  Either may be NULL.
+ * Errors: TQ_ERR_INVALID_ARG if d < 3 or d > TQ_MAX_D. */
+TQ_API tq_status tq_make_rotation(int32_t d, uint64_t seed, float* pi, float* s);
+
+/* Lloyd-Max codebook of f_d with 2^lm_bits levels (turboquant.net
+ * pseudo-code, "precompute Lloyd-Max centroids"; admirer.cn: Lloyd-Max solves
+ * the continuous 1-D k-means problem).  For the two-stage quantizer use
+ * lm_bits = b - 1.  Computed in double: thresholds at midpoints, centroids at
+ * the conditional means of f_d (incomplete-beta cell masses, closed-form first
+ * moments), until max |delta c| < tol; the result is exactly symmetric
+ * (c[k] == -c[K-1-k]).
+ *   centroids: host float[1 << lm_bits], ascending, caller-owned.
+ *   distortion_out (nullable): d * E[(X - c(X))^2], the per-vector MSE of a
+ *   unit vector.  iters_out (nullable): iterations run.
+ * Errors: TQ_ERR_INVALID_ARG for d < 3, d > TQ_MAX_D, lm_bits outside 1..4,
+ * max_iter < 1, tol <= 0 or centroids == NULL; TQ_ERR_NOT_CONVERGED if
+ * max_iter was reached (centroids then hold the last iterate). */
+TQ_API tq_status tq_lloyd_max(int32_t d, int32_t lm_bits, int32_t max_iter, double tol,
+                              float* centroids, double* distortion_out, int32_t* iters_out);
+
+/* ---- context: device copies of the tables --------------------------------
+ * Uploads to the current HIP device: Pi and S (fp32 and hi/lo fp16 splits),
+ * M = S Pi^T (formed in double), the centroids, their midpoints and the
+ * Walsh expansion of the codebook used by the logit kernel.
+ *   pi, s: host float[d*d] (as from tq_make_rotation); centroids: host
+ *   float[1 << (b-1)], ascending and exactly symmetric.
+ * Errors: TQ_ERR_UNSUPPORTED if d is not a multiple of 8 in 8..TQ_MAX_D or b is
+ * outside {2,3,4};
+ * TQ_ERR_INVALID_ARG for NULL pointers, non-finite values or a codebook that
+ * is not strictly ascending and symmetric; TQ_ERR_ALLOC / TQ_ERR_HIP if the
+ * device copies fail (nothing is leaked). */
+typedef struct tq_ctx tq_ctx;
+TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const float* s,
+                               const float* centroids, tq_ctx** out);
+/* Frees the device tables (synchronises the device first).  NULL is a no-op. */
+TQ_API tq_status tq_ctx_destroy(tq_ctx* ctx);
+TQ_API int32_t tq_ctx_dim(const tq_ctx* ctx);
+TQ_API int32_t tq_ctx_bits(const tq_ctx* ctx);
+
+/* ---- hot path -------------------------------------------------------------- */
+
+/* Quantize n_heads * n_tokens vectors (turboquant.net pseudo-code "quant",
+ * plus the QJL stage of the admirer.cn two-stage description):
+ *   nu = ||x||, y = Pi x / nu, idx_j = nearest centroid, r = x/nu - Pi^T c[idx],
+ *   gamma = ||r||, s = sign(S r); codes, signs and fp16 (nu, gamma) packed.
+ * x: device, element (h, t, j) at x[h*x_stride_head + t*x_stride_token + j]
+ *   (strides in elements; rows contiguous), x_dtype TQ_F32 or TQ_BF16.
+ * Output record of (h, t) at index h*dst_stride_head + dst_token0 + t of
+ *   planes (uint32 [.][W][b], 16-byte aligned base) and norms (uint16 [.][2]).
+ * Errors: TQ_ERR_INVALID_ARG for NULL ctx/pointers with n > 0, negative sizes,
+ * strides below d, misaligned planes/x, unknown dtype.  n_tokens == 0 or
+ * n_heads == 0 is a no-op.  Inputs with ||x|| > 65504 overflow fp16 and are
+ * not supported (not checked on the hot path). */
+TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                                int64_t dst_stride_head, int64_t dst_token0, void* stream);
+
+/* Dequantize n records (turboquant.net pseudo-code "dequant", with the QJL
+ * term so that <q, out_i> equals est(q, record i) for every q):
+ *   out_i = nu * (Pi^T c[idx] + alpha * gamma * S^T s).
+ * out: device float, row i at out + i*out_ld (out_ld >= d).
+ * Errors: TQ_ERR_INVALID_ARG for NULL pointers with n > 0, n < 0, out_ld < d,
+ * misaligned planes.  n == 0 is a no-op. */
+TQ_API tq_status tq_dequantize(const tq_ctx* ctx, const uint32_t* planes,
+                               const uint16_t* norms, int64_t n, float* out, int64_t out_ld,
+                               void* stream);
+
+/* Workspace for tq_attn_logits (prepared queries), in bytes. */
+TQ_API size_t tq_attn_logits_workspace_bytes(const tq_ctx* ctx, int32_t batch,
+                                             int32_t n_q_heads, int32_t n_kv_heads);
+
+/* Attention logits from packed keys (turboquant.net pseudo-code "integrate
+ * into attention": keys stored quantized, inner products estimated with QJL;
+ * admirer.cn: 4-bit keys for logits).  Each query is rotated and projected
+ * once (Pi q, S q), then every cached key record is streamed:
+ *   logits[hq*logits_stride_head + seq_start[bi] + t] =
+ *       scale * est(q[bi, hq], key record (hq / G, bi, t)),  G = n_q/n_kv,
+ * with the key record of (kv head h, sequence bi, token t) at index
+ *   h*keys_stride_head + seq_start[bi] + t.
+ * q: device float [batch][n_q_heads][d] with row stride d and batch stride
+ *   q_stride_batch (elements).  seq_start (int64) and seq_len (int32): device
+ *   arrays [batch]; max_seq_len (host) bounds every seq_len[bi] (the grid is
+ *   sized from it; the caller guarantees 0 <= seq_len[bi] <= max_seq_len and
+ *   that the addressed records exist).
+ * workspace: device memory of at least tq_attn_logits_workspace_bytes(),
+ *   16-byte aligned; it is overwritten.
+ * Errors: TQ_ERR_INVALID_ARG for NULL pointers with work to do, batch < 0,
+ * n_kv_heads < 1, n_q_heads % n_kv_heads != 0, a too small workspace,
+ * misaligned planes/workspace.  batch == 0 or max_seq_len == 0 is a no-op. */
+TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
+                                int32_t n_q_heads, int64_t q_stride_batch,
+                                const uint32_t* planes, const uint16_t* norms,
+                                int32_t n_kv_heads, int64_t keys_stride_head,
+                                const int64_t* seq_start, const int32_t* seq_len,
+                                int32_t max_seq_len, float scale, float* logits,
+                                int64_t logits_stride_head, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Workspace for tq_search_topk, in bytes. */
+TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db,
+                                        int32_t k);
+
+/* Nearest-neighbour search over a quantized database (zingnex.cn digest,
+ * nearest-neighbour section; admirer.cn vector-search paragraph: quantize the
+ * database with near-zero indexing time, then score from the codes).  For
+ * each query a, the k records with the largest est(q_a, record) (scale 1),
+ * ordered by (score descending, index ascending); scores of all pairs are
+ * never written to memory.
+ * queries: device float [n_queries][d]; planes/norms: n_db records.
+ * out_idx: device int64 [n_queries][k]; out_score: device float [n_queries][k]
+ *   (entries beyond n_db hold index -1 and score -inf).
+ * workspace: device memory of at least tq_search_workspace_bytes(),
+ *   16-byte aligned; it is overwritten.
+ * Errors: TQ_ERR_INVALID_ARG for NULL pointers with work to do, negative
+ * sizes, k outside 1..64, a too small workspace, misaligned pointers.
+ * n_queries == 0 is a no-op. */
+TQ_API tq_status tq_search_topk(const tq_ctx* ctx, const float* queries, int64_t n_queries,
+                                const uint32_t* planes, const uint16_t* norms, int64_t n_db,
+                                int32_t k, int64_t* out_idx, float* out_score,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,257 @@
+"""Python binding of libtq, the MI355X TurboQuant hot path.
+
+Thin ctypes marshalling over the C ABI in ``include/tq.h``: every function
+here has the name of the C entry point it calls and does no arithmetic of its
+own.  PyTorch provides device memory and the current HIP stream; all work on
+the hot path runs in the HIP kernels of ``libtq.so``.  Importing this package
+fails loudly when the built library is missing -- there is no fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK = 0
+TQ_ERR_INVALID_ARG = -1
+TQ_ERR_UNSUPPORTED = -2
+TQ_ERR_NOT_CONVERGED = -3
+TQ_ERR_HIP = -4
+TQ_ERR_ALLOC = -5
+TQ_F32 = 0
+TQ_BF16 = 1
+
+# every symbol include/tq.h declares
+EXPORTS = [
+    "tq_status_string", "tq_last_error", "tq_words_per_plane", "tq_record_words",
+    "tq_make_rotation", "tq_lloyd_max", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim",
+    "tq_ctx_bits", "tq_quantize_kv", "tq_dequantize", "tq_attn_logits_workspace_bytes",
+    "tq_attn_logits", "tq_search_workspace_bytes", "tq_search_topk",
+]
+
+
+class TqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libtq.so not built at {LIB_PATH}; run "
+                      "`python -m kv_cache_vector_pi_amd.build` (no fallback exists)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_i32, _i64, _u64, _f32, _f64, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                     ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_sig("tq_status_string", ctypes.c_char_p, [_i32])
+_sig("tq_last_error", ctypes.c_char_p, [])
+_sig("tq_words_per_plane", _i32, [_i32])
+_sig("tq_record_words", _i32, [_i32, _i32])
+_sig("tq_make_rotation", _i32, [_i32, _u64, _P, _P])
+_sig("tq_lloyd_max", _i32, [_i32, _i32, _i32, _f64, _P, _P, _P])
+_sig("tq_ctx_create", _i32, [_i32, _i32, _P, _P, _P, ctypes.POINTER(_P)])
+_sig("tq_ctx_destroy", _i32, [_P])
+_sig("tq_ctx_dim", _i32, [_P])
+_sig("tq_ctx_bits", _i32, [_P])
+_sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
+_sig("tq_dequantize", _i32, [_P, _P, _P, _i64, _P, _i64, _P])
+_sig("tq_attn_logits_workspace_bytes", _sz, [_P, _i32, _i32, _i32])
+_sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P, _i32, _f32,
+                              _P, _i64, _P, _sz, _P])
+_sig("tq_search_workspace_bytes", _sz, [_P, _i64, _i64, _i32])
+_sig("tq_search_topk", _i32, [_P, _P, _i64, _P, _P, _i64, _i32, _P, _P, _P, _sz, _P])
+
+
+def lib():
+    return _lib
+
+
+def _check(status, what):
+    if status != TQ_OK:
+        msg = _lib.tq_last_error().decode() or what
+        raise TqError(status, msg)
+
+
+def _ptr(t):
+    """Device or host address of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---- small helpers --------------------------------------------------------
+def tq_status_string(status):
+    return _lib.tq_status_string(status).decode()
+
+
+def tq_last_error():
+    return _lib.tq_last_error().decode()
+
+
+def tq_words_per_plane(d):
+    return _lib.tq_words_per_plane(d)
+
+
+def tq_record_words(d, b):
+    return _lib.tq_record_words(d, b)
+
+
+# ---- offline set-up (host) ------------------------------------------------
+def tq_make_rotation(d, seed):
+    """(pi, s): float32 [d, d] host arrays (see tq.h)."""
+    pi = np.empty((d, d), np.float32)
+    s = np.empty((d, d), np.float32)
+    _check(_lib.tq_make_rotation(d, seed, pi.ctypes.data, s.ctypes.data), "tq_make_rotation")
+    return pi, s
+
+
+def tq_lloyd_max(d, lm_bits, max_iter=100000, tol=1e-13):
+    """(centroids float32 [2**lm_bits], distortion, iterations)."""
+    c = np.empty(1 << lm_bits, np.float32)
+    dist = ctypes.c_double(0.0)
+    it = ctypes.c_int32(0)
+    st = _lib.tq_lloyd_max(d, lm_bits, max_iter, tol, c.ctypes.data, ctypes.addressof(dist),
+                           ctypes.addressof(it))
+    _check(st, "tq_lloyd_max")
+    return c, dist.value, it.value
+
+
+class TqContext:
+    """Owns a tq_ctx (device tables on the current HIP device)."""
+
+    def __init__(self, d, b, pi, s, centroids):
+        pi = np.ascontiguousarray(pi, np.float32)
+        s = np.ascontiguousarray(s, np.float32)
+        c = np.ascontiguousarray(centroids, np.float32)
+        h = _P()
+        _check(_lib.tq_ctx_create(d, b, pi.ctypes.data, s.ctypes.data, c.ctypes.data,
+                                  ctypes.byref(h)), "tq_ctx_create")
+        self.handle = h.value
+        self.d, self.b = d, b
+
+    @property
+    def W(self):
+        return tq_words_per_plane(self.d)
+
+    def close(self):
+        if self.handle:
+            _check(_lib.tq_ctx_destroy(self.handle), "tq_ctx_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tq_ctx_create(d, b, pi, s, centroids):
+    return TqContext(d, b, pi, s, centroids)
+
+
+def tq_ctx_destroy(ctx):
+    ctx.close()
+
+
+# ---- device buffers -------------------------------------------------------
+def alloc_records(n, d, b, device="cuda"):
+    """(planes uint32-as-int32 [n, W*b], norms int16 [n, 2]) device tensors."""
+    import torch
+    planes = torch.zeros((n, tq_record_words(d, b)), dtype=torch.int32, device=device)
+    norms = torch.zeros((n, 2), dtype=torch.int16, device=device)
+    return planes, norms
+
+
+# ---- hot path -------------------------------------------------------------
+def tq_quantize_kv(ctx, x, planes, norms, n_tokens=None, n_heads=None, x_stride_token=None,
+                   x_stride_head=None, dst_stride_head=None, dst_token0=0, stream=None):
+    """Quantize x ([n_heads, n_tokens, d] or [n, d] torch tensor, float32 or
+    bfloat16) into planes/norms (see tq.h for the record indexing)."""
+    import torch
+    if x.dtype == torch.bfloat16:
+        dt = TQ_BF16
+    elif x.dtype == torch.float32:
+        dt = TQ_F32
+    else:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if x.dim() == 2:
+        x3 = x.unsqueeze(0)
+    else:
+        x3 = x
+    if n_heads is None:
+        n_heads = x3.shape[0]
+    if n_tokens is None:
+        n_tokens = x3.shape[1]
+    if x_stride_token is None:
+        x_stride_token = x3.stride(1)
+    if x_stride_head is None:
+        x_stride_head = x3.stride(0)
+    if dst_stride_head is None:
+        dst_stride_head = n_tokens
+    st = _lib.tq_quantize_kv(ctx.handle, _ptr(x), dt, n_tokens, n_heads, x_stride_token,
+                             x_stride_head, _ptr(planes), _ptr(norms), dst_stride_head,
+                             dst_token0, _stream(stream))
+    _check(st, "tq_quantize_kv")
+
+
+def tq_dequantize(ctx, planes, norms, n, out, out_ld=None, stream=None):
+    if out_ld is None:
+        out_ld = out.stride(0)
+    _check(_lib.tq_dequantize(ctx.handle, _ptr(planes), _ptr(norms), n, _ptr(out), out_ld,
+                              _stream(stream)), "tq_dequantize")
+
+
+def tq_attn_logits_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads):
+    return _lib.tq_attn_logits_workspace_bytes(ctx.handle, batch, n_q_heads, n_kv_heads)
+
+
+def tq_attn_logits(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv_heads,
+                   keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                   logits_stride_head, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_attn_logits(ctx.handle, _ptr(q), batch, n_q_heads, q_stride_batch,
+                             _ptr(planes), _ptr(norms), n_kv_heads, keys_stride_head,
+                             _ptr(seq_start), _ptr(seq_len), max_seq_len, float(scale),
+                             _ptr(logits), logits_stride_head, _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    _check(st, "tq_attn_logits")
+
+
+def tq_search_workspace_bytes(ctx, n_queries, n_db, k):
+    return _lib.tq_search_workspace_bytes(ctx.handle, n_queries, n_db, k)
+
+
+def tq_search_topk(ctx, queries, n_queries, planes, norms, n_db, k, out_idx, out_score,
+                   workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_search_topk(ctx.handle, _ptr(queries), n_queries, _ptr(planes), _ptr(norms),
+                             n_db, k, _ptr(out_idx), _ptr(out_score), _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    _check(st, "tq_search_topk")
+
+
+def workspace(nbytes, device="cuda"):
+    """A 256-byte aligned uint8 device buffer of at least nbytes."""
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host code and the HIP kernels of libtq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxK = 8;         // centroids for b <= 4
+constexpr int kMaxVec = 5;       // odd Walsh monomials (b = 4) + QJL signs
+
+// Device tables of a context.  All matrices are zero-padded to Dp = 32*W rows
+// and columns so that kernels never branch on the ragged edge of d.
+struct DevTables {
+  const __half* pi_hi;   // [Dp][Dp] row-major, fp16 hi part of Pi
+  const __half* pi_lo;   // [Dp][Dp] fp16 of (Pi - pi_hi)
+  const __half* m_hi;    // [Dp][Dp] M = S Pi^T (formed in double), hi part
+  const __half* m_lo;    // [Dp][Dp] lo part
+  const __half* pit_hi;  // [Rp][Dp] Pi^T hi/lo (rows padded to a multiple of 64)
+  const __half* pit_lo;
+  const __half* st_hi;   // [Rp][Dp] S^T hi/lo
+  const __half* st_lo;
+  const float* pi32;     // [d][d] Pi
+  const float* s32;      // [d][d] S
+};
+
+}  // namespace tq
+
+struct tq_ctx {
+  int32_t d, b, W, Dp, K;
+  int device;
+  float cent[tq::kMaxK];      // centroids (ascending)
+  float mid[tq::kMaxK];       // midpoints t_k = (c_k + c_{k+1}) / 2, k < K-1
+  // Walsh expansion of the codebook over the code bits: c[idx] = c0 - 2 sum_m w_m u_m,
+  // u_m = XOR of the code planes in mask_m (odd masks only for a symmetric codebook).
+  int32_t n_mono;
+  int32_t mono_mask[tq::kMaxVec];
+  double mono_w[tq::kMaxVec];
+  double c0;
+  void* dev_block;            // one allocation holding every device table
+  tq::DevTables t;
+};
+
+namespace tq {
+
+// Launchers (defined in the .hip files).  They assume validated arguments and
+// return hipGetLastError() of the launch.
+hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, int64_t n_tokens,
+                           int32_t n_heads, int64_t x_stride_token, int64_t x_stride_head,
+                           uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
+                           int64_t dst_token0, hipStream_t stream);
+
+size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads);
+hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
+                              int32_t n_q_heads, int64_t q_stride_batch, const uint32_t* planes,
+                              const uint16_t* norms, int32_t n_kv_heads,
+                              int64_t keys_stride_head, const int64_t* seq_start,
+                              const int32_t* seq_len, int32_t max_seq_len, float scale,
+                              float* logits, int64_t logits_stride_head, void* workspace,
+                              hipStream_t stream);
+
+size_t search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db, int32_t k);
+hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n_queries,
+                              const uint32_t* planes, const uint16_t* norms, int64_t n_db,
+                              int32_t k, int64_t* out_idx, float* out_score, void* workspace,
+                              hipStream_t stream);
+hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const uint16_t* norms,
+                             int64_t n, float* out, int64_t out_ld, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,406 @@
+// Attention logits straight from packed keys (turboquant.net pseudo-code,
+// "integrate into attention": keys are stored quantized and inner products
+// are estimated with QJL; admirer.cn article: logits computed from 4-bit keys).
+//
+//   logit = scale * nu * ( <Pi q, c[idx]> + alpha * gamma * <S q, s> )
+//
+// Design (gfx950): the estimate is rewritten as integer dot products of 0/1
+// bit vectors with fixed-point query weights, and those run on the int8
+// matrix cores (v_mfma_i32_16x16x64_i8), so a key record is decoded with one
+// VALU AND per four coordinates.
+//
+//  * Codebook: with a symmetric Lloyd-Max codebook, c[idx] expands over the
+//    code bits as c[idx] = c_0 - 2 sum_m w_m u_m, where u_m is the XOR of the
+//    code planes in an odd-sized subset m (Walsh expansion; 1, 2, 4 subsets for
+//    b = 2, 3, 4).  So <Pi q, c[idx]> = c_0 sum(Pi q) - 2 sum_m w_m <Pi q, u_m>.
+//  * Signs: <S q, s> = 2 <S q, beta_s> - sum(S q), beta_s the sign plane.
+//  * Bits -> int8 lanes: a 32-bit plane word ANDed with 0x01010101 << k gives
+//    four int8 lanes holding bit (8e+k) of the word times 2^k (times -128 for
+//    k = 7).  The 2^k is folded into the query weights: the weight for a bit
+//    at shift k is round(Q / 2^k), written as four balanced int8 limbs, so no
+//    shift is ever applied to the key bits.
+//  * MFMA: A = 16 rows = 4 query heads x 4 limbs of the fixed-point weights
+//    (prepared once per query), B = 16 key tokens x 64 K-slots of masked bits,
+//    C = int32 partial dot products; a lane then holds the 4 limbs of one
+//    (head, token) pair and finishes the logit on its own.
+#include <algorithm>
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;          // key tokens per MFMA tile
+constexpr int kWaves = 4;          // waves per workgroup
+
+__host__ __device__ inline int n_calls(int b) { return 2 * (1 << (b - 2)) + 2; }   // MFMA calls per word step
+__host__ __device__ inline int n_ws(int W) { return (W + 3) / 4; }                  // word steps of 4 words
+
+// Workspace layout for one (batch, kv head, row block of 4 q heads):
+//   int4 frag[n_ws][n_calls][64 lanes]   A operands (16 int8 each)
+//   float4 consts[4]                      per q head: mse scale, qjl scale,
+//                                         mse offset, qjl offset
+__host__ __device__ inline size_t rb_bytes(int W, int b) {
+  return (size_t)n_ws(W) * n_calls(b) * 64 * 16 + 4 * 16;
+}
+
+struct PrepArgs {
+  const float* q;          // [batch][n_q][d], batch stride q_stride_batch
+  int64_t q_stride_batch;
+  const float* pi;         // [d][d]
+  const float* s;          // [d][d]
+  char* ws;
+  int d, W, b, G, n_kv, n_rb, n_q;
+  float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
+  int mask[kMaxVec];       // code-plane subsets
+  int nv;                  // number of subsets
+  float c0;                // c[0]
+};
+
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// rint(Q / 2^k) for k >= 1 (half away from -inf), Q for k == 0
+__device__ inline int shift_round(int Q, int k) {
+  return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
+}
+
+// Query preparation: one block per (q head slot, kv head, batch).  Computes
+// Pi q and S q in fp32, picks a power-of-two fixed-point scale per part, and
+// writes the int8-limb A operands in the exact lane order the logit kernel
+// consumes.  Slots beyond the GQA group size get zero weights.
+__global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
+  extern __shared__ float sm[];
+  float* qv = sm;                 // [d] query
+  float* qr = qv + a.d;           // [32W] Pi q (zero padded)
+  float* qp = qr + 32 * a.W;      // [32W] S q
+  __shared__ float red[4][4];
+  __shared__ int qfix_e[2];
+
+  const int slot = blockIdx.x;              // rb * 4 + hh
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool valid = slot < a.G;
+  const int hq = h * a.G + slot;
+  const int Dp = 32 * a.W;
+
+  for (int j = tid; j < a.d; j += 256)
+    qv[j] = valid ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)hq * a.d + j] : 0.f;
+  __syncthreads();
+  // one wave per output row, lanes split the dot product
+  for (int r = wave; r < Dp; r += 4) {
+    float s1 = 0.f, s2 = 0.f;
+    if (r < a.d) {
+      for (int j = lane; j < a.d; j += 64) {
+        s1 = fmaf(a.pi[(int64_t)r * a.d + j], qv[j], s1);
+        s2 = fmaf(a.s[(int64_t)r * a.d + j], qv[j], s2);
+      }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+      qr[r] = s1;
+      qp[r] = s2;
+    }
+  }
+  __syncthreads();
+  // block reductions: max |Pi q|, max |S q|, sum Pi q, sum S q
+  float m1 = 0.f, m2 = 0.f, t1 = 0.f, t2 = 0.f;
+  for (int j = tid; j < Dp; j += 256) {
+    m1 = fmaxf(m1, fabsf(qr[j]));
+    m2 = fmaxf(m2, fabsf(qp[j]));
+    t1 += qr[j];
+    t2 += qp[j];
+  }
+  m1 = wave_max(m1);
+  m2 = wave_max(m2);
+  t1 = wave_sum(t1);
+  t2 = wave_sum(t2);
+  if (lane == 0) {
+    red[wave][0] = m1;
+    red[wave][1] = m2;
+    red[wave][2] = t1;
+    red[wave][3] = t2;
+  }
+  __syncthreads();
+  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + slot / 4) * rb_bytes(a.W, a.b);
+  if (tid == 0) {
+    float mx1 = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    float mx2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
+    float sum1 = (red[0][2] + red[1][2]) + (red[2][2] + red[3][2]);
+    float sum2 = (red[0][3] + red[1][3]) + (red[2][3] + red[3][3]);
+    float wmax = 0.f;
+    for (int v = 0; v < a.nv; ++v) wmax = fmaxf(wmax, fabsf(a.wm2[v]));
+    const float vmax1 = wmax * mx1, vmax2 = 2.f * mx2;
+    int e1 = 0, e2 = 0;
+    if (vmax1 > 0.f) { int ex; frexpf(vmax1, &ex); e1 = min(30 - ex, 120); }
+    if (vmax2 > 0.f) { int ex; frexpf(vmax2, &ex); e2 = min(30 - ex, 120); }
+    qfix_e[0] = e1;
+    qfix_e[1] = e2;
+    float4 cst;
+    cst.x = ldexpf(1.f, -e1);
+    cst.y = ldexpf(1.f, -e2);
+    cst.z = a.c0 * sum1;
+    cst.w = -sum2;
+    float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * n_calls(a.b) * 64 * 16);
+    cdst[slot % 4] = cst;
+  }
+  __syncthreads();
+  const int e1 = qfix_e[0], e2 = qfix_e[1];
+  const int nc = n_calls(a.b), nws = n_ws(a.W);
+  const int hh = slot % 4;
+  // items: (ws, call, lane group g, limb L) -> 16 bytes of lane (16g + 4hh + L)
+  const int items = nws * nc * 16;
+  for (int it = tid; it < items; it += 256) {
+    const int L = it & 3, g = (it >> 2) & 3;
+    const int c = (it >> 4) % nc, wsi = (it >> 4) / nc;
+    const int w = 4 * wsi + g;
+    uint32_t outw[4];
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      uint32_t word = 0;
+      for (int e = 0; e < 4; ++e) {
+        int k, vec;
+        if (c < 2 * a.nv) { vec = c / 2; k = 4 * (c % 2) + sidx; }
+        else { vec = -1; k = 4 * (c - 2 * a.nv) + sidx; }
+        const int j = 32 * w + 8 * e + k;
+        int Q = 0;
+        if (w < a.W && j < a.d) {
+          float v = (vec >= 0) ? a.wm2[vec] * qr[j] : 2.f * qp[j];
+          Q = (int)rintf(ldexpf(v, vec >= 0 ? e1 : e2));
+        }
+        int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+        // balanced base-256 limbs: Ap = sum_L 256^L a_L, a_L in [-128, 127]
+        int limb = 0;
+        for (int l = 0; l <= L; ++l) {
+          limb = ((Ap + 128) & 255) - 128;
+          Ap = (Ap - limb) >> 8;
+        }
+        word |= (uint32_t)(limb & 255) << (8 * e);
+      }
+      outw[sidx] = word;
+    }
+    const int lanei = 16 * g + 4 * hh + L;
+    uint4* dst = (uint4*)(rbase + (((size_t)wsi * nc + c) * 64 + lanei) * 16);
+    *dst = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+}
+
+struct AttnArgs {
+  const char* ws;
+  const uint32_t* planes;
+  const uint32_t* norms;      // (nu, gamma) fp16 pairs as one word per record
+  const int64_t* seq_start;
+  const int32_t* seq_len;
+  float* logits;
+  int64_t keys_stride_head, logits_stride_head;
+  int W, G, n_kv, n_rb, tiles_per_wave;
+  float scale, alpha;
+  int mask[kMaxVec];
+};
+
+template <int NB>
+__device__ inline void load_group(const uint32_t* p, uint32_t (&w)[NB]) {
+  if constexpr (NB == 4) {
+    uint4 v = *(const uint4*)p;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (NB == 2) {
+    uint2 v = *(const uint2*)p;
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    for (int i = 0; i < NB; ++i) w[i] = p[i];
+  }
+}
+
+// masked int8 lanes of a plane word for shifts 4*half .. 4*half+3
+__device__ inline v4i bit_lanes(uint32_t u, int half) {
+  const uint32_t m = 0x01010101u << (4 * half);
+  v4i r;
+  r[0] = (int)(u & m);
+  r[1] = (int)(u & (m << 1));
+  r[2] = (int)(u & (m << 2));
+  r[3] = (int)(u & (m << 3));
+  return r;
+}
+
+// Logit stream.  grid = (token chunks, kv heads, batch); each wave owns
+// tiles_per_wave tiles of 16 tokens of one (batch, kv head) sequence.
+// Lane (g = lane/16, n = lane%16): loads word group g of token n's record
+// (per word step), and after the MFMAs holds the 4 limbs of q head 4rb+g
+// for token n.  RES: all A operands fit one word step and one row block,
+// so they stay in registers for the whole chunk.
+template <int NB, bool RES>
+__global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
+  constexpr int NV = 1 << (NB - 2);        // Walsh subsets
+  constexpr int NC = 2 * NV + 2;           // MFMA calls per word step
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int len = a.seq_len[bi];
+  const int64_t start = a.seq_start[bi];
+  const int chunk = a.tiles_per_wave * kTile;
+  const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
+  if (t_begin >= len) return;
+  const int t_end = min(len, t_begin + chunk);
+  const int nws = (a.W + 3) >> 2;
+  const size_t rbb = (size_t)nws * NC * 64 * 16 + 64;
+  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * a.n_rb * rbb;
+  const int64_t rec0 = (int64_t)h * a.keys_stride_head + start;
+
+  v4i A[RES ? NC : 1];
+  float4 cst = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (RES) {
+    const v4i* fr = (const v4i*)wsb;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) A[c] = fr[c * 64 + lane];
+    cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
+  }
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+    const int tok = t0 + n;
+    const bool valid = tok < t_end;
+    const int64_t rec = rec0 + tok;
+    const uint32_t nrm = valid ? a.norms[rec] : 0u;
+    for (int rb = 0; rb < a.n_rb; ++rb) {
+      const char* rbase = wsb + rb * rbb;
+      v4i acc_m = {0, 0, 0, 0}, acc_q = {0, 0, 0, 0};
+      for (int wsi = 0; wsi < nws; ++wsi) {
+        const int w = 4 * wsi + g;
+        uint32_t wd[NB];
+#pragma unroll
+        for (int p = 0; p < NB; ++p) wd[p] = 0u;
+        if (valid && w < a.W) load_group<NB>(a.planes + (rec * a.W + w) * NB, wd);
+        const v4i* fr = (const v4i*)(rbase + (size_t)wsi * NC * 64 * 16);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          uint32_t u = 0u;
+#pragma unroll
+          for (int p = 0; p < NB - 1; ++p)
+            if ((a.mask[v] >> p) & 1) u ^= wd[p];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const v4i Aop = RES ? A[2 * v + half] : fr[(2 * v + half) * 64 + lane];
+            acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, bit_lanes(u, half), acc_m, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const v4i Aop = RES ? A[2 * NV + half] : fr[(2 * NV + half) * 64 + lane];
+          acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, bit_lanes(wd[NB - 1], half), acc_q,
+                                                        0, 0, 0);
+        }
+      }
+      const int hh = 4 * rb + g;
+      if (valid && hh < a.G) {
+        if constexpr (!RES) cst = ((const float4*)(rbase + (size_t)nws * NC * 64 * 16))[g];
+        const float vm = fmaf((float)acc_m[3], 16777216.f,
+                              fmaf((float)acc_m[2], 65536.f,
+                                   fmaf((float)acc_m[1], 256.f, (float)acc_m[0])));
+        const float vq = fmaf((float)acc_q[3], 16777216.f,
+                              fmaf((float)acc_q[2], 65536.f,
+                                   fmaf((float)acc_q[1], 256.f, (float)acc_q[0])));
+        const float mse = fmaf(vm, cst.x, cst.z);
+        const float qjl = fmaf(vq, cst.y, cst.w);
+        const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
+        const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
+        const float est = nu * fmaf(a.alpha * ga, qjl, mse);
+        a.logits[(int64_t)(h * a.G + hh) * a.logits_stride_head + start + tok] = a.scale * est;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads) {
+  const int G = n_q_heads / n_kv_heads;
+  const int n_rb = (G + 3) / 4;
+  return (size_t)batch * n_kv_heads * n_rb * rb_bytes(ctx->W, ctx->b);
+}
+
+hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
+                              int32_t n_q_heads, int64_t q_stride_batch, const uint32_t* planes,
+                              const uint16_t* norms, int32_t n_kv_heads,
+                              int64_t keys_stride_head, const int64_t* seq_start,
+                              const int32_t* seq_len, int32_t max_seq_len, float scale,
+                              float* logits, int64_t logits_stride_head, void* workspace,
+                              hipStream_t stream) {
+  const int G = n_q_heads / n_kv_heads;
+  const int n_rb = (G + 3) / 4;
+  PrepArgs p{};
+  p.q = q;
+  p.q_stride_batch = q_stride_batch;
+  p.pi = ctx->t.pi32;
+  p.s = ctx->t.s32;
+  p.ws = (char*)workspace;
+  p.d = ctx->d;
+  p.W = ctx->W;
+  p.b = ctx->b;
+  p.G = G;
+  p.n_kv = n_kv_heads;
+  p.n_rb = n_rb;
+  p.n_q = n_q_heads;
+  p.nv = ctx->n_mono;
+  for (int v = 0; v < ctx->n_mono; ++v) {
+    p.wm2[v] = (float)(-2.0 * ctx->mono_w[v]);
+    p.mask[v] = ctx->mono_mask[v];
+  }
+  p.c0 = (float)ctx->c0;
+  const size_t shm = sizeof(float) * (ctx->d + 64 * ctx->W);
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb * 4, n_kv_heads, batch), dim3(256), shm,
+                     stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  AttnArgs a{};
+  a.ws = (const char*)workspace;
+  a.planes = planes;
+  a.norms = (const uint32_t*)norms;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.logits = logits;
+  a.keys_stride_head = keys_stride_head;
+  a.logits_stride_head = logits_stride_head;
+  a.W = ctx->W;
+  a.G = G;
+  a.n_kv = n_kv_heads;
+  a.n_rb = n_rb;
+  a.scale = scale;
+  a.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
+  for (int v = 0; v < ctx->n_mono; ++v) a.mask[v] = ctx->mono_mask[v];
+  // chunk size: aim at ~8 waves per SIMD across the grid, at most 64 tiles each
+  const int64_t tiles_total = (int64_t)batch * n_kv_heads * ((max_seq_len + kTile - 1) / kTile);
+  int64_t tpw = tiles_total / (256 * 4 * 8);
+  tpw = std::max<int64_t>(1, std::min<int64_t>(64, tpw));
+  a.tiles_per_wave = (int)tpw;
+  const int64_t tok_per_block = (int64_t)kWaves * tpw * kTile;
+  const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
+                  batch);
+  const bool res = (ctx->W <= 4) && (n_rb == 1);
+  switch (ctx->b) {
+    case 2:
+      if (res) hipLaunchKernelGGL((attn_logits_kernel<2, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_logits_kernel<2, false>), grid, dim3(256), 0, stream, a);
+      break;
+    case 3:
+      if (res) hipLaunchKernelGGL((attn_logits_kernel<3, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_logits_kernel<3, false>), grid, dim3(256), 0, stream, a);
+      break;
+    default:
+      if (res) hipLaunchKernelGGL((attn_logits_kernel<4, true>), grid, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((attn_logits_kernel<4, false>), grid, dim3(256), 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP kernels against the CPU oracle, through the C ABI.
+
+Quantize: codes bit-exact except within 1e-5 of a threshold (oracle margin);
+signs bit-exact except |z| < 1e-5 (vectors whose codes all match); fp16
+norms within one ulp.  Logits, dequantized vectors and search scores are fed
+oracle-produced (or arbitrary) records and must agree within 1e-3 of
+max(|ref|, rms of the row).  All inputs are seeded.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_vector_pi_amd as tq  # noqa: E402
+import workloads  # noqa: E402
+from helpers import (CODE_MARGIN, SIGN_MARGIN, TOL, clear_padding, f16_ulp_diff,  # noqa: E402
+                     oracle_tables, rel_err_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+_ctx_cache = {}
+
+
+def ctx_for(orc, d, b, seed=0):
+    key = (d, b, seed)
+    if key not in _ctx_cache:
+        pi, s, c = oracle_tables(orc, d, b, seed)
+        _ctx_cache[key] = (tq.TqContext(d, b, pi, s, c), pi, s, c)
+    return _ctx_cache[key]
+
+
+def gpu_quantize(ctx, x):
+    """x: torch [n, d] on the GPU -> numpy planes uint32 [n, W*b], norms uint16 [n, 2]."""
+    n, d = x.shape
+    planes, norms = tq.alloc_records(n, d, ctx.b)
+    tq.tq_quantize_kv(ctx, x.contiguous(), planes, norms)
+    torch.cuda.synchronize()
+    return planes.cpu().numpy().view(np.uint32), norms.cpu().numpy().view(np.uint16)
+
+
+def check_quantize(orc, d, b, x, pi, s, c, planes, norms, rows=None):
+    """Compare GPU records of x (rows `rows` of the GPU output) with the oracle."""
+    xd = x.double().cpu().numpy()
+    if rows is not None:
+        xd = xd[rows]
+        planes, norms = planes[rows], norms[rows]
+    ref = orc.quantize(d, b, pi, s, c, xd, margins=True)
+    gi, gs = orc.unpack_records(d, b, planes)
+    ri, rs = orc.unpack_records(d, b, ref["planes"])
+    code_bad = gi != ri
+    assert not np.any(code_bad & (ref["code_margin"] >= CODE_MARGIN)), \
+        f"code mismatch outside the margin: {np.argwhere(code_bad & (ref['code_margin'] >= CODE_MARGIN))[:5]}"
+    same = ~code_bad.any(axis=1)
+    sign_bad = (gs != rs) & same[:, None]
+    assert not np.any(sign_bad & (ref["sign_margin"] >= SIGN_MARGIN)), \
+        f"sign mismatch outside the margin: {np.argwhere(sign_bad & (ref['sign_margin'] >= SIGN_MARGIN))[:5]}"
+    assert f16_ulp_diff(norms[:, 0], ref["norms"][:, 0]).max() <= 1
+    assert f16_ulp_diff(norms[same, 1], ref["norms"][same, 1]).max(initial=0) <= 1
+    # padding bits stay zero
+    if d % 32:
+        pc = planes.copy()
+        clear_padding(pc, d, b)
+        assert np.array_equal(pc, planes)
+    return {"code_mismatch": int(code_bad.sum()), "sign_mismatch": int(sign_bad.sum()),
+            "exempt_vectors": int((~same).sum())}
+
+
+# ---------------------------------------------------------------- quantize
+@pytest.mark.parametrize("d,b,dtype,n", [
+    (128, 3, torch.float32, 1024),        # tiny workload shape
+    (128, 4, torch.bfloat16, 1000),       # ragged tail (1000 = 15 tiles + 40)
+    (128, 2, torch.bfloat16, 257),
+    (128, 4, torch.float32, 64),
+    (200, 2, torch.float32, 300),
+    (200, 4, torch.float32, 130),
+    (64, 3, torch.float32, 77),
+    (1536, 2, torch.float32, 40),
+    (1536, 4, torch.float32, 33),
+])
+def test_quantize_parity(orc, d, b, dtype, n):
+    say("quantize", d, b, dtype, n)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    x = workloads.normal((n, d), 3, 10, DEV) * 2.0
+    x[5] = 0.0                          # zero vector
+    x = x.to(dtype)
+    planes, norms = gpu_quantize(ctx, x)
+    stats = check_quantize(orc, d, b, x, pi, s, c, planes, norms)
+    say("ok", stats)
+
+
+def test_quantize_bf16_outliers_strided(orc):
+    """[n_kv, n_tok, d] bf16 with outlier channels, quantized head by head with
+    a token offset into a larger cache."""
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    K = workloads.kv_with_outliers(3, 600, d, 1, 10, DEV)
+    say("quantize strided", K.shape)
+    cap = 1000
+    planes, norms = tq.alloc_records(3 * cap, d, b)
+    tq.tq_quantize_kv(ctx, K, planes, norms, dst_stride_head=cap, dst_token0=123)
+    torch.cuda.synchronize()
+    P = planes.cpu().numpy().view(np.uint32).reshape(3, cap, -1)
+    N = norms.cpu().numpy().view(np.uint16).reshape(3, cap, 2)
+    assert not P[:, :123].any() and not P[:, 723:].any()
+    for h in range(3):
+        check_quantize(orc, d, b, K[h], pi, s, c, P[h, 123:723], N[h, 123:723])
+
+
+def test_quantize_empty_and_deterministic(orc):
+    d, b = 128, 3
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    x = workloads.normal((500, d), 4, 10, DEV)
+    planes, norms = tq.alloc_records(500, d, b)
+    tq.tq_quantize_kv(ctx, x[:0], planes, norms, n_tokens=0)   # no-op
+    torch.cuda.synchronize()
+    assert not planes.any()
+    p1, n1 = gpu_quantize(ctx, x)
+    p2, n2 = gpu_quantize(ctx, x)
+    assert np.array_equal(p1, p2) and np.array_equal(n1, n2)
+
+
+def test_quantize_rejects_bad_arguments(orc):
+    ctx, pi, s, c = ctx_for(orc, 128, 3)
+    L = tq.lib()
+    x = torch.zeros((4, 128), device=DEV)
+    planes, norms = tq.alloc_records(4, 128, 3)
+    st = L.tq_quantize_kv(ctx.handle, x.data_ptr(), 7, 4, 1, 128, 0, planes.data_ptr(),
+                          norms.data_ptr(), 4, 0, None)
+    assert st == tq.TQ_ERR_INVALID_ARG
+    st = L.tq_quantize_kv(ctx.handle, x.data_ptr(), 0, 4, 1, 64, 0, planes.data_ptr(),
+                          norms.data_ptr(), 4, 0, None)
+    assert st == tq.TQ_ERR_INVALID_ARG          # stride < d
+    st = L.tq_quantize_kv(ctx.handle, x.data_ptr() + 4, 0, 4, 1, 128, 0, planes.data_ptr(),
+                          norms.data_ptr(), 4, 0, None)
+    assert st == tq.TQ_ERR_INVALID_ARG          # misaligned
+    st = L.tq_quantize_kv(ctx.handle, x.data_ptr(), 0, -1, 1, 128, 0, planes.data_ptr(),
+                          norms.data_ptr(), 4, 0, None)
+    assert st == tq.TQ_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------------ logits
+def run_logits(ctx, q, planes, norms, n_kv, keys_stride_head, starts, lens, scale, n_q,
+               logits_stride_head, total_len):
+    batch = len(lens)
+    q_t = torch.as_tensor(q, dtype=torch.float32, device=DEV).contiguous()
+    ss = torch.as_tensor(starts, dtype=torch.int64, device=DEV)
+    sl = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    logits = torch.full((n_q, logits_stride_head), float("nan"), device=DEV)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, batch, n_q, n_kv))
+    tq.tq_attn_logits(ctx, q_t, batch, n_q, n_q * ctx.d, planes, norms, n_kv,
+                      keys_stride_head, ss, sl, max(lens), scale, logits, logits_stride_head, ws)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,b,n_q,n_kv,lens", [
+    (128, 3, 16, 1, [1024]),                  # tiny workload layout
+    (128, 4, 32, 8, [1000, 37, 513]),         # GQA 4, ragged batch
+    (128, 2, 32, 8, [777]),
+    (128, 3, 8, 8, [300, 1]),                 # G = 1
+    (128, 4, 6, 2, [129]),                    # G = 3 (partial row block)
+    (200, 4, 8, 2, [333, 70]),
+    (1536, 2, 4, 1, [100]),
+])
+def test_logits_parity_oracle_records(orc, d, b, n_q, n_kv, lens):
+    say("logits", d, b, n_q, n_kv, lens)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    total = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).tolist()
+    x = workloads.normal((n_kv, total, d), 5, 10, "cpu").double().numpy()
+    q = workloads.normal((len(lens), n_q, d), 5, 12, "cpu").numpy()
+    recs = [orc.quantize(d, b, pi, s, c, x[h]) for h in range(n_kv)]
+    planes = np.concatenate([r["planes"] for r in recs])
+    norms = np.concatenate([r["norms"] for r in recs])
+    P = torch.as_tensor(planes.view(np.int32), device=DEV)
+    N = torch.as_tensor(norms.view(np.int16), device=DEV)
+    scale = 1.0 / np.sqrt(d)
+    got = run_logits(ctx, q, P, N, n_kv, total, starts, lens, scale, n_q, total, total)
+    G = n_q // n_kv
+    for bi, (st, ln) in enumerate(zip(starts, lens)):
+        for h in range(n_kv):
+            rp = planes[h * total + st: h * total + st + ln]
+            rn = norms[h * total + st: h * total + st + ln]
+            ref = orc.estimate(d, b, pi, s, c, q[bi, h * G:(h + 1) * G].astype(np.float64),
+                               rp, rn, scale=scale)
+            g = got[h * G:(h + 1) * G, st:st + ln]
+            assert rel_err_rows(g, ref) < TOL, (bi, h, rel_err_rows(g, ref))
+
+
+def test_logits_random_records_and_zero_query(orc):
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    n = 2000
+    P, N = workloads.random_records(n, tq.tq_record_words(d, b), 2, DEV)
+    q = workloads.normal((1, 4, d), 2, 12, "cpu").numpy()
+    q[0, 2] = 0.0                              # an all-zero query head
+    got = run_logits(ctx, q, P, N, 1, n, [0], [n], 1.0, 4, n, n)
+    ref = orc.estimate(d, b, pi, s, c, q[0].astype(np.float64), P.cpu().numpy().view(np.uint32),
+                       N.cpu().numpy().view(np.uint16))
+    assert rel_err_rows(np.delete(got, 2, 0), np.delete(ref, 2, 0)) < TOL
+    assert np.all(got[2] == 0.0)
+
+
+def test_logits_empty_sequence_writes_nothing(orc):
+    d, b = 128, 3
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    P, N = workloads.random_records(64, tq.tq_record_words(d, b), 3, DEV)
+    q = np.ones((2, 4, d), np.float32)
+    got = run_logits(ctx, q, P, N, 1, 64, [0, 10], [0, 20], 1.0, 4, 64, 64)
+    assert np.all(np.isnan(got[:, :10])) and np.all(np.isnan(got[:, 30:]))
+    assert np.all(np.isfinite(got[:, 10:30]))
+
+
+# ---------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("d,b,n", [(128, 3, 1024), (128, 4, 100), (200, 2, 130), (1536, 4, 20),
+                                   (64, 2, 70)])
+def test_dequantize_parity(orc, d, b, n):
+    say("dequantize", d, b, n)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    x = workloads.normal((n, d), 6, 10, "cpu").double().numpy()
+    ref_rec = orc.quantize(d, b, pi, s, c, x)
+    ref = orc.dequantize(d, b, pi, s, c, ref_rec["planes"], ref_rec["norms"])
+    P = torch.as_tensor(ref_rec["planes"].view(np.int32), device=DEV)
+    N = torch.as_tensor(ref_rec["norms"].view(np.int16), device=DEV)
+    out = torch.full((n, d + 3), float("nan"), device=DEV)
+    tq.tq_dequantize(ctx, P, N, n, out, out_ld=d + 3)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[:, d:]))
+    assert rel_err_rows(got[:, :d], ref) < TOL
+
+
+# -------------------------------------------------------------------- search
+def topk_ok(gi, gs, ref_scores, k, tol=TOL):
+    """GPU (idx, score) rows vs exact oracle scores: every returned index is
+    within tolerance of the k-th best, scores match, order is valid."""
+    for a in range(gi.shape[0]):
+        row = ref_scores[a]
+        rms = np.sqrt(np.mean(row ** 2))
+        order = np.lexsort((np.arange(row.size), -row))
+        kth = row[order[k - 1]]
+        assert len(set(gi[a].tolist())) == k
+        for j in range(k):
+            idx = gi[a, j]
+            assert 0 <= idx < row.size
+            assert abs(gs[a, j] - row[idx]) <= tol * max(abs(row[idx]), rms)
+            assert row[idx] >= kth - 2 * tol * rms          # a true top-k member up to ties
+        # true top-k members clearly above the boundary must be returned
+        for idx in order[:k]:
+            if row[idx] > kth + 2 * tol * rms:
+                assert idx in gi[a]
+        assert np.all(np.diff(gs[a]) <= 0)
+
+
+@pytest.mark.parametrize("d,b,n_db,n_q,k", [(128, 4, 5000, 70, 10), (200, 2, 40000, 5, 10),
+                                            (200, 4, 3000, 3, 1), (1536, 2, 2000, 4, 10),
+                                            (128, 3, 100, 2, 64)])
+def test_search_parity(orc, d, b, n_db, n_q, k):
+    say("search", d, b, n_db, n_q, k)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    db = workloads.unit_rows(n_db, d, 7, 15, "cpu").double().numpy()
+    qs = workloads.unit_rows(n_q, d, 7, 16, "cpu").numpy()
+    rec = orc.quantize(d, b, pi, s, c, db)
+    ref = orc.estimate(d, b, pi, s, c, qs.astype(np.float64), rec["planes"], rec["norms"])
+    P = torch.as_tensor(rec["planes"].view(np.int32), device=DEV)
+    N = torch.as_tensor(rec["norms"].view(np.int16), device=DEV)
+    Q = torch.as_tensor(qs, device=DEV)
+    oi = torch.empty((n_q, k), dtype=torch.int64, device=DEV)
+    os_ = torch.empty((n_q, k), dtype=torch.float32, device=DEV)
+    ws = tq.workspace(tq.tq_search_workspace_bytes(ctx, n_q, n_db, k))
+    tq.tq_search_topk(ctx, Q, n_q, P, N, n_db, k, oi, os_, ws)
+    torch.cuda.synchronize()
+    topk_ok(oi.cpu().numpy(), os_.cpu().numpy(), ref, k)
+
+
+def test_search_fewer_records_than_k(orc):
+    d, b = 128, 2
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    P, N = workloads.random_records(5, tq.tq_record_words(d, b), 4, DEV)
+    Q = workloads.unit_rows(2, d, 4, 16, DEV)
+    oi = torch.empty((2, 8), dtype=torch.int64, device=DEV)
+    os_ = torch.empty((2, 8), dtype=torch.float32, device=DEV)
+    ws = tq.workspace(tq.tq_search_workspace_bytes(ctx, 2, 5, 8))
+    tq.tq_search_topk(ctx, Q, 2, P, N, 5, 8, oi, os_, ws)
+    torch.cuda.synchronize()
+    gi = oi.cpu().numpy()
+    assert np.all(gi[:, 5:] == -1) and np.all(np.isneginf(os_.cpu().numpy()[:, 5:]))
+    assert sorted(gi[0, :5].tolist()) == [0, 1, 2, 3, 4]

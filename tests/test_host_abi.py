@@ -1,0 +1,130 @@
+"""C-ABI library: loads, exports every declared symbol, host set-up matches the
+oracle's independent implementation, and argument validation fails before any
+device work (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import kv_cache_vector_pi_amd as tq
+    return tq
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    return sorted(set(re.findall(r"TQ_API\s+[\w\s\*]+?\b(tq_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree(tq):
+    assert declared_symbols() == sorted(tq.EXPORTS)
+
+
+def test_library_exports_every_symbol(tq):
+    out = subprocess.run(["nm", "-D", "--defined-only", tq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_symbols():
+        assert name in exported, name
+        assert hasattr(tq.lib(), name)
+
+
+def test_status_strings(tq):
+    assert tq.tq_status_string(0) == "TQ_OK"
+    assert tq.tq_status_string(tq.TQ_ERR_NOT_CONVERGED) == "TQ_ERR_NOT_CONVERGED"
+    assert tq.tq_status_string(99) == "TQ_ERR_UNKNOWN"
+    assert tq.tq_words_per_plane(128) == 4 and tq.tq_words_per_plane(200) == 7
+    assert tq.tq_record_words(200, 3) == 21 and tq.tq_words_per_plane(0) == 0
+
+
+@pytest.mark.parametrize("d", [3, 16, 128, 200])
+def test_rotation_matches_oracle(tq, orc, d):
+    pi, s = tq.tq_make_rotation(d, 7)
+    _, _, opi, os_ = orc.make_rotation(d, 7)
+    assert np.array_equal(s, os_)              # same generator spec, bit for bit
+    ulp = np.abs(pi.view(np.int32).astype(np.int64) - opi.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1                      # Gram-Schmidt vs Householder, then fp32
+    assert (ulp > 0).mean() < 1e-3
+    assert np.abs(pi.astype(np.float64).T @ pi - np.eye(d)).max() < 1e-6
+
+
+def test_rotation_large_d_orthogonal(tq):
+    pi, s = tq.tq_make_rotation(512, 3)
+    assert np.abs(pi.astype(np.float64).T @ pi - np.eye(512)).max() < 2e-6
+
+
+@pytest.mark.parametrize("d", [3, 128, 200, 1536])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lloyd_matches_oracle(tq, orc, d, bits):
+    c, dist, it = tq.tq_lloyd_max(d, bits)
+    oc, odist, oit, ok = orc.lloyd_max(d, bits)
+    assert ok
+    assert np.array_equal(c, -c[::-1])
+    ulp = np.abs(c.view(np.int32).astype(np.int64) - oc.astype(np.float32).view(np.int32))
+    assert ulp.max() <= 1
+    assert np.allclose(c.astype(np.float64), oc, rtol=1e-7, atol=0)
+    assert dist == pytest.approx(odist, rel=1e-9, abs=1e-12)
+
+
+def test_lloyd_errors(tq):
+    with pytest.raises(tq.TqError) as e:
+        tq.tq_lloyd_max(128, 3, max_iter=2)
+    assert e.value.status == tq.TQ_ERR_NOT_CONVERGED
+    for args in [(2, 2), (128, 0), (128, 5), (4096, 2)]:
+        with pytest.raises(tq.TqError) as e:
+            tq.tq_lloyd_max(*args)
+        assert e.value.status == tq.TQ_ERR_INVALID_ARG
+    L = tq.lib()
+    c = np.empty(8, np.float32)
+    assert L.tq_lloyd_max(128, 3, 100, 0.0, c.ctypes.data, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_lloyd_max(128, 3, 100, 1e-12, None, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert "tq_lloyd_max" in tq.tq_last_error()
+
+
+def test_rotation_errors(tq):
+    L = tq.lib()
+    assert L.tq_make_rotation(2, 0, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_make_rotation(5000, 0, None, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_make_rotation(16, 0, None, None) == tq.TQ_OK   # nothing requested
+
+
+def test_ctx_create_validation(tq, orc):
+    L = tq.lib()
+    h = ctypes.c_void_p()
+    pi, s = tq.tq_make_rotation(128, 0)
+    c, _, _ = tq.tq_lloyd_max(128, 2)
+    P = lambda a: a.ctypes.data
+    assert L.tq_ctx_create(128, 3, P(pi), P(s), P(c), None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_ctx_create(100, 3, P(pi), P(s), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create(128, 5, P(pi), P(s), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create(4096, 3, P(pi), P(s), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create(128, 3, None, P(s), P(c), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    bad = c.copy(); bad[0] *= 1.001                       # not symmetric
+    assert L.tq_ctx_create(128, 3, P(pi), P(s), P(bad), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    bad = c[::-1].copy()                                  # descending
+    assert L.tq_ctx_create(128, 3, P(pi), P(s), P(bad), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    badpi = pi.copy(); badpi[3, 4] = np.nan
+    assert L.tq_ctx_create(128, 3, P(badpi), P(s), P(c), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    assert h.value is None
+    assert L.tq_ctx_destroy(None) == tq.TQ_OK
+
+
+def test_hot_path_rejects_null_context(tq):
+    L = tq.lib()
+    assert L.tq_quantize_kv(None, None, 0, 1, 1, 128, 0, None, None, 0, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_dequantize(None, None, None, 1, None, 128, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_attn_logits(None, None, 1, 32, 4096, None, None, 8, 0, None, None, 1, 1.0,
+                            None, 0, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_search_topk(None, None, 1, None, None, 1, 10, None, None, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_attn_logits_workspace_bytes(None, 1, 32, 8) == 0
+    assert L.tq_search_workspace_bytes(None, 1, 1, 10) == 0
+    assert L.tq_ctx_dim(None) == 0 and L.tq_ctx_bits(None) == 0
