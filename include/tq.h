@@ -204,6 +204,25 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
                                 int64_t logits_stride_head, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* The two halves of tq_attn_logits, for callers that reuse prepared queries
+ * (several caches or chunks scored against the same queries) or time the key
+ * stream on its own.  tq_attn_prepare rotates and projects the queries (Pi q,
+ * S q) and writes the prepared operands into `workspace` (same size and
+ * alignment rules as tq_attn_logits); tq_attn_logits_prepared streams the
+ * keys against a workspace prepared with the same ctx, batch, n_q_heads and
+ * n_kv_heads.  Arguments and errors as for tq_attn_logits. */
+TQ_API tq_status tq_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
+                                 int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+TQ_API tq_status tq_attn_logits_prepared(const tq_ctx* ctx, const void* workspace,
+                                         size_t workspace_bytes, int32_t batch,
+                                         int32_t n_q_heads, const uint32_t* planes,
+                                         const uint16_t* norms, int32_t n_kv_heads,
+                                         int64_t keys_stride_head, const int64_t* seq_start,
+                                         const int32_t* seq_len, int32_t max_seq_len,
+                                         float scale, float* logits,
+                                         int64_t logits_stride_head, void* stream);
+
 /* Workspace for tq_search_topk, in bytes. */
 TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db,
                                         int32_t k);

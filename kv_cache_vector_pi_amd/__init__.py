@@ -28,7 +28,8 @@ EXPORTS = [
     "tq_status_string", "tq_last_error", "tq_words_per_plane", "tq_record_words",
     "tq_make_rotation", "tq_lloyd_max", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim",
     "tq_ctx_bits", "tq_quantize_kv", "tq_dequantize", "tq_attn_logits_workspace_bytes",
-    "tq_attn_logits", "tq_search_workspace_bytes", "tq_search_topk",
+    "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
+    "tq_search_workspace_bytes", "tq_search_topk",
 ]
 
 
@@ -40,7 +41,7 @@ class TqError(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"libtq.so not built at {LIB_PATH}; run "
-                      "`python -m kv_cache_vector_pi_amd.build` (no fallback exists)")
+                      "`python kv_cache_vector_pi_amd/build.py` (no fallback exists)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
@@ -70,6 +71,9 @@ _sig("tq_dequantize", _i32, [_P, _P, _P, _i64, _P, _i64, _P])
 _sig("tq_attn_logits_workspace_bytes", _sz, [_P, _i32, _i32, _i32])
 _sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P, _i32, _f32,
                               _P, _i64, _P, _sz, _P])
+_sig("tq_attn_prepare", _i32, [_P, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
+_sig("tq_attn_logits_prepared", _i32, [_P, _P, _sz, _i32, _i32, _P, _P, _i32, _i64, _P, _P, _i32,
+                                       _f32, _P, _i64, _P])
 _sig("tq_search_workspace_bytes", _sz, [_P, _i64, _i64, _i32])
 _sig("tq_search_topk", _i32, [_P, _P, _i64, _P, _P, _i64, _i32, _P, _P, _P, _sz, _P])
 
@@ -236,6 +240,25 @@ def tq_attn_logits(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv
                              _ptr(logits), logits_stride_head, _ptr(workspace), ws_bytes,
                              _stream(stream))
     _check(st, "tq_attn_logits")
+
+
+def tq_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
+                    stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_attn_prepare(ctx.handle, _ptr(q), batch, n_q_heads, q_stride_batch, n_kv_heads,
+                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "tq_attn_prepare")
+
+
+def tq_attn_logits_prepared(ctx, workspace, batch, n_q_heads, planes, norms, n_kv_heads,
+                            keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                            logits_stride_head, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_attn_logits_prepared(ctx.handle, _ptr(workspace), ws_bytes, batch, n_q_heads,
+                                      _ptr(planes), _ptr(norms), n_kv_heads, keys_stride_head,
+                                      _ptr(seq_start), _ptr(seq_len), max_seq_len, float(scale),
+                                      _ptr(logits), logits_stride_head, _stream(stream))
+    _check(st, "tq_attn_logits_prepared")
 
 
 def tq_search_workspace_bytes(ctx, n_queries, n_db, k):

@@ -1,6 +1,7 @@
 """Build libtq.so (HIP, gfx950) in-tree with hipcc.
 
-``python -m kv_cache_vector_pi_amd.build`` or ``build()``.  Every call
+``python kv_cache_vector_pi_amd/build.py`` (run as a file: importing the
+package would load the library being rebuilt) or ``build()``.  Every call
 recompiles; the objects are built in parallel and linked into
 ``kv_cache_vector_pi_amd/libtq.so``.
 """

@@ -314,10 +314,13 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
     }
   }
   hipError_t e = hipGetDevice(&ctx->device);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&ctx->n_cu, hipDeviceAttributeMultiprocessorCount, ctx->device);
   if (e != hipSuccess) {
     delete ctx;
-    return hip_fail(e, "tq_ctx_create: hipGetDevice");
+    return hip_fail(e, "tq_ctx_create: device query");
   }
+  if (ctx->n_cu < 1) ctx->n_cu = 1;
   const int Dp = ctx->Dp;
   const int Rp = (Dp + 63) / 64 * 64;
   const size_t dpp = (size_t)Dp * Dp;
@@ -480,11 +483,70 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
     return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits: workspace %zu < %zu bytes", workspace_bytes,
                 need);
   if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits: scale not finite");
-  hipError_t e = tq::launch_attn_logits(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms,
+  hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
+                                         workspace, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_attn_stream(ctx, workspace, batch, n_q_heads, planes, norms, n_kv_heads,
+                               keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                               logits_stride_head, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_logits: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
+                                 int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: ctx is NULL");
+  if (batch < 0 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: batch=%d n_q=%d n_kv=%d", batch,
+                n_q_heads, n_kv_heads);
+  if (batch == 0) return ok();
+  if (!q || !workspace) return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: NULL pointer");
+  if (q_stride_batch < (int64_t)n_q_heads * ctx->d && batch > 1)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: q_stride_batch too small");
+  if (!aligned(workspace, 16) || !aligned(q, 4))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: misaligned pointer");
+  const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
+                                         workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_prepare: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_attn_logits_prepared(const tq_ctx* ctx, const void* workspace,
+                                         size_t workspace_bytes, int32_t batch,
+                                         int32_t n_q_heads, const uint32_t* planes,
+                                         const uint16_t* norms, int32_t n_kv_heads,
+                                         int64_t keys_stride_head, const int64_t* seq_start,
+                                         const int32_t* seq_len, int32_t max_seq_len,
+                                         float scale, float* logits,
+                                         int64_t logits_stride_head, void* stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: ctx is NULL");
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: batch=%d n_q=%d n_kv=%d", batch,
+                n_q_heads, n_kv_heads);
+  if (batch == 0 || max_seq_len == 0) return ok();
+  if (!workspace || !planes || !norms || !seq_start || !seq_len || !logits)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: NULL pointer");
+  if (keys_stride_head < 0 || logits_stride_head < 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: negative stride");
+  if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(workspace, 16))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: misaligned pointer");
+  const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: workspace %zu < %zu bytes",
+                workspace_bytes, need);
+  if (!std::isfinite(scale))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits_prepared: scale not finite");
+  hipError_t e = tq::launch_attn_stream(ctx, workspace, batch, n_q_heads, planes, norms,
                                         n_kv_heads, keys_stride_head, seq_start, seq_len,
                                         max_seq_len, scale, logits, logits_stride_head,
-                                        workspace, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "tq_attn_logits: launch");
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_logits_prepared: launch");
   return ok();
 }
 

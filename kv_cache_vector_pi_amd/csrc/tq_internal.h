@@ -42,6 +42,7 @@ struct tq_ctx {
   int32_t mono_mask[tq::kMaxVec];
   double mono_w[tq::kMaxVec];
   double c0;
+  int n_cu;                   // compute units of the device (grid sizing)
   void* dev_block;            // one allocation holding every device table
   tq::DevTables t;
 };
@@ -57,13 +58,15 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
 
 size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads);
-hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
-                              int32_t n_q_heads, int64_t q_stride_batch, const uint32_t* planes,
-                              const uint16_t* norms, int32_t n_kv_heads,
-                              int64_t keys_stride_head, const int64_t* seq_start,
-                              const int32_t* seq_len, int32_t max_seq_len, float scale,
-                              float* logits, int64_t logits_stride_head, void* workspace,
-                              hipStream_t stream);
+hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
+                               int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
+                               void* workspace, hipStream_t stream);
+hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
+                              int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
+                              int32_t n_kv_heads, int64_t keys_stride_head,
+                              const int64_t* seq_start, const int32_t* seq_len,
+                              int32_t max_seq_len, float scale, float* logits,
+                              int64_t logits_stride_head, hipStream_t stream);
 
 size_t search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db, int32_t k);
 hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n_queries,

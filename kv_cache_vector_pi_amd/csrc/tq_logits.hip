@@ -318,6 +318,109 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
   }
 }
 
+// Resident variant (d <= 128, at most 4 query heads per KV head): the A
+// operands and constants stay in registers, and key records are streamed in
+// groups of U tiles with double buffering, so every wave keeps 2U tiles of
+// loads in flight while its MFMAs run.
+template <int NB, int U>
+__global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
+  constexpr int NV = 1 << (NB - 2);
+  constexpr int NC = 2 * NV + 2;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int len = a.seq_len[bi];
+  const int64_t start = a.seq_start[bi];
+  const int chunk = a.tiles_per_wave * kTile;
+  const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
+  if (t_begin >= len) return;
+  const int t_end = min(len, t_begin + chunk);
+  const size_t rbb = (size_t)NC * 64 * 16 + 64;
+  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
+  const int64_t rec0 = (int64_t)h * a.keys_stride_head + start;
+  const bool has_word = g < a.W;
+  const bool store_head = g < a.G;
+  float* out = a.logits + (int64_t)(h * a.G + g) * a.logits_stride_head + start;
+
+  v4i A[NC];
+  {
+    const v4i* fr = (const v4i*)wsb;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) A[c] = fr[c * 64 + lane];
+  }
+  const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
+  const float alpha = a.alpha, scale = a.scale;
+
+  struct Grp {
+    uint32_t wd[U][NB];
+    uint32_t nr[U];
+  };
+  auto load = [&](Grp& gr, int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tok = t0 + kTile * u + n;
+      const bool valid = tok < t_end;
+      const int64_t rec = rec0 + tok;
+#pragma unroll
+      for (int p = 0; p < NB; ++p) gr.wd[u][p] = 0u;
+      if (valid && has_word) load_group<NB>(a.planes + (rec * a.W + g) * NB, gr.wd[u]);
+      gr.nr[u] = valid ? a.norms[rec] : 0u;
+    }
+  };
+  auto compute = [&](const Grp& gr, int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + kTile * u >= t_end) break;
+      v4i acc_m = {0, 0, 0, 0}, acc_q = {0, 0, 0, 0};
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        uint32_t uw = 0u;
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p)
+          if ((a.mask[v] >> p) & 1) uw ^= gr.wd[u][p];
+        acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(uw, 0), acc_m, 0, 0, 0);
+        acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(uw, 1), acc_m, 0, 0,
+                                                      0);
+      }
+      acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(gr.wd[u][NB - 1], 0),
+                                                    acc_q, 0, 0, 0);
+      acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(gr.wd[u][NB - 1], 1),
+                                                    acc_q, 0, 0, 0);
+      const int tok = t0 + kTile * u + n;
+      if (tok < t_end && store_head) {
+        const float vm = fmaf((float)acc_m[3], 16777216.f,
+                              fmaf((float)acc_m[2], 65536.f,
+                                   fmaf((float)acc_m[1], 256.f, (float)acc_m[0])));
+        const float vq = fmaf((float)acc_q[3], 16777216.f,
+                              fmaf((float)acc_q[2], 65536.f,
+                                   fmaf((float)acc_q[1], 256.f, (float)acc_q[0])));
+        const float mse = fmaf(vm, cst.x, cst.z);
+        const float qjl = fmaf(vq, cst.y, cst.w);
+        const uint32_t nrm = gr.nr[u];
+        const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
+        const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
+        out[tok] = scale * nu * fmaf(alpha * ga, qjl, mse);
+      }
+    }
+  };
+  Grp g0, g1;
+  load(g0, t_begin);
+  for (int t = t_begin; t < t_end; t += 2 * kTile * U) {
+    load(g1, t + kTile * U);
+    compute(g0, t);
+    load(g0, t + 2 * kTile * U);
+    compute(g1, t + kTile * U);
+  }
+}
+
+template <typename K>
+int resident_blocks_per_cu(K kernel) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, 256, 0) != hipSuccess || nb < 1)
+    nb = 1;
+  return nb;
+}
+
 }  // namespace
 
 size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
@@ -327,13 +430,9 @@ size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
   return (size_t)batch * n_kv_heads * n_rb * rb_bytes(ctx->W, ctx->b);
 }
 
-hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
-                              int32_t n_q_heads, int64_t q_stride_batch, const uint32_t* planes,
-                              const uint16_t* norms, int32_t n_kv_heads,
-                              int64_t keys_stride_head, const int64_t* seq_start,
-                              const int32_t* seq_len, int32_t max_seq_len, float scale,
-                              float* logits, int64_t logits_stride_head, void* workspace,
-                              hipStream_t stream) {
+hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
+                               int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
+                               void* workspace, hipStream_t stream) {
   const int G = n_q_heads / n_kv_heads;
   const int n_rb = (G + 3) / 4;
   PrepArgs p{};
@@ -358,9 +457,17 @@ hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
   const size_t shm = sizeof(float) * (ctx->d + 64 * ctx->W);
   hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb * 4, n_kv_heads, batch), dim3(256), shm,
                      stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
+                              int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
+                              int32_t n_kv_heads, int64_t keys_stride_head,
+                              const int64_t* seq_start, const int32_t* seq_len,
+                              int32_t max_seq_len, float scale, float* logits,
+                              int64_t logits_stride_head, hipStream_t stream) {
+  const int G = n_q_heads / n_kv_heads;
+  const int n_rb = (G + 3) / 4;
   AttnArgs a{};
   a.ws = (const char*)workspace;
   a.planes = planes;
@@ -377,26 +484,33 @@ hipError_t launch_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch,
   a.scale = scale;
   a.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   for (int v = 0; v < ctx->n_mono; ++v) a.mask[v] = ctx->mono_mask[v];
-  // chunk size: aim at ~8 waves per SIMD across the grid, at most 64 tiles each
-  const int64_t tiles_total = (int64_t)batch * n_kv_heads * ((max_seq_len + kTile - 1) / kTile);
-  int64_t tpw = tiles_total / (256 * 4 * 8);
-  tpw = std::max<int64_t>(1, std::min<int64_t>(64, tpw));
+  const bool res = (ctx->W <= 4) && (n_rb == 1);
+  // Grid: one round of resident waves over all tiles (each wave takes a
+  // contiguous chunk of one sequence), so no partial second round is left.
+  static const int nb_res[3] = {resident_blocks_per_cu(attn_logits_res_kernel<2, 4>),
+                                resident_blocks_per_cu(attn_logits_res_kernel<3, 4>),
+                                resident_blocks_per_cu(attn_logits_res_kernel<4, 4>)};
+  const int nb = res ? nb_res[ctx->b - 2] : 4;
+  const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
+  const int64_t tiles_total = (int64_t)batch * n_kv_heads * tiles_seq;
+  const int64_t resident_waves = (int64_t)ctx->n_cu * nb * kWaves;
+  int64_t tpw = (tiles_total + resident_waves - 1) / resident_waves;
+  tpw = std::max<int64_t>(1, std::min<int64_t>(4096, tpw));
   a.tiles_per_wave = (int)tpw;
   const int64_t tok_per_block = (int64_t)kWaves * tpw * kTile;
   const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
                   batch);
-  const bool res = (ctx->W <= 4) && (n_rb == 1);
   switch (ctx->b) {
     case 2:
-      if (res) hipLaunchKernelGGL((attn_logits_kernel<2, true>), grid, dim3(256), 0, stream, a);
+      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<2, 4>), grid, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL((attn_logits_kernel<2, false>), grid, dim3(256), 0, stream, a);
       break;
     case 3:
-      if (res) hipLaunchKernelGGL((attn_logits_kernel<3, true>), grid, dim3(256), 0, stream, a);
+      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<3, 4>), grid, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL((attn_logits_kernel<3, false>), grid, dim3(256), 0, stream, a);
       break;
     default:
-      if (res) hipLaunchKernelGGL((attn_logits_kernel<4, true>), grid, dim3(256), 0, stream, a);
+      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<4, 4>), grid, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL((attn_logits_kernel<4, false>), grid, dim3(256), 0, stream, a);
       break;
   }

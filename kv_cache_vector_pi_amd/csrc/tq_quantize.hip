@@ -97,12 +97,86 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
   const int VPP = 64 / LPV;                     // vectors per wave pass
   const int CPL = (nchunk + LPV - 1) / LPV;     // chunks per lane
 
+  // RES (d = 128, 4 waves, 64 vectors per tile): each lane owns one 8-element
+  // chunk of 4 vectors per tile -- pass p covers vector 4*wave + 16p + lane/16,
+  // chunk lane%16.  The next tile's chunks are fetched into registers while the
+  // current tile is in its MFMA phases.
+  constexpr int NPRE = RES ? (BF16 ? 4 : 8) : 1;
+  uint4 pre[NPRE];
+  auto fetch = [&](int64_t tl) {
+    if constexpr (RES) {
+      const int hf = (int)(tl / a.tiles_per_head);
+      const int64_t tf = (tl % a.tiles_per_head) * T;
+      const int cf = (int)std::min<int64_t>(T, a.n_tokens - tf);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int v = 4 * wave + 16 * p + (lane >> 4);
+        const int64_t off = (int64_t)hf * a.x_stride_head + (tf + v) * a.x_stride_token +
+                            8 * (lane & 15);
+        if constexpr (BF16) {
+          pre[p] = (tl < a.n_tiles && v < cf) ? *(const uint4*)((const uint16_t*)a.x + off)
+                                              : make_uint4(0u, 0u, 0u, 0u);
+        } else {
+          const bool ok = tl < a.n_tiles && v < cf;
+          pre[2 * p] = ok ? *(const uint4*)((const float*)a.x + off) : make_uint4(0u, 0u, 0u, 0u);
+          pre[2 * p + 1] =
+              ok ? *(const uint4*)((const float*)a.x + off + 4) : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+  };
+  if constexpr (RES) fetch(blockIdx.x);
+
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     const int h = (int)(tile / a.tiles_per_head);
     const int64_t t0 = (tile % a.tiles_per_head) * T;
     const int cnt = (int)std::min<int64_t>(T, a.n_tokens - t0);
 
     // ---- 1. load, norm, scale, fp16 split --------------------------------
+    if constexpr (RES) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int v = 4 * wave + 16 * p + (lane >> 4);
+        const int c = lane & 15;
+        float xv[8];
+        if constexpr (BF16) {
+          const uint32_t wv[4] = {pre[p].x, pre[p].y, pre[p].z, pre[p].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[2 * e] = __uint_as_float(wv[e] << 16);
+            xv[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+          }
+        } else {
+          const uint4 u0 = pre[2 * p], u1 = pre[2 * p + 1];
+          xv[0] = __uint_as_float(u0.x); xv[1] = __uint_as_float(u0.y);
+          xv[2] = __uint_as_float(u0.z); xv[3] = __uint_as_float(u0.w);
+          xv[4] = __uint_as_float(u1.x); xv[5] = __uint_as_float(u1.y);
+          xv[6] = __uint_as_float(u1.z); xv[7] = __uint_as_float(u1.w);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(xv[e], xv[e], ss);
+        ss = lane_sum(ss, 16);
+        const float nu = sqrtf(ss);
+        int ex = 0;
+        if (nu > 0.f) frexpf(nu, &ex);
+        const float sc = ldexpf(1.f, -ex);
+        v8h hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float xs = xv[e] * sc;
+          const _Float16 hv = (_Float16)xs;
+          hi[e] = hv;
+          lo[e] = (_Float16)(xs - (float)hv);
+        }
+        *(v8h*)(bufA + v * ldx + 8 * c) = hi;
+        if constexpr (!BF16) *(v8h*)(bufB + v * ldx + 8 * c) = lo;
+        if (c == 0) {
+          ysc[v] = (nu > 0.f) ? ldexpf(1.f / nu, ex) : 0.f;
+          nu16[v] = (uint32_t)__half_as_ushort(__float2half_rn(nu));
+        }
+      }
+    } else
     for (int vb = wave * VPP; vb < T; vb += NW * VPP) {
       const int v = vb + lane / LPV;
       const int sub = lane % LPV;
@@ -163,6 +237,7 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
       }
     }
     __syncthreads();
+    if constexpr (RES) fetch(tile + gridDim.x);   // next tile, in flight during MFMA
 
     // ---- 2. Y = Pi x_s ------------------------------------------------------
     // words of this wave: w = wave + NW * wi
@@ -358,9 +433,11 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
 template <int NB, bool BF16, int NCB, int WPW, bool RES>
 hipError_t launch_one(const QuantArgs& a, size_t shm, dim3 grid, dim3 block, hipStream_t st) {
   auto fn = quantize_kernel<NB, BF16, NCB, WPW, RES>;
-  hipError_t e = hipFuncSetAttribute((const void*)fn,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-  if (e != hipSuccess) return e;
+  // raise the dynamic-LDS limit once per instantiation (the largest tile
+  // shape needs ~134 KB); never inside a launch sequence a caller may capture
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(fn, grid, block, shm, st, a);
   return hipGetLastError();
 }
@@ -411,13 +488,7 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
   a.n_tiles = a.tiles_per_head * n_heads;
   const size_t shm = (size_t)2 * a.T * a.ldx * sizeof(_Float16) + (size_t)a.T * (2 + a.NW) * 4;
   // persistent grid: a few workgroups per CU
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        v > 0)
-      cus = v;
-  }
+  const int cus = ctx->n_cu;
   const int per_cu = shm > 80 * 1024 ? 1 : (shm > 50 * 1024 ? 2 : 4);
   const int64_t grid = std::min<int64_t>(a.n_tiles, (int64_t)cus * per_cu);
   const dim3 block(64 * a.NW);

@@ -198,6 +198,38 @@ def test_logits_parity_oracle_records(orc, d, b, n_q, n_kv, lens):
             assert rel_err_rows(g, ref) < TOL, (bi, h, rel_err_rows(g, ref))
 
 
+def test_prepared_queries_match_one_call(orc):
+    """tq_attn_prepare + tq_attn_logits_prepared == tq_attn_logits, and one
+    prepared workspace serves two caches."""
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    n = 700
+    P, N = workloads.random_records(2 * n, tq.tq_record_words(d, b), 5, DEV)
+    q = workloads.normal((1, 8, d), 5, 12, DEV)
+    ss = torch.zeros(1, dtype=torch.int64, device=DEV)
+    sl = torch.full((1,), n, dtype=torch.int32, device=DEV)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, 8, 2))
+    one = torch.empty((8, n), device=DEV)
+    tq.tq_attn_logits(ctx, q, 1, 8, 8 * d, P, N, 2, n, ss, sl, n, 0.5, one, n, ws)
+    ws2 = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, 8, 2))
+    tq.tq_attn_prepare(ctx, q, 1, 8, 8 * d, 2, ws2)
+    two = torch.empty((8, n), device=DEV)
+    tq.tq_attn_logits_prepared(ctx, ws2, 1, 8, P, N, 2, n, ss, sl, n, 0.5, two, n)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    # second cache (records n..2n-1 addressed through seq_start) with the same workspace
+    ss2 = torch.full((1,), 0, dtype=torch.int64, device=DEV)
+    three = torch.empty((8, n), device=DEV)
+    tq.tq_attn_logits_prepared(ctx, ws2, 1, 8, P[n:], N[n:], 2, 0, ss2, sl, n, 0.5, three, n)
+    torch.cuda.synchronize()
+    ref = orc.estimate(d, b, pi, s, c, q[0, :4].double().cpu().numpy(),
+                       P[n:].cpu().numpy().view(np.uint32), N[n:].cpu().numpy().view(np.uint16),
+                       scale=0.5)
+    assert rel_err_rows(three[:4].cpu().numpy(), ref) < TOL
+    with pytest.raises(tq.TqError):
+        tq.tq_attn_logits_prepared(ctx, ws2[:64], 1, 8, P, N, 2, n, ss, sl, n, 0.5, two, n)
+
+
 def test_logits_random_records_and_zero_query(orc):
     d, b = 128, 4
     ctx, pi, s, c = ctx_for(orc, d, b)
