@@ -56,6 +56,11 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
                            uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
                            int64_t dst_token0, hipStream_t stream);
 
+hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                              int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                              int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                              int64_t dst_stride_head, int64_t dst_token0, hipStream_t stream);
+
 size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads);
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
