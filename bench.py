@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--fill-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this size (for scaling HBM "
+                         "byte counters)")
     return ap.parse_args()
 
 
@@ -91,6 +94,17 @@ def main():
     logits = torch.empty((N_Q, L * N_TOK), dtype=torch.float32, device=dev)
     ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, L, N_Q, N_KV), dev)
     scale = 1.0 / math.sqrt(D)
+
+    if args.copy_calibration_mb:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE readings give
+        # the scale between those counters and bytes actually moved
+        nb = args.copy_calibration_mb * (1 << 20)
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- cache-fill leg: quantize every K and V vector ---------------------
     def fill():

@@ -158,33 +158,37 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
   const int e1 = qfix_e[0], e2 = qfix_e[1];
   const int nc = n_calls(a.b), nws = n_ws(a.W);
   const int hh = slot % 4;
-  // items: (ws, call, lane group g, limb L) -> 16 bytes of lane (16g + 4hh + L)
+  // fixed-point weights Q[vec][j] (vec < nv: -2 w_vec Pi q; vec == nv: 2 S q)
+  int* qfix = (int*)(qp + Dp);                    // [(nv + 1) * Dp]
+  for (int it = tid; it < (a.nv + 1) * Dp; it += 256) {
+    const int vec = it / Dp, j = it % Dp;
+    const float v = (vec < a.nv) ? a.wm2[vec] * qr[j] : 2.f * qp[j];
+    qfix[it] = (j < a.d) ? (int)rintf(ldexpf(v, vec < a.nv ? e1 : e2)) : 0;
+  }
+  __syncthreads();
+  // items: (ws, call, lane group g, limb L) -> 16 bytes of lane (16g + 4hh + L).
+  // The weight of a bit at shift k is A' = round(Q / 2^k) (negated for k = 7,
+  // where the byte reads -128); its balanced base-256 digit L is
+  // ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that byte ^ 0x80.
   const int items = nws * nc * 16;
   for (int it = tid; it < items; it += 256) {
     const int L = it & 3, g = (it >> 2) & 3;
     const int c = (it >> 4) % nc, wsi = (it >> 4) / nc;
     const int w = 4 * wsi + g;
+    const int vec = (c < 2 * a.nv) ? c / 2 : a.nv;
+    const int kbase = (c < 2 * a.nv) ? 4 * (c % 2) : 4 * (c - 2 * a.nv);
     uint32_t outw[4];
+#pragma unroll
     for (int sidx = 0; sidx < 4; ++sidx) {
+      const int k = kbase + sidx;
       uint32_t word = 0;
+#pragma unroll
       for (int e = 0; e < 4; ++e) {
-        int k, vec;
-        if (c < 2 * a.nv) { vec = c / 2; k = 4 * (c % 2) + sidx; }
-        else { vec = -1; k = 4 * (c - 2 * a.nv) + sidx; }
         const int j = 32 * w + 8 * e + k;
-        int Q = 0;
-        if (w < a.W && j < a.d) {
-          float v = (vec >= 0) ? a.wm2[vec] * qr[j] : 2.f * qp[j];
-          Q = (int)rintf(ldexpf(v, vec >= 0 ? e1 : e2));
-        }
-        int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
-        // balanced base-256 limbs: Ap = sum_L 256^L a_L, a_L in [-128, 127]
-        int limb = 0;
-        for (int l = 0; l <= L; ++l) {
-          limb = ((Ap + 128) & 255) - 128;
-          Ap = (Ap - limb) >> 8;
-        }
-        word |= (uint32_t)(limb & 255) << (8 * e);
+        const int Q = (w < a.W) ? qfix[vec * Dp + j] : 0;
+        const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+        const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
+        word |= (digit ^ 0x80u) << (8 * e);
       }
       outw[sidx] = word;
     }
@@ -318,15 +322,48 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
   }
 }
 
+// Odd-sized subsets of the code planes (Walsh expansion of a symmetric
+// codebook), in the order the context lists them: masks 1, 2, 4, 7.
+template <int NB>
+__device__ constexpr int walsh_mask(int v) {
+  return NB == 2 ? 1 : (NB == 3 ? (v == 0 ? 1 : 2) : (v == 0 ? 1 : v == 1 ? 2 : v == 2 ? 4 : 7));
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int NB>
+__device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
+  if constexpr (NB == 4) {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+  } else if constexpr (NB == 3) {
+    typedef int v3i __attribute__((ext_vector_type(3)));
+    const v3i v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
+  } else {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0]; w[1] = v[1];
+  }
+}
+
 // Resident variant (d <= 128, at most 4 query heads per KV head): the A
 // operands and constants stay in registers, and key records are streamed in
 // groups of U tiles with double buffering, so every wave keeps 2U tiles of
-// loads in flight while its MFMAs run.
+// loads in flight while its MFMAs run.  Records and norms are read through
+// buffer resources bounded to the wave's token range, so loads past the end
+// of the sequence (and of word groups beyond d) return zeros without branches.
 template <int NB, int U>
 __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
+  static_assert(U % 2 == 0, "tiles are processed in pairs");
   constexpr int NV = 1 << (NB - 2);
   constexpr int NC = 2 * NV + 2;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int g = lane >> 4, n = lane & 15;
   const int h = blockIdx.y, bi = blockIdx.z;
   const int len = a.seq_len[bi];
@@ -335,10 +372,15 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
   if (t_begin >= len) return;
   const int t_end = min(len, t_begin + chunk);
+  const int n_tok = t_end - t_begin;
   const size_t rbb = (size_t)NC * 64 * 16 + 64;
   const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
-  const int64_t rec0 = (int64_t)h * a.keys_stride_head + start;
-  const bool has_word = g < a.W;
+  const int64_t rec_first = (int64_t)h * a.keys_stride_head + start + t_begin;
+  const uint32_t rec_bytes = (uint32_t)(a.W * NB * 4);
+  const rsrc_t rp = make_rsrc(a.planes + rec_first * a.W * NB, (uint32_t)n_tok * rec_bytes);
+  const rsrc_t rn = make_rsrc(a.norms + rec_first, (uint32_t)n_tok * 4u);
+  // word group g of this lane's token; groups beyond d read out of range (0)
+  const uint32_t goff = g < a.W ? (uint32_t)(g * NB * 4) : 0x80000000u;
   const bool store_head = g < a.G;
   float* out = a.logits + (int64_t)(h * a.G + g) * a.logits_stride_head + start;
 
@@ -348,68 +390,77 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) A[c] = fr[c * 64 + lane];
   }
+  // per-head constants with the logit scale and the QJL factor folded in:
+  // logit = nu * (vm X + Z + gamma (vq Y + W))
   const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
-  const float alpha = a.alpha, scale = a.scale;
+  const float cX = a.scale * cst.x, cZ = a.scale * cst.z;
+  const float cY = a.scale * a.alpha * cst.y, cW = a.scale * a.alpha * cst.w;
 
   struct Grp {
     uint32_t wd[U][NB];
     uint32_t nr[U];
   };
-  auto load = [&](Grp& gr, int t0) {
+  // tl: local index (from t_begin) of the group's first token
+  auto load = [&](Grp& gr, int tl) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tok = t0 + kTile * u + n;
-      const bool valid = tok < t_end;
-      const int64_t rec = rec0 + tok;
-#pragma unroll
-      for (int p = 0; p < NB; ++p) gr.wd[u][p] = 0u;
-      if (valid && has_word) load_group<NB>(a.planes + (rec * a.W + g) * NB, gr.wd[u]);
-      gr.nr[u] = valid ? a.norms[rec] : 0u;
+      const uint32_t t = (uint32_t)(tl + kTile * u + n);
+      buf_group<NB>(rp, t * rec_bytes + goff, gr.wd[u]);
+      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4u, 0, 0);
     }
   };
-  auto compute = [&](const Grp& gr, int t0) {
+  // limbs -> float: |limb accumulators| < 2^21.1 (at most 16 NV K-slots per
+  // shift, |A| <= 128, |B| <= 2^k), so limb pairs combine exactly in int32
+  auto limbs = [](v4i c) {
+    const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
+    return fmaf((float)hi, 65536.f, (float)lo);
+  };
+  auto finish = [&](v4i am, v4i aq, uint32_t nrm, int tloc) {
+    if (tloc < n_tok && store_head) {
+      const float ms = fmaf(limbs(am), cX, cZ);
+      const float qs = fmaf(limbs(aq), cY, cW);
+      const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
+      const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
+      __builtin_nontemporal_store(nu * fmaf(ga, qs, ms), &out[t_begin + tloc]);   // streamed, never re-read
+    }
+  };
+  // two tiles at a time: their MFMA chains interleave, hiding each other's
+  // dependent-issue latency
+  auto compute = [&](const Grp& gr, int tl) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (t0 + kTile * u >= t_end) break;
-      v4i acc_m = {0, 0, 0, 0}, acc_q = {0, 0, 0, 0};
+    for (int u = 0; u < U; u += 2) {
+      if (tl + kTile * u >= n_tok) break;
+      v4i am0 = {0, 0, 0, 0}, aq0 = {0, 0, 0, 0}, am1 = {0, 0, 0, 0}, aq1 = {0, 0, 0, 0};
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        uint32_t uw = 0u;
+        uint32_t u0 = 0u, u1 = 0u;
 #pragma unroll
         for (int p = 0; p < NB - 1; ++p)
-          if ((a.mask[v] >> p) & 1) uw ^= gr.wd[u][p];
-        acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(uw, 0), acc_m, 0, 0, 0);
-        acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(uw, 1), acc_m, 0, 0,
-                                                      0);
+          if ((walsh_mask<NB>(v) >> p) & 1) {
+            u0 ^= gr.wd[u][p];
+            u1 ^= gr.wd[u + 1][p];
+          }
+        am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(u0, 0), am0, 0, 0, 0);
+        am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(u1, 0), am1, 0, 0, 0);
+        am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u0, 1), am0, 0, 0, 0);
+        am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u1, 1), am1, 0, 0, 0);
       }
-      acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(gr.wd[u][NB - 1], 0),
-                                                    acc_q, 0, 0, 0);
-      acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(gr.wd[u][NB - 1], 1),
-                                                    acc_q, 0, 0, 0);
-      const int tok = t0 + kTile * u + n;
-      if (tok < t_end && store_head) {
-        const float vm = fmaf((float)acc_m[3], 16777216.f,
-                              fmaf((float)acc_m[2], 65536.f,
-                                   fmaf((float)acc_m[1], 256.f, (float)acc_m[0])));
-        const float vq = fmaf((float)acc_q[3], 16777216.f,
-                              fmaf((float)acc_q[2], 65536.f,
-                                   fmaf((float)acc_q[1], 256.f, (float)acc_q[0])));
-        const float mse = fmaf(vm, cst.x, cst.z);
-        const float qjl = fmaf(vq, cst.y, cst.w);
-        const uint32_t nrm = gr.nr[u];
-        const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
-        const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
-        out[tok] = scale * nu * fmaf(alpha * ga, qjl, mse);
-      }
+      const uint32_t s0 = gr.wd[u][NB - 1], s1 = gr.wd[u + 1][NB - 1];
+      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s0, 0), aq0, 0, 0, 0);
+      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s1, 0), aq1, 0, 0, 0);
+      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
+      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
+      finish(am0, aq0, gr.nr[u], tl + kTile * u + n);
+      finish(am1, aq1, gr.nr[u + 1], tl + kTile * (u + 1) + n);
     }
   };
   Grp g0, g1;
-  load(g0, t_begin);
-  for (int t = t_begin; t < t_end; t += 2 * kTile * U) {
-    load(g1, t + kTile * U);
-    compute(g0, t);
-    load(g0, t + 2 * kTile * U);
-    compute(g1, t + kTile * U);
+  load(g0, 0);
+  for (int tl = 0; tl < n_tok; tl += 2 * kTile * U) {
+    load(g1, tl + kTile * U);
+    compute(g0, tl);
+    load(g0, tl + 2 * kTile * U);
+    compute(g1, tl + kTile * U);
   }
 }
 
@@ -454,7 +505,8 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
     p.mask[v] = ctx->mono_mask[v];
   }
   p.c0 = (float)ctx->c0;
-  const size_t shm = sizeof(float) * (ctx->d + 64 * ctx->W);
+  const size_t shm = sizeof(float) * (ctx->d + 64 * ctx->W) +
+                     sizeof(int) * (ctx->n_mono + 1) * 32 * ctx->W;
   hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb * 4, n_kv_heads, batch), dim3(256), shm,
                      stream, p);
   return hipGetLastError();
@@ -484,7 +536,11 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
   a.scale = scale;
   a.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   for (int v = 0; v < ctx->n_mono; ++v) a.mask[v] = ctx->mono_mask[v];
-  const bool res = (ctx->W <= 4) && (n_rb == 1);
+  // the resident kernel hard-codes the Walsh subsets 1 / 1,2 / 1,2,4,7
+  static const int kMasks[3][4] = {{1, 0, 0, 0}, {1, 2, 0, 0}, {1, 2, 4, 7}};
+  bool masks_ok = true;
+  for (int v = 0; v < ctx->n_mono; ++v) masks_ok &= ctx->mono_mask[v] == kMasks[ctx->b - 2][v];
+  const bool res = (ctx->W <= 4) && (n_rb == 1) && masks_ok;
   // Grid: one round of resident waves over all tiles (each wave takes a
   // contiguous chunk of one sequence), so no partial second round is left.
   static const int nb_res[3] = {resident_blocks_per_cu(attn_logits_res_kernel<2, 4>),
@@ -493,9 +549,12 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
   const int nb = res ? nb_res[ctx->b - 2] : 4;
   const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
   const int64_t tiles_total = (int64_t)batch * n_kv_heads * tiles_seq;
+  // short chunks (about 8 rounds of resident waves) keep many independent
+  // read/write streams in flight, which measured best on the mixed
+  // record-read / logit-write traffic; at least 8 tiles per wave
   const int64_t resident_waves = (int64_t)ctx->n_cu * nb * kWaves;
-  int64_t tpw = (tiles_total + resident_waves - 1) / resident_waves;
-  tpw = std::max<int64_t>(1, std::min<int64_t>(4096, tpw));
+  int64_t tpw = (tiles_total + 8 * resident_waves - 1) / (8 * resident_waves);
+  tpw = std::max<int64_t>(8, std::min<int64_t>(256, tpw));
   a.tiles_per_wave = (int)tpw;
   const int64_t tok_per_block = (int64_t)kWaves * tpw * kTile;
   const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
