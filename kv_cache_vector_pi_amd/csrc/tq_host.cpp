@@ -368,10 +368,17 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
                 hipGetErrorString(e));
   }
   char* p = (char*)blk;
+  // fp32 transposes for the query projections (one thread per output row
+  // reads a contiguous column)
+  std::vector<float> t32(2 * dd);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      t32[(size_t)j * d + i] = pi[(size_t)i * d + j];
+      t32[dd + (size_t)j * d + i] = s[(size_t)i * d + j];
+    }
   e = hipMemcpy(p, h16.data(), bytes16, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(p + bytes16, pi, dd * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess)
-    e = hipMemcpy(p + bytes16 + dd * sizeof(float), s, dd * sizeof(float), hipMemcpyHostToDevice);
+    e = hipMemcpy(p + bytes16, t32.data(), 2 * dd * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(blk);
     delete ctx;
@@ -387,8 +394,8 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
   ctx->t.pit_lo = h + 4 * dpp + rpp;
   ctx->t.st_hi = h + 4 * dpp + 2 * rpp;
   ctx->t.st_lo = h + 4 * dpp + 3 * rpp;
-  ctx->t.pi32 = (const float*)(p + bytes16);
-  ctx->t.s32 = (const float*)(p + bytes16) + dd;
+  ctx->t.pit32 = (const float*)(p + bytes16);
+  ctx->t.st32 = (const float*)(p + bytes16) + dd;
   *out = ctx;
   return ok();
 }

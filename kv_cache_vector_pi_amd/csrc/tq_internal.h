@@ -25,8 +25,8 @@ struct DevTables {
   const __half* pit_lo;
   const __half* st_hi;   // [Rp][Dp] S^T hi/lo
   const __half* st_lo;
-  const float* pi32;     // [d][d] Pi
-  const float* s32;      // [d][d] S
+  const float* pit32;    // [d][d] Pi^T (column r of Pi is contiguous: pit32[j*d + r] = Pi[r][j])
+  const float* st32;     // [d][d] S^T
 };
 
 }  // namespace tq

@@ -50,8 +50,8 @@ __host__ __device__ inline size_t rb_bytes(int W, int b) {
 struct PrepArgs {
   const float* q;          // [batch][n_q][d], batch stride q_stride_batch
   int64_t q_stride_batch;
-  const float* pi;         // [d][d]
-  const float* s;          // [d][d]
+  const float* pit;        // [d][d] Pi^T
+  const float* st;         // [d][d] S^T
   char* ws;
   int d, W, b, G, n_kv, n_rb, n_q;
   float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
@@ -74,121 +74,118 @@ __device__ inline int shift_round(int Q, int k) {
   return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
 }
 
-// Query preparation: one block per (q head slot, kv head, batch).  Computes
-// Pi q and S q in fp32, picks a power-of-two fixed-point scale per part, and
-// writes the int8-limb A operands in the exact lane order the logit kernel
-// consumes.  Slots beyond the GQA group size get zero weights.
+// Query preparation: one block per (row block of 4 q heads, kv head, batch).
+// Computes Pi q and S q in fp32 (one thread per output row over a contiguous
+// column of Pi^T / S^T, the 4 queries sharing every table load), picks a
+// power-of-two fixed-point scale per head and part, and writes the int8-limb
+// A operands in the exact lane order the logit kernel consumes.  Slots
+// beyond the GQA group size get zero weights.
 __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
   extern __shared__ float sm[];
-  float* qv = sm;                 // [d] query
-  float* qr = qv + a.d;           // [32W] Pi q (zero padded)
-  float* qp = qr + 32 * a.W;      // [32W] S q
-  __shared__ float red[4][4];
-  __shared__ int qfix_e[2];
-
-  const int slot = blockIdx.x;              // rb * 4 + hh
-  const int h = blockIdx.y, bi = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool valid = slot < a.G;
-  const int hq = h * a.G + slot;
   const int Dp = 32 * a.W;
+  float* qv = sm;                 // [d][4]: coordinate j of slot hh at 4j + hh
+  float* qr = qv + 4 * a.d;       // [4][Dp] Pi q (zero padded)
+  float* qp = qr + 4 * Dp;        // [4][Dp] S q
+  __shared__ int qfix_e[4][2];
 
-  for (int j = tid; j < a.d; j += 256)
-    qv[j] = valid ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)hq * a.d + j] : 0.f;
+  const int rb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int it = tid; it < 4 * a.d; it += 256) {
+    const int hh = it / a.d, j = it - hh * a.d;
+    const int slot = 4 * rb + hh;
+    qv[4 * j + hh] = slot < a.G
+        ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.d + j] : 0.f;
+  }
   __syncthreads();
-  // one wave per output row, lanes split the dot product
-  for (int r = wave; r < Dp; r += 4) {
-    float s1 = 0.f, s2 = 0.f;
+  for (int o = tid; o < 2 * Dp; o += 256) {
+    const bool sk = o >= Dp;
+    const int r = sk ? o - Dp : o;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < a.d) {
-      for (int j = lane; j < a.d; j += 64) {
-        s1 = fmaf(a.pi[(int64_t)r * a.d + j], qv[j], s1);
-        s2 = fmaf(a.s[(int64_t)r * a.d + j], qv[j], s2);
+      const float* col = (sk ? a.st : a.pit) + r;
+#pragma unroll 8
+      for (int j = 0; j < a.d; ++j) {
+        const float t = col[(int64_t)j * a.d];
+        const float4 qq = *(const float4*)&qv[4 * j];
+        acc.x = fmaf(t, qq.x, acc.x);
+        acc.y = fmaf(t, qq.y, acc.y);
+        acc.z = fmaf(t, qq.z, acc.z);
+        acc.w = fmaf(t, qq.w, acc.w);
       }
     }
-    s1 = wave_sum(s1);
-    s2 = wave_sum(s2);
+    float* dst = (sk ? qp : qr) + r;
+    dst[0] = acc.x;
+    dst[Dp] = acc.y;
+    dst[2 * Dp] = acc.z;
+    dst[3 * Dp] = acc.w;
+  }
+  __syncthreads();
+  // wave hh: max |Pi q|, max |S q|, sum Pi q, sum S q of slot hh
+  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rb_bytes(a.W, a.b);
+  {
+    const float* r1 = qr + wave * Dp;
+    const float* r2 = qp + wave * Dp;
+    float m1 = 0.f, m2 = 0.f, t1 = 0.f, t2 = 0.f;
+    for (int j = lane; j < Dp; j += 64) {
+      m1 = fmaxf(m1, fabsf(r1[j]));
+      m2 = fmaxf(m2, fabsf(r2[j]));
+      t1 += r1[j];
+      t2 += r2[j];
+    }
+    m1 = wave_max(m1);
+    m2 = wave_max(m2);
+    t1 = wave_sum(t1);
+    t2 = wave_sum(t2);
     if (lane == 0) {
-      qr[r] = s1;
-      qp[r] = s2;
+      float wmax = 0.f;
+      for (int v = 0; v < a.nv; ++v) wmax = fmaxf(wmax, fabsf(a.wm2[v]));
+      const float vmax1 = wmax * m1, vmax2 = 2.f * m2;
+      int e1 = 0, e2 = 0;
+      if (vmax1 > 0.f) { int ex; frexpf(vmax1, &ex); e1 = min(30 - ex, 120); }
+      if (vmax2 > 0.f) { int ex; frexpf(vmax2, &ex); e2 = min(30 - ex, 120); }
+      qfix_e[wave][0] = e1;
+      qfix_e[wave][1] = e2;
+      float4 cst;
+      cst.x = ldexpf(1.f, -e1);
+      cst.y = ldexpf(1.f, -e2);
+      cst.z = a.c0 * t1;
+      cst.w = -t2;
+      float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * n_calls(a.b) * 64 * 16);
+      cdst[wave] = cst;
     }
   }
   __syncthreads();
-  // block reductions: max |Pi q|, max |S q|, sum Pi q, sum S q
-  float m1 = 0.f, m2 = 0.f, t1 = 0.f, t2 = 0.f;
-  for (int j = tid; j < Dp; j += 256) {
-    m1 = fmaxf(m1, fabsf(qr[j]));
-    m2 = fmaxf(m2, fabsf(qp[j]));
-    t1 += qr[j];
-    t2 += qp[j];
-  }
-  m1 = wave_max(m1);
-  m2 = wave_max(m2);
-  t1 = wave_sum(t1);
-  t2 = wave_sum(t2);
-  if (lane == 0) {
-    red[wave][0] = m1;
-    red[wave][1] = m2;
-    red[wave][2] = t1;
-    red[wave][3] = t2;
-  }
-  __syncthreads();
-  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + slot / 4) * rb_bytes(a.W, a.b);
-  if (tid == 0) {
-    float mx1 = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
-    float mx2 = fmaxf(fmaxf(red[0][1], red[1][1]), fmaxf(red[2][1], red[3][1]));
-    float sum1 = (red[0][2] + red[1][2]) + (red[2][2] + red[3][2]);
-    float sum2 = (red[0][3] + red[1][3]) + (red[2][3] + red[3][3]);
-    float wmax = 0.f;
-    for (int v = 0; v < a.nv; ++v) wmax = fmaxf(wmax, fabsf(a.wm2[v]));
-    const float vmax1 = wmax * mx1, vmax2 = 2.f * mx2;
-    int e1 = 0, e2 = 0;
-    if (vmax1 > 0.f) { int ex; frexpf(vmax1, &ex); e1 = min(30 - ex, 120); }
-    if (vmax2 > 0.f) { int ex; frexpf(vmax2, &ex); e2 = min(30 - ex, 120); }
-    qfix_e[0] = e1;
-    qfix_e[1] = e2;
-    float4 cst;
-    cst.x = ldexpf(1.f, -e1);
-    cst.y = ldexpf(1.f, -e2);
-    cst.z = a.c0 * sum1;
-    cst.w = -sum2;
-    float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * n_calls(a.b) * 64 * 16);
-    cdst[slot % 4] = cst;
-  }
-  __syncthreads();
-  const int e1 = qfix_e[0], e2 = qfix_e[1];
   const int nc = n_calls(a.b), nws = n_ws(a.W);
-  const int hh = slot % 4;
-  // fixed-point weights Q[vec][j] (vec < nv: -2 w_vec Pi q; vec == nv: 2 S q)
-  int* qfix = (int*)(qp + Dp);                    // [(nv + 1) * Dp]
-  for (int it = tid; it < (a.nv + 1) * Dp; it += 256) {
-    const int vec = it / Dp, j = it % Dp;
-    const float v = (vec < a.nv) ? a.wm2[vec] * qr[j] : 2.f * qp[j];
-    qfix[it] = (j < a.d) ? (int)rintf(ldexpf(v, vec < a.nv ? e1 : e2)) : 0;
-  }
-  __syncthreads();
-  // items: (ws, call, lane group g, limb L) -> 16 bytes of lane (16g + 4hh + L).
-  // The weight of a bit at shift k is A' = round(Q / 2^k) (negated for k = 7,
-  // where the byte reads -128); its balanced base-256 digit L is
-  // ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that byte ^ 0x80.
-  const int items = nws * nc * 16;
+  // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
+  // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
+  // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
+  // (-2 w_vec Pi q, or 2 S q for the sign plane); its balanced base-256
+  // digit L is ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that
+  // byte ^ 0x80.
+  const int items = 4 * nws * nc * 16;
   for (int it = tid; it < items; it += 256) {
     const int L = it & 3, g = (it >> 2) & 3;
-    const int c = (it >> 4) % nc, wsi = (it >> 4) / nc;
+    const int rest = it >> 4;
+    const int c = rest % nc, wsi = (rest / nc) % nws, hh = rest / (nc * nws);
     const int w = 4 * wsi + g;
-    const int vec = (c < 2 * a.nv) ? c / 2 : a.nv;
-    const int kbase = (c < 2 * a.nv) ? 4 * (c % 2) : 4 * (c - 2 * a.nv);
+    const bool sgn = c >= 2 * a.nv;
+    const int kbase = sgn ? 4 * (c - 2 * a.nv) : 4 * (c % 2);
+    const float wv = sgn ? 2.f : a.wm2[c / 2];
+    const float* src = (sgn ? qp : qr) + hh * Dp;
+    const int e = qfix_e[hh][sgn ? 1 : 0];
     uint32_t outw[4];
 #pragma unroll
     for (int sidx = 0; sidx < 4; ++sidx) {
       const int k = kbase + sidx;
       uint32_t word = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 32 * w + 8 * e + k;
-        const int Q = (w < a.W) ? qfix[vec * Dp + j] : 0;
+      for (int el = 0; el < 4; ++el) {
+        const int j = 32 * w + 8 * el + k;
+        const int Q = (w < a.W && j < a.d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
         const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
         const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
-        word |= (digit ^ 0x80u) << (8 * e);
+        word |= (digit ^ 0x80u) << (8 * el);
       }
       outw[sidx] = word;
     }
@@ -489,8 +486,8 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
   PrepArgs p{};
   p.q = q;
   p.q_stride_batch = q_stride_batch;
-  p.pi = ctx->t.pi32;
-  p.s = ctx->t.s32;
+  p.pit = ctx->t.pit32;
+  p.st = ctx->t.st32;
   p.ws = (char*)workspace;
   p.d = ctx->d;
   p.W = ctx->W;
@@ -505,10 +502,8 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
     p.mask[v] = ctx->mono_mask[v];
   }
   p.c0 = (float)ctx->c0;
-  const size_t shm = sizeof(float) * (ctx->d + 64 * ctx->W) +
-                     sizeof(int) * (ctx->n_mono + 1) * 32 * ctx->W;
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb * 4, n_kv_heads, batch), dim3(256), shm,
-                     stream, p);
+  const size_t shm = sizeof(float) * (4 * ctx->d + 8 * ctx->Dp);     // <= 48 KB at d = 2048
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb, n_kv_heads, batch), dim3(256), shm, stream, p);
   return hipGetLastError();
 }
 

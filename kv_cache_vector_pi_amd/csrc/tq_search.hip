@@ -33,45 +33,73 @@ constexpr int kLdsRow = 40;      // halves per decoded record row (32 + pad)
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---- row preparation: Pi q and S q, split into hi/lo fp16 -----------------
+// Block (row group of kPrepRows queries, chunk of 256 outputs): each thread
+// owns one output row of Pi or S, reads that row as a contiguous column of
+// Pi^T / S^T (coalesced across the wave) and accumulates it against the
+// group's queries, which are staged through LDS 256 coordinates at a time.
+constexpr int kPrepRows = 16;
+constexpr int kPrepJ = 256;
+
 struct RowPrepArgs {
   const float* q;        // [n][d]
-  const float* pi;       // [d][d]
-  const float* s;
+  const float* pit;      // [d][d] Pi^T
+  const float* st;       // [d][d] S^T
   __half* qr_hi;         // [n_pad][Dp]
   __half* qr_lo;
   __half* qp_hi;
   __half* qp_lo;
   int d, Dp;
-  int64_t n;
+  int64_t n, n_pad;
 };
 
-__device__ inline float wsum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
-  extern __shared__ float qv[];
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool live = row < a.n;
-  for (int j = tid; j < a.d; j += 256) qv[j] = live ? a.q[row * a.d + j] : 0.f;
-  __syncthreads();
-  for (int r = wave; r < a.Dp; r += 4) {
-    float s1 = 0.f, s2 = 0.f;
-    if (r < a.d)
-      for (int j = lane; j < a.d; j += 64) {
-        s1 = fmaf(a.pi[(int64_t)r * a.d + j], qv[j], s1);
-        s2 = fmaf(a.s[(int64_t)r * a.d + j], qv[j], s2);
+  __shared__ __align__(16) float qv[kPrepJ][kPrepRows];
+  const int tid = threadIdx.x;
+  const int64_t row0 = (int64_t)blockIdx.x * kPrepRows;
+  const int o = blockIdx.y * 256 + tid;          // output index over [Pi rows | S rows]
+  const bool sk = o >= a.Dp;
+  const int r = sk ? o - a.Dp : o;
+  const bool live = o < 2 * a.Dp && r < a.d;
+  const float* col = (sk ? a.st : a.pit) + (live ? r : 0);
+  float acc[kPrepRows];
+#pragma unroll
+  for (int i = 0; i < kPrepRows; ++i) acc[i] = 0.f;
+  for (int j0 = 0; j0 < a.d; j0 += kPrepJ) {
+    const int nj = min(kPrepJ, a.d - j0);
+    __syncthreads();
+    for (int it = tid; it < kPrepJ * kPrepRows; it += 256) {
+      const int i = it / kPrepJ, j = it % kPrepJ;
+      const int64_t row = row0 + i;
+      qv[j][i] = (row < a.n && j < nj) ? a.q[row * a.d + j0 + j] : 0.f;
+    }
+    __syncthreads();
+    if (live) {
+#pragma unroll 4
+      for (int j = 0; j < nj; ++j) {
+        const float t = col[(int64_t)(j0 + j) * a.d];
+        const float4* qq = (const float4*)&qv[j][0];
+#pragma unroll
+        for (int i4 = 0; i4 < kPrepRows / 4; ++i4) {
+          const float4 v = qq[i4];
+          acc[4 * i4 + 0] = fmaf(t, v.x, acc[4 * i4 + 0]);
+          acc[4 * i4 + 1] = fmaf(t, v.y, acc[4 * i4 + 1]);
+          acc[4 * i4 + 2] = fmaf(t, v.z, acc[4 * i4 + 2]);
+          acc[4 * i4 + 3] = fmaf(t, v.w, acc[4 * i4 + 3]);
+        }
       }
-    s1 = wsum(s1);
-    s2 = wsum(s2);
-    if (lane == 0) {
-      const __half h1 = __float2half(s1), h2 = __float2half(s2);
-      a.qr_hi[row * a.Dp + r] = h1;
-      a.qr_lo[row * a.Dp + r] = __float2half(s1 - __half2float(h1));
-      a.qp_hi[row * a.Dp + r] = h2;
-      a.qp_lo[row * a.Dp + r] = __float2half(s2 - __half2float(h2));
+    }
+  }
+  if (o >= 2 * a.Dp) return;
+  __half* hi = sk ? a.qp_hi : a.qr_hi;
+  __half* lo = sk ? a.qp_lo : a.qr_lo;
+#pragma unroll
+  for (int i = 0; i < kPrepRows; ++i) {
+    const int64_t row = row0 + i;
+    if (row < a.n_pad) {
+      const float v = live ? acc[i] : 0.f;
+      const __half vh = __float2half(v);
+      hi[row * a.Dp + r] = vh;
+      lo[row * a.Dp + r] = __float2half(v - __half2float(vh));
     }
   }
 }
@@ -307,8 +335,8 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   char* ws = (char*)workspace;
   RowPrepArgs p{};
   p.q = queries;
-  p.pi = ctx->t.pi32;
-  p.s = ctx->t.s32;
+  p.pit = ctx->t.pit32;
+  p.st = ctx->t.st32;
   p.qr_hi = (__half*)(ws + L.qr_hi);
   p.qr_lo = (__half*)(ws + L.qr_lo);
   p.qp_hi = (__half*)(ws + L.qp_hi);
@@ -316,8 +344,11 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   p.d = ctx->d;
   p.Dp = ctx->Dp;
   p.n = n_queries;
-  hipLaunchKernelGGL(row_prep_kernel, dim3((unsigned)L.rows_pad), dim3(256),
-                     sizeof(float) * ctx->d, stream, p);
+  p.n_pad = L.rows_pad;
+  hipLaunchKernelGGL(row_prep_kernel,
+                     dim3((unsigned)((L.rows_pad + kPrepRows - 1) / kPrepRows),
+                          (unsigned)((2 * ctx->Dp + 255) / 256)),
+                     dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
