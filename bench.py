@@ -14,7 +14,18 @@ Outside the timed steps: a cache-fill leg times tq_quantize_kv on all K and V
 of the 32 layers (quantize vectors/s), and the CPU oracle is timed on a
 bounded sample of the same decode work (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Other workloads (each prints its own JSON line; the default is the one above):
+  --workload long     8 KV heads x 131072 tokens, bf16 N(0,1), b in {2,3,4}:
+                      quantize K+V and 32 x 131072 logits per b (MALL-cold
+                      reps: a 1 GiB buffer is written before each rep)
+  --workload batched  16 ragged sequences (4096..8192 tokens), b = 3: quantize
+                      a 512-token chunk per sequence, then logits for one
+                      query of 32 heads per sequence
+  --workload search   1e6 unit vectors at d = 1536 or 200 (--search-d), b in
+                      {2, 4} (--bits): quantize the database, then score 1000
+                      queries against all of it and keep the top 10
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
 """
 import argparse
@@ -40,18 +51,47 @@ def parse():
     ap.add_argument("--fill-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", default="decode", choices=["decode", "long", "batched", "search"])
+    ap.add_argument("--search-d", type=int, default=1536)
+    ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling HBM "
                          "byte counters)")
     return ap.parse_args()
 
 
+PROFILE_LOGITS = os.path.join(ROOT, "profiles", "attn_logits_llama8b_decode_32layers.md")
+LOGIT_SOURCE = os.path.join(ROOT, "kv_cache_vector_pi_amd", "csrc", "tq_logits.hip")
+
+
+def profiled_traffic(profile, source):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(profile).read()
+        src = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith("- `"):
+            k, v = line.strip()[3:].split("`", 1)[0], line.split(":", 1)[1].strip()
+            vals[k] = v.strip("` ")
+    if vals.get("kernel_source_sha256") != src:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}); the hot path has no multi-GPU leg in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the hot path has no multi-GPU leg.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -61,6 +101,10 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload != "decode":
+        out = {"long": run_long, "batched": run_batched, "search": run_search}[args.workload](args)
+        print(json.dumps(out), flush=True)
+        return
     dev = "cuda"
     L = args.layers
     stream = torch.cuda.current_stream()
@@ -221,9 +265,10 @@ def main():
                                "layer caches per step",
                    "layers_per_step": L, "cached_tokens": N_TOK, "head_dim": D, "bits": B,
                    "q_heads": N_Q, "kv_heads": N_KV, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "attn_logits_kernel<4>",
+        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,4>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic(PROFILE_LOGITS, LOGIT_SOURCE),
                      "alg_bytes_per_launch": alg_bytes,
                      "kernel_ms_mean": k_mean_ms, "kernel_ms_median": k_ms},
         "logit_keys_per_s": keys_per_step / (k_mean_ms * 1e-3),
@@ -234,6 +279,234 @@ def main():
     }
     print(json.dumps(out), flush=True)
     ctx.close()
+
+
+# ---- other workloads ---------------------------------------------------------
+def _timed(fn, reps, stream, flush=None):
+    """(mean, median) ms of fn() over reps with HIP events on `stream`;
+    flush() (untimed) runs before each rep."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return sum(ts) / len(ts), ts[len(ts) // 2]
+
+
+def _common(args, d, b, seed=0):
+    import kv_cache_vector_pi_amd as tq
+    pi, s = tq.tq_make_rotation(d, seed)
+    cent, _, _ = tq.tq_lloyd_max(d, b - 1)
+    return tq.TqContext(d, b, pi, s, cent)
+
+
+def _line(args, metric, value, unit, workload, extra):
+    out = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic (seeded)", "config": workload}
+    out.update(extra)
+    return out
+
+
+def run_long(args):
+    """8 KV heads x 131072 tokens, b in {2, 3, 4}: quantize K+V, 32 x 131072 logits."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d, n_kv, n_q, n_tok = "cuda", 128, 8, 32, 131072
+    stream = torch.cuda.current_stream()
+    wl = workloads.long_context(dev)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+
+    def flush():
+        flush_buf.fill_(0.0)
+
+    per_b = {}
+    reps = max(5, min(args.steps, 20))
+    for b in ([args.bits] if args.bits else [2, 3, 4]):
+        ctx = _common(args, d, b)
+        rec = tq.tq_record_words(d, b)
+        kp = torch.zeros((n_kv * n_tok, rec), dtype=torch.int32, device=dev)
+        kn = torch.zeros((n_kv * n_tok, 2), dtype=torch.int16, device=dev)
+        vp, vn = torch.zeros_like(kp), torch.zeros_like(kn)
+
+        def quant():
+            tq.tq_quantize_kv(ctx, wl["K"], kp, kn)
+            tq.tq_quantize_kv(ctx, wl["V"], vp, vn)
+
+        for _ in range(args.warmup):
+            quant()
+        q_ms, _ = _timed(quant, reps, stream, flush)
+        logits = torch.empty((n_q, n_tok), dtype=torch.float32, device=dev)
+        ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, n_q, n_kv), dev)
+        ss = torch.zeros(1, dtype=torch.int64, device=dev)
+        sl = torch.full((1,), n_tok, dtype=torch.int32, device=dev)
+
+        def logit():
+            tq.tq_attn_logits(ctx, wl["q"], 1, n_q, n_q * d, kp, kn, n_kv, n_tok, ss, sl, n_tok,
+                              1.0 / math.sqrt(d), logits, n_tok, ws)
+
+        for _ in range(args.warmup):
+            logit()
+        l_ms, l_med = _timed(logit, reps, stream, flush)
+        rb = b * d // 8 + 4
+        n_vec = 2 * n_kv * n_tok
+        per_b[str(b)] = {
+            "quantize_vec_per_s": n_vec / (q_ms * 1e-3),
+            "quantize_GB_per_s": n_vec * (2 * d + rb) / (q_ms * 1e-3) / 1e9,
+            "logit_keys_per_s": n_kv * n_tok / (l_ms * 1e-3),
+            "logits_per_s": n_q * n_tok / (l_ms * 1e-3),
+            "logit_GB_per_s": n_kv * n_tok * (rb + 4 * (n_q // n_kv)) / (l_ms * 1e-3) / 1e9,
+            "logit_ms_mean": l_ms, "logit_ms_median": l_med, "quantize_ms_mean": q_ms}
+        ctx.close()
+        del kp, kn, vp, vn
+    top = per_b[max(per_b, key=int)]
+    return _line(args, "packed-key attention logits/sec (long context, MALL-cold)",
+                 top["logits_per_s"], "logits/s",
+                 {"workload": "long context: 8 kv heads x 131072 tokens x 128, 32 q heads, "
+                              "bf16 N(0,1) K/V; logits include query prep; a 1 GiB buffer is "
+                              "written before each timed rep"},
+                 {"dtype": "int8-mfma/fp32", "per_bits": per_b,
+                  "peak_GB_per_s": HBM_PEAK_GBS})
+
+
+def run_batched(args):
+    """16 ragged sequences, b = 3: quantize a 512-token chunk per sequence,
+    then logits for one 32-head query per sequence."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d, b = "cuda", 128, 3
+    stream = torch.cuda.current_stream()
+    wl = workloads.batched(dev)
+    lens, chunk, n_kv, n_q = wl["lens"], wl["chunk"], wl["n_kv"], wl["n_q"]
+    batch = len(lens)
+    offs = [0]
+    for n in lens[:-1]:
+        offs.append(offs[-1] + n)
+    total = sum(lens)
+    ctx = _common(args, d, b)
+    rec = tq.tq_record_words(d, b)
+    kp = torch.zeros((n_kv * total, rec), dtype=torch.int32, device=dev)
+    kn = torch.zeros((n_kv * total, 2), dtype=torch.int16, device=dev)
+    vp, vn = torch.zeros_like(kp), torch.zeros_like(kn)
+    K, V = wl["K"], wl["V"]
+    for i in range(batch):                       # prefixes, untimed
+        a, n = offs[i], lens[i] - chunk
+        tq.tq_quantize_kv(ctx, K[:, a:a + n], kp, kn, dst_stride_head=total, dst_token0=a)
+        tq.tq_quantize_kv(ctx, V[:, a:a + n], vp, vn, dst_stride_head=total, dst_token0=a)
+
+    def quant():
+        for i in range(batch):
+            a = offs[i] + lens[i] - chunk
+            tq.tq_quantize_kv(ctx, K[:, a:a + chunk], kp, kn, dst_stride_head=total,
+                              dst_token0=a)
+            tq.tq_quantize_kv(ctx, V[:, a:a + chunk], vp, vn, dst_stride_head=total,
+                              dst_token0=a)
+
+    ss = torch.tensor(offs, dtype=torch.int64, device=dev)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    logits = torch.empty((n_q, total), dtype=torch.float32, device=dev)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, batch, n_q, n_kv), dev)
+
+    def logit():
+        tq.tq_attn_logits(ctx, wl["q"], batch, n_q, n_q * d, kp, kn, n_kv, total, ss, sl,
+                          max(lens), 1.0 / math.sqrt(d), logits, total, ws)
+
+    reps = max(5, min(args.steps, 50))
+    for _ in range(args.warmup):
+        quant()
+        logit()
+    q_ms, _ = _timed(quant, reps, stream)
+    l_ms, l_med = _timed(logit, reps, stream)
+    rb = b * d // 8 + 4
+    alg = n_kv * total * (rb + 4 * (n_q // n_kv))
+    ctx.close()
+    return _line(args, "packed-key attention logits/sec (batched ragged decode)",
+                 n_q * total / (l_ms * 1e-3), "logits/s",
+                 {"workload": f"batched decode: {batch} sequences, lengths {min(lens)}..{max(lens)} "
+                              f"(total {total}), 8 kv / 32 q heads, d=128, b=3; quantize a "
+                              f"512-token chunk per sequence (K and V), logits include query prep"},
+                 {"dtype": "int8-mfma/fp32", "logit_ms_mean": l_ms, "logit_ms_median": l_med,
+                  "logit_keys_per_s": n_kv * total / (l_ms * 1e-3),
+                  "logit_GB_per_s": alg / (l_ms * 1e-3) / 1e9,
+                  "logit_hbm_frac": alg / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "chunk_quantize_ms": q_ms,
+                  "chunk_quantize_vec_per_s": 2 * n_kv * chunk * batch / (q_ms * 1e-3)})
+
+
+def run_search(args):
+    """1e6 unit vectors at d (1536 or 200), b in {2, 4}: quantize the
+    database, then top-10 of 1000 queries over all of it."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d, k = "cuda", args.search_d, 10
+    stream = torch.cuda.current_stream()
+    wl = workloads.search(dev, d)
+    db, qs = wl["db"], wl["queries"]
+    n_db, n_q = db.shape[0], qs.shape[0]
+    # exact float top-10 for the recall diagnostic
+    exact = torch.empty((n_q, k), dtype=torch.int64, device=dev)
+    best = torch.full((n_q, k), -float("inf"), device=dev)
+    for c0 in range(0, n_db, 131072):
+        sc = qs @ db[c0:c0 + 131072].T
+        cand_s = torch.cat([best, sc], dim=1)
+        cand_i = torch.cat([exact, torch.arange(c0, c0 + sc.shape[1], device=dev)
+                            .expand(n_q, -1)], dim=1)
+        best, pos = cand_s.topk(k, dim=1)
+        exact = torch.gather(cand_i, 1, pos)
+    per_b = {}
+    reps = max(3, min(args.steps, 10))
+    for b in ([args.bits] if args.bits else [2, 4]):
+        ctx = _common(args, d, b)
+        planes, norms = tq.alloc_records(n_db, d, b, dev)
+
+        def quant():
+            tq.tq_quantize_kv(ctx, db, planes, norms)
+
+        for _ in range(max(1, args.warmup)):
+            quant()
+        q_ms, _ = _timed(quant, reps, stream)
+        ws = tq.workspace(tq.tq_search_workspace_bytes(ctx, n_q, n_db, k), dev)
+        oi = torch.empty((n_q, k), dtype=torch.int64, device=dev)
+        osc = torch.empty((n_q, k), dtype=torch.float32, device=dev)
+
+        def search():
+            tq.tq_search_topk(ctx, qs, n_q, planes, norms, n_db, k, oi, osc, ws)
+
+        for _ in range(max(1, args.warmup)):
+            search()
+        s_ms, s_med = _timed(search, reps, stream)
+        hit = sum(len(set(a) & set(e)) for a, e in zip(oi.cpu().tolist(), exact.cpu().tolist()))
+        pairs = n_q * n_db
+        rb = b * d // 8 + 4
+        per_b[str(b)] = {
+            "quantize_vec_per_s": n_db / (q_ms * 1e-3),
+            "quantize_GB_per_s": n_db * (4 * d + rb) / (q_ms * 1e-3) / 1e9,
+            "quantize_ms": q_ms,
+            "search_ms_mean": s_ms, "search_ms_median": s_med,
+            "scores_per_s": pairs / (s_ms * 1e-3),
+            "queries_per_s": n_q / (s_ms * 1e-3),
+            "alg_TFLOP_per_s": 4 * d * pairs / (s_ms * 1e-3) / 1e12,
+            "alg_frac_of_fp16_mfma": 4 * d * pairs / (s_ms * 1e-3) / 2.5e15,
+            "recall_at_10_vs_exact_fp32": hit / (n_q * k)}
+        ctx.close()
+        del planes, norms, ws
+    top = per_b[max(per_b, key=int)]
+    return _line(args, "vector search: scores/sec from packed codes (top-10)",
+                 top["scores_per_s"], "scores/s",
+                 {"workload": f"vector search: {n_db} unit vectors (normalised N(0,I)) at d={d}, "
+                              f"{n_q} queries, top-{k}; fp32 input"},
+                 {"dtype": "fp16-mfma/fp32", "per_bits": per_b})
 
 
 if __name__ == "__main__":
