@@ -98,29 +98,66 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
         ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.d + j] : 0.f;
   }
   __syncthreads();
-  for (int o = tid; o < 2 * Dp; o += 256) {
-    const bool sk = o >= Dp;
-    const int r = sk ? o - Dp : o;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (r < a.d) {
-      const float* col = (sk ? a.st : a.pit) + r;
-#pragma unroll 8
-      for (int j = 0; j < a.d; ++j) {
-        const float t = col[(int64_t)j * a.d];
-        const float4 qq = *(const float4*)&qv[4 * j];
-        acc.x = fmaf(t, qq.x, acc.x);
-        acc.y = fmaf(t, qq.y, acc.y);
-        acc.z = fmaf(t, qq.z, acc.z);
-        acc.w = fmaf(t, qq.w, acc.w);
+  // Outputs in chunks of 256 (Pi rows, then S rows): thread (quad, jg)
+  // accumulates 4 consecutive outputs x 4 slots over the jg-th quarter of the
+  // coordinates, reading float4 rows of Pi^T / S^T; the four partial sums are
+  // then added in a fixed order (deterministic).
+  {
+    const int quad = tid & 63, jg = tid >> 6;
+    const int jl = (a.d + 3) / 4;
+    const int ja = jg * jl, jb = min(a.d, ja + jl);
+    for (int o0 = 0; o0 < 2 * Dp; o0 += 256) {
+      const int o = o0 + 4 * quad;
+      const bool in = o < 2 * Dp;
+      const bool sk = o >= Dp;
+      const int r = sk ? o - Dp : o;                 // multiple of 4; r < d => r + 3 < d
+      float4 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (in && r < a.d) {
+        const float* tab = (sk ? a.st : a.pit) + r;
+        auto fma16 = [&](const float4 t, const float4 qq) {
+          acc[0].x = fmaf(t.x, qq.x, acc[0].x); acc[0].y = fmaf(t.y, qq.x, acc[0].y);
+          acc[0].z = fmaf(t.z, qq.x, acc[0].z); acc[0].w = fmaf(t.w, qq.x, acc[0].w);
+          acc[1].x = fmaf(t.x, qq.y, acc[1].x); acc[1].y = fmaf(t.y, qq.y, acc[1].y);
+          acc[1].z = fmaf(t.z, qq.y, acc[1].z); acc[1].w = fmaf(t.w, qq.y, acc[1].w);
+          acc[2].x = fmaf(t.x, qq.z, acc[2].x); acc[2].y = fmaf(t.y, qq.z, acc[2].y);
+          acc[2].z = fmaf(t.z, qq.z, acc[2].z); acc[2].w = fmaf(t.w, qq.z, acc[2].w);
+          acc[3].x = fmaf(t.x, qq.w, acc[3].x); acc[3].y = fmaf(t.y, qq.w, acc[3].y);
+          acc[3].z = fmaf(t.z, qq.w, acc[3].z); acc[3].w = fmaf(t.w, qq.w, acc[3].w);
+        };
+        int j = ja;
+        // batches of 8 independent row loads in flight
+        for (; j + 8 <= jb; j += 8) {
+          float4 t[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t[u] = *(const float4*)(tab + (int64_t)(j + u) * a.d);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) fma16(t[u], *(const float4*)&qv[4 * (j + u)]);
+        }
+        for (; j < jb; ++j)
+          fma16(*(const float4*)(tab + (int64_t)j * a.d), *(const float4*)&qv[4 * j]);
+      }
+      // slot i of outputs r..r+3 -> (sk ? qp : qr)[i * Dp + r ..]
+      float* dst = (sk ? qp : qr) + r;
+      for (int g = 0; g < 4; ++g) {
+        if (jg == g && in) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float4* d4 = (float4*)(dst + i * Dp);
+            if (g == 0) {
+              *d4 = acc[i];
+            } else {
+              float4 v = *d4;
+              v.x += acc[i].x; v.y += acc[i].y; v.z += acc[i].z; v.w += acc[i].w;
+              *d4 = v;
+            }
+          }
+        }
+        __syncthreads();
       }
     }
-    float* dst = (sk ? qp : qr) + r;
-    dst[0] = acc.x;
-    dst[Dp] = acc.y;
-    dst[2 * Dp] = acc.z;
-    dst[3 * Dp] = acc.w;
   }
-  __syncthreads();
   // wave hh: max |Pi q|, max |S q|, sum Pi q, sum S q of slot hh
   char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rb_bytes(a.W, a.b);
   {

@@ -74,9 +74,7 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
     }
     __syncthreads();
     if (live) {
-#pragma unroll 4
-      for (int j = 0; j < nj; ++j) {
-        const float t = col[(int64_t)(j0 + j) * a.d];
+      auto step = [&](const float t, const int j) {
         const float4* qq = (const float4*)&qv[j][0];
 #pragma unroll
         for (int i4 = 0; i4 < kPrepRows / 4; ++i4) {
@@ -86,7 +84,17 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
           acc[4 * i4 + 2] = fmaf(t, v.z, acc[4 * i4 + 2]);
           acc[4 * i4 + 3] = fmaf(t, v.w, acc[4 * i4 + 3]);
         }
+      };
+      int j = 0;
+      // batches of 16 independent column loads in flight
+      for (; j + 16 <= nj; j += 16) {
+        float t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = col[(int64_t)(j0 + j + u) * a.d];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) step(t[u], j + u);
       }
+      for (; j < nj; ++j) step(col[(int64_t)(j0 + j) * a.d], j);
     }
   }
   if (o >= 2 * a.Dp) return;
