@@ -36,3 +36,23 @@ def clear_padding(planes, d, b):
 def f16_ulp_diff(a, b):
     """|a - b| in units of fp16 ulps for non-negative fp16 bit patterns."""
     return np.abs(np.asarray(a, np.int64) - np.asarray(b, np.int64))
+
+
+def check_records(orc, d, b, pi, s, c, x, planes, norms):
+    """GPU records of the rows x (float64 [n, d]) against the oracle: codes
+    bit-exact except within CODE_MARGIN of a threshold, signs bit-exact
+    except |z| < SIGN_MARGIN (in vectors whose codes all match), fp16 norms
+    within one ulp.  Returns the number of exempt vectors."""
+    ref = orc.quantize(d, b, pi, s, c, x, margins=True)
+    gi, gs = orc.unpack_records(d, b, planes)
+    ri, rs = orc.unpack_records(d, b, ref["planes"])
+    code_bad = gi != ri
+    assert not np.any(code_bad & (ref["code_margin"] >= CODE_MARGIN)), \
+        f"code mismatch outside the margin: {np.argwhere(code_bad & (ref['code_margin'] >= CODE_MARGIN))[:5]}"
+    same = ~code_bad.any(axis=1)
+    sign_bad = (gs != rs) & same[:, None]
+    assert not np.any(sign_bad & (ref["sign_margin"] >= SIGN_MARGIN)), \
+        f"sign mismatch outside the margin: {np.argwhere(sign_bad & (ref['sign_margin'] >= SIGN_MARGIN))[:5]}"
+    assert f16_ulp_diff(norms[:, 0], ref["norms"][:, 0]).max(initial=0) <= 1
+    assert f16_ulp_diff(norms[same, 1], ref["norms"][same, 1]).max(initial=0) <= 1
+    return int((~same).sum())
