@@ -2,18 +2,26 @@
 // (zingnex.cn digest, nearest-neighbour section; admirer.cn vector-search
 // paragraph; turboquant.net pseudo-code "dequant").
 //
-// Both are one "decoded GEMM":
+// Both are "decoded GEMMs" over the packed records:
 //   score[q][n] = nu_n * ( sum_j QR[q][j] c[idx_nj] + alpha * gamma_n * sum_j QP[q][j] s_nj )
 // For search QR = Pi q and QP = S q (one row per query).  For dequantization
 // the rows are the unit vectors e_j, i.e. QR = Pi^T and QP = S^T, so the
 // "score" of row j is coordinate j of nu (Pi^T c[idx] + alpha gamma S^T s).
 //
-// Records are decoded once per 64-row tile into fp16 operands in LDS
-// (centroid hi and lo parts, signs +-1), the rows are split hi + lo fp16, and
-// the contraction runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation:
-//   mse += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo,   qjl += QP_hi s + QP_lo s.
-// Search then keeps the top-k of each query with a one-wave-per-query merge
-// over chunks of scores (ordered by score descending, index ascending).
+// Search: records are decoded once per 128-record tile and 32-coordinate word
+// into fp16 LDS operands -- centroid hi and lo parts and gamma * s (gamma is
+// an fp16 value and s = +-1, so the product is exact) -- and the query rows,
+// split hi + lo with alpha folded into the sketch half, are staged next to
+// them.  One accumulator then takes all five passes on
+// v_mfma_f32_32x32x16_f16:
+//   acc += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo + (alpha QP)_hi gs + (alpha QP)_lo gs,
+// and score = nu * acc.  Instead of writing every score, the epilogue keeps
+// only those above the query's running k-th best score (candidates appended
+// with one atomic per wave and query row), and a one-wave-per-query merge
+// after each chunk of records folds them into the running top-k (score
+// descending, index ascending) and raises the threshold.
+//
+// Dequantization keeps the two-accumulator form on 16x16x32 tiles.
 #include <algorithm>
 #include <cmath>
 
@@ -24,11 +32,15 @@ namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kRowsTile = 64;    // query rows per workgroup
-constexpr int kRecTile = 64;     // records per workgroup
-constexpr int kChunk = 32768;    // records scored per search pass
-constexpr int kLdsRow = 40;      // halves per decoded record row (32 + pad)
+constexpr int kRowsTile = 64;    // dequantize: rows per workgroup
+constexpr int kRecTile = 64;     // dequantize: records per workgroup
+constexpr int kLdsRow = 40;      // halves per staged row of one word (32 + pad)
+constexpr int kQT = 128;         // search: queries per workgroup
+constexpr int kRT = 128;         // search: records per workgroup
+constexpr int kFirst = 2048;     // search: records of the first chunk (sets the thresholds)
+constexpr int kChunk = 16384;    // search: records per later chunk = candidate capacity
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -48,6 +60,7 @@ struct RowPrepArgs {
   __half* qr_lo;
   __half* qp_hi;
   __half* qp_lo;
+  float pscale;          // factor on S q (alpha for search)
   int d, Dp;
   int64_t n, n_pad;
 };
@@ -104,7 +117,7 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
   for (int i = 0; i < kPrepRows; ++i) {
     const int64_t row = row0 + i;
     if (row < a.n_pad) {
-      const float v = live ? acc[i] : 0.f;
+      const float v = live ? (sk ? a.pscale * acc[i] : acc[i]) : 0.f;
       const __half vh = __float2half(v);
       hi[row * a.Dp + r] = vh;
       lo[row * a.Dp + r] = __float2half(v - __half2float(vh));
@@ -126,7 +139,7 @@ struct GemmArgs {
   float alpha;
   _Float16 c_hi[kMaxK];
   _Float16 c_lo[kMaxK];
-  // output: mode 0 -> scores[row * out_ld + (rec - rec0)], mode 1 -> out[rec * out_ld + row]
+  // output: out[rec * out_ld + row]
   float* out;
   int64_t out_ld;
 };
@@ -211,17 +224,163 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
       const int64_t r = qt * kRowsTile + 16 * wave + 4 * g + i;
       if (r >= a.n_rows) continue;
       const float v = nu * fmaf(ag, aq[cb][i], am[cb][i]);
-      if constexpr (MODE == 0) a.out[r * a.out_ld + rec] = v;
-      else a.out[(a.rec0 + rec) * a.out_ld + r] = v;
+      a.out[(a.rec0 + rec) * a.out_ld + r] = v;
     }
   }
 }
 
-// ---- top-k merge: one wave per query ----------------------------------------
-struct TopkArgs {
-  const float* scores;   // [n_q][kChunk] for this chunk
-  int64_t n_q, chunk_len, base;  // records base .. base + chunk_len - 1
+// ---- search GEMM with threshold-filter epilogue -------------------------------
+struct SearchArgs {
+  const __half* qa[4];   // QR hi, QR lo, (alpha QP) hi, (alpha QP) lo: [rows_pad][Dp]
+  int64_t n_q;
+  const uint32_t* planes;
+  const uint32_t* norms;
+  int64_t rec0, n_rec;   // records rec0 .. rec0 + n_rec - 1 of this chunk
+  int W, Dp;
+  uint32_t ctab[kMaxK];  // centroid k: fp16 hi | fp16 lo << 16
+  const float* thr;      // [n_q] running k-th best score (-inf: fewer than k yet)
+  int* cnt;              // [n_q] candidates of this chunk
+  float* cand_s;         // [n_q][kChunk]
+  int* cand_i;           // [n_q][kChunk] record index within the chunk
+};
+
+template <int NB>
+__global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
+  __shared__ __align__(16) _Float16 As[4][kQT * kLdsRow];
+  __shared__ __align__(16) _Float16 Bs[3][kRT * kLdsRow];
+  __shared__ float thr_s[kQT];
+  __shared__ uint32_t ctab_s[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  const int wq = wave & 1, wr = wave >> 1;       // wave tile: 64 queries x 64 records
+  const int64_t r0 = (int64_t)blockIdx.x * kRT, q0 = (int64_t)blockIdx.y * kQT;
+
+  if (tid < kQT) {
+    const int64_t q = q0 + tid;
+    thr_s[tid] = q < a.n_q ? a.thr[q] : INFINITY;   // padded rows never pass
+  }
+  if (tid < kMaxK) ctab_s[tid] = a.ctab[tid];
+  // decode role: record dr, coordinates 16 dh .. 16 dh + 15 of each word
+  const int dr = tid >> 1, dh = tid & 1;
+  const bool dlive = r0 + dr < a.n_rec;
+  const uint32_t* drec = a.planes + (a.rec0 + r0 + dr) * (int64_t)a.W * NB;
+  const uint16_t gbits =
+      dlive ? (uint16_t)(a.norms[a.rec0 + r0 + dr] >> 16) : (uint16_t)0;   // fp16 gamma
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
+
+  for (int w = 0; w < a.W; ++w) {
+    __syncthreads();              // previous word's operands fully read
+    // stage the query rows: 4 arrays x 128 rows x 32 halves, 16 bytes a thread x 8
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j;
+      const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
+      const v8h v = *(const v8h*)(a.qa[ar] + (q0 + row) * a.Dp + 32 * w + 8 * part);
+      *(v8h*)(&As[ar][row * kLdsRow + 8 * part]) = v;
+    }
+    // decode word w of record dr
+    {
+      uint32_t wd[NB];
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
+      v8h vh[2], vl[2], vg[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int bit = 16 * dh + e;
+        uint32_t idx = 0;
+#pragma unroll
+        for (int p = 0; p < NB - 1; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
+        const uint32_t hl = ctab_s[idx];
+        const uint16_t sgn = ((wd[NB - 1] >> bit) & 1u) ? (uint16_t)0 : (uint16_t)0x8000;
+        vh[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
+        vl[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
+        vg[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(gbits ^ sgn));
+      }
+      const int off = dr * kLdsRow + 16 * dh;
+      *(v8h*)(&Bs[0][off]) = vh[0];
+      *(v8h*)(&Bs[0][off + 8]) = vh[1];
+      *(v8h*)(&Bs[1][off]) = vl[0];
+      *(v8h*)(&Bs[1][off + 8]) = vl[1];
+      *(v8h*)(&Bs[2][off]) = vg[0];
+      *(v8h*)(&Bs[2][off + 8]) = vg[1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      v8h A[2][4], B[2][3];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int off = (64 * wq + 32 * qb + col) * kLdsRow + 16 * kk + 8 * hh;
+#pragma unroll
+        for (int ar = 0; ar < 4; ++ar) A[qb][ar] = *(const v8h*)(&As[ar][off]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int off = (64 * wr + 32 * rb + col) * kLdsRow + 16 * kk + 8 * hh;
+#pragma unroll
+        for (int ar = 0; ar < 3; ++ar) B[rb][ar] = *(const v8h*)(&Bs[ar][off]);
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          v16f c = acc[qb][rb];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][3], B[rb][2], c, 0, 0, 0);
+          acc[qb][rb] = c;
+        }
+    }
+  }
+
+  // epilogue: element i of tile (qb, rb) is query 64wq + 32qb + 8(i/4) + 4hh + i%4
+  // and record 64wr + 32rb + col; keep scores above the query's threshold
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t rl = r0 + 64 * wr + 32 * rb + col;
+    const bool rlive = rl < a.n_rec;
+    const float nu =
+        rlive ? __half2float(__ushort_as_half((unsigned short)(a.norms[a.rec0 + rl] & 0xffffu)))
+              : 0.f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ql = 64 * wq + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const float sc = nu * acc[qb][rb][i];
+        const bool pass = rlive && sc > thr_s[ql];
+        const uint64_t m = __ballot(pass);
+        if (m) {
+          // lanes 0..31 share one query row, lanes 32..63 another
+          const uint32_t mh = hh ? (uint32_t)(m >> 32) : (uint32_t)m;
+          int base = 0;
+          if (col == 0 && mh) base = atomicAdd(&a.cnt[q0 + ql], __popc(mh));
+          base = __shfl(base, 32 * hh);
+          if (pass) {
+            const int64_t slot = (q0 + ql) * (int64_t)kChunk + base + __popc(mh & ((1u << col) - 1u));
+            a.cand_s[slot] = sc;
+            a.cand_i[slot] = (int)rl;
+          }
+        }
+      }
+  }
+}
+
+// ---- candidate merge: one wave per query ---------------------------------------
+struct MergeArgs {
+  int64_t n_q, base;     // candidate indices are relative to record `base`
   int k;
+  float* thr;
+  int* cnt;
+  const float* cand_s;
+  const int* cand_i;
   float* run_score;      // [n_q][k]
   int64_t* run_idx;
   int first, last;
@@ -233,31 +392,33 @@ __device__ inline bool beats(float as, int64_t ai, float bs, int64_t bi) {
   return as > bs || (as == bs && ai < bi);
 }
 
-__global__ void __launch_bounds__(256) topk_merge_kernel(TopkArgs a) {
+__global__ void __launch_bounds__(256) cand_merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t q = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (q >= a.n_q) return;
+  const int k = a.k;
   float sv = -INFINITY;
   int64_t iv = -1;
-  if (!a.first && lane < a.k) {
-    sv = a.run_score[q * a.k + lane];
-    iv = a.run_idx[q * a.k + lane];
+  if (!a.first && lane < k) {
+    sv = a.run_score[q * k + lane];
+    iv = a.run_idx[q * k + lane];
   }
-  const int k = a.k;
   float ts = __shfl(sv, k - 1);
   int64_t ti = __shfl(iv, k - 1);
-  const float* row = a.scores + q * (int64_t)kChunk;
-  for (int64_t b0 = 0; b0 < a.chunk_len; b0 += 64) {
-    const bool in = b0 + lane < a.chunk_len;
-    const float v = in ? row[b0 + lane] : -INFINITY;
-    const int64_t id = a.base + b0 + lane;
+  const int n = a.cnt[q];
+  const float* cs = a.cand_s + q * (int64_t)kChunk;
+  const int* ci = a.cand_i + q * (int64_t)kChunk;
+  for (int b0 = 0; b0 < n; b0 += 64) {
+    const bool in = b0 + lane < n;
+    const float v = in ? cs[b0 + lane] : -INFINITY;
+    const int64_t id = in ? a.base + ci[b0 + lane] : -1;
     uint64_t mask = __ballot(in && beats(v, id, ts, ti));
     while (mask) {
       const int src = __ffsll((unsigned long long)mask) - 1;
       const float cv = __shfl(v, src);
-      const int64_t ci = __shfl(id, src);
+      const int64_t cid = __shfl(id, src);
       // entries that beat the candidate form a prefix of the sorted list
-      const uint64_t bm = __ballot(lane < k && beats(sv, iv, cv, ci));
+      const uint64_t bm = __ballot(lane < k && beats(sv, iv, cv, cid));
       const int p = __popcll(bm);
       const float us = __shfl_up(sv, 1);
       const int64_t ui = __shfl_up(iv, 1);
@@ -268,7 +429,7 @@ __global__ void __launch_bounds__(256) topk_merge_kernel(TopkArgs a) {
         }
         if (lane == p) {
           sv = cv;
-          iv = ci;
+          iv = cid;
         }
       }
       ts = __shfl(sv, k - 1);
@@ -285,6 +446,18 @@ __global__ void __launch_bounds__(256) topk_merge_kernel(TopkArgs a) {
       a.run_score[q * k + lane] = sv;
       a.run_idx[q * k + lane] = iv;
     }
+  }
+  if (lane == 0) {
+    a.thr[q] = ts;     // k-th best so far (-inf while fewer than k)
+    a.cnt[q] = 0;
+  }
+}
+
+__global__ void search_init_kernel(float* thr, int* cnt, int64_t n_q) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q < n_q) {
+    thr[q] = -INFINITY;
+    cnt[q] = 0;
   }
 }
 
@@ -308,20 +481,23 @@ hipError_t launch_gemm(int b, const GemmArgs& g, dim3 grid, hipStream_t st) {
 }
 
 struct SearchLayout {
-  size_t qr_hi, qr_lo, qp_hi, qp_lo, scores, run_s, run_i, total;
+  size_t qa[4], thr, cnt, cand_s, cand_i, run_s, run_i, total;
   int64_t rows_pad;
 };
 
 SearchLayout search_layout(const tq_ctx* ctx, int64_t n_queries, int32_t k) {
   SearchLayout L{};
-  L.rows_pad = (n_queries + kRowsTile - 1) / kRowsTile * kRowsTile;
+  L.rows_pad = (n_queries + kQT - 1) / kQT * kQT;
   const size_t mat = align256((size_t)L.rows_pad * ctx->Dp * sizeof(__half));
   size_t off = 0;
-  L.qr_hi = off; off += mat;
-  L.qr_lo = off; off += mat;
-  L.qp_hi = off; off += mat;
-  L.qp_lo = off; off += mat;
-  L.scores = off; off += align256((size_t)L.rows_pad * kChunk * sizeof(float));
+  for (int i = 0; i < 4; ++i) {
+    L.qa[i] = off;
+    off += mat;
+  }
+  L.thr = off; off += align256((size_t)n_queries * sizeof(float));
+  L.cnt = off; off += align256((size_t)n_queries * sizeof(int));
+  L.cand_s = off; off += align256((size_t)n_queries * kChunk * sizeof(float));
+  L.cand_i = off; off += align256((size_t)n_queries * kChunk * sizeof(int));
   L.run_s = off; off += align256((size_t)n_queries * k * sizeof(float));
   L.run_i = off; off += align256((size_t)n_queries * k * sizeof(int64_t));
   L.total = off;
@@ -341,14 +517,16 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
                               hipStream_t stream) {
   const SearchLayout L = search_layout(ctx, n_queries, k);
   char* ws = (char*)workspace;
+  const float alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   RowPrepArgs p{};
   p.q = queries;
   p.pit = ctx->t.pit32;
   p.st = ctx->t.st32;
-  p.qr_hi = (__half*)(ws + L.qr_hi);
-  p.qr_lo = (__half*)(ws + L.qr_lo);
-  p.qp_hi = (__half*)(ws + L.qp_hi);
-  p.qp_lo = (__half*)(ws + L.qp_lo);
+  p.qr_hi = (__half*)(ws + L.qa[0]);
+  p.qr_lo = (__half*)(ws + L.qa[1]);
+  p.qp_hi = (__half*)(ws + L.qa[2]);
+  p.qp_lo = (__half*)(ws + L.qa[3]);
+  p.pscale = alpha;
   p.d = ctx->d;
   p.Dp = ctx->Dp;
   p.n = n_queries;
@@ -360,50 +538,68 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  GemmArgs g{};
-  g.qr_hi = p.qr_hi;
-  g.qr_lo = p.qr_lo;
-  g.qp_hi = p.qp_hi;
-  g.qp_lo = p.qp_lo;
-  g.n_rows = n_queries;
+  SearchArgs g{};
+  for (int i = 0; i < 4; ++i) g.qa[i] = (const __half*)(ws + L.qa[i]);
+  g.n_q = n_queries;
   g.planes = planes;
   g.norms = (const uint32_t*)norms;
   g.W = ctx->W;
   g.Dp = ctx->Dp;
-  g.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
-  fill_centroid_split(ctx, g);
-  g.out = (float*)(ws + L.scores);
-  g.out_ld = kChunk;
+  for (int j = 0; j < kMaxK; ++j) {
+    const float c = j < ctx->K ? ctx->cent[j] : 0.f;
+    const _Float16 h = (_Float16)c;
+    const _Float16 l = (_Float16)(c - (float)h);
+    g.ctab[j] = (uint32_t)__builtin_bit_cast(uint16_t, h) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+  }
+  g.thr = (float*)(ws + L.thr);
+  g.cnt = (int*)(ws + L.cnt);
+  g.cand_s = (float*)(ws + L.cand_s);
+  g.cand_i = (int*)(ws + L.cand_i);
 
-  TopkArgs t{};
-  t.scores = g.out;
-  t.n_q = n_queries;
-  t.k = k;
-  t.run_score = (float*)(ws + L.run_s);
-  t.run_idx = (int64_t*)(ws + L.run_i);
-  t.out_score = out_score;
-  t.out_idx = out_idx;
-  const int64_t n_chunks = std::max<int64_t>(1, (n_db + kChunk - 1) / kChunk);
-  for (int64_t c = 0; c < n_chunks; ++c) {
-    const int64_t base = c * kChunk;
-    const int64_t len = std::max<int64_t>(0, std::min<int64_t>(kChunk, n_db - base));
+  MergeArgs m{};
+  m.n_q = n_queries;
+  m.k = k;
+  m.thr = (float*)(ws + L.thr);
+  m.cnt = g.cnt;
+  m.cand_s = g.cand_s;
+  m.cand_i = g.cand_i;
+  m.run_score = (float*)(ws + L.run_s);
+  m.run_idx = (int64_t*)(ws + L.run_i);
+  m.out_score = out_score;
+  m.out_idx = out_idx;
+
+  hipLaunchKernelGGL(search_init_kernel, dim3((unsigned)((n_queries + 255) / 256)), dim3(256), 0,
+                     stream, m.thr, m.cnt, n_queries);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // chunks: a small first one sets the thresholds, then kChunk records each
+  int64_t base = 0;
+  bool first = true;
+  do {
+    const int64_t len = std::min<int64_t>(n_db - base, first ? kFirst : kChunk);
     if (len > 0) {
       g.rec0 = base;
       g.n_rec = len;
-      const dim3 grid((unsigned)((len + kRecTile - 1) / kRecTile),
-                      (unsigned)(L.rows_pad / kRowsTile));
-      e = launch_gemm<0>(ctx->b, g, grid, stream);
+      const dim3 grid((unsigned)((len + kRT - 1) / kRT), (unsigned)(L.rows_pad / kQT));
+      switch (ctx->b) {
+        case 2: hipLaunchKernelGGL(search_gemm_kernel<2>, grid, dim3(256), 0, stream, g); break;
+        case 3: hipLaunchKernelGGL(search_gemm_kernel<3>, grid, dim3(256), 0, stream, g); break;
+        default: hipLaunchKernelGGL(search_gemm_kernel<4>, grid, dim3(256), 0, stream, g); break;
+      }
+      e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    t.chunk_len = len;
-    t.base = base;
-    t.first = c == 0;
-    t.last = c == n_chunks - 1;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((n_queries + 3) / 4)), dim3(256), 0,
-                       stream, t);
+    m.base = base;
+    m.first = first;
+    m.last = base + len >= n_db;
+    hipLaunchKernelGGL(cand_merge_kernel, dim3((unsigned)((n_queries + 3) / 4)), dim3(256), 0,
+                       stream, m);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-  }
+    base += len;
+    first = false;
+  } while (base < n_db);
   return hipSuccess;
 }
 
