@@ -240,18 +240,28 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
     if constexpr (RES) fetch(tile + gridDim.x);   // next tile, in flight during MFMA
 
     // ---- 2. Y = Pi x_s ------------------------------------------------------
-    // words of this wave: w = wave + NW * wi
+    // words of this wave: w = wave + NW * wi.  The K step is the outer loop,
+    // so all waves (and the workgroups in step with them) read one narrow
+    // column slice of Pi at a time, which stays in L2.
     v4f acc[WPW][2][NCB];
 #pragma unroll
-    for (int wi = 0; wi < WPW; ++wi) {
-      const int w = wave + NW * wi;
-      if (w >= W) continue;
+    for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[wi][rb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll 2
+    for (int ks = 0; ks < KS; ++ks) {
+      v8h xh[NCB], xl[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        xh[cb] = lds_v8h(bufA + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+        if constexpr (!BF16) xl[cb] = lds_v8h(bufB + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+      }
+#pragma unroll
+      for (int wi = 0; wi < WPW; ++wi) {
+        const int w = wave + NW * wi;
+        if (w >= W) continue;
         v8h ph[2], pl[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -265,19 +275,15 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
           }
         }
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const v8h xh = lds_v8h(bufA + (16 * cb + n) * ldx + 32 * ks + 8 * g);
-          v8h xl;
-          if constexpr (!BF16) xl = lds_v8h(bufB + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
             v4f c = acc[wi][rb][cb];
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rb], xh, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[rb], xh, c, 0, 0, 0);
-            if constexpr (!BF16) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rb], xl, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rb], xh[cb], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[rb], xh[cb], c, 0, 0, 0);
+            if constexpr (!BF16) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[rb], xl[cb], c, 0, 0, 0);
             acc[wi][rb][cb] = c;
           }
-        }
       }
     }
     __syncthreads();   // every wave is done reading x before r overwrites it
@@ -355,19 +361,27 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
     }
     __syncthreads();
 
-    // ---- 4. Z = M r, signs, 5. store ---------------------------------------
+    // ---- 4. Z = M r (K step outer, as for Y), signs, 5. store ---------------
     {
+      v4f zacc[WPW][2][NCB];
 #pragma unroll
-      for (int wi = 0; wi < WPW; ++wi) {
-        const int w = wave + NW * wi;
-        if (w >= W) continue;
-        v4f z[2][NCB];
+      for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) z[rb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
-  #pragma unroll 4
+          for (int cb = 0; cb < NCB; ++cb) zacc[wi][rb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
       for (int ks = 0; ks < KS; ++ks) {
+        v8h rh[NCB], rl[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          rh[cb] = lds_v8h(bufA + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+          rl[cb] = lds_v8h(bufB + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+        }
+#pragma unroll
+        for (int wi = 0; wi < WPW; ++wi) {
+          const int w = wave + NW * wi;
+          if (w >= W) continue;
           v8h mh[2], ml[2];
 #pragma unroll
           for (int rb = 0; rb < 2; ++rb) {
@@ -381,19 +395,21 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
             }
           }
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            const v8h rh = lds_v8h(bufA + (16 * cb + n) * ldx + 32 * ks + 8 * g);
-            const v8h rl = lds_v8h(bufB + (16 * cb + n) * ldx + 32 * ks + 8 * g);
+          for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
-              v4f c = z[rb][cb];
-              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh[rb], rh, c, 0, 0, 0);
-              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ml[rb], rh, c, 0, 0, 0);
-              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh[rb], rl, c, 0, 0, 0);
-              z[rb][cb] = c;
+              v4f c = zacc[wi][rb][cb];
+              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh[rb], rh[cb], c, 0, 0, 0);
+              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ml[rb], rh[cb], c, 0, 0, 0);
+              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(mh[rb], rl[cb], c, 0, 0, 0);
+              zacc[wi][rb][cb] = c;
             }
-          }
         }
+      }
+#pragma unroll
+      for (int wi = 0; wi < WPW; ++wi) {
+        const int w = wave + NW * wi;
+        if (w >= W) continue;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           uint32_t sw = 0u;
@@ -402,7 +418,7 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int pos = 16 * rb + 4 * g + i;
-              if (32 * w + pos < d && z[rb][cb][i] >= 0.f) sw |= 1u << pos;
+              if (32 * w + pos < d && zacc[wi][rb][cb][i] >= 0.f) sw |= 1u << pos;
             }
           sw |= __shfl_xor(sw, 16);
           sw |= __shfl_xor(sw, 32);
