@@ -223,6 +223,36 @@ TQ_API tq_status tq_attn_logits_prepared(const tq_ctx* ctx, const void* workspac
                                          float scale, float* logits,
                                          int64_t logits_stride_head, void* stream);
 
+/* Workspace for tq_attn_output, in bytes (0 for invalid sizes). */
+TQ_API size_t tq_attn_output_workspace_bytes(const tq_ctx* ctx, int32_t batch,
+                                             int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t max_seq_len);
+
+/* Attention output from packed values (turboquant.net pseudo-code "integrate
+ * into Transformer attention": values are quantized like keys; a query head's
+ * output is the weighted sum of the values, here the dequantized values of
+ * the pseudo-code "dequant"):
+ *   out[bi*out_stride_batch + hq*d + i] =
+ *       sum_{t < seq_len[bi]} p[hq*p_stride_head + seq_start[bi] + t]
+ *                             * dequant(value record (hq / G, bi, t))_i,
+ * computed as Pi^T (sum_t p nu c[idx]) + alpha S^T (sum_t p nu gamma s) (the
+ * transforms applied once per head).  The value record of (kv head h,
+ * sequence bi, token t) is at h*values_stride_head + seq_start[bi] + t, as for
+ * tq_attn_logits; p uses the logits' indexing (e.g. softmax of those logits).
+ * p, seq_start, seq_len, out: device memory; max_seq_len bounds every seq_len.
+ * workspace: at least tq_attn_output_workspace_bytes(), 16-byte aligned;
+ * overwritten.  Errors: TQ_ERR_INVALID_ARG for NULL pointers with work to do,
+ * batch < 0, n_kv_heads < 1, n_q_heads % n_kv_heads != 0, a too small
+ * workspace, misaligned planes/workspace.  batch == 0 is a no-op; an empty
+ * sequence gets a zero output. */
+TQ_API tq_status tq_attn_output(const tq_ctx* ctx, const float* p, int64_t p_stride_head,
+                                int32_t batch, int32_t n_q_heads, const uint32_t* planes,
+                                const uint16_t* norms, int32_t n_kv_heads,
+                                int64_t values_stride_head, const int64_t* seq_start,
+                                const int32_t* seq_len, int32_t max_seq_len, float* out,
+                                int64_t out_stride_batch, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace for tq_search_topk, in bytes. */
 TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db,
                                         int32_t k);

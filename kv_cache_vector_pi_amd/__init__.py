@@ -29,7 +29,8 @@ EXPORTS = [
     "tq_make_rotation", "tq_lloyd_max", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim",
     "tq_ctx_bits", "tq_quantize_kv", "tq_dequantize", "tq_attn_logits_workspace_bytes",
     "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
-    "tq_search_workspace_bytes", "tq_search_topk",
+    "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
+    "tq_attn_output",
 ]
 
 
@@ -74,6 +75,9 @@ _sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, 
 _sig("tq_attn_prepare", _i32, [_P, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
 _sig("tq_attn_logits_prepared", _i32, [_P, _P, _sz, _i32, _i32, _P, _P, _i32, _i64, _P, _P, _i32,
                                        _f32, _P, _i64, _P])
+_sig("tq_attn_output_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32])
+_sig("tq_attn_output", _i32, [_P, _P, _i64, _i32, _i32, _P, _P, _i32, _i64, _P, _P, _i32, _P, _i64,
+                              _P, _sz, _P])
 _sig("tq_search_workspace_bytes", _sz, [_P, _i64, _i64, _i32])
 _sig("tq_search_topk", _i32, [_P, _P, _i64, _P, _P, _i64, _i32, _P, _P, _P, _sz, _P])
 
@@ -259,6 +263,22 @@ def tq_attn_logits_prepared(ctx, workspace, batch, n_q_heads, planes, norms, n_k
                                       _ptr(seq_start), _ptr(seq_len), max_seq_len, float(scale),
                                       _ptr(logits), logits_stride_head, _stream(stream))
     _check(st, "tq_attn_logits_prepared")
+
+
+def tq_attn_output_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len):
+    return _lib.tq_attn_output_workspace_bytes(ctx.handle, batch, n_q_heads, n_kv_heads,
+                                               max_seq_len)
+
+
+def tq_attn_output(ctx, p, p_stride_head, batch, n_q_heads, planes, norms, n_kv_heads,
+                   values_stride_head, seq_start, seq_len, max_seq_len, out, out_stride_batch,
+                   workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_attn_output(ctx.handle, _ptr(p), p_stride_head, batch, n_q_heads, _ptr(planes),
+                             _ptr(norms), n_kv_heads, values_stride_head, _ptr(seq_start),
+                             _ptr(seq_len), max_seq_len, _ptr(out), out_stride_batch,
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "tq_attn_output")
 
 
 def tq_search_workspace_bytes(ctx, n_queries, n_db, k):

@@ -1,0 +1,262 @@
+// Attention output from packed values (turboquant.net pseudo-code
+// "integrate into Transformer attention": V is quantized like K; the output
+// of a query head is the attention-weighted sum of the values, here of the
+// dequantized values of the pseudo-code "dequant").
+//
+// With v~_t = nu_t (Pi^T c[idx_t] + alpha gamma_t S^T s_t) the output
+//   o = sum_t p_t v~_t = Pi^T a_rot + alpha S^T a_sk,
+//   a_rot = sum_t (p_t nu_t) c[idx_t],   a_sk = sum_t (p_t nu_t gamma_t) s_t,
+// so the token stream accumulates in rotated / sketch space (per coordinate:
+// one centroid lookup and one FMA per query head) and the two d x d
+// transforms run once per query head at the end.
+//
+//  1. vout_accum_kernel: workgroup = (chunk of tokens, kv head and block of 4
+//     query heads, sequence).  The chunk's packed records, norms and weights
+//     are staged in LDS with coalesced loads; each thread owns coordinates
+//     and accumulates both sums for the 4 heads; partial sums per chunk go to
+//     the workspace.
+//  2. vout_final_kernel: workgroup = (query head, sequence): sum the chunk
+//     partials, then o_i = sum_j Pi[j][i] a_rot[j] + alpha sum_j S[j][i] a_sk[j].
+#include <algorithm>
+#include <cmath>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+struct VAccArgs {
+  const float* p;           // weights, p[hq * p_stride_head + seq_start[bi] + t]
+  int64_t p_stride_head;
+  const uint32_t* planes;
+  const uint32_t* norms;
+  int64_t values_stride_head;
+  const int64_t* seq_start;
+  const int32_t* seq_len;
+  float* part;              // [batch][n_kv][n_rb][n_chunk][2][4][Dp]
+  int d, W, Dp, G, n_kv, n_rb, n_chunk, chunk;
+  float cent[kMaxK];
+};
+
+inline int n_rb_of(int G) { return (G + 3) / 4; }
+
+// Tokens per chunk: the chunk's records must fit the LDS staging area.
+inline int chunk_of(const tq_ctx* ctx) {
+  const int rec_bytes = ctx->W * ctx->b * 4 + 4 + 32;     // words, norms, 8 weights
+  int ch = 256;
+  while (ch > 16 && (size_t)ch * rec_bytes > 48 * 1024) ch >>= 1;
+  return ch;
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
+  extern __shared__ __align__(16) uint32_t sm[];
+  const int RW = a.W * NB;                       // words per record
+  uint32_t* words = sm;                          // [chunk][RW]
+  float* wts = (float*)(words + a.chunk * RW);   // [chunk][8]: p nu (4 heads), p nu gamma (4)
+
+  const int tid = threadIdx.x;
+  const int chunk_i = blockIdx.x;
+  const int h = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
+  const int bi = blockIdx.z;
+  const int len = a.seq_len[bi];
+  const int64_t start = a.seq_start[bi];
+  const int t0 = chunk_i * a.chunk;
+  const int nt = max(0, min(a.chunk, len - t0));
+
+  // ---- stage the chunk -------------------------------------------------------
+  const int64_t rec0 = (int64_t)h * a.values_stride_head + start + t0;
+  for (int i = tid; i < nt * RW; i += 256) words[i] = a.planes[rec0 * RW + i];
+  for (int i = tid; i < nt * 8; i += 256) {
+    const int t = i >> 3, k = i & 7, hh = k & 3;
+    const int g = 4 * rb + hh;
+    const uint32_t nr = a.norms[rec0 + t];
+    const float nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
+    float w = 0.f;
+    if (g < a.G) w = a.p[(int64_t)(h * a.G + g) * a.p_stride_head + start + t0 + t] * nu;
+    if (k >= 4) w *= __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
+    wts[i] = w;
+  }
+  __syncthreads();
+
+  // ---- accumulate ------------------------------------------------------------
+  // coordinate lanes NL = min(Dp, 256) (coordinates lc + 256 k), token groups TT
+  const int NL = min(a.Dp, 256);
+  const int TT = 256 / NL;
+  const int lc = tid % NL, tg = tid / NL;
+  constexpr int kMaxCpt = 8;                     // Dp <= 2048
+  const int cpt = (a.Dp + 255) / 256;
+  float ar[kMaxCpt][4], as[kMaxCpt][4];
+#pragma unroll
+  for (int k = 0; k < kMaxCpt; ++k)
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) ar[k][hh] = as[k][hh] = 0.f;
+  if (tg < TT) {
+    for (int t = tg; t < nt; t += TT) {
+      const uint32_t* rw = words + t * RW;
+      const float4 w1 = *(const float4*)(wts + 8 * t);
+      const float4 w2 = *(const float4*)(wts + 8 * t + 4);
+#pragma unroll
+      for (int k = 0; k < kMaxCpt; ++k) {
+        if (k >= cpt) break;
+        const int j = lc + 256 * k;
+        if (j >= a.d) continue;
+        const uint32_t* gw = rw + (j >> 5) * NB;
+        const int bit = j & 31;
+        int idx = 0;
+#pragma unroll
+        for (int q = 0; q < NB - 1; ++q) idx |= (int)((gw[q] >> bit) & 1u) << q;
+        float c = a.cent[0];
+#pragma unroll
+        for (int m = 1; m < (1 << (NB - 1)); ++m) c = (idx == m) ? a.cent[m] : c;
+        const bool sp = (gw[NB - 1] >> bit) & 1u;
+        ar[k][0] = fmaf(w1.x, c, ar[k][0]);
+        ar[k][1] = fmaf(w1.y, c, ar[k][1]);
+        ar[k][2] = fmaf(w1.z, c, ar[k][2]);
+        ar[k][3] = fmaf(w1.w, c, ar[k][3]);
+        as[k][0] += sp ? w2.x : -w2.x;
+        as[k][1] += sp ? w2.y : -w2.y;
+        as[k][2] += sp ? w2.z : -w2.z;
+        as[k][3] += sp ? w2.w : -w2.w;
+      }
+    }
+  }
+  __syncthreads();          // staging area is reused for the token-group sums
+
+  // ---- reduce the token groups and write the chunk partials ------------------
+  float* red = (float*)sm;                       // [TT][8][NL] (TT > 1 only when cpt == 1)
+  float* dst = a.part +
+      ((((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk + chunk_i) * 8 * (int64_t)a.Dp;
+  if (TT > 1) {
+    if (tg < TT)
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        red[(tg * 8 + hh) * NL + lc] = ar[0][hh];
+        red[(tg * 8 + 4 + hh) * NL + lc] = as[0][hh];
+      }
+    __syncthreads();
+    for (int i = tid; i < 8 * NL; i += 256) {
+      float s = 0.f;
+      for (int g = 0; g < TT; ++g) s += red[g * 8 * NL + i];
+      const int sel = i / NL, j = i % NL;
+      dst[sel * a.Dp + j] = s;                   // sel: 0..3 rot heads, 4..7 sketch heads
+    }
+  } else if (tg < TT) {
+#pragma unroll
+    for (int k = 0; k < kMaxCpt; ++k) {
+      if (k >= cpt) break;
+      const int j = lc + 256 * k;
+      if (j >= a.Dp) continue;
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        dst[hh * a.Dp + j] = ar[k][hh];
+        dst[(4 + hh) * a.Dp + j] = as[k][hh];
+      }
+    }
+  }
+}
+
+struct VFinArgs {
+  const float* part;
+  const float* pi32;        // [d][d] row-major
+  const float* s32;
+  float* out;               // out[bi * out_stride_batch + hq * d + i]
+  int64_t out_stride_batch;
+  int d, Dp, G, n_kv, n_rb, n_chunk;
+  float alpha;
+};
+
+__global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
+  extern __shared__ float fsm[];
+  float* arot = fsm;               // [Dp]
+  float* ask = fsm + a.Dp;         // [Dp]
+  const int tid = threadIdx.x;
+  const int hq = blockIdx.x, bi = blockIdx.y;
+  const int h = hq / a.G, g = hq % a.G, rb = g / 4, hh = g % 4;
+  const float* src = a.part + (((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk * 8 * (int64_t)a.Dp;
+  for (int j = tid; j < a.Dp; j += 256) {
+    float s1 = 0.f, s2 = 0.f;
+    for (int c = 0; c < a.n_chunk; ++c) {
+      s1 += src[((int64_t)c * 8 + hh) * a.Dp + j];
+      s2 += src[((int64_t)c * 8 + 4 + hh) * a.Dp + j];
+    }
+    arot[j] = s1;
+    ask[j] = s2;
+  }
+  __syncthreads();
+  for (int i = tid; i < a.d; i += 256) {
+    float o1 = 0.f, o2 = 0.f;
+    for (int j = 0; j < a.d; ++j) {
+      o1 = fmaf(a.pi32[(int64_t)j * a.d + i], arot[j], o1);
+      o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
+    }
+    a.out[(int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d + i] = fmaf(a.alpha, o2, o1);
+  }
+}
+
+}  // namespace
+
+size_t vout_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t max_seq_len) {
+  const int G = n_q_heads / n_kv_heads;
+  const int ch = chunk_of(ctx);
+  const int64_t n_chunk = std::max<int64_t>(1, ((int64_t)max_seq_len + ch - 1) / ch);
+  return (size_t)batch * n_kv_heads * n_rb_of(G) * n_chunk * 8 * ctx->Dp * sizeof(float);
+}
+
+hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_stride_head,
+                              int32_t batch, int32_t n_q_heads, const uint32_t* planes,
+                              const uint16_t* norms, int32_t n_kv_heads,
+                              int64_t values_stride_head, const int64_t* seq_start,
+                              const int32_t* seq_len, int32_t max_seq_len, float* out,
+                              int64_t out_stride_batch, void* workspace, hipStream_t stream) {
+  const int G = n_q_heads / n_kv_heads;
+  VAccArgs a{};
+  a.p = p;
+  a.p_stride_head = p_stride_head;
+  a.planes = planes;
+  a.norms = (const uint32_t*)norms;
+  a.values_stride_head = values_stride_head;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.part = (float*)workspace;
+  a.d = ctx->d;
+  a.W = ctx->W;
+  a.Dp = ctx->Dp;
+  a.G = G;
+  a.n_kv = n_kv_heads;
+  a.n_rb = n_rb_of(G);
+  a.chunk = chunk_of(ctx);
+  a.n_chunk = std::max(1, (max_seq_len + a.chunk - 1) / a.chunk);
+  for (int k = 0; k < kMaxK; ++k) a.cent[k] = k < ctx->K ? ctx->cent[k] : 0.f;
+  const int NL = std::min(ctx->Dp, 256), TT = 256 / NL;
+  const size_t stage = (size_t)a.chunk * (ctx->W * ctx->b + 8) * 4;
+  const size_t red = TT > 1 ? (size_t)TT * 8 * NL * 4 : 0;
+  const size_t shm = std::max(stage, red);
+  const dim3 grid(a.n_chunk, n_kv_heads * a.n_rb, batch);
+  switch (ctx->b) {
+    case 2: hipLaunchKernelGGL(vout_accum_kernel<2>, grid, dim3(256), shm, stream, a); break;
+    case 3: hipLaunchKernelGGL(vout_accum_kernel<3>, grid, dim3(256), shm, stream, a); break;
+    default: hipLaunchKernelGGL(vout_accum_kernel<4>, grid, dim3(256), shm, stream, a); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  VFinArgs f{};
+  f.part = a.part;
+  f.pi32 = ctx->t.pi32;
+  f.s32 = ctx->t.s32;
+  f.out = out;
+  f.out_stride_batch = out_stride_batch;
+  f.d = ctx->d;
+  f.Dp = ctx->Dp;
+  f.G = G;
+  f.n_kv = n_kv_heads;
+  f.n_rb = a.n_rb;
+  f.n_chunk = a.n_chunk;
+  f.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
+  hipLaunchKernelGGL(vout_final_kernel, dim3(n_q_heads, batch), dim3(256),
+                     2 * ctx->Dp * sizeof(float), stream, f);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -359,7 +359,7 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
       }
   }
   const size_t bytes16 = (4 * dpp + 4 * rpp) * sizeof(__half);
-  const size_t bytes32 = 2 * dd * sizeof(float);
+  const size_t bytes32 = 4 * dd * sizeof(float);
   void* blk = nullptr;
   e = hipMalloc(&blk, bytes16 + bytes32);
   if (e != hipSuccess) {
@@ -368,17 +368,20 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
                 hipGetErrorString(e));
   }
   char* p = (char*)blk;
-  // fp32 transposes for the query projections (one thread per output row
-  // reads a contiguous column)
-  std::vector<float> t32(2 * dd);
+  // fp32 tables: Pi^T and S^T for the query projections (one thread per
+  // output row reads a contiguous column), Pi and S row-major for the
+  // value-output transforms (one thread per output column)
+  std::vector<float> t32(4 * dd);
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) {
       t32[(size_t)j * d + i] = pi[(size_t)i * d + j];
       t32[dd + (size_t)j * d + i] = s[(size_t)i * d + j];
+      t32[2 * dd + (size_t)i * d + j] = pi[(size_t)i * d + j];
+      t32[3 * dd + (size_t)i * d + j] = s[(size_t)i * d + j];
     }
   e = hipMemcpy(p, h16.data(), bytes16, hipMemcpyHostToDevice);
   if (e == hipSuccess)
-    e = hipMemcpy(p + bytes16, t32.data(), 2 * dd * sizeof(float), hipMemcpyHostToDevice);
+    e = hipMemcpy(p + bytes16, t32.data(), 4 * dd * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(blk);
     delete ctx;
@@ -396,6 +399,8 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
   ctx->t.st_lo = h + 4 * dpp + 3 * rpp;
   ctx->t.pit32 = (const float*)(p + bytes16);
   ctx->t.st32 = (const float*)(p + bytes16) + dd;
+  ctx->t.pi32 = (const float*)(p + bytes16) + 2 * dd;
+  ctx->t.s32 = (const float*)(p + bytes16) + 3 * dd;
   *out = ctx;
   return ok();
 }
@@ -561,6 +566,49 @@ TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, in
                                         int32_t k) {
   if (!ctx || n_queries < 0 || n_db < 0 || k < 1 || k > 64) return 0;
   return tq::search_workspace_bytes(ctx, n_queries, n_db, k);
+}
+
+TQ_API size_t tq_attn_output_workspace_bytes(const tq_ctx* ctx, int32_t batch,
+                                             int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t max_seq_len) {
+  if (!ctx || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads ||
+      max_seq_len < 0)
+    return 0;
+  return tq::vout_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len);
+}
+
+TQ_API tq_status tq_attn_output(const tq_ctx* ctx, const float* p, int64_t p_stride_head,
+                                int32_t batch, int32_t n_q_heads, const uint32_t* planes,
+                                const uint16_t* norms, int32_t n_kv_heads,
+                                int64_t values_stride_head, const int64_t* seq_start,
+                                const int32_t* seq_len, int32_t max_seq_len, float* out,
+                                int64_t out_stride_batch, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: ctx is NULL");
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: batch=%d n_q=%d n_kv=%d max_seq_len=%d",
+                batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (batch == 0) return ok();
+  if (!p || !planes || !norms || !seq_start || !seq_len || !out || !workspace)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: NULL pointer");
+  if (p_stride_head < 0 || values_stride_head < 0 ||
+      (batch > 1 && out_stride_batch < (int64_t)n_q_heads * ctx->d))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: bad stride");
+  if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(workspace, 16) || !aligned(p, 4) ||
+      !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: misaligned pointer");
+  const size_t need =
+      tq::vout_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_output: workspace %zu < %zu bytes", workspace_bytes,
+                need);
+  hipError_t e = tq::launch_attn_output(ctx, p, p_stride_head, batch, n_q_heads, planes, norms,
+                                        n_kv_heads, values_stride_head, seq_start, seq_len,
+                                        max_seq_len, out, out_stride_batch, workspace,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_output: launch");
+  return ok();
 }
 
 TQ_API tq_status tq_search_topk(const tq_ctx* ctx, const float* queries, int64_t n_queries,

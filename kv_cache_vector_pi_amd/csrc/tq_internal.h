@@ -27,6 +27,8 @@ struct DevTables {
   const __half* st_lo;
   const float* pit32;    // [d][d] Pi^T (column r of Pi is contiguous: pit32[j*d + r] = Pi[r][j])
   const float* st32;     // [d][d] S^T
+  const float* pi32;     // [d][d] Pi, row-major
+  const float* s32;      // [d][d] S, row-major
 };
 
 }  // namespace tq
@@ -78,6 +80,14 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
                               const uint32_t* planes, const uint16_t* norms, int64_t n_db,
                               int32_t k, int64_t* out_idx, float* out_score, void* workspace,
                               hipStream_t stream);
+size_t vout_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
+                            int32_t n_kv_heads, int32_t max_seq_len);
+hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_stride_head,
+                              int32_t batch, int32_t n_q_heads, const uint32_t* planes,
+                              const uint16_t* norms, int32_t n_kv_heads,
+                              int64_t values_stride_head, const int64_t* seq_start,
+                              const int32_t* seq_len, int32_t max_seq_len, float* out,
+                              int64_t out_stride_batch, void* workspace, hipStream_t stream);
 hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const uint16_t* norms,
                              int64_t n, float* out, int64_t out_ld, hipStream_t stream);
 

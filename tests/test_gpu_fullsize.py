@@ -177,6 +177,43 @@ def test_long_context(orc, b):
     ctx.close()
 
 
+def test_llama_attn_output(orc):
+    """Values of the Llama-shaped layer (8 KV heads x 32768 tokens, b = 4,
+    outlier channels), weights = softmax of the packed-key logits of a
+    seeded query: sampled query heads against the oracle's weighted sum of
+    dequantized values."""
+    d, b, n_kv, n_q, n_tok = 128, 4, 8, 32, 32768
+    say("llama attn output")
+    ctx, pi, s, c = make_ctx(orc, d, b)
+    wl = workloads.llama(DEV, n_tok=n_tok)
+    rw = tq.tq_record_words(d, b)
+    kp = torch.zeros((n_kv * n_tok, rw), dtype=torch.int32, device=DEV)
+    kn = torch.zeros((n_kv * n_tok, 2), dtype=torch.int16, device=DEV)
+    vp, vn = torch.zeros_like(kp), torch.zeros_like(kn)
+    tq.tq_quantize_kv(ctx, wl["K"], kp, kn)
+    tq.tq_quantize_kv(ctx, wl["V"], vp, vn)
+    ss = torch.zeros(1, dtype=torch.int64, device=DEV)
+    sl = torch.full((1,), n_tok, dtype=torch.int32, device=DEV)
+    logits = torch.empty((n_q, n_tok), device=DEV)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, n_q, n_kv), DEV)
+    tq.tq_attn_logits(ctx, wl["q"], 1, n_q, n_q * d, kp, kn, n_kv, n_tok, ss, sl, n_tok,
+                      1.0 / math.sqrt(d), logits, n_tok, ws)
+    p = torch.softmax(logits, dim=1).contiguous()
+    out = torch.empty((1, n_q, d), device=DEV)
+    wo = tq.workspace(tq.tq_attn_output_workspace_bytes(ctx, 1, n_q, n_kv, n_tok), DEV)
+    tq.tq_attn_output(ctx, p, n_tok, 1, n_q, vp, vn, n_kv, n_tok, ss, sl, n_tok, out, n_q * d, wo)
+    torch.cuda.synchronize()
+    pn = p.cpu().numpy().astype(np.float64)
+    for hq in [0, 9, 22, 31]:
+        h = hq // (n_q // n_kv)
+        P, N = np_records(vp, vn, np.arange(h * n_tok, (h + 1) * n_tok))
+        deq = orc.dequantize(d, b, pi, s, c, P, N)
+        ref = pn[hq] @ deq
+        got = out[0, hq].cpu().numpy()
+        assert rel_err_rows(got[None], ref[None]) < TOL, (hq, rel_err_rows(got[None], ref[None]))
+    ctx.close()
+
+
 @pytest.mark.parametrize("d,b", [(1536, 2), (1536, 4), (200, 2), (200, 4)])
 def test_vector_search_1m(orc, d, b):
     k = 10

@@ -254,6 +254,81 @@ def test_logits_empty_sequence_writes_nothing(orc):
     assert np.all(np.isfinite(got[:, 10:30]))
 
 
+# ---------------------------------------------------------- attention output
+def run_vout(ctx, p, P, N, n_kv, vstride, starts, lens, n_q, p_stride):
+    """tq_attn_output with weights p (numpy [n_q, p_stride]) -> numpy [batch, n_q, d]."""
+    batch = len(lens)
+    p_t = torch.as_tensor(np.ascontiguousarray(p, np.float32), device=DEV)
+    ss = torch.as_tensor(np.asarray(starts, np.int64), device=DEV)
+    sl = torch.as_tensor(np.asarray(lens, np.int32), device=DEV)
+    out = torch.full((batch, n_q, ctx.d), float("nan"), device=DEV)
+    mx = max(lens) if lens else 0
+    ws = tq.workspace(tq.tq_attn_output_workspace_bytes(ctx, batch, n_q, n_kv, mx))
+    tq.tq_attn_output(ctx, p_t, p_stride, batch, n_q, P, N, n_kv, vstride, ss, sl, mx, out,
+                      n_q * ctx.d, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,b,n_q,n_kv,lens,signed", [
+    (128, 3, 16, 1, [1024], False),           # tiny layout: G = 16 (4 row blocks)
+    (128, 4, 32, 8, [1000, 37, 513], False),  # GQA 4, ragged batch
+    (128, 2, 8, 8, [300, 1], True),           # G = 1, signed weights (the sum is linear)
+    (128, 4, 6, 2, [700], False),             # G = 3 (partial row block)
+    (200, 4, 8, 2, [333, 70], False),
+    (1536, 2, 4, 1, [150], True),
+])
+def test_attn_output_parity(orc, d, b, n_q, n_kv, lens, signed):
+    say("attn output", d, b, n_q, n_kv, lens)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    total = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).tolist()
+    x = workloads.normal((n_kv, total, d), 8, 11, "cpu").double().numpy()
+    recs = [orc.quantize(d, b, pi, s, c, x[h]) for h in range(n_kv)]
+    planes = np.concatenate([r["planes"] for r in recs])
+    norms = np.concatenate([r["norms"] for r in recs])
+    rng = np.random.default_rng(9)
+    p = rng.random((n_q, total)) if not signed else rng.standard_normal((n_q, total))
+    p = p.astype(np.float32)
+    P = torch.as_tensor(planes.view(np.int32), device=DEV)
+    N = torch.as_tensor(norms.view(np.int16), device=DEV)
+    got = run_vout(ctx, p, P, N, n_kv, total, starts, lens, n_q, total)
+    G = n_q // n_kv
+    deq = [orc.dequantize(d, b, pi, s, c, r["planes"], r["norms"]) for r in recs]   # [total, d]
+    for bi, (st, ln) in enumerate(zip(starts, lens)):
+        for hq in range(n_q):
+            ref = p[hq, st:st + ln].astype(np.float64) @ deq[hq // G][st:st + ln]
+            assert rel_err_rows(got[bi, hq][None], ref[None]) < TOL, (bi, hq)
+
+
+def test_attn_output_empty_sequence_is_zero(orc):
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    P, N = workloads.random_records(64, tq.tq_record_words(d, b), 3, DEV)
+    p = np.ones((4, 64), np.float32)
+    got = run_vout(ctx, p, P, N, 1, 64, [0, 10], [0, 20], 4, 64)
+    assert np.all(got[0] == 0.0)
+    deq = orc.dequantize(d, b, pi, s, c, P.cpu().numpy().view(np.uint32),
+                         N.cpu().numpy().view(np.uint16))
+    ref = deq[10:30].sum(axis=0)
+    assert rel_err_rows(got[1], np.tile(ref, (4, 1))) < TOL
+
+
+def test_attn_output_rejects_bad_arguments(orc):
+    d, b = 128, 3
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    P, N = workloads.random_records(16, tq.tq_record_words(d, b), 3, DEV)
+    p = torch.ones((4, 16), device=DEV)
+    ss = torch.zeros(1, dtype=torch.int64, device=DEV)
+    sl = torch.full((1,), 16, dtype=torch.int32, device=DEV)
+    out = torch.empty((1, 4, d), device=DEV)
+    ws = tq.workspace(tq.tq_attn_output_workspace_bytes(ctx, 1, 4, 1, 16))
+    with pytest.raises(tq.TqError):      # n_q not a multiple of n_kv
+        tq.tq_attn_output(ctx, p, 16, 1, 4, P, N, 3, 16, ss, sl, 16, out, 4 * d, ws)
+    with pytest.raises(tq.TqError):      # workspace too small
+        tq.tq_attn_output(ctx, p, 16, 1, 4, P, N, 1, 16, ss, sl, 16, out, 4 * d, ws[:16])
+
+
 # ---------------------------------------------------------------- dequantize
 @pytest.mark.parametrize("d,b,n", [(128, 3, 1024), (128, 4, 100), (200, 2, 130), (1536, 4, 20),
                                    (64, 2, 70)])
