@@ -21,6 +21,9 @@ Other workloads (each prints its own JSON line; the default is the one above):
   --workload batched  16 ragged sequences (4096..8192 tokens), b = 3: quantize
                       a 512-token chunk per sequence, then logits for one
                       query of 32 heads per sequence
+  --workload attn_out the value side of the Llama-shaped decode layer over 32
+                      layer caches: tq_attn_output (weights from a softmax of
+                      seeded logits) over all packed values of every layer
   --workload search   1e6 unit vectors at d = 1536 or 200 (--search-d), b in
                       {2, 4} (--bits): quantize the database, then score 1000
                       queries against all of it and keep the top 10
@@ -51,7 +54,8 @@ def parse():
     ap.add_argument("--fill-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--workload", default="decode", choices=["decode", "long", "batched", "search"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "long", "batched", "search", "attn_out"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -102,7 +106,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload != "decode":
-        out = {"long": run_long, "batched": run_batched, "search": run_search}[args.workload](args)
+        out = {"long": run_long, "batched": run_batched, "search": run_search,
+               "attn_out": run_attn_out}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     dev = "cuda"
@@ -441,6 +446,51 @@ def run_batched(args):
                   "logit_hbm_frac": alg / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "chunk_quantize_ms": q_ms,
                   "chunk_quantize_vec_per_s": 2 * n_kv * chunk * batch / (q_ms * 1e-3)})
+
+
+def run_attn_out(args):
+    """tq_attn_output over the packed values of 32 Llama-shaped layer caches
+    (8 KV heads x 32768 tokens, b = 4), one launch pair for all layers."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d, b, n_kv, n_q, n_tok, L = "cuda", 128, 4, 8, 32, 32768, args.layers
+    stream = torch.cuda.current_stream()
+    ctx = _common(args, d, b)
+    rw = tq.tq_record_words(d, b)
+    vp = torch.zeros((n_kv * L * n_tok, rw), dtype=torch.int32, device=dev)
+    vn = torch.zeros((n_kv * L * n_tok, 2), dtype=torch.int16, device=dev)
+    Vx = torch.empty((n_kv, L * n_tok, d), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        Vx[:, l * n_tok:(l + 1) * n_tok] = workloads.llama(dev, seed=l, n_tok=n_tok)["V"]
+    tq.tq_quantize_kv(ctx, Vx, vp, vn)
+    del Vx
+    g = workloads.gen(0, workloads.STREAM_Q, dev)
+    p = torch.softmax(torch.randn((n_q, L * n_tok), generator=g, device=dev).view(n_q, L, n_tok),
+                      dim=2).view(n_q, L * n_tok).contiguous()
+    seq_start = torch.arange(L, dtype=torch.int64, device=dev) * n_tok
+    seq_len = torch.full((L,), n_tok, dtype=torch.int32, device=dev)
+    out = torch.empty((L, n_q, d), device=dev)
+    ws = tq.workspace(tq.tq_attn_output_workspace_bytes(ctx, L, n_q, n_kv, n_tok), dev)
+
+    def run():
+        tq.tq_attn_output(ctx, p, L * n_tok, L, n_q, vp, vn, n_kv, L * n_tok, seq_start, seq_len,
+                          n_tok, out, n_q * d, ws)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    ms, med = _timed(run, max(5, min(args.steps, 50)), stream)
+    rec = n_kv * L * n_tok
+    alg = rec * (b * d // 8 + 4) + n_q * L * n_tok * 4           # values + weights read
+    ctx.close()
+    return _line(args, "attention output from packed values: values/sec", rec / (ms * 1e-3),
+                 "values/s",
+                 {"workload": "llama-3.1-8b decode layer values: 8 kv / 32 q heads, d=128, "
+                              "32768 tokens, b=4; 32 layer caches per launch"},
+                 {"dtype": "f32", "ms_mean": ms, "ms_median": med,
+                  "GB_per_s": alg / (ms * 1e-3) / 1e9,
+                  "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "alg_bytes_per_call": alg})
 
 
 def run_search(args):

@@ -55,7 +55,9 @@ __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   uint32_t* words = sm;                          // [chunk][RW]
   float* wts = (float*)(words + a.chunk * RW);   // [chunk][8]: p nu (4 heads), p nu gamma (4)
 
+  __shared__ float ctab[kMaxK];
   const int tid = threadIdx.x;
+  if (tid < kMaxK) ctab[tid] = a.cent[tid];
   const int chunk_i = blockIdx.x;
   const int h = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
   const int bi = blockIdx.z;
@@ -103,21 +105,20 @@ __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
         if (j >= a.d) continue;
         const uint32_t* gw = rw + (j >> 5) * NB;
         const int bit = j & 31;
-        int idx = 0;
+        uint32_t idx = 0;
 #pragma unroll
-        for (int q = 0; q < NB - 1; ++q) idx |= (int)((gw[q] >> bit) & 1u) << q;
-        float c = a.cent[0];
-#pragma unroll
-        for (int m = 1; m < (1 << (NB - 1)); ++m) c = (idx == m) ? a.cent[m] : c;
-        const bool sp = (gw[NB - 1] >> bit) & 1u;
+        for (int q = 0; q < NB - 1; ++q) idx |= __builtin_amdgcn_ubfe(gw[q], bit, 1) << q;
+        const float c = ctab[idx];
+        // +1.0 for a set sign bit, -1.0 otherwise
+        const float sg = __uint_as_float(0xbf800000u ^ (__builtin_amdgcn_ubfe(gw[NB - 1], bit, 1) << 31));
         ar[k][0] = fmaf(w1.x, c, ar[k][0]);
         ar[k][1] = fmaf(w1.y, c, ar[k][1]);
         ar[k][2] = fmaf(w1.z, c, ar[k][2]);
         ar[k][3] = fmaf(w1.w, c, ar[k][3]);
-        as[k][0] += sp ? w2.x : -w2.x;
-        as[k][1] += sp ? w2.y : -w2.y;
-        as[k][2] += sp ? w2.z : -w2.z;
-        as[k][3] += sp ? w2.w : -w2.w;
+        as[k][0] = fmaf(w2.x, sg, as[k][0]);
+        as[k][1] = fmaf(w2.y, sg, as[k][1]);
+        as[k][2] = fmaf(w2.z, sg, as[k][2]);
+        as[k][3] = fmaf(w2.w, sg, as[k][3]);
       }
     }
   }
