@@ -253,6 +253,34 @@ TQ_API tq_status tq_attn_output(const tq_ctx* ctx, const float* p, int64_t p_str
                                 int64_t out_stride_batch, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Workspace for tq_attn_decode, in bytes (0 for invalid sizes). */
+TQ_API size_t tq_attn_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch,
+                                             int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t max_seq_len);
+
+/* Fused decode attention over packed keys and values (turboquant.net
+ * pseudo-code "integrate into Transformer attention": keys and values stored
+ * quantized, inner products estimated with QJL):
+ *   out[bi*out_stride_batch + hq*d + i] =
+ *       sum_t softmax_t(scale * est(q[bi, hq], key (hq/G, bi, t)))
+ *             * dequant(value (hq/G, bi, t))_i,
+ * in one pass over keys and values (chunks of tokens: logits, running
+ * softmax statistics and the value sums stay on chip; the chunks are combined
+ * with log-sum-exp rescaling).  Key and value records of (kv head h, sequence
+ * bi, token t) are both at h*kv_stride_head + seq_start[bi] + t.  Other
+ * arguments as for tq_attn_logits and tq_attn_output; an empty sequence gets
+ * a zero output.  workspace: at least tq_attn_decode_workspace_bytes(),
+ * 16-byte aligned; overwritten.  Errors as for tq_attn_logits. */
+TQ_API tq_status tq_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch,
+                                int32_t n_q_heads, int64_t q_stride_batch,
+                                const uint32_t* k_planes, const uint16_t* k_norms,
+                                const uint32_t* v_planes, const uint16_t* v_norms,
+                                int32_t n_kv_heads, int64_t kv_stride_head,
+                                const int64_t* seq_start, const int32_t* seq_len,
+                                int32_t max_seq_len, float scale, float* out,
+                                int64_t out_stride_batch, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Workspace for tq_search_topk, in bytes. */
 TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db,
                                         int32_t k);

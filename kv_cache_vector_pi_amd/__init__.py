@@ -30,7 +30,7 @@ EXPORTS = [
     "tq_ctx_bits", "tq_quantize_kv", "tq_dequantize", "tq_attn_logits_workspace_bytes",
     "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
-    "tq_attn_output",
+    "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
 ]
 
 
@@ -78,6 +78,9 @@ _sig("tq_attn_logits_prepared", _i32, [_P, _P, _sz, _i32, _i32, _P, _P, _i32, _i
 _sig("tq_attn_output_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32])
 _sig("tq_attn_output", _i32, [_P, _P, _i64, _i32, _i32, _P, _P, _i32, _i64, _P, _P, _i32, _P, _i64,
                               _P, _sz, _P])
+_sig("tq_attn_decode_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32])
+_sig("tq_attn_decode", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _i32, _i64, _P, _P, _i32,
+                              _f32, _P, _i64, _P, _sz, _P])
 _sig("tq_search_workspace_bytes", _sz, [_P, _i64, _i64, _i32])
 _sig("tq_search_topk", _i32, [_P, _P, _i64, _P, _P, _i64, _i32, _P, _P, _P, _sz, _P])
 
@@ -279,6 +282,23 @@ def tq_attn_output(ctx, p, p_stride_head, batch, n_q_heads, planes, norms, n_kv_
                              _ptr(seq_len), max_seq_len, _ptr(out), out_stride_batch,
                              _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "tq_attn_output")
+
+
+def tq_attn_decode_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len):
+    return _lib.tq_attn_decode_workspace_bytes(ctx.handle, batch, n_q_heads, n_kv_heads,
+                                               max_seq_len)
+
+
+def tq_attn_decode(ctx, q, batch, n_q_heads, q_stride_batch, k_planes, k_norms, v_planes,
+                   v_norms, n_kv_heads, kv_stride_head, seq_start, seq_len, max_seq_len, scale,
+                   out, out_stride_batch, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_attn_decode(ctx.handle, _ptr(q), batch, n_q_heads, q_stride_batch,
+                             _ptr(k_planes), _ptr(k_norms), _ptr(v_planes), _ptr(v_norms),
+                             n_kv_heads, kv_stride_head, _ptr(seq_start), _ptr(seq_len),
+                             max_seq_len, float(scale), _ptr(out), out_stride_batch,
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "tq_attn_decode")
 
 
 def tq_search_workspace_bytes(ctx, n_queries, n_db, k):

@@ -20,6 +20,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "tq_dev.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -81,80 +82,10 @@ __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   }
   __syncthreads();
 
-  // ---- accumulate ------------------------------------------------------------
-  // coordinate lanes NL = min(Dp, 256) (coordinates lc + 256 k), token groups TT
-  const int NL = min(a.Dp, 256);
-  const int TT = 256 / NL;
-  const int lc = tid % NL, tg = tid / NL;
-  constexpr int kMaxCpt = 8;                     // Dp <= 2048
-  const int cpt = (a.Dp + 255) / 256;
-  float ar[kMaxCpt][4], as[kMaxCpt][4];
-#pragma unroll
-  for (int k = 0; k < kMaxCpt; ++k)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) ar[k][hh] = as[k][hh] = 0.f;
-  if (tg < TT) {
-    for (int t = tg; t < nt; t += TT) {
-      const uint32_t* rw = words + t * RW;
-      const float4 w1 = *(const float4*)(wts + 8 * t);
-      const float4 w2 = *(const float4*)(wts + 8 * t + 4);
-#pragma unroll
-      for (int k = 0; k < kMaxCpt; ++k) {
-        if (k >= cpt) break;
-        const int j = lc + 256 * k;
-        if (j >= a.d) continue;
-        const uint32_t* gw = rw + (j >> 5) * NB;
-        const int bit = j & 31;
-        uint32_t idx = 0;
-#pragma unroll
-        for (int q = 0; q < NB - 1; ++q) idx |= __builtin_amdgcn_ubfe(gw[q], bit, 1) << q;
-        const float c = ctab[idx];
-        // +1.0 for a set sign bit, -1.0 otherwise
-        const float sg = __uint_as_float(0xbf800000u ^ (__builtin_amdgcn_ubfe(gw[NB - 1], bit, 1) << 31));
-        ar[k][0] = fmaf(w1.x, c, ar[k][0]);
-        ar[k][1] = fmaf(w1.y, c, ar[k][1]);
-        ar[k][2] = fmaf(w1.z, c, ar[k][2]);
-        ar[k][3] = fmaf(w1.w, c, ar[k][3]);
-        as[k][0] = fmaf(w2.x, sg, as[k][0]);
-        as[k][1] = fmaf(w2.y, sg, as[k][1]);
-        as[k][2] = fmaf(w2.z, sg, as[k][2]);
-        as[k][3] = fmaf(w2.w, sg, as[k][3]);
-      }
-    }
-  }
-  __syncthreads();          // staging area is reused for the token-group sums
-
-  // ---- reduce the token groups and write the chunk partials ------------------
-  float* red = (float*)sm;                       // [TT][8][NL] (TT > 1 only when cpt == 1)
+  // ---- accumulate and write the chunk partials ---------------------------------
   float* dst = a.part +
       ((((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk + chunk_i) * 8 * (int64_t)a.Dp;
-  if (TT > 1) {
-    if (tg < TT)
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        red[(tg * 8 + hh) * NL + lc] = ar[0][hh];
-        red[(tg * 8 + 4 + hh) * NL + lc] = as[0][hh];
-      }
-    __syncthreads();
-    for (int i = tid; i < 8 * NL; i += 256) {
-      float s = 0.f;
-      for (int g = 0; g < TT; ++g) s += red[g * 8 * NL + i];
-      const int sel = i / NL, j = i % NL;
-      dst[sel * a.Dp + j] = s;                   // sel: 0..3 rot heads, 4..7 sketch heads
-    }
-  } else if (tg < TT) {
-#pragma unroll
-    for (int k = 0; k < kMaxCpt; ++k) {
-      if (k >= cpt) break;
-      const int j = lc + 256 * k;
-      if (j >= a.Dp) continue;
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        dst[hh * a.Dp + j] = ar[k][hh];
-        dst[(4 + hh) * a.Dp + j] = as[k][hh];
-      }
-    }
-  }
+  dev::vacc_block<NB>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)sm, dst);
 }
 
 struct VFinArgs {

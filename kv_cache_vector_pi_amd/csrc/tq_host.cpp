@@ -611,6 +611,51 @@ TQ_API tq_status tq_attn_output(const tq_ctx* ctx, const float* p, int64_t p_str
   return ok();
 }
 
+TQ_API size_t tq_attn_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch,
+                                             int32_t n_q_heads, int32_t n_kv_heads,
+                                             int32_t max_seq_len) {
+  if (!ctx || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads ||
+      max_seq_len < 0)
+    return 0;
+  return tq::decode_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len);
+}
+
+TQ_API tq_status tq_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch,
+                                int32_t n_q_heads, int64_t q_stride_batch,
+                                const uint32_t* k_planes, const uint16_t* k_norms,
+                                const uint32_t* v_planes, const uint16_t* v_norms,
+                                int32_t n_kv_heads, int64_t kv_stride_head,
+                                const int64_t* seq_start, const int32_t* seq_len,
+                                int32_t max_seq_len, float scale, float* out,
+                                int64_t out_stride_batch, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: ctx is NULL");
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: batch=%d n_q=%d n_kv=%d max_seq_len=%d",
+                batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (batch == 0) return ok();
+  if (!q || !k_planes || !k_norms || !v_planes || !v_norms || !seq_start || !seq_len || !out ||
+      !workspace)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: NULL pointer");
+  if ((batch > 1 && q_stride_batch < (int64_t)n_q_heads * ctx->d) || kv_stride_head < 0 ||
+      (batch > 1 && out_stride_batch < (int64_t)n_q_heads * ctx->d))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: bad stride");
+  if (!aligned(k_planes, 16) || !aligned(v_planes, 16) || !aligned(k_norms, 4) ||
+      !aligned(v_norms, 4) || !aligned(workspace, 16) || !aligned(q, 4) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: misaligned pointer");
+  const size_t need = tq::decode_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "tq_attn_decode: workspace %zu < %zu bytes", workspace_bytes,
+                need);
+  hipError_t e = tq::launch_attn_decode(ctx, q, batch, n_q_heads, q_stride_batch, k_planes,
+                                        k_norms, v_planes, v_norms, n_kv_heads, kv_stride_head,
+                                        seq_start, seq_len, max_seq_len, scale, out,
+                                        out_stride_batch, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_decode: launch");
+  return ok();
+}
+
 TQ_API tq_status tq_search_topk(const tq_ctx* ctx, const float* queries, int64_t n_queries,
                                 const uint32_t* planes, const uint16_t* norms, int64_t n_db,
                                 int32_t k, int64_t* out_idx, float* out_score, void* workspace,

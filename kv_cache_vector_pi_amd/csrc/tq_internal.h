@@ -88,6 +88,16 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
                               int64_t values_stride_head, const int64_t* seq_start,
                               const int32_t* seq_len, int32_t max_seq_len, float* out,
                               int64_t out_stride_batch, void* workspace, hipStream_t stream);
+size_t decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
+                              int32_t n_kv_heads, int32_t max_seq_len);
+hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,
+                              int64_t q_stride_batch, const uint32_t* k_planes,
+                              const uint16_t* k_norms, const uint32_t* v_planes,
+                              const uint16_t* v_norms, int32_t n_kv_heads,
+                              int64_t kv_stride_head, const int64_t* seq_start,
+                              const int32_t* seq_len, int32_t max_seq_len, float scale,
+                              float* out, int64_t out_stride_batch, void* workspace,
+                              hipStream_t stream);
 hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const uint16_t* norms,
                              int64_t n, float* out, int64_t out_ld, hipStream_t stream);
 

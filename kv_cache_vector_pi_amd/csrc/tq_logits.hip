@@ -26,26 +26,20 @@
 #include <algorithm>
 #include <cmath>
 
+#include "tq_dev.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-constexpr int kTile = 16;          // key tokens per MFMA tile
-constexpr int kWaves = 4;          // waves per workgroup
-
-__host__ __device__ inline int n_calls(int b) { return 2 * (1 << (b - 2)) + 2; }   // MFMA calls per word step
-__host__ __device__ inline int n_ws(int W) { return (W + 3) / 4; }                  // word steps of 4 words
-
-// Workspace layout for one (batch, kv head, row block of 4 q heads):
-//   int4 frag[n_ws][n_calls][64 lanes]   A operands (16 int8 each)
-//   float4 consts[4]                      per q head: mse scale, qjl scale,
-//                                         mse offset, qjl offset
-__host__ __device__ inline size_t rb_bytes(int W, int b) {
-  return (size_t)n_ws(W) * n_calls(b) * 64 * 16 + 4 * 16;
-}
+using dev::v4i;
+using dev::kTile;
+using dev::kWaves;
+using dev::n_calls;
+using dev::n_ws;
+using dev::rb_bytes;
+using dev::load_group;
+using dev::bit_lanes;
 
 struct PrepArgs {
   const float* q;          // [batch][n_q][d], batch stride q_stride_batch
@@ -244,30 +238,6 @@ struct AttnArgs {
   float scale, alpha;
   int mask[kMaxVec];
 };
-
-template <int NB>
-__device__ inline void load_group(const uint32_t* p, uint32_t (&w)[NB]) {
-  if constexpr (NB == 4) {
-    uint4 v = *(const uint4*)p;
-    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  } else if constexpr (NB == 2) {
-    uint2 v = *(const uint2*)p;
-    w[0] = v.x; w[1] = v.y;
-  } else {
-    for (int i = 0; i < NB; ++i) w[i] = p[i];
-  }
-}
-
-// masked int8 lanes of a plane word for shifts 4*half .. 4*half+3
-__device__ inline v4i bit_lanes(uint32_t u, int half) {
-  const uint32_t m = 0x01010101u << (4 * half);
-  v4i r;
-  r[0] = (int)(u & m);
-  r[1] = (int)(u & (m << 1));
-  r[2] = (int)(u & (m << 2));
-  r[3] = (int)(u & (m << 3));
-  return r;
-}
 
 // Logit stream.  grid = (token chunks, kv heads, batch); each wave owns
 // tiles_per_wave tiles of 16 tokens of one (batch, kv head) sequence.

@@ -214,6 +214,43 @@ def test_llama_attn_output(orc):
     ctx.close()
 
 
+def test_llama_decode_fused(orc):
+    """Fused decode attention over the Llama-shaped layer (8 KV heads x 32768
+    tokens, b = 4): sampled query heads against softmax(oracle logits) @
+    oracle-dequantized values on the GPU's records."""
+    d, b, n_kv, n_q, n_tok = 128, 4, 8, 32, 32768
+    say("llama fused decode")
+    ctx, pi, s, c = make_ctx(orc, d, b)
+    wl = workloads.llama(DEV, n_tok=n_tok)
+    rw = tq.tq_record_words(d, b)
+    kp = torch.zeros((n_kv * n_tok, rw), dtype=torch.int32, device=DEV)
+    kn = torch.zeros((n_kv * n_tok, 2), dtype=torch.int16, device=DEV)
+    vp, vn = torch.zeros_like(kp), torch.zeros_like(kn)
+    tq.tq_quantize_kv(ctx, wl["K"], kp, kn)
+    tq.tq_quantize_kv(ctx, wl["V"], vp, vn)
+    ss = torch.zeros(1, dtype=torch.int64, device=DEV)
+    sl = torch.full((1,), n_tok, dtype=torch.int32, device=DEV)
+    out = torch.empty((1, n_q, d), device=DEV)
+    ws = tq.workspace(tq.tq_attn_decode_workspace_bytes(ctx, 1, n_q, n_kv, n_tok), DEV)
+    scale = 1.0 / math.sqrt(d)
+    tq.tq_attn_decode(ctx, wl["q"], 1, n_q, n_q * d, kp, kn, vp, vn, n_kv, n_tok, ss, sl, n_tok,
+                      scale, out, n_q * d, ws)
+    torch.cuda.synchronize()
+    for hq in [0, 13, 31]:
+        h = hq // (n_q // n_kv)
+        rows = np.arange(h * n_tok, (h + 1) * n_tok)
+        KP, KN = np_records(kp, kn, rows)
+        VP, VN = np_records(vp, vn, rows)
+        lg = orc.estimate(d, b, pi, s, c, wl["q"][hq:hq + 1].double().cpu().numpy(), KP, KN,
+                          scale=scale)[0]
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        ref = p @ orc.dequantize(d, b, pi, s, c, VP, VN)
+        got = out[0, hq].cpu().numpy()
+        assert rel_err_rows(got[None], ref[None]) < TOL, (hq, rel_err_rows(got[None], ref[None]))
+    ctx.close()
+
+
 @pytest.mark.parametrize("d,b", [(1536, 2), (1536, 4), (200, 2), (200, 4)])
 def test_vector_search_1m(orc, d, b):
     k = 10

@@ -329,6 +329,69 @@ def test_attn_output_rejects_bad_arguments(orc):
         tq.tq_attn_output(ctx, p, 16, 1, 4, P, N, 1, 16, ss, sl, 16, out, 4 * d, ws[:16])
 
 
+# ---------------------------------------------------- fused decode attention
+def softmax_rows(x):
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("d,b,n_q,n_kv,lens", [
+    (128, 3, 16, 1, [1024]),                  # tiny layout, G = 16
+    (128, 4, 32, 8, [1000, 37, 513]),         # GQA 4, ragged batch
+    (128, 2, 8, 8, [300, 1]),                 # G = 1, a one-token sequence
+    (128, 4, 6, 2, [700]),                    # G = 3
+    (200, 4, 8, 2, [333, 70]),
+    (1536, 2, 4, 1, [150]),
+])
+def test_attn_decode_parity(orc, d, b, n_q, n_kv, lens):
+    say("attn decode", d, b, n_q, n_kv, lens)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    total = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).tolist()
+    xk = workloads.normal((n_kv, total, d), 12, 10, "cpu").double().numpy()
+    xv = workloads.normal((n_kv, total, d), 12, 11, "cpu").double().numpy()
+    q = workloads.normal((len(lens), n_q, d), 12, 12, "cpu").numpy()
+    rk = [orc.quantize(d, b, pi, s, c, xk[h]) for h in range(n_kv)]
+    rv = [orc.quantize(d, b, pi, s, c, xv[h]) for h in range(n_kv)]
+    cat = lambda rs, key: np.concatenate([r[key] for r in rs])
+    KP = torch.as_tensor(cat(rk, "planes").view(np.int32), device=DEV)
+    KN = torch.as_tensor(cat(rk, "norms").view(np.int16), device=DEV)
+    VP = torch.as_tensor(cat(rv, "planes").view(np.int32), device=DEV)
+    VN = torch.as_tensor(cat(rv, "norms").view(np.int16), device=DEV)
+    batch, scale = len(lens), 1.0 / np.sqrt(d)
+    ss = torch.as_tensor(np.asarray(starts, np.int64), device=DEV)
+    sl = torch.as_tensor(np.asarray(lens, np.int32), device=DEV)
+    out = torch.full((batch, n_q, d), float("nan"), device=DEV)
+    ws = tq.workspace(tq.tq_attn_decode_workspace_bytes(ctx, batch, n_q, n_kv, max(lens)))
+    tq.tq_attn_decode(ctx, torch.as_tensor(q, device=DEV), batch, n_q, n_q * d, KP, KN, VP, VN,
+                      n_kv, total, ss, sl, max(lens), scale, out, n_q * d, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    G = n_q // n_kv
+    deq = [orc.dequantize(d, b, pi, s, c, r["planes"], r["norms"]) for r in rv]
+    for bi, (st, ln) in enumerate(zip(starts, lens)):
+        for h in range(n_kv):
+            lg = orc.estimate(d, b, pi, s, c, q[bi, h * G:(h + 1) * G].astype(np.float64),
+                              rk[h]["planes"][st:st + ln], rk[h]["norms"][st:st + ln], scale=scale)
+            ref = softmax_rows(lg) @ deq[h][st:st + ln]
+            assert rel_err_rows(got[bi, h * G:(h + 1) * G], ref) < TOL, (bi, h)
+
+
+def test_attn_decode_empty_sequence_is_zero(orc):
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    P, N = workloads.random_records(64, tq.tq_record_words(d, b), 3, DEV)
+    q = workloads.normal((2, 4, d), 3, 12, DEV)
+    ss = torch.tensor([0, 10], dtype=torch.int64, device=DEV)
+    sl = torch.tensor([0, 20], dtype=torch.int32, device=DEV)
+    out = torch.full((2, 4, d), float("nan"), device=DEV)
+    ws = tq.workspace(tq.tq_attn_decode_workspace_bytes(ctx, 2, 4, 1, 20))
+    tq.tq_attn_decode(ctx, q, 2, 4, 4 * d, P, N, P, N, 1, 64, ss, sl, 20, 1.0, out, 4 * d, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.isfinite(out[1]).all()
+
+
 # ---------------------------------------------------------------- dequantize
 @pytest.mark.parametrize("d,b,n", [(128, 3, 1024), (128, 4, 100), (200, 2, 130), (1536, 4, 20),
                                    (64, 2, 70)])
