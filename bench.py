@@ -24,6 +24,8 @@ Other workloads (each prints its own JSON line; the default is the one above):
   --workload attn_out the value side of the Llama-shaped decode layer over 32
                       layer caches: tq_attn_output (weights from a softmax of
                       seeded logits) over all packed values of every layer
+  --workload decode_fused  fused decode attention (tq_attn_decode: logits,
+                      softmax, value sums) over the same 32 layer caches
   --workload search   1e6 unit vectors at d = 1536 or 200 (--search-d), b in
                       {2, 4} (--bits): quantize the database, then score 1000
                       queries against all of it and keep the top 10
@@ -55,7 +57,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "long", "batched", "search", "attn_out"])
+                    choices=["decode", "long", "batched", "search", "attn_out", "decode_fused"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -107,7 +109,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload != "decode":
         out = {"long": run_long, "batched": run_batched, "search": run_search,
-               "attn_out": run_attn_out}[args.workload](args)
+               "attn_out": run_attn_out, "decode_fused": run_decode_fused}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     dev = "cuda"
@@ -488,6 +490,50 @@ def run_attn_out(args):
                  {"workload": "llama-3.1-8b decode layer values: 8 kv / 32 q heads, d=128, "
                               "32768 tokens, b=4; 32 layer caches per launch"},
                  {"dtype": "f32", "ms_mean": ms, "ms_median": med,
+                  "GB_per_s": alg / (ms * 1e-3) / 1e9,
+                  "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "alg_bytes_per_call": alg})
+
+
+def run_decode_fused(args):
+    """tq_attn_decode over 32 Llama-shaped layer caches (8 KV heads x 32768
+    tokens, b = 4, K and V packed), one call for all layers."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d, b, n_kv, n_q, n_tok, L = "cuda", 128, 4, 8, 32, 32768, args.layers
+    stream = torch.cuda.current_stream()
+    ctx = _common(args, d, b)
+    rw = tq.tq_record_words(d, b)
+    kp = torch.zeros((n_kv * L * n_tok, rw), dtype=torch.int32, device=dev)
+    kn = torch.zeros((n_kv * L * n_tok, 2), dtype=torch.int16, device=dev)
+    vp, vn = torch.zeros_like(kp), torch.zeros_like(kn)
+    for l in range(L):
+        wl = workloads.llama(dev, seed=l, n_tok=n_tok)
+        tq.tq_quantize_kv(ctx, wl["K"], kp, kn, dst_stride_head=L * n_tok, dst_token0=l * n_tok)
+        tq.tq_quantize_kv(ctx, wl["V"], vp, vn, dst_stride_head=L * n_tok, dst_token0=l * n_tok)
+        del wl
+    q_all = torch.stack([workloads.normal((n_q, d), l, workloads.STREAM_Q, dev) for l in range(L)])
+    seq_start = torch.arange(L, dtype=torch.int64, device=dev) * n_tok
+    seq_len = torch.full((L,), n_tok, dtype=torch.int32, device=dev)
+    out = torch.empty((L, n_q, d), device=dev)
+    ws = tq.workspace(tq.tq_attn_decode_workspace_bytes(ctx, L, n_q, n_kv, n_tok), dev)
+
+    def run():
+        tq.tq_attn_decode(ctx, q_all, L, n_q, n_q * d, kp, kn, vp, vn, n_kv, L * n_tok, seq_start,
+                          seq_len, n_tok, 1.0 / math.sqrt(d), out, n_q * d, ws)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    ms, med = _timed(run, max(5, min(args.steps, 50)), stream)
+    rec = n_kv * L * n_tok
+    alg = 2 * rec * (b * d // 8 + 4)                 # keys and values read once
+    ctx.close()
+    return _line(args, "fused decode attention from packed K/V: tokens/sec (all heads)",
+                 L * n_tok / (ms * 1e-3), "tokens/s",
+                 {"workload": "llama-3.1-8b decode layer: 8 kv / 32 q heads, d=128, 32768 "
+                              "cached tokens, b=4 K and V; 32 layer caches per call"},
+                 {"dtype": "int8-mfma/fp32", "ms_mean": ms, "ms_median": med,
                   "GB_per_s": alg / (ms * 1e-3) / 1e9,
                   "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "alg_bytes_per_call": alg})
