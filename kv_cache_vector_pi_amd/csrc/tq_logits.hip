@@ -373,27 +373,35 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
   const int chunk = a.tiles_per_wave * kTile;
+  const size_t rbb = (size_t)NC * 64 * 16 + 64;
+  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
+  // the 4 waves share (sequence, kv head): the prepared operands are read
+  // from memory once per workgroup
+  __shared__ v4i Asm[NC * 64];
+  for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
+  __syncthreads();
   const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
   if (t_begin >= len) return;
   const int t_end = min(len, t_begin + chunk);
   const int n_tok = t_end - t_begin;
-  const size_t rbb = (size_t)NC * 64 * 16 + 64;
-  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
   const int64_t rec_first = (int64_t)h * a.keys_stride_head + start + t_begin;
   const uint32_t rec_bytes = (uint32_t)(a.W * NB * 4);
   const rsrc_t rp = make_rsrc(a.planes + rec_first * a.W * NB, (uint32_t)n_tok * rec_bytes);
   const rsrc_t rn = make_rsrc(a.norms + rec_first, (uint32_t)n_tok * 4u);
   // word group g of this lane's token; groups beyond d read out of range (0)
   const uint32_t goff = g < a.W ? (uint32_t)(g * NB * 4) : 0x80000000u;
-  const bool store_head = g < a.G;
-  float* out = a.logits + (int64_t)(h * a.G + g) * a.logits_stride_head + start;
+  // stores: lane half hf (0/1) writes 32 consecutive tokens of head gs + hf
+  // (gs = 0 for the first store of a tile pair, 2 for the second)
+  const int hf = lane >> 5, ts = lane & 31;
+  float* out_a = a.logits + (int64_t)(h * a.G + hf) * a.logits_stride_head + start;
+  float* out_b = a.logits + (int64_t)(h * a.G + 2 + hf) * a.logits_stride_head + start;
+  const bool head_a = hf < a.G, head_b = 2 + hf < a.G;
+  // source lanes (head g, token n) of the values this lane stores
+  const int src_a = 16 * hf + (ts & 15), src_b = 32 + src_a;
 
   v4i A[NC];
-  {
-    const v4i* fr = (const v4i*)wsb;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) A[c] = fr[c * 64 + lane];
-  }
+  for (int c = 0; c < NC; ++c) A[c] = Asm[c * 64 + lane];
   // per-head constants with the logit scale and the QJL factor folded in:
   // logit = nu * (vm X + Z + gamma (vq Y + W))
   const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
@@ -419,13 +427,23 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
     const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
     return fmaf((float)hi, 65536.f, (float)lo);
   };
-  auto finish = [&](v4i am, v4i aq, uint32_t nrm, int tloc) {
-    if (tloc < n_tok && store_head) {
-      const float ms = fmaf(limbs(am), cX, cZ);
-      const float qs = fmaf(limbs(aq), cY, cW);
-      const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
-      const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
-      __builtin_nontemporal_store(nu * fmaf(ga, qs, ms), &out[t_begin + tloc]);   // streamed, never re-read
+  auto logit = [&](v4i am, v4i aq, uint32_t nrm) {
+    const float ms = fmaf(limbs(am), cX, cZ);
+    const float qs = fmaf(limbs(aq), cY, cW);
+    const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
+    const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
+    return nu * fmaf(ga, qs, ms);
+  };
+  // tile pair at local token tl: lane (g, n) holds head g of tokens tl + n
+  // (v0) and tl + 16 + n (v1); permuted so each store instruction writes two
+  // whole 32-token rows (128 bytes each), streamed (never re-read)
+  auto finish2 = [&](float v0, float v1, int tl) {
+    const float a0 = __shfl(v0, src_a), a1 = __shfl(v1, src_a);
+    const float b0 = __shfl(v0, src_b), b1 = __shfl(v1, src_b);
+    const int tloc = tl + ts;
+    if (tloc < n_tok) {
+      if (head_a) __builtin_nontemporal_store(ts < 16 ? a0 : a1, &out_a[t_begin + tloc]);
+      if (head_b) __builtin_nontemporal_store(ts < 16 ? b0 : b1, &out_b[t_begin + tloc]);
     }
   };
   // two tiles at a time: their MFMA chains interleave, hiding each other's
@@ -454,8 +472,7 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
       aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s1, 0), aq1, 0, 0, 0);
       aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
       aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
-      finish(am0, aq0, gr.nr[u], tl + kTile * u + n);
-      finish(am1, aq1, gr.nr[u + 1], tl + kTile * (u + 1) + n);
+      finish2(logit(am0, aq0, gr.nr[u]), logit(am1, aq1, gr.nr[u + 1]), tl + kTile * u);
     }
   };
   Grp g0, g1;
