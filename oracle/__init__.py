@@ -61,6 +61,12 @@ def lib():
         L.orc_dequantize.argtypes = [i32, i32, P, P, P, i64, P, P, P, i64]
         L.orc_estimate.restype = None
         L.orc_estimate.argtypes = [i32, i32, P, P, P, i64, P, i64, i64, P, P, P, P, dbl, P]
+        L.orc_quantize_mse.restype = None
+        L.orc_quantize_mse.argtypes = [i32, i32, P, P, i64, P, i64, P, P, P]
+        L.orc_dequantize_mse.restype = None
+        L.orc_dequantize_mse.argtypes = [i32, i32, P, P, i64, P, P, P, i64]
+        L.orc_estimate_mse.restype = None
+        L.orc_estimate_mse.argtypes = [i32, i32, P, P, i64, P, i64, i64, P, P, dbl, P]
         L.orc_topk.restype = None
         L.orc_topk.argtypes = [i64, i64, P, i32, P, P]
         L.orc_num_threads.restype = i32
@@ -193,6 +199,53 @@ def quantize(d, b, pi32, s32, cen32, x, margins=False):
                        _p(_c(cen32, np.float32)), n, _p(x), d, _p(planes), _p(norms),
                        _p(cm), _p(sm), _p(nu), _p(ga), _p(y))
     return out
+
+
+def quantize_mse(d, b, pi32, cen32, x, margins=False):
+    """MSE-only variant: b code planes, no QJL stage.  Returns dict with planes
+    (uint32 [n, W*b]), norms (uint16 [n, 2], gamma slot 0) and, with
+    margins=True, code_margin ([n, d])."""
+    x = _c(x, np.float64).reshape(-1, d)
+    n = x.shape[0]
+    planes = np.empty((n, record_words(d, b)), np.uint32)
+    norms = np.empty((n, 2), np.uint16)
+    cm = np.empty((n, d)) if margins else None
+    lib().orc_quantize_mse(d, b, _p(_c(pi32, np.float32)), _p(_c(cen32, np.float32)), n, _p(x), d,
+                           _p(planes), _p(norms), _p(cm))
+    out = {"planes": planes, "norms": norms}
+    if margins:
+        out["code_margin"] = cm
+    return out
+
+
+def dequantize_mse(d, b, pi32, cen32, planes, norms):
+    planes = _c(planes, np.uint32).reshape(-1, record_words(d, b))
+    norms = _c(norms, np.uint16).reshape(-1, 2)
+    n = planes.shape[0]
+    out = np.empty((n, d), np.float64)
+    lib().orc_dequantize_mse(d, b, _p(_c(pi32, np.float32)), _p(_c(cen32, np.float32)), n,
+                             _p(planes), _p(norms), _p(out), d)
+    return out
+
+
+def estimate_mse(d, b, pi32, cen32, q, planes, norms, scale=1.0):
+    """out[a, i] = scale * nu_i * <Pi q_a, c[idx_i]> (MSE-only records)."""
+    q = _c(q, np.float64).reshape(-1, d)
+    planes = _c(planes, np.uint32).reshape(-1, record_words(d, b))
+    norms = _c(norms, np.uint16).reshape(-1, 2)
+    nq, n = q.shape[0], planes.shape[0]
+    out = np.empty((nq, n), np.float64)
+    lib().orc_estimate_mse(d, b, _p(_c(pi32, np.float32)), _p(_c(cen32, np.float32)), nq, _p(q),
+                           d, n, _p(planes), _p(norms), float(scale), _p(out))
+    return out
+
+
+def unpack_codes_mse(d, b, planes):
+    """uint32 [n, W*b] MSE records -> idx int32 [n, d] (numpy, for tests)."""
+    planes = _c(planes, np.uint32).reshape(-1, (d + 31) // 32, b)
+    j = np.arange(d)
+    bits = (planes[:, j // 32, :] >> (j % 32)[None, :, None].astype(np.uint32)) & 1
+    return (bits.astype(np.int32) << np.arange(b)[None, None, :]).sum(axis=2).astype(np.int32)
 
 
 def dequantize(d, b, pi32, s32, cen32, planes, norms):

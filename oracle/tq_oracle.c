@@ -564,6 +564,121 @@ ORC_API void orc_estimate(int32_t d, int32_t b, const float* pi, const float* s,
 }
 
 /* ------------------------------------------------------------------------ */
+/* MSE-only variant ([P2] pseudo-code "quant" / "dequant" as printed: b-bit
+ * Lloyd-Max codes of the rotated coordinates, no QJL stage; [P1] notes that
+ * this stage alone biases inner products).  Record: W groups of b code-plane
+ * words (bit p of idx in word p), fp16 nu, and 0 in the gamma slot.
+ *   quantize:   nu = ||x||, y = Pi x / nu, idx_j = argmin_k |y_j - c_k|
+ *   dequantize: xt = nu16 * Pi^T c[idx]
+ *   estimate:   est(q, rec) = nu16 * <Pi q, c[idx]>                            */
+static void unpack_codes(int32_t d, int32_t b, const uint32_t* rec, int32_t* idx) {
+    for (int j = 0; j < d; ++j) {
+        int w = j / 32, bit = j % 32, v = 0;
+        for (int p = 0; p < b; ++p) v |= (int)((rec[w * b + p] >> bit) & 1u) << p;
+        idx[j] = v;
+    }
+}
+
+ORC_API void orc_quantize_mse(int32_t d, int32_t b, const float* pi, const float* cen, int64_t n,
+                              const double* x, int64_t ld, uint32_t* planes, uint16_t* norms,
+                              double* code_margin) {
+    int K = 1 << b;
+    int W = (d + 31) / 32;
+    double c[256], t[256];
+    for (int k = 0; k < K; ++k) c[k] = (double)cen[k];
+    for (int k = 0; k + 1 < K; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+#pragma omp parallel
+    {
+        double* y = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            const double* xi = x + i * ld;
+            double nu2 = 0.0;
+            for (int j = 0; j < d; ++j) nu2 += xi[j] * xi[j];
+            double nu = sqrt(nu2);
+            for (int jr = 0; jr < d; ++jr) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j)
+                    acc += (double)pi[(int64_t)jr * d + j] * ((nu > 0.0) ? xi[j] / nu : 0.0);
+                y[jr] = acc;
+            }
+            uint32_t* rec = planes + i * (int64_t)W * b;
+            memset(rec, 0, sizeof(uint32_t) * (size_t)W * b);
+            for (int j = 0; j < d; ++j) {
+                int best = 0;
+                double bd = fabs(y[j] - c[0]);
+                for (int k = 1; k < K; ++k) {
+                    double dk = fabs(y[j] - c[k]);
+                    if (dk < bd) { bd = dk; best = k; }
+                }
+                for (int p = 0; p < b; ++p)
+                    if ((best >> p) & 1) rec[(j / 32) * b + p] |= 1u << (j % 32);
+                if (code_margin) {
+                    double m = INFINITY;
+                    for (int k = 0; k + 1 < K; ++k) m = fmin(m, fabs(y[j] - t[k]));
+                    code_margin[i * d + j] = m;
+                }
+            }
+            norms[2 * i] = orc_f16_from_double(nu);
+            norms[2 * i + 1] = 0;
+        }
+        free(y);
+    }
+}
+
+ORC_API void orc_dequantize_mse(int32_t d, int32_t b, const float* pi, const float* cen,
+                                int64_t n, const uint32_t* planes, const uint16_t* norms,
+                                double* out, int64_t ld) {
+    int W = (d + 31) / 32;
+#pragma omp parallel
+    {
+        int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * d);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            unpack_codes(d, b, planes + i * (int64_t)W * b, idx);
+            double nu = orc_f16_to_double(norms[2 * i]);
+            for (int j = 0; j < d; ++j) {
+                double a1 = 0.0;
+                for (int jr = 0; jr < d; ++jr)
+                    a1 += (double)pi[(int64_t)jr * d + j] * (double)cen[idx[jr]];
+                out[i * ld + j] = nu * a1;
+            }
+        }
+        free(idx);
+    }
+}
+
+ORC_API void orc_estimate_mse(int32_t d, int32_t b, const float* pi, const float* cen,
+                              int64_t nq, const double* q, int64_t ldq, int64_t n,
+                              const uint32_t* planes, const uint16_t* norms, double scale,
+                              double* out) {
+    int W = (d + 31) / 32;
+    double* qr = (double*)malloc(sizeof(double) * (size_t)nq * d);
+    for (int64_t a = 0; a < nq; ++a)
+        for (int jr = 0; jr < d; ++jr) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j) acc += (double)pi[(int64_t)jr * d + j] * q[a * ldq + j];
+            qr[a * d + jr] = acc;
+        }
+#pragma omp parallel
+    {
+        int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * d);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            unpack_codes(d, b, planes + i * (int64_t)W * b, idx);
+            double nu = orc_f16_to_double(norms[2 * i]);
+            for (int64_t a = 0; a < nq; ++a) {
+                double m1 = 0.0;
+                for (int j = 0; j < d; ++j) m1 += qr[a * d + j] * (double)cen[idx[j]];
+                out[a * n + i] = scale * nu * m1;
+            }
+        }
+        free(idx);
+    }
+    free(qr);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Top-k over a score matrix ([P1] nearest-neighbour section; [P3] vector
  * search paragraph): for each query row, the k largest scores, ordered by
  * (score descending, index ascending).  scores[a * n + i]. */

@@ -242,3 +242,78 @@ def test_topk_matches_lexsort(orc):
         assert np.array_equal(idx[a], order) and np.array_equal(val[a], sc[a, order])
     idx, val = orc.topk(sc[:, :4], 6)
     assert np.all(idx[:, 4:] == -1)
+
+
+# ---------------------------------------------------------------- MSE-only mode
+# turboquant.net pseudo-code "quant" / "dequant": b-bit Lloyd-Max codes of the
+# rotated coordinates, no QJL stage.
+def mse_tables(orc, d, b, seed=0):
+    pi64, s64, pi32, s32 = orc.make_rotation(d, seed)
+    return pi32, orc.lloyd_max(d, b)[0].astype(np.float32)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_mse_mode_distortion(orc, b):
+    """Unit x (nu16 = 1 exactly): E||x - dequant(x)||^2 equals the Lloyd-Max
+    distortion of the b-bit codebook, decreasing in b; at b = 1 it is the
+    closed form 1 - d E|X|^2 with E|X| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))."""
+    from scipy.special import gammaln
+    d = 128
+    pi32, c = mse_tables(orc, d, b)
+    D = orc.lloyd_max(d, b)[1]
+    x = unit_rows(np.random.default_rng(30 + b), 20000, d)
+    rec = orc.quantize_mse(d, b, pi32, c, x)
+    assert np.all(rec["norms"][:, 0] == np.float16(1.0).view(np.uint16))
+    assert np.all(rec["norms"][:, 1] == 0)
+    xt = orc.dequantize_mse(d, b, pi32, c, rec["planes"], rec["norms"])
+    e2 = np.sum((x - xt) ** 2, axis=1)
+    assert abs(e2.mean() - D) < 4 * e2.std() / np.sqrt(e2.size) + 1e-6
+    if b == 1:
+        eabs = np.exp(gammaln(d / 2) - 0.5 * np.log(np.pi) - gammaln((d + 1) / 2))
+        assert abs(D - (1 - d * eabs ** 2)) < 1e-9
+    if b > 1:
+        assert D < orc.lloyd_max(d, b - 1)[1]
+
+
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_mse_codes_equal_two_stage_codes(orc, b):
+    """The MSE record's codes are the code planes of the (b+1)-bit two-stage
+    record (same b-bit codebook, same rotation)."""
+    d = 200
+    pi64, s64, pi32, s32 = orc.make_rotation(d, 4)
+    c = orc.lloyd_max(d, b)[0].astype(np.float32)
+    x = np.random.default_rng(40 + b).standard_normal((300, d))
+    m = orc.quantize_mse(d, b, pi32, c, x)
+    t = orc.quantize(d, b + 1, pi32, s32, c, x)
+    idx_t, _ = orc.unpack_records(d, b + 1, t["planes"])
+    assert np.array_equal(orc.unpack_codes_mse(d, b, m["planes"]), idx_t)
+    assert np.array_equal(m["norms"][:, 0], t["norms"][:, 0])
+
+
+@pytest.mark.parametrize("d", [3, 4])
+@pytest.mark.parametrize("b", [1, 2])
+def test_mse_nearest_centroid_exhaustive(orc, d, b):
+    pi32, c = mse_tables(orc, d, b, seed=5)
+    K = 1 << b
+    x = np.random.default_rng(d + 7 * b).standard_normal((50, d))
+    idx = orc.unpack_codes_mse(d, b, orc.quantize_mse(d, b, pi32, c, x)["planes"])
+    y = (x / np.linalg.norm(x, axis=1, keepdims=True)) @ pi32.astype(np.float64).T
+    cb = np.array(list(itertools.product(range(K), repeat=d)))
+    dist = ((y[:, None, :] - c.astype(np.float64)[cb][None]) ** 2).sum(axis=2)
+    assert np.array_equal(cb[np.argmin(dist, axis=1)], idx)
+
+
+def test_mse_estimate_and_zero_vector(orc):
+    d, b = 96, 3
+    pi32, c = mse_tables(orc, d, b, seed=6)
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((40, d))
+    x[3] = 0.0
+    q = rng.standard_normal((5, d))
+    rec = orc.quantize_mse(d, b, pi32, c, x)
+    xt = orc.dequantize_mse(d, b, pi32, c, rec["planes"], rec["norms"])
+    est = orc.estimate_mse(d, b, pi32, c, q, rec["planes"], rec["norms"], scale=0.5)
+    np.testing.assert_allclose(est, 0.5 * q @ xt.T, rtol=1e-11, atol=1e-12)
+    # y = 0: every coordinate ties between c[K/2 - 1] and c[K/2] -> lower index
+    assert np.all(orc.unpack_codes_mse(d, b, rec["planes"][3:4]) == (1 << (b - 1)) - 1)
+    assert np.all(rec["norms"][3] == 0) and np.all(xt[3] == 0)
