@@ -144,6 +144,26 @@ TQ_API tq_status tq_ctx_destroy(tq_ctx* ctx);
 TQ_API int32_t tq_ctx_dim(const tq_ctx* ctx);
 TQ_API int32_t tq_ctx_bits(const tq_ctx* ctx);
 
+/* MSE-only context (turboquant.net pseudo-code "quant" / "dequant" without
+ * the QJL stage; admirer.cn: the first stage alone is the MSE-optimal
+ * quantizer, whose inner products are biased): every one of the b bits per
+ * coordinate is a code bit, records hold b code planes per 32-coordinate
+ * group and no sign plane, and the gamma slot of the norms is stored as 0.
+ *   pi: host float[d*d]; centroids: host float[1 << b] (tq_lloyd_max with
+ *   lm_bits = b), ascending and exactly symmetric.
+ * Every hot-path entry point below takes such a context and then computes
+ *   quantize: idx_j = nearest centroid of (Pi x / nu)_j, norms (nu, 0)
+ *   dequantize: out = nu Pi^T c[idx]
+ *   est(q, k) = nu <Pi q, c[idx]>   (logits, search, attention output and
+ *   fused decode use this estimate and these dequantized values)
+ * with the same record layout rules (W groups of b words).
+ * Errors: TQ_ERR_UNSUPPORTED if d is not a multiple of 8 in 8..TQ_MAX_D or b
+ * is outside {1,2,3}; otherwise as tq_ctx_create. */
+TQ_API tq_status tq_ctx_create_mse(int32_t d, int32_t b, const float* pi,
+                                   const float* centroids, tq_ctx** out);
+/* 1 for a context from tq_ctx_create_mse, 0 otherwise (and for NULL). */
+TQ_API int32_t tq_ctx_is_mse(const tq_ctx* ctx);
+
 /* ---- hot path -------------------------------------------------------------- */
 
 /* Quantize n_heads * n_tokens vectors (turboquant.net pseudo-code "quant",

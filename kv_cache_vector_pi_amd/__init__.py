@@ -31,6 +31,7 @@ EXPORTS = [
     "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
     "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
+    "tq_ctx_create_mse", "tq_ctx_is_mse",
 ]
 
 
@@ -65,6 +66,8 @@ _sig("tq_make_rotation", _i32, [_i32, _u64, _P, _P])
 _sig("tq_lloyd_max", _i32, [_i32, _i32, _i32, _f64, _P, _P, _P])
 _sig("tq_ctx_create", _i32, [_i32, _i32, _P, _P, _P, ctypes.POINTER(_P)])
 _sig("tq_ctx_destroy", _i32, [_P])
+_sig("tq_ctx_create_mse", _i32, [_i32, _i32, _P, _P, ctypes.POINTER(_P)])
+_sig("tq_ctx_is_mse", _i32, [_P])
 _sig("tq_ctx_dim", _i32, [_P])
 _sig("tq_ctx_bits", _i32, [_P])
 _sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
@@ -149,17 +152,23 @@ def tq_lloyd_max(d, lm_bits, max_iter=100000, tol=1e-13):
 
 
 class TqContext:
-    """Owns a tq_ctx (device tables on the current HIP device)."""
+    """Owns a tq_ctx (device tables on the current HIP device).  s=None makes
+    an MSE-only context (tq_ctx_create_mse: b code bits, no QJL stage)."""
 
     def __init__(self, d, b, pi, s, centroids):
         pi = np.ascontiguousarray(pi, np.float32)
-        s = np.ascontiguousarray(s, np.float32)
         c = np.ascontiguousarray(centroids, np.float32)
         h = _P()
-        _check(_lib.tq_ctx_create(d, b, pi.ctypes.data, s.ctypes.data, c.ctypes.data,
-                                  ctypes.byref(h)), "tq_ctx_create")
+        if s is None:
+            _check(_lib.tq_ctx_create_mse(d, b, pi.ctypes.data, c.ctypes.data, ctypes.byref(h)),
+                   "tq_ctx_create_mse")
+        else:
+            s = np.ascontiguousarray(s, np.float32)
+            _check(_lib.tq_ctx_create(d, b, pi.ctypes.data, s.ctypes.data, c.ctypes.data,
+                                      ctypes.byref(h)), "tq_ctx_create")
         self.handle = h.value
         self.d, self.b = d, b
+        self.mse = s is None
 
     @property
     def W(self):
@@ -179,6 +188,14 @@ class TqContext:
 
 def tq_ctx_create(d, b, pi, s, centroids):
     return TqContext(d, b, pi, s, centroids)
+
+
+def tq_ctx_create_mse(d, b, pi, centroids):
+    return TqContext(d, b, pi, None, centroids)
+
+
+def tq_ctx_is_mse(ctx):
+    return int(_lib.tq_ctx_is_mse(ctx.handle if ctx is not None else None))
 
 
 def tq_ctx_destroy(ctx):

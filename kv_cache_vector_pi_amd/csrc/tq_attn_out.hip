@@ -17,6 +17,8 @@
 //     the workspace.
 //  2. vout_final_kernel: workgroup = (query head, sequence): sum the chunk
 //     partials, then o_i = sum_j Pi[j][i] a_rot[j] + alpha sum_j S[j][i] a_sk[j].
+// MSE-only records (no QJL stage) have no sketch part: a_sk = 0, and the S^T
+// product is skipped.
 #include <algorithm>
 #include <cmath>
 
@@ -49,7 +51,7 @@ inline int chunk_of(const tq_ctx* ctx) {
   return ch;
 }
 
-template <int NB>
+template <int NB, bool MSE>
 __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   extern __shared__ __align__(16) uint32_t sm[];
   const int RW = a.W * NB;                       // words per record
@@ -85,7 +87,7 @@ __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   // ---- accumulate and write the chunk partials ---------------------------------
   float* dst = a.part +
       ((((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk + chunk_i) * 8 * (int64_t)a.Dp;
-  dev::vacc_block<NB>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)sm, dst);
+  dev::vacc_block<NB, MSE>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)sm, dst);
 }
 
 struct VFinArgs {
@@ -95,6 +97,7 @@ struct VFinArgs {
   float* out;               // out[bi * out_stride_batch + hq * d + i]
   int64_t out_stride_batch;
   int d, Dp, G, n_kv, n_rb, n_chunk;
+  int qjl;                  // 0: MSE-only records, no sketch part
   float alpha;
 };
 
@@ -120,7 +123,7 @@ __global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
     float o1 = 0.f, o2 = 0.f;
     for (int j = 0; j < a.d; ++j) {
       o1 = fmaf(a.pi32[(int64_t)j * a.d + i], arot[j], o1);
-      o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
+      if (a.qjl) o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
     }
     a.out[(int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d + i] = fmaf(a.alpha, o2, o1);
   }
@@ -166,10 +169,18 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
   const size_t red = TT > 1 ? (size_t)TT * 8 * NL * 4 : 0;
   const size_t shm = std::max(stage, red);
   const dim3 grid(a.n_chunk, n_kv_heads * a.n_rb, batch);
-  switch (ctx->b) {
-    case 2: hipLaunchKernelGGL(vout_accum_kernel<2>, grid, dim3(256), shm, stream, a); break;
-    case 3: hipLaunchKernelGGL(vout_accum_kernel<3>, grid, dim3(256), shm, stream, a); break;
-    default: hipLaunchKernelGGL(vout_accum_kernel<4>, grid, dim3(256), shm, stream, a); break;
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: hipLaunchKernelGGL((vout_accum_kernel<1, true>), grid, dim3(256), shm, stream, a); break;
+      case 2: hipLaunchKernelGGL((vout_accum_kernel<2, true>), grid, dim3(256), shm, stream, a); break;
+      default: hipLaunchKernelGGL((vout_accum_kernel<3, true>), grid, dim3(256), shm, stream, a); break;
+    }
+  } else {
+    switch (ctx->b) {
+      case 2: hipLaunchKernelGGL((vout_accum_kernel<2, false>), grid, dim3(256), shm, stream, a); break;
+      case 3: hipLaunchKernelGGL((vout_accum_kernel<3, false>), grid, dim3(256), shm, stream, a); break;
+      default: hipLaunchKernelGGL((vout_accum_kernel<4, false>), grid, dim3(256), shm, stream, a); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -185,6 +196,7 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
   f.n_kv = n_kv_heads;
   f.n_rb = a.n_rb;
   f.n_chunk = a.n_chunk;
+  f.qjl = ctx->mse ? 0 : 1;
   f.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   hipLaunchKernelGGL(vout_final_kernel, dim3(n_q_heads, batch), dim3(256),
                      2 * ctx->Dp * sizeof(float), stream, f);

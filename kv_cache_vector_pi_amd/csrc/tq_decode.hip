@@ -16,7 +16,8 @@
 //  3. decode_final_kernel, per (query head, sequence): rescale the chunks by
 //     exp(m_c - M), divide by L = sum_c l_c exp(m_c - M), and apply Pi^T and
 //     S^T once.
-// An empty sequence gets a zero output.
+// An empty sequence gets a zero output.  MSE-only records (no QJL stage)
+// drop every sketch term: no sign MFMAs, no S^T product.
 #include <algorithm>
 #include <cmath>
 
@@ -61,10 +62,11 @@ __device__ inline float wsum(float v) {
   return v;
 }
 
-template <int NB>
+template <int NB, bool MSE>
 __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
-  constexpr int NV = 1 << (NB - 2);
-  constexpr int NC = 2 * NV + 2;
+  constexpr int CP = MSE ? NB : NB - 1;          // code planes
+  constexpr int NV = 1 << (CP - 1);
+  constexpr int NC = 2 * NV + (MSE ? 0 : 2);
   extern __shared__ __align__(16) uint32_t sm[];
   const int CH = a.chunk;
   const int RW = a.W * NB;
@@ -88,7 +90,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
 
   // ---- 1. logits of the chunk (tiles of 16 tokens, one per wave at a time) ----
   const int nws = dev::n_ws(a.W);
-  const size_t rbb = dev::rb_bytes(a.W, NB);
+  const size_t rbb = dev::rb_bytes(a.W, NC);
   const char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rbb;
   const float4 cst = ((const float4*)(rbase + (size_t)nws * NC * 64 * 16))[g];
   const bool head_ok = 4 * rb + g < a.G;
@@ -109,7 +111,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
       for (int v = 0; v < NV; ++v) {
         uint32_t u = 0u;
 #pragma unroll
-        for (int p = 0; p < NB - 1; ++p)
+        for (int p = 0; p < CP; ++p)
           if ((a.mask[v] >> p) & 1) u ^= wd[p];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
                                                         dev::bit_lanes(u, half), acc_m, 0, 0, 0);
       }
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int half = 0; half < (MSE ? 0 : 2); ++half)
         acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(fr[(2 * NV + half) * 64 + lane],
                                                       dev::bit_lanes(wd[NB - 1], half), acc_q,
                                                       0, 0, 0);
@@ -126,7 +128,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     const float qjl = fmaf(dev::limbs_to_float(acc_q), cst.y, cst.w);
     const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
     const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
-    const float logit = a.scale * nu * fmaf(a.alpha * ga, qjl, mse);
+    const float logit = a.scale * nu * (MSE ? mse : fmaf(a.alpha * ga, qjl, mse));
     lg[g * CH + tl] = (valid && head_ok) ? logit : -INFINITY;
   }
   // stage the chunk's value records meanwhile
@@ -171,7 +173,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     a.stats[cidx * 8 + 2 * tid + 1] = st_l[tid];
   }
   // the token-group scratch of vacc_block aliases the staged records
-  dev::vacc_block<NB>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)words, dst);
+  dev::vacc_block<NB, MSE>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)words, dst);
 }
 
 struct DecFinArgs {
@@ -182,6 +184,7 @@ struct DecFinArgs {
   float* out;
   int64_t out_stride_batch;
   int d, Dp, G, n_kv, n_rb, n_chunk;
+  int qjl;                      // 0: MSE-only records, no sketch part
   float alpha;
 };
 
@@ -230,7 +233,7 @@ __global__ void __launch_bounds__(256) decode_final_kernel(DecFinArgs a) {
     float o1 = 0.f, o2 = 0.f;
     for (int j = 0; j < a.d; ++j) {
       o1 = fmaf(a.pi32[(int64_t)j * a.d + i], arot[j], o1);
-      o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
+      if (a.qjl) o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
     }
     a.out[(int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d + i] = fmaf(a.alpha, o2, o1);
   }
@@ -306,10 +309,18 @@ hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, 
   const size_t red = (size_t)4 * CH * 4 + (size_t)TT * 8 * NL * 4;
   const size_t shm = std::max(stage, red);
   const dim3 grid(L.n_chunk, n_kv_heads * L.n_rb, batch);
-  switch (ctx->b) {
-    case 2: hipLaunchKernelGGL(decode_chunk_kernel<2>, grid, dim3(256), shm, stream, a); break;
-    case 3: hipLaunchKernelGGL(decode_chunk_kernel<3>, grid, dim3(256), shm, stream, a); break;
-    default: hipLaunchKernelGGL(decode_chunk_kernel<4>, grid, dim3(256), shm, stream, a); break;
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: hipLaunchKernelGGL((decode_chunk_kernel<1, true>), grid, dim3(256), shm, stream, a); break;
+      case 2: hipLaunchKernelGGL((decode_chunk_kernel<2, true>), grid, dim3(256), shm, stream, a); break;
+      default: hipLaunchKernelGGL((decode_chunk_kernel<3, true>), grid, dim3(256), shm, stream, a); break;
+    }
+  } else {
+    switch (ctx->b) {
+      case 2: hipLaunchKernelGGL((decode_chunk_kernel<2, false>), grid, dim3(256), shm, stream, a); break;
+      case 3: hipLaunchKernelGGL((decode_chunk_kernel<3, false>), grid, dim3(256), shm, stream, a); break;
+      default: hipLaunchKernelGGL((decode_chunk_kernel<4, false>), grid, dim3(256), shm, stream, a); break;
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -326,6 +337,7 @@ hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, 
   f.n_kv = n_kv_heads;
   f.n_rb = L.n_rb;
   f.n_chunk = L.n_chunk;
+  f.qjl = ctx->mse ? 0 : 1;
   f.alpha = a.alpha;
   hipLaunchKernelGGL(decode_final_kernel, dim3(n_q_heads, batch), dim3(256),
                      (2 * (size_t)ctx->Dp + L.n_chunk) * sizeof(float), stream, f);

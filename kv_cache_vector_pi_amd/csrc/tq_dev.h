@@ -12,19 +12,22 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kTile = 16;          // key tokens per MFMA tile
 constexpr int kWaves = 4;          // waves per workgroup
 
-__host__ __device__ inline int n_calls(int b) { return 2 * (1 << (b - 2)) + 2; }   // MFMA calls per word step
+// MFMA calls per word step: two per Walsh subset of the cp code planes, and
+// two for the sign plane when the records carry the QJL stage
+__host__ __device__ inline int n_calls(int cp, bool qjl) { return 2 * (1 << (cp - 1)) + (qjl ? 2 : 0); }
 __host__ __device__ inline int n_ws(int W) { return (W + 3) / 4; }                  // word steps of 4 words
 
 // Prepared-query workspace for one (batch, kv head, row block of 4 q heads):
 //   int4 frag[n_ws][n_calls][64 lanes]   A operands (16 int8 each)
 //   float4 consts[4]                      per q head: mse scale, qjl scale,
 //                                         mse offset, qjl offset
-__host__ __device__ inline size_t rb_bytes(int W, int b) {
-  return (size_t)n_ws(W) * n_calls(b) * 64 * 16 + 4 * 16;
+__host__ __device__ inline size_t rb_bytes(int W, int nc) {
+  return (size_t)n_ws(W) * nc * 64 * 16 + 4 * 16;
 }
 
 template <int NB>
 __device__ inline void load_group(const uint32_t* p, uint32_t (&w)[NB]) {
+  // NB words per record group
   if constexpr (NB == 4) {
     uint4 v = *(const uint4*)p;
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
@@ -57,12 +60,13 @@ __device__ inline float limbs_to_float(const v4i& c) {
 //   dst[hh][j]     = sum_t wts[t][hh]     * c[idx_tj]
 //   dst[4 + hh][j] = sum_t wts[t][4 + hh] * s_tj        (s = +-1)
 // for j < Dp (coordinates j >= d hold the contributions of zero bits and are
-// ignored by the consumers).  words: LDS [nt][RW] packed records (RW = W*NB),
+// ignored by the consumers).  MSE records (NB code planes, no sign plane)
+// leave dst[4 + hh] zero.  words: LDS [nt][RW] packed records (RW = W*NB),
 // wts: LDS [nt][8], ctab: LDS centroids, red: LDS scratch of
 // max(1, 256 / Dp) * 8 * Dp floats that may alias `words` (a barrier separates
 // the reads from the reuse).  Threads own coordinates lc + 256k of token group
 // tg (tokens tg, tg + TT, ...).
-template <int NB>
+template <int NB, bool MSE>
 __device__ void vacc_block(const uint32_t* words, const float* wts, const float* ctab, int nt,
                            int RW, int d, int Dp, float* red, float* dst) {
   const int tid = threadIdx.x;
@@ -90,15 +94,16 @@ __device__ void vacc_block(const uint32_t* words, const float* wts, const float*
         const int bit = j & 31;
         uint32_t idx = 0;
 #pragma unroll
-        for (int q = 0; q < NB - 1; ++q) idx |= __builtin_amdgcn_ubfe(gw[q], bit, 1) << q;
+        for (int q = 0; q < (MSE ? NB : NB - 1); ++q) idx |= __builtin_amdgcn_ubfe(gw[q], bit, 1) << q;
         const float c = ctab[idx];
-        // +1.0 for a set sign bit, -1.0 otherwise
-        const float sg =
-            __uint_as_float(0xbf800000u ^ (__builtin_amdgcn_ubfe(gw[NB - 1], bit, 1) << 31));
         ar[k][0] = fmaf(w1.x, c, ar[k][0]);
         ar[k][1] = fmaf(w1.y, c, ar[k][1]);
         ar[k][2] = fmaf(w1.z, c, ar[k][2]);
         ar[k][3] = fmaf(w1.w, c, ar[k][3]);
+        if constexpr (MSE) continue;
+        // +1.0 for a set sign bit, -1.0 otherwise
+        const float sg =
+            __uint_as_float(0xbf800000u ^ (__builtin_amdgcn_ubfe(gw[NB - 1], bit, 1) << 31));
         as[k][0] = fmaf(w2.x, sg, as[k][0]);
         as[k][1] = fmaf(w2.y, sg, as[k][1]);
         as[k][2] = fmaf(w2.z, sg, as[k][2]);

@@ -259,16 +259,24 @@ TQ_API tq_status tq_lloyd_max(int32_t d, int32_t lm_bits, int32_t max_iter, doub
 }
 
 // ---------------------------------------------------------------------------
-TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const float* s,
-                               const float* centroids, tq_ctx** out) {
+namespace {
+
+// Shared by tq_ctx_create (two-stage records: b-1 code planes + QJL signs)
+// and tq_ctx_create_mse (b code planes, no QJL stage; s == NULL).
+tq_status create_ctx(int32_t d, int32_t b, const float* pi, const float* s,
+                     const float* centroids, bool mse, tq_ctx** out) {
   if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: out is NULL");
   *out = nullptr;
   if (d < 8 || d > TQ_MAX_D || d % 8 != 0)
     return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create: d=%d (need a multiple of 8 in 8..%d)", d,
                 TQ_MAX_D);
-  if (b < 2 || b > 4) return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create: b=%d (need 2..4)", b);
-  if (!pi || !s || !centroids) return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: NULL table");
-  const int K = 1 << (b - 1);
+  if (!mse && (b < 2 || b > 4)) return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create: b=%d (need 2..4)", b);
+  if (mse && (b < 1 || b > 3))
+    return fail(TQ_ERR_UNSUPPORTED, "tq_ctx_create_mse: b=%d (need 1..3)", b);
+  if (!pi || (!mse && !s) || !centroids)
+    return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: NULL table");
+  const int CP = mse ? b : b - 1;
+  const int K = 1 << CP;
   for (int k = 0; k < K; ++k) {
     if (!std::isfinite(centroids[k]))
       return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: centroid %d not finite", k);
@@ -278,6 +286,11 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
       return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: centroids not symmetric");
   }
   const size_t dd = (size_t)d * d;
+  std::vector<float> zeros;
+  if (mse) {              // no sketch: S (and M = S Pi^T) are zero tables
+    zeros.assign(dd, 0.f);
+    s = zeros.data();
+  }
   for (size_t i = 0; i < dd; ++i)
     if (!std::isfinite(pi[i]) || !std::isfinite(s[i]))
       return fail(TQ_ERR_INVALID_ARG, "tq_ctx_create: non-finite Pi or S entry");
@@ -285,6 +298,8 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
   tq_ctx* ctx = new tq_ctx();
   ctx->d = d;
   ctx->b = b;
+  ctx->mse = mse ? 1 : 0;
+  ctx->cp = CP;
   ctx->W = (d + 31) / 32;
   ctx->Dp = 32 * ctx->W;
   ctx->K = K;
@@ -292,12 +307,12 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
     ctx->cent[k] = k < K ? centroids[k] : 0.f;
     ctx->mid[k] = k + 1 < K ? 0.5f * (centroids[k] + centroids[k + 1]) : 0.f;
   }
-  // Walsh expansion over the B = b-1 code bits: chi_m(beta) = (-1)^(XOR of the
+  // Walsh expansion over the B code bits: chi_m(beta) = (-1)^(XOR of the
   // bits in m) = 1 - 2 u_m.  c(beta) = sum_m w_m chi_m(beta) with
   // w_m = mean over beta of c(beta) chi_m(beta); a symmetric codebook has
   // w_m = 0 for every even-sized m, and c(beta) = c(0) - 2 sum_{m != 0} w_m u_m.
   {
-    const int B = b - 1;
+    const int B = CP;
     ctx->n_mono = 0;
     ctx->c0 = centroids[0];
     for (int m = 1; m < (1 << B); ++m) {
@@ -330,7 +345,7 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
   std::vector<__half> h16(4 * dpp + 4 * rpp, __float2half(0.f));
   {
     std::vector<double> M(dd, 0.0);   // M = S Pi^T in double
-    for (int i = 0; i < d; ++i)
+    for (int i = 0; i < (mse ? 0 : d); ++i)
       for (int j = 0; j < d; ++j) {
         double acc = 0.0;
         for (int k = 0; k < d; ++k) acc += (double)s[(size_t)i * d + k] * (double)pi[(size_t)j * d + k];
@@ -404,6 +419,20 @@ TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const floa
   *out = ctx;
   return ok();
 }
+
+}  // namespace
+
+TQ_API tq_status tq_ctx_create(int32_t d, int32_t b, const float* pi, const float* s,
+                               const float* centroids, tq_ctx** out) {
+  return create_ctx(d, b, pi, s, centroids, false, out);
+}
+
+TQ_API tq_status tq_ctx_create_mse(int32_t d, int32_t b, const float* pi, const float* centroids,
+                                   tq_ctx** out) {
+  return create_ctx(d, b, pi, nullptr, centroids, true, out);
+}
+
+TQ_API int32_t tq_ctx_is_mse(const tq_ctx* ctx) { return ctx ? ctx->mse : 0; }
 
 TQ_API tq_status tq_ctx_destroy(tq_ctx* ctx) {
   if (!ctx) return ok();

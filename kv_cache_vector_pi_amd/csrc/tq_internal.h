@@ -35,6 +35,8 @@ struct DevTables {
 
 struct tq_ctx {
   int32_t d, b, W, Dp, K;
+  int32_t mse;                // 1: MSE-only records (b code planes, no QJL stage)
+  int32_t cp;                 // code planes per group: b - 1, or b in MSE mode
   int device;
   float cent[tq::kMaxK];      // centroids (ascending)
   float mid[tq::kMaxK];       // midpoints t_k = (c_k + c_{k+1}) / 2, k < K-1

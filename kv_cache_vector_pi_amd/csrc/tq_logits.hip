@@ -14,6 +14,8 @@
 //    code planes in an odd-sized subset m (Walsh expansion; 1, 2, 4 subsets for
 //    b = 2, 3, 4).  So <Pi q, c[idx]> = c_0 sum(Pi q) - 2 sum_m w_m <Pi q, u_m>.
 //  * Signs: <S q, s> = 2 <S q, beta_s> - sum(S q), beta_s the sign plane.
+//    MSE-only records (no QJL stage) have b code planes and no sign plane:
+//    the estimate is the first term alone and the sign MFMAs are left out.
 //  * Bits -> int8 lanes: a 32-bit plane word ANDed with 0x01010101 << k gives
 //    four int8 lanes holding bit (8e+k) of the word times 2^k (times -128 for
 //    k = 7).  The 2^k is folded into the query weights: the weight for a bit
@@ -47,7 +49,7 @@ struct PrepArgs {
   const float* pit;        // [d][d] Pi^T
   const float* st;         // [d][d] S^T
   char* ws;
-  int d, W, b, G, n_kv, n_rb, n_q;
+  int d, W, nc, G, n_kv, n_rb, n_q;     // nc: MFMA calls per word step
   float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
   int mask[kMaxVec];       // code-plane subsets
   int nv;                  // number of subsets
@@ -153,7 +155,7 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
     }
   }
   // wave hh: max |Pi q|, max |S q|, sum Pi q, sum S q of slot hh
-  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rb_bytes(a.W, a.b);
+  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rb_bytes(a.W, a.nc);
   {
     const float* r1 = qr + wave * Dp;
     const float* r2 = qp + wave * Dp;
@@ -182,12 +184,12 @@ __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
       cst.y = ldexpf(1.f, -e2);
       cst.z = a.c0 * t1;
       cst.w = -t2;
-      float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * n_calls(a.b) * 64 * 16);
+      float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * a.nc * 64 * 16);
       cdst[wave] = cst;
     }
   }
   __syncthreads();
-  const int nc = n_calls(a.b), nws = n_ws(a.W);
+  const int nc = a.nc, nws = n_ws(a.W);
   // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
   // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
   // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
@@ -245,10 +247,11 @@ struct AttnArgs {
 // (per word step), and after the MFMAs holds the 4 limbs of q head 4rb+g
 // for token n.  RES: all A operands fit one word step and one row block,
 // so they stay in registers for the whole chunk.
-template <int NB, bool RES>
+template <int NB, bool MSE, bool RES>
 __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
-  constexpr int NV = 1 << (NB - 2);        // Walsh subsets
-  constexpr int NC = 2 * NV + 2;           // MFMA calls per word step
+  constexpr int CP = MSE ? NB : NB - 1;    // code planes
+  constexpr int NV = 1 << (CP - 1);        // Walsh subsets
+  constexpr int NC = 2 * NV + (MSE ? 0 : 2);   // MFMA calls per word step
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
   const int h = blockIdx.y, bi = blockIdx.z;
@@ -291,7 +294,7 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
         for (int v = 0; v < NV; ++v) {
           uint32_t u = 0u;
 #pragma unroll
-          for (int p = 0; p < NB - 1; ++p)
+          for (int p = 0; p < CP; ++p)
             if ((a.mask[v] >> p) & 1) u ^= wd[p];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
@@ -300,7 +303,7 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
           }
         }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int half = 0; half < (MSE ? 0 : 2); ++half) {
           const v4i Aop = RES ? A[2 * NV + half] : fr[(2 * NV + half) * 64 + lane];
           acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, bit_lanes(wd[NB - 1], half), acc_q,
                                                         0, 0, 0);
@@ -328,9 +331,9 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
 
 // Odd-sized subsets of the code planes (Walsh expansion of a symmetric
 // codebook), in the order the context lists them: masks 1, 2, 4, 7.
-template <int NB>
+template <int CP>
 __device__ constexpr int walsh_mask(int v) {
-  return NB == 2 ? 1 : (NB == 3 ? (v == 0 ? 1 : 2) : (v == 0 ? 1 : v == 1 ? 2 : v == 2 ? 4 : 7));
+  return CP == 1 ? 1 : (CP == 2 ? (v == 0 ? 1 : 2) : (v == 0 ? 1 : v == 1 ? 2 : v == 2 ? 4 : 7));
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -348,10 +351,12 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
     typedef int v3i __attribute__((ext_vector_type(3)));
     const v3i v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
-  } else {
+  } else if constexpr (NB == 2) {
     typedef int v2i __attribute__((ext_vector_type(2)));
     const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     w[0] = v[0]; w[1] = v[1];
+  } else {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   }
 }
 
@@ -361,11 +366,12 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // loads in flight while its MFMAs run.  Records and norms are read through
 // buffer resources bounded to the wave's token range, so loads past the end
 // of the sequence (and of word groups beyond d) return zeros without branches.
-template <int NB, int U>
+template <int NB, bool MSE, int U>
 __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
-  constexpr int NV = 1 << (NB - 2);
-  constexpr int NC = 2 * NV + 2;
+  constexpr int CP = MSE ? NB : NB - 1;
+  constexpr int NV = 1 << (CP - 1);
+  constexpr int NC = 2 * NV + (MSE ? 0 : 2);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int g = lane >> 4, n = lane & 15;
@@ -429,8 +435,9 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   };
   auto logit = [&](v4i am, v4i aq, uint32_t nrm) {
     const float ms = fmaf(limbs(am), cX, cZ);
-    const float qs = fmaf(limbs(aq), cY, cW);
     const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
+    if constexpr (MSE) return nu * ms;
+    const float qs = fmaf(limbs(aq), cY, cW);
     const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
     return nu * fmaf(ga, qs, ms);
   };
@@ -457,8 +464,8 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
       for (int v = 0; v < NV; ++v) {
         uint32_t u0 = 0u, u1 = 0u;
 #pragma unroll
-        for (int p = 0; p < NB - 1; ++p)
-          if ((walsh_mask<NB>(v) >> p) & 1) {
+        for (int p = 0; p < CP; ++p)
+          if ((walsh_mask<CP>(v) >> p) & 1) {
             u0 ^= gr.wd[u][p];
             u1 ^= gr.wd[u + 1][p];
           }
@@ -467,11 +474,13 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
         am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u0, 1), am0, 0, 0, 0);
         am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u1, 1), am1, 0, 0, 0);
       }
-      const uint32_t s0 = gr.wd[u][NB - 1], s1 = gr.wd[u + 1][NB - 1];
-      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s0, 0), aq0, 0, 0, 0);
-      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s1, 0), aq1, 0, 0, 0);
-      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
-      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
+      if constexpr (!MSE) {
+        const uint32_t s0 = gr.wd[u][NB - 1], s1 = gr.wd[u + 1][NB - 1];
+        aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s0, 0), aq0, 0, 0, 0);
+        aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s1, 0), aq1, 0, 0, 0);
+        aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
+        aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
+      }
       finish2(logit(am0, aq0, gr.nr[u]), logit(am1, aq1, gr.nr[u + 1]), tl + kTile * u);
     }
   };
@@ -499,7 +508,7 @@ size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads) {
   const int G = n_q_heads / n_kv_heads;
   const int n_rb = (G + 3) / 4;
-  return (size_t)batch * n_kv_heads * n_rb * rb_bytes(ctx->W, ctx->b);
+  return (size_t)batch * n_kv_heads * n_rb * rb_bytes(ctx->W, n_calls(ctx->cp, !ctx->mse));
 }
 
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
@@ -515,7 +524,7 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
   p.ws = (char*)workspace;
   p.d = ctx->d;
   p.W = ctx->W;
-  p.b = ctx->b;
+  p.nc = n_calls(ctx->cp, !ctx->mse);
   p.G = G;
   p.n_kv = n_kv_heads;
   p.n_rb = n_rb;
@@ -558,14 +567,19 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
   // the resident kernel hard-codes the Walsh subsets 1 / 1,2 / 1,2,4,7
   static const int kMasks[3][4] = {{1, 0, 0, 0}, {1, 2, 0, 0}, {1, 2, 4, 7}};
   bool masks_ok = true;
-  for (int v = 0; v < ctx->n_mono; ++v) masks_ok &= ctx->mono_mask[v] == kMasks[ctx->b - 2][v];
+  for (int v = 0; v < ctx->n_mono; ++v) masks_ok &= ctx->mono_mask[v] == kMasks[ctx->cp - 1][v];
   const bool res = (ctx->W <= 4) && (n_rb == 1) && masks_ok;
   // Grid: one round of resident waves over all tiles (each wave takes a
   // contiguous chunk of one sequence), so no partial second round is left.
-  static const int nb_res[3] = {resident_blocks_per_cu(attn_logits_res_kernel<2, 4>),
-                                resident_blocks_per_cu(attn_logits_res_kernel<3, 4>),
-                                resident_blocks_per_cu(attn_logits_res_kernel<4, 4>)};
-  const int nb = res ? nb_res[ctx->b - 2] : 4;
+  // Variants by code planes 1..3, two-stage then MSE-only.
+  static const int nb_res[2][3] = {
+      {resident_blocks_per_cu(attn_logits_res_kernel<2, false, 4>),
+       resident_blocks_per_cu(attn_logits_res_kernel<3, false, 4>),
+       resident_blocks_per_cu(attn_logits_res_kernel<4, false, 4>)},
+      {resident_blocks_per_cu(attn_logits_res_kernel<1, true, 4>),
+       resident_blocks_per_cu(attn_logits_res_kernel<2, true, 4>),
+       resident_blocks_per_cu(attn_logits_res_kernel<3, true, 4>)}};
+  const int nb = res ? nb_res[ctx->mse][ctx->cp - 1] : 4;
   const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
   const int64_t tiles_total = (int64_t)batch * n_kv_heads * tiles_seq;
   // short chunks (about 8 rounds of resident waves) keep many independent
@@ -578,20 +592,25 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
   const int64_t tok_per_block = (int64_t)kWaves * tpw * kTile;
   const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
                   batch);
-  switch (ctx->b) {
-    case 2:
-      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<2, 4>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_logits_kernel<2, false>), grid, dim3(256), 0, stream, a);
-      break;
-    case 3:
-      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<3, 4>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_logits_kernel<3, false>), grid, dim3(256), 0, stream, a);
-      break;
-    default:
-      if (res) hipLaunchKernelGGL((attn_logits_res_kernel<4, 4>), grid, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((attn_logits_kernel<4, false>), grid, dim3(256), 0, stream, a);
-      break;
+#define TQ_LOGITS(NB, MSE)                                                                     \
+  do {                                                                                         \
+    if (res) hipLaunchKernelGGL((attn_logits_res_kernel<NB, MSE, 4>), grid, dim3(256), 0, stream, a); \
+    else hipLaunchKernelGGL((attn_logits_kernel<NB, MSE, false>), grid, dim3(256), 0, stream, a);     \
+  } while (0)
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: TQ_LOGITS(1, true); break;
+      case 2: TQ_LOGITS(2, true); break;
+      default: TQ_LOGITS(3, true); break;
+    }
+  } else {
+    switch (ctx->b) {
+      case 2: TQ_LOGITS(2, false); break;
+      case 3: TQ_LOGITS(3, false); break;
+      default: TQ_LOGITS(4, false); break;
+    }
   }
+#undef TQ_LOGITS
   return hipGetLastError();
 }
 

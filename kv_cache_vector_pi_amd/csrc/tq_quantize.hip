@@ -56,12 +56,15 @@ __device__ inline float lane_sum(float v, int width) {
 __device__ inline v8h lds_v8h(const _Float16* p) { return *(const v8h*)p; }
 __device__ inline v8h gbl_v8h(const __half* p) { return *(const v8h*)p; }
 
-// NB: bits per coordinate; BF16: input type; NCB: 16-vector column blocks per
-// tile; WPW: words per wave (word w = wave + NW * i); RES: one word per wave
-// and Dp == 128 -> Pi and M fragments stay in registers for the whole kernel.
-template <int NB, bool BF16, int NCB, int WPW, bool RES>
+// NB: words per record group (bits per coordinate); MSE: all NB are code
+// planes and the QJL stage (residual, Z = M r, signs, gamma) is left out;
+// BF16: input type; NCB: 16-vector column blocks per tile; WPW: words per
+// wave (word w = wave + NW * i); RES: one word per wave and Dp == 128 -> Pi
+// and M fragments stay in registers for the whole kernel.
+template <int NB, bool MSE, bool BF16, int NCB, int WPW, bool RES>
 __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) {
-  constexpr int K = 1 << (NB - 1);
+  constexpr int CP = MSE ? NB : NB - 1;     // code planes
+  constexpr int K = 1 << CP;
   constexpr int T = 16 * NCB;
   extern __shared__ __align__(16) char smem[];
   _Float16* bufA = (_Float16*)smem;                       // x_hi, then r_hi  [T][ldx]
@@ -325,9 +328,10 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
               g2[cb] = fmaf(r, r, g2[cb]);
               if (j < d) {
 #pragma unroll
-                for (int p = 0; p < NB - 1; ++p) cw[p] |= (uint32_t)((idx >> p) & 1) << pos;
+                for (int p = 0; p < CP; ++p) cw[p] |= (uint32_t)((idx >> p) & 1) << pos;
               }
             }
+            if constexpr (MSE) continue;
             // residual to LDS as hi + lo fp16
             const int j0 = 32 * w + 16 * rb + 4 * g;
             typedef _Float16 v4h __attribute__((ext_vector_type(4)));
@@ -342,7 +346,7 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
             *(v4h*)(bufB + v * ldx + j0) = rl;
           }
 #pragma unroll
-          for (int p = 0; p < NB - 1; ++p) {
+          for (int p = 0; p < CP; ++p) {
             uint32_t x = cw[p];
             x |= __shfl_xor(x, 16);
             x |= __shfl_xor(x, 32);
@@ -353,7 +357,7 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
     }
     // partial gamma^2 of this wave's coordinates, per vector
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int cb = 0; cb < (MSE ? 0 : NCB); ++cb) {
       float x = g2[cb];
       x += __shfl_xor(x, 16);
       x += __shfl_xor(x, 32);
@@ -362,7 +366,25 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
     __syncthreads();
 
     // ---- 4. Z = M r (K step outer, as for Y), signs, 5. store ---------------
-    {
+    if constexpr (MSE) {
+#pragma unroll
+      for (int wi = 0; wi < WPW; ++wi) {
+        const int w = wave + NW * wi;
+        if (w >= W) continue;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int v = 16 * cb + n;
+          if (g < NB && v < cnt) {
+            uint32_t val = 0u;
+#pragma unroll
+            for (int p = 0; p < NB; ++p)
+              if (g == p) val = codew[wi][cb][p];
+            const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + v;
+            a.planes[(rec * W + w) * NB + g] = val;
+          }
+        }
+      }
+    } else {
       v4f zacc[WPW][2][NCB];
 #pragma unroll
       for (int wi = 0; wi < WPW; ++wi)
@@ -436,7 +458,8 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
     }
     if (tid < T && tid < cnt) {
       float s = 0.f;
-      for (int ww = 0; ww < NW; ++ww) s += gpart[ww * T + tid];
+      if (!MSE)
+        for (int ww = 0; ww < NW; ++ww) s += gpart[ww * T + tid];
       const float gam = sqrtf(s);
       const uint32_t gb = (uint32_t)__half_as_ushort(__float2half_rn(gam));
       const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + tid;
@@ -446,9 +469,9 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
   }
 }
 
-template <int NB, bool BF16, int NCB, int WPW, bool RES>
+template <int NB, bool MSE, bool BF16, int NCB, int WPW, bool RES>
 hipError_t launch_one(const QuantArgs& a, size_t shm, dim3 grid, dim3 block, hipStream_t st) {
-  auto fn = quantize_kernel<NB, BF16, NCB, WPW, RES>;
+  auto fn = quantize_kernel<NB, MSE, BF16, NCB, WPW, RES>;
   // raise the dynamic-LDS limit once per instantiation (the largest tile
   // shape needs ~134 KB); never inside a launch sequence a caller may capture
   static const hipError_t attr = hipFuncSetAttribute(
@@ -460,13 +483,13 @@ hipError_t launch_one(const QuantArgs& a, size_t shm, dim3 grid, dim3 block, hip
 
 // tile shapes by padded dimension: (column blocks, words per wave)
 //   Dp <= 256: (4, 1)   Dp <= 512: (4, 2)   Dp <= 1024: (2, 4)   else (1, 8)
-template <int NB, bool BF16>
+template <int NB, bool MSE, bool BF16>
 hipError_t launch_nb(const QuantArgs& a, size_t shm, dim3 grid, dim3 block, hipStream_t st) {
-  if (a.Dp == 128) return launch_one<NB, BF16, 4, 1, true>(a, shm, grid, block, st);
-  if (a.Dp <= 256) return launch_one<NB, BF16, 4, 1, false>(a, shm, grid, block, st);
-  if (a.Dp <= 512) return launch_one<NB, BF16, 4, 2, false>(a, shm, grid, block, st);
-  if (a.Dp <= 1024) return launch_one<NB, BF16, 2, 4, false>(a, shm, grid, block, st);
-  return launch_one<NB, BF16, 1, 8, false>(a, shm, grid, block, st);
+  if (a.Dp == 128) return launch_one<NB, MSE, BF16, 4, 1, true>(a, shm, grid, block, st);
+  if (a.Dp <= 256) return launch_one<NB, MSE, BF16, 4, 1, false>(a, shm, grid, block, st);
+  if (a.Dp <= 512) return launch_one<NB, MSE, BF16, 4, 2, false>(a, shm, grid, block, st);
+  if (a.Dp <= 1024) return launch_one<NB, MSE, BF16, 2, 4, false>(a, shm, grid, block, st);
+  return launch_one<NB, MSE, BF16, 1, 8, false>(a, shm, grid, block, st);
 }
 
 }  // namespace
@@ -512,17 +535,22 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
   const int64_t grid = std::min<int64_t>(a.n_tiles, (int64_t)cus * per_cu);
   const dim3 block(64 * a.NW);
   const bool bf = x_dtype == TQ_BF16;
-  switch (ctx->b) {
-    case 2:
-      return bf ? launch_nb<2, true>(a, shm, dim3(grid), block, stream)
-                : launch_nb<2, false>(a, shm, dim3(grid), block, stream);
-    case 3:
-      return bf ? launch_nb<3, true>(a, shm, dim3(grid), block, stream)
-                : launch_nb<3, false>(a, shm, dim3(grid), block, stream);
-    default:
-      return bf ? launch_nb<4, true>(a, shm, dim3(grid), block, stream)
-                : launch_nb<4, false>(a, shm, dim3(grid), block, stream);
+#define TQ_QNB(NB, MSE)                                                   \
+  return bf ? launch_nb<NB, MSE, true>(a, shm, dim3(grid), block, stream) \
+            : launch_nb<NB, MSE, false>(a, shm, dim3(grid), block, stream)
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: TQ_QNB(1, true);
+      case 2: TQ_QNB(2, true);
+      default: TQ_QNB(3, true);
+    }
   }
+  switch (ctx->b) {
+    case 2: TQ_QNB(2, false);
+    case 3: TQ_QNB(3, false);
+    default: TQ_QNB(4, false);
+  }
+#undef TQ_QNB
 }
 
 }  // namespace tq

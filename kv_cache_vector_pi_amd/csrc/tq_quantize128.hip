@@ -133,9 +133,12 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
   }
 }
 
-template <int NB, bool BF16>
+// NB: words per record group; MSE: all NB planes are code planes (no QJL
+// stage, gamma stored as 0), else NB-1 code planes and the sign plane.
+template <int NB, bool BF16, bool MSE>
 __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
-  constexpr int K = 1 << (NB - 1);
+  constexpr int CP = MSE ? NB : NB - 1;   // code planes
+  constexpr int K = 1 << CP;
   constexpr int KH = K / 2;           // positive centroids
   constexpr int NT = KH - 1;          // positive thresholds
   constexpr int YP = BF16 ? 2 : 3;    // MFMA passes per K step of Y
@@ -284,10 +287,10 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
       const float r = y - c;
       rr[i] = r;
       g2 = fmaf(r, r, g2);
-      bacc[NB - 2] = shift_in(bacc[NB - 2], P);
-      if constexpr (NB == 3) {
+      bacc[CP - 1] = shift_in(bacc[CP - 1], P);
+      if constexpr (CP == 2) {
         bacc[0] = shift_in(bacc[0], ~(G[0] ^ P));
-      } else if constexpr (NB == 4) {
+      } else if constexpr (CP == 3) {
         bacc[1] = shift_in(bacc[1], ~(G[1] ^ P));
         bacc[0] = shift_in(bacc[0], ~(G[0] ^ G[1] ^ G[2] ^ P));
       }
@@ -295,7 +298,7 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
     }
     // residual -> LDS as hi/lo fp16 (rows 8j + 4hh .. +3 hold 4 consecutive i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < (MSE ? 0 : 4); ++j) {
       v4h rh, rl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -309,8 +312,9 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
       *(v4h*)(rl_s + off) = rl;
     }
 #pragma unroll
-    for (int p = 0; p < NB - 1; ++p) codew[cb][p] = halves_or(spread16(bacc[p], hh));
-    gpart[wave][v] = halves_sum(g2) * (sv * sv);    // both halves write the same value
+    for (int p = 0; p < CP; ++p) codew[cb][p] = halves_or(spread16(bacc[p], hh));
+    if constexpr (!MSE)
+      gpart[wave][v] = halves_sum(g2) * (sv * sv);  // both halves write the same value
   };
 
   // ---- MFMA m (0..23) of Z = M r for block cb ------------------------------
@@ -329,6 +333,16 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
 
   // ---- signs of block cb and its record words into the staging buffer ------
   auto signs = [&](const v16f& z, int cb, int pb, auto&& hook) {
+    if constexpr (MSE) {      // code words only
+      const int v = 32 * cb + col;
+      uint32_t* dst = outw[pb] + (v * 4 + wave) * NB;
+      if (hh == 0)
+#pragma unroll
+        for (int p = 0; p < NB; ++p) dst[p] = codew[cb][p];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) hook(e);
+      return;
+    }
     uint32_t sb = 0u;
 #pragma unroll
     for (int i = 15; i >= 0; --i) {
@@ -407,14 +421,16 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
     if (!BF16 && has_next) load_tile<BF16>(raw, a, next, wave, lane);    // fp32: no prefetch
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+      if constexpr (!MSE)
 #pragma unroll
-      for (int m = 6 * p; m < 6 * p + 3; ++m) z_mfma(z0, 0, m);
+        for (int m = 6 * p; m < 6 * p + 3; ++m) z_mfma(z0, 0, m);
       x_pass(p, cnt_n, par ^ 1);
+      if constexpr (!MSE)
 #pragma unroll
-      for (int m = 6 * p + 3; m < 6 * p + 6; ++m) z_mfma(z0, 0, m);
+        for (int m = 6 * p + 3; m < 6 * p + 6; ++m) z_mfma(z0, 0, m);
     }
     signs(z0, 0, par, [&](int e) {
-      if (e < 12) {
+      if (!MSE && e < 12) {
 #pragma unroll
         for (int m = 2 * e; m < 2 * e + 2; ++m) z_mfma(z1, 1, m);
       }
@@ -422,8 +438,8 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
     signs(z1, 1, par, none);
 
     if (tid < cnt) {
-      const float sq = (gpart[0][tid] + gpart[1][tid]) + (gpart[2][tid] + gpart[3][tid]);
-      const float gam = ysc[par][tid] == 0.f ? 0.f : sqrtf(sq);
+      const float sq = MSE ? 0.f : (gpart[0][tid] + gpart[1][tid]) + (gpart[2][tid] + gpart[3][tid]);
+      const float gam = (MSE || ysc[par][tid] == 0.f) ? 0.f : sqrtf(sq);
       const uint32_t gb = (uint32_t)__half_as_ushort(__float2half_rn(gam));
       outn[par][tid] = nu16[par][tid] | (gb << 16);
     }
@@ -434,18 +450,18 @@ __global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
   flush(par ^ 1);
 }
 
-template <int NB, bool BF16>
+template <int NB, bool BF16, bool MSE>
 hipError_t launch128(const Q128Args& a, int n_cu, hipStream_t st) {
   static int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize128_kernel<NB, BF16>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize128_kernel<NB, BF16, MSE>, 256, 0) !=
             hipSuccess ||
         nb < 1)
       nb = 1;
     return nb;
   }();
   const int64_t grid = std::min<int64_t>((int64_t)a.n_tiles, (int64_t)n_cu * per_cu);
-  hipLaunchKernelGGL((quantize128_kernel<NB, BF16>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((quantize128_kernel<NB, BF16, MSE>), dim3((unsigned)grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -487,10 +503,19 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
     ah.dst_token0 = dst_token0 + h0 * dst_stride_head;
     ah.n_tiles = (uint32_t)(tph * nh);
     hipError_t e;
-    switch (ctx->b) {
-      case 2: e = bf ? launch128<2, true>(ah, ctx->n_cu, stream) : launch128<2, false>(ah, ctx->n_cu, stream); break;
-      case 3: e = bf ? launch128<3, true>(ah, ctx->n_cu, stream) : launch128<3, false>(ah, ctx->n_cu, stream); break;
-      default: e = bf ? launch128<4, true>(ah, ctx->n_cu, stream) : launch128<4, false>(ah, ctx->n_cu, stream); break;
+    const int n_cu = ctx->n_cu;
+    if (ctx->mse) {
+      switch (ctx->b) {
+        case 1: e = bf ? launch128<1, true, true>(ah, n_cu, stream) : launch128<1, false, true>(ah, n_cu, stream); break;
+        case 2: e = bf ? launch128<2, true, true>(ah, n_cu, stream) : launch128<2, false, true>(ah, n_cu, stream); break;
+        default: e = bf ? launch128<3, true, true>(ah, n_cu, stream) : launch128<3, false, true>(ah, n_cu, stream); break;
+      }
+    } else {
+      switch (ctx->b) {
+        case 2: e = bf ? launch128<2, true, false>(ah, n_cu, stream) : launch128<2, false, false>(ah, n_cu, stream); break;
+        case 3: e = bf ? launch128<3, true, false>(ah, n_cu, stream) : launch128<3, false, false>(ah, n_cu, stream); break;
+        default: e = bf ? launch128<4, true, false>(ah, n_cu, stream) : launch128<4, false, false>(ah, n_cu, stream); break;
+      }
     }
     if (e != hipSuccess) return e;
   }

@@ -144,8 +144,10 @@ struct GemmArgs {
   int64_t out_ld;
 };
 
-template <int NB, int MODE>
+// MSE: records of NB code planes without the QJL stage (no sketch term).
+template <int NB, bool MSE, int MODE>
 __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
+  constexpr int CP = MSE ? NB : NB - 1;
   __shared__ __align__(16) _Float16 dh[kRecTile * kLdsRow];
   __shared__ __align__(16) _Float16 dl[kRecTile * kLdsRow];
   __shared__ __align__(16) _Float16 ds[kRecTile * kLdsRow];
@@ -181,32 +183,37 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
         const int bit = 8 * dq + e;
         int idx = 0;
 #pragma unroll
-        for (int p = 0; p < NB - 1; ++p) idx |= (int)((wd[p] >> bit) & 1u) << p;
+        for (int p = 0; p < CP; ++p) idx |= (int)((wd[p] >> bit) & 1u) << p;
         vh[e] = a.c_hi[idx];
         vl[e] = a.c_lo[idx];
-        vs[e] = ((wd[NB - 1] >> bit) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
+        if constexpr (!MSE) vs[e] = ((wd[NB - 1] >> bit) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
       }
       *(v8h*)(dh + dr * kLdsRow + 8 * dq) = vh;
       *(v8h*)(dl + dr * kLdsRow + 8 * dq) = vl;
-      *(v8h*)(ds + dr * kLdsRow + 8 * dq) = vs;
+      if constexpr (!MSE) *(v8h*)(ds + dr * kLdsRow + 8 * dq) = vs;
     }
     __syncthreads();
     const int64_t aoff = row * a.Dp + 32 * ks + 8 * g;
     const v8h rh = *(const v8h*)(a.qr_hi + aoff);
     const v8h rl = *(const v8h*)(a.qr_lo + aoff);
-    const v8h ph = *(const v8h*)(a.qp_hi + aoff);
-    const v8h pl = *(const v8h*)(a.qp_lo + aoff);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int off = (16 * cb + n) * kLdsRow + 8 * g;
       const v8h bh = *(const v8h*)(dh + off);
       const v8h bl = *(const v8h*)(dl + off);
-      const v8h bs = *(const v8h*)(ds + off);
       am[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh, bh, am[cb], 0, 0, 0);
       am[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rl, bh, am[cb], 0, 0, 0);
       am[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh, bl, am[cb], 0, 0, 0);
-      aq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bs, aq[cb], 0, 0, 0);
-      aq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bs, aq[cb], 0, 0, 0);
+    }
+    if constexpr (!MSE) {
+      const v8h ph = *(const v8h*)(a.qp_hi + aoff);
+      const v8h pl = *(const v8h*)(a.qp_lo + aoff);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const v8h bs = *(const v8h*)(ds + (16 * cb + n) * kLdsRow + 8 * g);
+        aq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, bs, aq[cb], 0, 0, 0);
+        aq[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bs, aq[cb], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
@@ -244,8 +251,10 @@ struct SearchArgs {
   int* cand_i;           // [n_q][kChunk] record index within the chunk
 };
 
-template <int NB>
+template <int NB, bool MSE>
 __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
+  constexpr int CP = MSE ? NB : NB - 1;         // code planes
+  constexpr int NA = MSE ? 2 : 4;               // staged query arrays
   __shared__ __align__(16) _Float16 As[4][kQT * kLdsRow];
   __shared__ __align__(16) _Float16 Bs[3][kRT * kLdsRow];
   __shared__ float thr_s[kQT];
@@ -275,9 +284,10 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
 
   for (int w = 0; w < a.W; ++w) {
     __syncthreads();              // previous word's operands fully read
-    // stage the query rows: 4 arrays x 128 rows x 32 halves, 16 bytes a thread x 8
+    // stage the query rows: NA arrays x 128 rows x 32 halves, 16 bytes a thread
+    // x 2 NA
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 2 * NA; ++j) {
       const int c = tid + 256 * j;
       const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
       const v8h v = *(const v8h*)(a.qa[ar] + (q0 + row) * a.Dp + 32 * w + 8 * part);
@@ -294,9 +304,9 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
         const int bit = 16 * dh + e;
         uint32_t idx = 0;
 #pragma unroll
-        for (int p = 0; p < NB - 1; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
+        for (int p = 0; p < CP; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
         const uint32_t hl = ctab_s[idx];
-        const uint16_t sgn = ((wd[NB - 1] >> bit) & 1u) ? (uint16_t)0 : (uint16_t)0x8000;
+        const uint16_t sgn = (MSE || ((wd[NB - 1] >> bit) & 1u)) ? (uint16_t)0 : (uint16_t)0x8000;
         vh[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
         vl[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
         vg[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(gbits ^ sgn));
@@ -306,8 +316,10 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
       *(v8h*)(&Bs[0][off + 8]) = vh[1];
       *(v8h*)(&Bs[1][off]) = vl[0];
       *(v8h*)(&Bs[1][off + 8]) = vl[1];
-      *(v8h*)(&Bs[2][off]) = vg[0];
-      *(v8h*)(&Bs[2][off + 8]) = vg[1];
+      if constexpr (!MSE) {
+        *(v8h*)(&Bs[2][off]) = vg[0];
+        *(v8h*)(&Bs[2][off + 8]) = vg[1];
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -317,13 +329,13 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
       for (int qb = 0; qb < 2; ++qb) {
         const int off = (64 * wq + 32 * qb + col) * kLdsRow + 16 * kk + 8 * hh;
 #pragma unroll
-        for (int ar = 0; ar < 4; ++ar) A[qb][ar] = *(const v8h*)(&As[ar][off]);
+        for (int ar = 0; ar < NA; ++ar) A[qb][ar] = *(const v8h*)(&As[ar][off]);
       }
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int off = (64 * wr + 32 * rb + col) * kLdsRow + 16 * kk + 8 * hh;
 #pragma unroll
-        for (int ar = 0; ar < 3; ++ar) B[rb][ar] = *(const v8h*)(&Bs[ar][off]);
+        for (int ar = 0; ar < (MSE ? 2 : 3); ++ar) B[rb][ar] = *(const v8h*)(&Bs[ar][off]);
       }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -333,8 +345,10 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][3], B[rb][2], c, 0, 0, 0);
+          if constexpr (!MSE) {
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][3], B[rb][2], c, 0, 0, 0);
+          }
           acc[qb][rb] = c;
         }
     }
@@ -471,11 +485,19 @@ void fill_centroid_split(const tq_ctx* ctx, GemmArgs& g) {
 }
 
 template <int MODE>
-hipError_t launch_gemm(int b, const GemmArgs& g, dim3 grid, hipStream_t st) {
-  switch (b) {
-    case 2: hipLaunchKernelGGL((decoded_gemm_kernel<2, MODE>), grid, dim3(256), 0, st, g); break;
-    case 3: hipLaunchKernelGGL((decoded_gemm_kernel<3, MODE>), grid, dim3(256), 0, st, g); break;
-    default: hipLaunchKernelGGL((decoded_gemm_kernel<4, MODE>), grid, dim3(256), 0, st, g); break;
+hipError_t launch_gemm(const tq_ctx* ctx, const GemmArgs& g, dim3 grid, hipStream_t st) {
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: hipLaunchKernelGGL((decoded_gemm_kernel<1, true, MODE>), grid, dim3(256), 0, st, g); break;
+      case 2: hipLaunchKernelGGL((decoded_gemm_kernel<2, true, MODE>), grid, dim3(256), 0, st, g); break;
+      default: hipLaunchKernelGGL((decoded_gemm_kernel<3, true, MODE>), grid, dim3(256), 0, st, g); break;
+    }
+  } else {
+    switch (ctx->b) {
+      case 2: hipLaunchKernelGGL((decoded_gemm_kernel<2, false, MODE>), grid, dim3(256), 0, st, g); break;
+      case 3: hipLaunchKernelGGL((decoded_gemm_kernel<3, false, MODE>), grid, dim3(256), 0, st, g); break;
+      default: hipLaunchKernelGGL((decoded_gemm_kernel<4, false, MODE>), grid, dim3(256), 0, st, g); break;
+    }
   }
   return hipGetLastError();
 }
@@ -531,9 +553,11 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   p.Dp = ctx->Dp;
   p.n = n_queries;
   p.n_pad = L.rows_pad;
+  // MSE-only records need the Pi q rows alone (the S q half is never read)
+  const int prep_out = ctx->mse ? ctx->Dp : 2 * ctx->Dp;
   hipLaunchKernelGGL(row_prep_kernel,
                      dim3((unsigned)((L.rows_pad + kPrepRows - 1) / kPrepRows),
-                          (unsigned)((2 * ctx->Dp + 255) / 256)),
+                          (unsigned)((prep_out + 255) / 256)),
                      dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -582,10 +606,18 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
       g.rec0 = base;
       g.n_rec = len;
       const dim3 grid((unsigned)((len + kRT - 1) / kRT), (unsigned)(L.rows_pad / kQT));
-      switch (ctx->b) {
-        case 2: hipLaunchKernelGGL(search_gemm_kernel<2>, grid, dim3(256), 0, stream, g); break;
-        case 3: hipLaunchKernelGGL(search_gemm_kernel<3>, grid, dim3(256), 0, stream, g); break;
-        default: hipLaunchKernelGGL(search_gemm_kernel<4>, grid, dim3(256), 0, stream, g); break;
+      if (ctx->mse) {
+        switch (ctx->b) {
+          case 1: hipLaunchKernelGGL((search_gemm_kernel<1, true>), grid, dim3(256), 0, stream, g); break;
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, true>), grid, dim3(256), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<3, true>), grid, dim3(256), 0, stream, g); break;
+        }
+      } else {
+        switch (ctx->b) {
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, false>), grid, dim3(256), 0, stream, g); break;
+          case 3: hipLaunchKernelGGL((search_gemm_kernel<3, false>), grid, dim3(256), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<4, false>), grid, dim3(256), 0, stream, g); break;
+        }
       }
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -623,7 +655,7 @@ hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const ui
   g.out_ld = out_ld;
   const dim3 grid((unsigned)((n + kRecTile - 1) / kRecTile),
                   (unsigned)((ctx->Dp + kRowsTile - 1) / kRowsTile));
-  return launch_gemm<1>(ctx->b, g, grid, stream);
+  return launch_gemm<1>(ctx, g, grid, stream);
 }
 
 }  // namespace tq

@@ -116,6 +116,26 @@ def test_ctx_create_validation(tq, orc):
     assert L.tq_ctx_destroy(None) == tq.TQ_OK
 
 
+def test_ctx_create_mse_validation(tq):
+    """MSE-only contexts: b in 1..3 with 2^b centroids; checked before any
+    device call."""
+    L = tq.lib()
+    h = ctypes.c_void_p()
+    pi, _ = tq.tq_make_rotation(128, 0)
+    c, _, _ = tq.tq_lloyd_max(128, 2)
+    P = lambda a: a.ctypes.data
+    assert L.tq_ctx_create_mse(128, 2, P(pi), P(c), None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_ctx_create_mse(128, 0, P(pi), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create_mse(128, 4, P(pi), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create_mse(100, 2, P(pi), P(c), ctypes.byref(h)) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_ctx_create_mse(128, 2, None, P(c), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_ctx_create_mse(128, 2, P(pi), None, ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    bad = c.copy(); bad[0] *= 1.001                       # not symmetric
+    assert L.tq_ctx_create_mse(128, 2, P(pi), P(bad), ctypes.byref(h)) == tq.TQ_ERR_INVALID_ARG
+    assert h.value is None
+    assert L.tq_ctx_is_mse(None) == 0
+
+
 def test_hot_path_rejects_null_context(tq):
     L = tq.lib()
     assert L.tq_quantize_kv(None, None, 0, 1, 1, 128, 0, None, None, 0, 0, None) == \
