@@ -60,6 +60,9 @@ def parse():
                     choices=["decode", "long", "batched", "search", "attn_out", "decode_fused"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
+    ap.add_argument("--mse", action="store_true",
+                    help="long / search / attn_out / decode_fused: MSE-only records (b code "
+                         "bits, no QJL stage; b = 1..3)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling HBM "
                          "byte counters)")
@@ -107,6 +110,10 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mse and args.workload in ("decode", "batched"):
+        print("--mse applies to the long, search, attn_out and decode_fused workloads",
+              file=sys.stderr)
+        sys.exit(2)
     if args.workload != "decode":
         out = {"long": run_long, "batched": run_batched, "search": run_search,
                "attn_out": run_attn_out, "decode_fused": run_decode_fused}[args.workload](args)
@@ -311,8 +318,17 @@ def _timed(fn, reps, stream, flush=None):
 def _common(args, d, b, seed=0):
     import kv_cache_vector_pi_amd as tq
     pi, s = tq.tq_make_rotation(d, seed)
+    if getattr(args, "mse", False):
+        cent, _, _ = tq.tq_lloyd_max(d, b)
+        return tq.TqContext(d, b, pi, None, cent)
     cent, _, _ = tq.tq_lloyd_max(d, b - 1)
     return tq.TqContext(d, b, pi, s, cent)
+
+
+def _bits(args, two_stage, mse):
+    if args.bits:
+        return [args.bits]
+    return mse if args.mse else two_stage
 
 
 def _line(args, metric, value, unit, workload, extra):
@@ -320,6 +336,8 @@ def _line(args, metric, value, unit, workload, extra):
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic (seeded)", "config": workload}
     out.update(extra)
+    if getattr(args, "mse", False):
+        out["config"] = dict(out["config"], records="MSE-only: b code bits, no QJL stage")
     return out
 
 
@@ -338,7 +356,7 @@ def run_long(args):
 
     per_b = {}
     reps = max(5, min(args.steps, 20))
-    for b in ([args.bits] if args.bits else [2, 3, 4]):
+    for b in _bits(args, [2, 3, 4], [1, 2, 3]):
         ctx = _common(args, d, b)
         rec = tq.tq_record_words(d, b)
         kp = torch.zeros((n_kv * n_tok, rec), dtype=torch.int32, device=dev)
@@ -456,7 +474,8 @@ def run_attn_out(args):
     import torch
     import kv_cache_vector_pi_amd as tq
     import workloads
-    dev, d, b, n_kv, n_q, n_tok, L = "cuda", 128, 4, 8, 32, 32768, args.layers
+    dev, d, n_kv, n_q, n_tok, L = "cuda", 128, 8, 32, 32768, args.layers
+    b = _bits(args, [4], [3])[0]
     stream = torch.cuda.current_stream()
     ctx = _common(args, d, b)
     rw = tq.tq_record_words(d, b)
@@ -488,7 +507,7 @@ def run_attn_out(args):
     return _line(args, "attention output from packed values: values/sec", rec / (ms * 1e-3),
                  "values/s",
                  {"workload": "llama-3.1-8b decode layer values: 8 kv / 32 q heads, d=128, "
-                              "32768 tokens, b=4; 32 layer caches per launch"},
+                              f"32768 tokens, b={b}; 32 layer caches per launch"},
                  {"dtype": "f32", "ms_mean": ms, "ms_median": med,
                   "GB_per_s": alg / (ms * 1e-3) / 1e9,
                   "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -501,7 +520,8 @@ def run_decode_fused(args):
     import torch
     import kv_cache_vector_pi_amd as tq
     import workloads
-    dev, d, b, n_kv, n_q, n_tok, L = "cuda", 128, 4, 8, 32, 32768, args.layers
+    dev, d, n_kv, n_q, n_tok, L = "cuda", 128, 8, 32, 32768, args.layers
+    b = _bits(args, [4], [3])[0]
     stream = torch.cuda.current_stream()
     ctx = _common(args, d, b)
     rw = tq.tq_record_words(d, b)
@@ -532,7 +552,7 @@ def run_decode_fused(args):
     return _line(args, "fused decode attention from packed K/V: tokens/sec (all heads)",
                  L * n_tok / (ms * 1e-3), "tokens/s",
                  {"workload": "llama-3.1-8b decode layer: 8 kv / 32 q heads, d=128, 32768 "
-                              "cached tokens, b=4 K and V; 32 layer caches per call"},
+                              f"cached tokens, b={b} K and V; 32 layer caches per call"},
                  {"dtype": "int8-mfma/fp32", "ms_mean": ms, "ms_median": med,
                   "GB_per_s": alg / (ms * 1e-3) / 1e9,
                   "hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -562,7 +582,7 @@ def run_search(args):
         exact = torch.gather(cand_i, 1, pos)
     per_b = {}
     reps = max(3, min(args.steps, 10))
-    for b in ([args.bits] if args.bits else [2, 4]):
+    for b in _bits(args, [2, 4], [2, 3]):
         ctx = _common(args, d, b)
         planes, norms = tq.alloc_records(n_db, d, b, dev)
 

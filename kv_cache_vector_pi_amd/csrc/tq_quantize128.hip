@@ -136,7 +136,7 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
 // NB: words per record group; MSE: all NB planes are code planes (no QJL
 // stage, gamma stored as 0), else NB-1 code planes and the sign plane.
 template <int NB, bool BF16, bool MSE>
-__global__ void __launch_bounds__(256, 2) quantize128_kernel(Q128Args a) {
+__global__ void __launch_bounds__(256, MSE ? 3 : 2) quantize128_kernel(Q128Args a) {
   constexpr int CP = MSE ? NB : NB - 1;   // code planes
   constexpr int K = 1 << CP;
   constexpr int KH = K / 2;           // positive centroids
