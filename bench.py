@@ -192,12 +192,11 @@ def main():
     ev_b = torch.cuda.Event(enable_timing=True)
 
     def step(times=None):
-        # quantize the new token of each (kv head, layer): "head" = (h, l) pair
-        tq.tq_quantize_kv(ctx, newK.view(N_KV * L, 1, D), k_planes, k_norms,
-                          dst_stride_head=N_TOK, dst_token0=N_TOK - 1)
-        tq.tq_quantize_kv(ctx, newV.view(N_KV * L, 1, D), v_planes, v_norms,
-                          dst_stride_head=N_TOK, dst_token0=N_TOK - 1)
-        tq.tq_attn_prepare(ctx, q_all, L, N_Q, N_Q * D, N_KV, ws)
+        # one launch: quantize the new K and V token of each (kv head, layer)
+        # ("head" = (h, l) pair) and prepare the 32 layers' queries
+        tq.tq_decode_step_prepare(ctx, newK.view(N_KV * L, 1, D), newV.view(N_KV * L, 1, D),
+                                  k_planes, k_norms, v_planes, v_norms, q_all, L, N_Q, N_Q * D,
+                                  N_KV, ws, dst_stride_head=N_TOK, dst_token0=N_TOK - 1)
         if times is not None:
             ev_a.record(stream)
         tq.tq_attn_logits_prepared(ctx, ws, L, N_Q, k_planes, k_norms, N_KV, L * N_TOK,

@@ -243,6 +243,30 @@ TQ_API tq_status tq_attn_logits_prepared(const tq_ctx* ctx, const void* workspac
                                          float scale, float* logits,
                                          int64_t logits_stride_head, void* stream);
 
+/* The start of a decode step (turboquant.net pseudo-code, "integrate into
+ * Transformer attention": the new key and value are quantized into the cache
+ * and the query is prepared for the logits over packed keys) in one launch:
+ * exactly tq_quantize_kv(k_new -> k_planes/k_norms),
+ * tq_quantize_kv(v_new -> v_planes/v_norms) and tq_attn_prepare(q ->
+ * workspace), with bit-identical results.  K and V share dtype, sizes,
+ * strides and the destination indexing (record (h, t) at
+ * h*dst_stride_head + dst_token0 + t of each cache); the preparation
+ * arguments are those of tq_attn_prepare.  At d = 128 the three jobs run in
+ * one grid (the small per-step jobs then cost one launch instead of three);
+ * other d run them as three launches.
+ * Errors: as tq_quantize_kv for either K or V, and as tq_attn_prepare;
+ * nothing is launched when any check fails.  n_tokens == 0 (or n_heads == 0)
+ * skips the quantization, batch == 0 the preparation. */
+TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, const void* v_new,
+                                        int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
+                                        int64_t x_stride_token, int64_t x_stride_head,
+                                        uint32_t* k_planes, uint16_t* k_norms,
+                                        uint32_t* v_planes, uint16_t* v_norms,
+                                        int64_t dst_stride_head, int64_t dst_token0,
+                                        const float* q, int32_t batch, int32_t n_q_heads,
+                                        int64_t q_stride_batch, int32_t n_kv_heads,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace for tq_attn_output, in bytes (0 for invalid sizes). */
 TQ_API size_t tq_attn_output_workspace_bytes(const tq_ctx* ctx, int32_t batch,
                                              int32_t n_q_heads, int32_t n_kv_heads,

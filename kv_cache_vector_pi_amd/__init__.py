@@ -31,7 +31,7 @@ EXPORTS = [
     "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
     "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
-    "tq_ctx_create_mse", "tq_ctx_is_mse",
+    "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare",
 ]
 
 
@@ -68,6 +68,8 @@ _sig("tq_ctx_create", _i32, [_i32, _i32, _P, _P, _P, ctypes.POINTER(_P)])
 _sig("tq_ctx_destroy", _i32, [_P])
 _sig("tq_ctx_create_mse", _i32, [_i32, _i32, _P, _P, ctypes.POINTER(_P)])
 _sig("tq_ctx_is_mse", _i32, [_P])
+_sig("tq_decode_step_prepare", _i32, [_P, _P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _P,
+                                      _i64, _i64, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
 _sig("tq_ctx_dim", _i32, [_P])
 _sig("tq_ctx_bits", _i32, [_P])
 _sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
@@ -108,8 +110,10 @@ def _ptr(t):
 
 
 def _stream(stream=None):
+    """Raw hipStream_t for a torch.cuda.Stream, a raw handle, or None (the
+    current stream)."""
     if stream is not None:
-        return stream
+        return getattr(stream, "cuda_stream", stream)
     import torch
     return torch.cuda.current_stream().cuda_stream
 
@@ -272,6 +276,33 @@ def tq_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, worksp
     st = _lib.tq_attn_prepare(ctx.handle, _ptr(q), batch, n_q_heads, q_stride_batch, n_kv_heads,
                               _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "tq_attn_prepare")
+
+
+def tq_decode_step_prepare(ctx, k_new, v_new, k_planes, k_norms, v_planes, v_norms, q, batch,
+                           n_q_heads, q_stride_batch, n_kv_heads, workspace, dst_stride_head,
+                           dst_token0=0, stream=None):
+    """Quantize k_new and v_new ([n_heads, n_tokens, d], same dtype, sizes and
+    strides) into the two caches and prepare q into workspace, in one launch
+    at d = 128 (see tq.h)."""
+    import torch
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or \
+            k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share dtype, shape and strides")
+    if k_new.dtype == torch.bfloat16:
+        dt = TQ_BF16
+    elif k_new.dtype == torch.float32:
+        dt = TQ_F32
+    else:
+        raise TypeError(f"unsupported dtype {k_new.dtype}")
+    n_heads, n_tokens = k_new.shape[0], k_new.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_decode_step_prepare(ctx.handle, _ptr(k_new), _ptr(v_new), dt, n_tokens, n_heads,
+                                     k_new.stride(1), k_new.stride(0), _ptr(k_planes),
+                                     _ptr(k_norms), _ptr(v_planes), _ptr(v_norms),
+                                     dst_stride_head, dst_token0, _ptr(q), batch, n_q_heads,
+                                     q_stride_batch, n_kv_heads, _ptr(workspace), ws_bytes,
+                                     _stream(stream))
+    _check(st, "tq_decode_step_prepare")
 
 
 def tq_attn_logits_prepared(ctx, workspace, batch, n_q_heads, planes, norms, n_kv_heads,

@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["tq_host.cpp", "tq_logits.hip", "tq_quantize.hip", "tq_quantize128.hip",
            "tq_search.hip", "tq_attn_out.hip",
-           "tq_decode.hip"]
+           "tq_decode.hip", "tq_step.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-fvisibility=hidden",

@@ -450,30 +450,107 @@ TQ_API int32_t tq_ctx_bits(const tq_ctx* ctx) { return ctx ? ctx->b : 0; }
 // ---------------------------------------------------------------------------
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+namespace {
+
+// Argument checks of one quantize job (fn names the entry point in messages);
+// *empty is set for a no-op job.
+tq_status check_quantize(const char* fn, const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                         int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                         int64_t x_stride_head, const uint32_t* planes, const uint16_t* norms,
+                         int64_t dst_stride_head, int64_t dst_token0, bool* empty) {
+  *empty = false;
+  if (n_tokens < 0 || n_heads < 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: n_tokens=%lld n_heads=%d", fn, (long long)n_tokens,
+                n_heads);
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16)
+    return fail(TQ_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, x_dtype);
+  if (n_tokens == 0 || n_heads == 0) {
+    *empty = true;
+    return TQ_OK;
+  }
+  if (!x || !planes || !norms) return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (x_stride_token < ctx->d || (n_heads > 1 && x_stride_head < 0) || dst_stride_head < 0 ||
+      dst_token0 < 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: bad strides", fn);
+  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(x, 16) ||
+      (x_stride_token * esz) % 16 != 0 || (x_stride_head * esz) % 16 != 0)
+    return fail(TQ_ERR_INVALID_ARG,
+                "%s: planes, x and x strides must be 16-byte aligned, norms 4-byte", fn);
+  return TQ_OK;
+}
+
+// Argument checks of one query preparation; *empty is set for batch == 0.
+tq_status check_prepare(const char* fn, const tq_ctx* ctx, const float* q, int32_t batch,
+                        int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
+                        const void* workspace, size_t workspace_bytes, bool* empty) {
+  *empty = false;
+  if (batch < 0 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: batch=%d n_q=%d n_kv=%d", fn, batch, n_q_heads,
+                n_kv_heads);
+  if (batch == 0) {
+    *empty = true;
+    return TQ_OK;
+  }
+  if (!q || !workspace) return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (q_stride_batch < (int64_t)n_q_heads * ctx->d && batch > 1)
+    return fail(TQ_ERR_INVALID_ARG, "%s: q_stride_batch too small", fn);
+  if (!aligned(workspace, 16) || !aligned(q, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  return TQ_OK;
+}
+
+}  // namespace
+
 TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                                 int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                                 int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                                 int64_t dst_stride_head, int64_t dst_token0, void* stream) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_kv: ctx is NULL");
-  if (n_tokens < 0 || n_heads < 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_kv: n_tokens=%lld n_heads=%d",
-                (long long)n_tokens, n_heads);
-  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16)
-    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_kv: unknown dtype %d", x_dtype);
-  if (n_tokens == 0 || n_heads == 0) return ok();
-  if (!x || !planes || !norms) return fail(TQ_ERR_INVALID_ARG, "tq_quantize_kv: NULL pointer");
-  if (x_stride_token < ctx->d || (n_heads > 1 && x_stride_head < 0) || dst_stride_head < 0 ||
-      dst_token0 < 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_quantize_kv: bad strides");
-  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
-  if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(x, 16) ||
-      (x_stride_token * esz) % 16 != 0 || (x_stride_head * esz) % 16 != 0)
-    return fail(TQ_ERR_INVALID_ARG,
-                "tq_quantize_kv: planes, x and x strides must be 16-byte aligned, norms 4-byte");
+  bool empty;
+  const tq_status st = check_quantize("tq_quantize_kv", ctx, x, x_dtype, n_tokens, n_heads,
+                                      x_stride_token, x_stride_head, planes, norms,
+                                      dst_stride_head, dst_token0, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
   hipError_t e = tq::launch_quantize(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
                                      x_stride_head, planes, norms, dst_stride_head, dst_token0,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_kv: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, const void* v_new,
+                                        int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
+                                        int64_t x_stride_token, int64_t x_stride_head,
+                                        uint32_t* k_planes, uint16_t* k_norms,
+                                        uint32_t* v_planes, uint16_t* v_norms,
+                                        int64_t dst_stride_head, int64_t dst_token0,
+                                        const float* q, int32_t batch, int32_t n_q_heads,
+                                        int64_t q_stride_batch, int32_t n_kv_heads,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_decode_step_prepare";
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+  bool no_k, no_v, no_q;
+  tq_status st = check_quantize(fn, ctx, k_new, x_dtype, n_tokens, n_heads, x_stride_token,
+                                x_stride_head, k_planes, k_norms, dst_stride_head, dst_token0,
+                                &no_k);
+  if (st == TQ_OK)
+    st = check_quantize(fn, ctx, v_new, x_dtype, n_tokens, n_heads, x_stride_token,
+                        x_stride_head, v_planes, v_norms, dst_stride_head, dst_token0, &no_v);
+  if (st == TQ_OK)
+    st = check_prepare(fn, ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
+                       workspace_bytes, &no_q);
+  if (st != TQ_OK) return st;
+  if (no_k && no_q) return ok();
+  hipError_t e = tq::launch_decode_step_prepare(
+      ctx, k_new, v_new, x_dtype, no_k ? 0 : n_tokens, no_k ? 0 : n_heads, x_stride_token,
+      x_stride_head, k_planes, k_norms, v_planes, v_norms, dst_stride_head, dst_token0, q,
+      no_q ? 0 : batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_decode_step_prepare: launch");
   return ok();
 }
 
@@ -538,19 +615,11 @@ TQ_API tq_status tq_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batc
                                  int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: ctx is NULL");
-  if (batch < 0 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0)
-    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: batch=%d n_q=%d n_kv=%d", batch,
-                n_q_heads, n_kv_heads);
-  if (batch == 0) return ok();
-  if (!q || !workspace) return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: NULL pointer");
-  if (q_stride_batch < (int64_t)n_q_heads * ctx->d && batch > 1)
-    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: q_stride_batch too small");
-  if (!aligned(workspace, 16) || !aligned(q, 4))
-    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: misaligned pointer");
-  const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
-  if (workspace_bytes < need)
-    return fail(TQ_ERR_INVALID_ARG, "tq_attn_prepare: workspace %zu < %zu bytes",
-                workspace_bytes, need);
+  bool empty;
+  const tq_status st = check_prepare("tq_attn_prepare", ctx, q, batch, n_q_heads, q_stride_batch,
+                                     n_kv_heads, workspace, workspace_bytes, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
   hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
                                          workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_attn_prepare: launch");

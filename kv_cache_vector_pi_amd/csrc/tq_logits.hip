@@ -30,6 +30,7 @@
 
 #include "tq_dev.h"
 #include "tq_internal.h"
+#include "tq_prep.h"
 
 namespace tq {
 namespace {
@@ -43,189 +44,8 @@ using dev::rb_bytes;
 using dev::load_group;
 using dev::bit_lanes;
 
-struct PrepArgs {
-  const float* q;          // [batch][n_q][d], batch stride q_stride_batch
-  int64_t q_stride_batch;
-  const float* pit;        // [d][d] Pi^T
-  const float* st;         // [d][d] S^T
-  char* ws;
-  int d, W, nc, G, n_kv, n_rb, n_q;     // nc: MFMA calls per word step
-  float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
-  int mask[kMaxVec];       // code-plane subsets
-  int nv;                  // number of subsets
-  float c0;                // c[0]
-};
-
-__device__ inline float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ inline float wave_max(float v) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// rint(Q / 2^k) for k >= 1 (half away from -inf), Q for k == 0
-__device__ inline int shift_round(int Q, int k) {
-  return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
-}
-
-// Query preparation: one block per (row block of 4 q heads, kv head, batch).
-// Computes Pi q and S q in fp32 (one thread per output row over a contiguous
-// column of Pi^T / S^T, the 4 queries sharing every table load), picks a
-// power-of-two fixed-point scale per head and part, and writes the int8-limb
-// A operands in the exact lane order the logit kernel consumes.  Slots
-// beyond the GQA group size get zero weights.
 __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
-  extern __shared__ float sm[];
-  const int Dp = 32 * a.W;
-  float* qv = sm;                 // [d][4]: coordinate j of slot hh at 4j + hh
-  float* qr = qv + 4 * a.d;       // [4][Dp] Pi q (zero padded)
-  float* qp = qr + 4 * Dp;        // [4][Dp] S q
-  __shared__ int qfix_e[4][2];
-
-  const int rb = blockIdx.x, h = blockIdx.y, bi = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int it = tid; it < 4 * a.d; it += 256) {
-    const int hh = it / a.d, j = it - hh * a.d;
-    const int slot = 4 * rb + hh;
-    qv[4 * j + hh] = slot < a.G
-        ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.d + j] : 0.f;
-  }
-  __syncthreads();
-  // Outputs in chunks of 256 (Pi rows, then S rows): thread (quad, jg)
-  // accumulates 4 consecutive outputs x 4 slots over the jg-th quarter of the
-  // coordinates, reading float4 rows of Pi^T / S^T; the four partial sums are
-  // then added in a fixed order (deterministic).
-  {
-    const int quad = tid & 63, jg = tid >> 6;
-    const int jl = (a.d + 3) / 4;
-    const int ja = jg * jl, jb = min(a.d, ja + jl);
-    for (int o0 = 0; o0 < 2 * Dp; o0 += 256) {
-      const int o = o0 + 4 * quad;
-      const bool in = o < 2 * Dp;
-      const bool sk = o >= Dp;
-      const int r = sk ? o - Dp : o;                 // multiple of 4; r < d => r + 3 < d
-      float4 acc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (in && r < a.d) {
-        const float* tab = (sk ? a.st : a.pit) + r;
-        auto fma16 = [&](const float4 t, const float4 qq) {
-          acc[0].x = fmaf(t.x, qq.x, acc[0].x); acc[0].y = fmaf(t.y, qq.x, acc[0].y);
-          acc[0].z = fmaf(t.z, qq.x, acc[0].z); acc[0].w = fmaf(t.w, qq.x, acc[0].w);
-          acc[1].x = fmaf(t.x, qq.y, acc[1].x); acc[1].y = fmaf(t.y, qq.y, acc[1].y);
-          acc[1].z = fmaf(t.z, qq.y, acc[1].z); acc[1].w = fmaf(t.w, qq.y, acc[1].w);
-          acc[2].x = fmaf(t.x, qq.z, acc[2].x); acc[2].y = fmaf(t.y, qq.z, acc[2].y);
-          acc[2].z = fmaf(t.z, qq.z, acc[2].z); acc[2].w = fmaf(t.w, qq.z, acc[2].w);
-          acc[3].x = fmaf(t.x, qq.w, acc[3].x); acc[3].y = fmaf(t.y, qq.w, acc[3].y);
-          acc[3].z = fmaf(t.z, qq.w, acc[3].z); acc[3].w = fmaf(t.w, qq.w, acc[3].w);
-        };
-        int j = ja;
-        // batches of 8 independent row loads in flight
-        for (; j + 8 <= jb; j += 8) {
-          float4 t[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) t[u] = *(const float4*)(tab + (int64_t)(j + u) * a.d);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) fma16(t[u], *(const float4*)&qv[4 * (j + u)]);
-        }
-        for (; j < jb; ++j)
-          fma16(*(const float4*)(tab + (int64_t)j * a.d), *(const float4*)&qv[4 * j]);
-      }
-      // slot i of outputs r..r+3 -> (sk ? qp : qr)[i * Dp + r ..]
-      float* dst = (sk ? qp : qr) + r;
-      for (int g = 0; g < 4; ++g) {
-        if (jg == g && in) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float4* d4 = (float4*)(dst + i * Dp);
-            if (g == 0) {
-              *d4 = acc[i];
-            } else {
-              float4 v = *d4;
-              v.x += acc[i].x; v.y += acc[i].y; v.z += acc[i].z; v.w += acc[i].w;
-              *d4 = v;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
-  // wave hh: max |Pi q|, max |S q|, sum Pi q, sum S q of slot hh
-  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rb_bytes(a.W, a.nc);
-  {
-    const float* r1 = qr + wave * Dp;
-    const float* r2 = qp + wave * Dp;
-    float m1 = 0.f, m2 = 0.f, t1 = 0.f, t2 = 0.f;
-    for (int j = lane; j < Dp; j += 64) {
-      m1 = fmaxf(m1, fabsf(r1[j]));
-      m2 = fmaxf(m2, fabsf(r2[j]));
-      t1 += r1[j];
-      t2 += r2[j];
-    }
-    m1 = wave_max(m1);
-    m2 = wave_max(m2);
-    t1 = wave_sum(t1);
-    t2 = wave_sum(t2);
-    if (lane == 0) {
-      float wmax = 0.f;
-      for (int v = 0; v < a.nv; ++v) wmax = fmaxf(wmax, fabsf(a.wm2[v]));
-      const float vmax1 = wmax * m1, vmax2 = 2.f * m2;
-      int e1 = 0, e2 = 0;
-      if (vmax1 > 0.f) { int ex; frexpf(vmax1, &ex); e1 = min(30 - ex, 120); }
-      if (vmax2 > 0.f) { int ex; frexpf(vmax2, &ex); e2 = min(30 - ex, 120); }
-      qfix_e[wave][0] = e1;
-      qfix_e[wave][1] = e2;
-      float4 cst;
-      cst.x = ldexpf(1.f, -e1);
-      cst.y = ldexpf(1.f, -e2);
-      cst.z = a.c0 * t1;
-      cst.w = -t2;
-      float4* cdst = (float4*)(rbase + (size_t)n_ws(a.W) * a.nc * 64 * 16);
-      cdst[wave] = cst;
-    }
-  }
-  __syncthreads();
-  const int nc = a.nc, nws = n_ws(a.W);
-  // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
-  // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
-  // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
-  // (-2 w_vec Pi q, or 2 S q for the sign plane); its balanced base-256
-  // digit L is ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that
-  // byte ^ 0x80.
-  const int items = 4 * nws * nc * 16;
-  for (int it = tid; it < items; it += 256) {
-    const int L = it & 3, g = (it >> 2) & 3;
-    const int rest = it >> 4;
-    const int c = rest % nc, wsi = (rest / nc) % nws, hh = rest / (nc * nws);
-    const int w = 4 * wsi + g;
-    const bool sgn = c >= 2 * a.nv;
-    const int kbase = sgn ? 4 * (c - 2 * a.nv) : 4 * (c % 2);
-    const float wv = sgn ? 2.f : a.wm2[c / 2];
-    const float* src = (sgn ? qp : qr) + hh * Dp;
-    const int e = qfix_e[hh][sgn ? 1 : 0];
-    uint32_t outw[4];
-#pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx) {
-      const int k = kbase + sidx;
-      uint32_t word = 0;
-#pragma unroll
-      for (int el = 0; el < 4; ++el) {
-        const int j = 32 * w + 8 * el + k;
-        const int Q = (w < a.W && j < a.d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
-        const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
-        const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
-        word |= (digit ^ 0x80u) << (8 * el);
-      }
-      outw[sidx] = word;
-    }
-    const int lanei = 16 * g + 4 * hh + L;
-    uint4* dst = (uint4*)(rbase + (((size_t)wsi * nc + c) * 64 + lanei) * 16);
-    *dst = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-  }
+  prep_block(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 struct AttnArgs {
@@ -514,29 +334,15 @@ size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
                                int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
                                void* workspace, hipStream_t stream) {
-  const int G = n_q_heads / n_kv_heads;
-  const int n_rb = (G + 3) / 4;
-  PrepArgs p{};
-  p.q = q;
-  p.q_stride_batch = q_stride_batch;
-  p.pit = ctx->t.pit32;
-  p.st = ctx->t.st32;
-  p.ws = (char*)workspace;
-  p.d = ctx->d;
-  p.W = ctx->W;
-  p.nc = n_calls(ctx->cp, !ctx->mse);
-  p.G = G;
-  p.n_kv = n_kv_heads;
-  p.n_rb = n_rb;
-  p.n_q = n_q_heads;
-  p.nv = ctx->n_mono;
-  for (int v = 0; v < ctx->n_mono; ++v) {
-    p.wm2[v] = (float)(-2.0 * ctx->mono_w[v]);
-    p.mask[v] = ctx->mono_mask[v];
-  }
-  p.c0 = (float)ctx->c0;
-  const size_t shm = sizeof(float) * (4 * ctx->d + 8 * ctx->Dp);     // <= 48 KB at d = 2048
-  hipLaunchKernelGGL(attn_prep_kernel, dim3(n_rb, n_kv_heads, batch), dim3(256), shm, stream, p);
+  PrepArgs p;
+  size_t shm;
+  dim3 grid;
+  prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, p, shm, grid);
+  // raise the dynamic-LDS limit once (never inside a sequence a caller may capture)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)attn_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(attn_prep_kernel, grid, dim3(256), shm, stream, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,243 @@
+// Query preparation for the logit kernels (turboquant.net pseudo-code,
+// "integrate into attention": the query is rotated and projected once, the
+// keys stay packed): Pi q and S q per query head, turned into the int8-limb
+// A operands of v_mfma_i32_16x16x64_i8 in the lane order the logit, fused
+// decode and step kernels consume.
+#pragma once
+#include <algorithm>
+#include <cmath>
+
+#include "tq_dev.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+struct PrepArgs {
+  const float* q;          // [batch][n_q][d], batch stride q_stride_batch
+  int64_t q_stride_batch;
+  const float* pit;        // [d][d] Pi^T
+  const float* st;         // [d][d] S^T
+  char* ws;
+  int d, W, nc, G, n_kv, n_rb, n_q;     // nc: MFMA calls per word step
+  int n_parts;                          // 2: code and sign parts, 1: MSE-only records
+  int nq;                               // output quads per chunk (power of two <= 64)
+  float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
+  int mask[kMaxVec];       // code-plane subsets
+  int nv;                  // number of subsets
+  float c0;                // c[0]
+};
+
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// rint(Q / 2^k) for k >= 1 (half away from -inf), Q for k == 0
+__device__ inline int shift_round(int Q, int k) {
+  return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
+}
+
+// Query preparation: one block per (row block of 4 q heads and part, kv
+// head, batch).  Part 0 computes Pi q and the A operands of the code calls,
+// part 1 (two-stage records only) S q and those of the sign calls.  Outputs
+// come in chunks of 4 nq: thread (quad, jg) accumulates 4 consecutive
+// outputs x 4 query slots over the jg-th of nj coordinate ranges (one float4
+// row of Pi^T / S^T per coordinate, all of a thread's row loads in flight),
+// and the nj partial sums are added in a fixed order (deterministic).  Then
+// a power-of-two fixed-point scale per head, and the int8-limb A operands in
+// the exact lane order the logit kernels consume.  Slots beyond the GQA
+// group size get zero weights.
+// The work of block (bx, by, bz) of that grid (the kernel body: 256 threads).
+__device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, int bz) {
+  extern __shared__ float sm[];
+  const int Dp = 32 * a.W;
+  const int nq = a.nq, nj = 256 / nq;
+  float* qv = sm;                 // [d][4]: coordinate j of slot hh at 4j + hh
+  float* out = qv + 4 * a.d;      // [4][Dp] this part's outputs (zero padded)
+  float* red = out + 4 * Dp;      // [4 waves][16][nq] partial sums
+  __shared__ int qfix_e[4];
+
+  const int rb = bx / a.n_parts, part = bx - rb * a.n_parts;
+  const int h = by, bi = bz;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int it = tid; it < 4 * a.d; it += 256) {
+    const int hh = it / a.d, j = it - hh * a.d;
+    const int slot = 4 * rb + hh;
+    qv[4 * j + hh] = slot < a.G
+        ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.d + j] : 0.f;
+  }
+  __syncthreads();
+  {
+    const float* tab = part ? a.st : a.pit;
+    const int quad = tid & (nq - 1), jg = tid / nq;    // nq: a power of two <= 64
+    const int jl = (a.d + nj - 1) / nj;
+    const int ja = min(a.d, jg * jl), jb = min(a.d, ja + jl);
+    for (int o0 = 0; o0 < Dp; o0 += 4 * nq) {
+      const int r = o0 + 4 * quad;                     // multiple of 4; r < d => r + 3 < d
+      float acc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+      if (r < a.d) {
+        auto fma16 = [&](const float4 t, const float4 qq) {
+          const float tv[4] = {t.x, t.y, t.z, t.w}, qs[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(tv[e], qs[i], acc[i][e]);
+        };
+        const float* tr = tab + r;
+        int j = ja;
+        for (; j + 16 <= jb; j += 16) {                // 16 independent row loads in flight
+          float4 t[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) t[u] = *(const float4*)(tr + (int64_t)(j + u) * a.d);
+#pragma unroll
+          for (int u = 0; u < 16; ++u) fma16(t[u], *(const float4*)&qv[4 * (j + u)]);
+        }
+        for (; j < jb; ++j) fma16(*(const float4*)(tr + (int64_t)j * a.d), *(const float4*)&qv[4 * j]);
+      }
+      // partial sums of the 64 / nq coordinate groups of a wave (lanes nq apart)
+      for (int off = nq; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
+      if (lane < nq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red[(wave * 16 + 4 * i + e) * nq + quad] = acc[i][e];
+      __syncthreads();
+      for (int it = tid; it < 16 * nq; it += 256) {
+        const int k = it / nq, qd = it - k * nq;       // k = 4 slot + element
+        const float v = (red[k * nq + qd] + red[(16 + k) * nq + qd]) +
+                        (red[(32 + k) * nq + qd] + red[(48 + k) * nq + qd]);
+        const int o = o0 + 4 * qd + (k & 3);
+        if (o < Dp) out[(k >> 2) * Dp + o] = v;
+      }
+      __syncthreads();
+    }
+  }
+  // wave hh: max |out| and sum of out for slot hh -> scale and offsets
+  char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * dev::rb_bytes(a.W, a.nc);
+  {
+    const float* r1 = out + wave * Dp;
+    float m1 = 0.f, t1 = 0.f;
+    for (int j = lane; j < Dp; j += 64) {
+      m1 = fmaxf(m1, fabsf(r1[j]));
+      t1 += r1[j];
+    }
+    m1 = wave_max(m1);
+    t1 = wave_sum(t1);
+    if (lane == 0) {
+      float wmax = 2.f;                                 // sign calls: weight 2 S q
+      if (part == 0) {
+        wmax = 0.f;
+        for (int v = 0; v < a.nv; ++v) wmax = fmaxf(wmax, fabsf(a.wm2[v]));
+      }
+      const float vmax = wmax * m1;
+      int e = 0;
+      if (vmax > 0.f) { int ex; frexpf(vmax, &ex); e = min(30 - ex, 120); }
+      qfix_e[wave] = e;
+      // per slot: x mse scale, y qjl scale, z mse offset, w qjl offset
+      float* cdst = (float*)(rbase + (size_t)dev::n_ws(a.W) * a.nc * 64 * 16) + 4 * wave;
+      if (part == 0) {
+        cdst[0] = ldexpf(1.f, -e);
+        cdst[2] = a.c0 * t1;
+        if (a.n_parts == 1) {        // no sign calls: the QJL terms are zero
+          cdst[1] = 0.f;
+          cdst[3] = 0.f;
+        }
+      } else {
+        cdst[1] = ldexpf(1.f, -e);
+        cdst[3] = -t1;
+      }
+    }
+  }
+  __syncthreads();
+  const int nws = dev::n_ws(a.W);
+  const int c_begin = part ? 2 * a.nv : 0, n_c = part ? a.nc - 2 * a.nv : 2 * a.nv;
+  // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
+  // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
+  // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
+  // (-2 w_vec Pi q, or 2 S q for the sign plane); its balanced base-256
+  // digit L is ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that
+  // byte ^ 0x80.
+  const int items = 4 * nws * n_c * 16;
+  for (int it = tid; it < items; it += 256) {
+    const int L = it & 3, g = (it >> 2) & 3;
+    const int rest = it >> 4;
+    const int cl = rest % n_c, wsi = (rest / n_c) % nws, hh = rest / (n_c * nws);
+    const int c = c_begin + cl;
+    const int w = 4 * wsi + g;
+    const int kbase = part ? 4 * cl : 4 * (c % 2);
+    const float wv = part ? 2.f : a.wm2[c / 2];
+    const float* src = out + hh * Dp;
+    const int e = qfix_e[hh];
+    uint32_t outw[4];
+#pragma unroll
+    for (int sidx = 0; sidx < 4; ++sidx) {
+      const int k = kbase + sidx;
+      uint32_t word = 0;
+#pragma unroll
+      for (int el = 0; el < 4; ++el) {
+        const int j = 32 * w + 8 * el + k;
+        const int Q = (w < a.W && j < a.d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
+        const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+        const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
+        word |= (digit ^ 0x80u) << (8 * el);
+      }
+      outw[sidx] = word;
+    }
+    const int lanei = 16 * g + 4 * hh + L;
+    uint4* dst = (uint4*)(rbase + (((size_t)wsi * a.nc + c) * 64 + lanei) * 16);
+    *dst = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+  }
+}
+
+// ---- host side -------------------------------------------------------------
+// Arguments, dynamic LDS bytes and grid of the preparation of `batch` query
+// sets of n_q_heads heads against n_kv_heads key heads into `workspace`.
+inline void prep_args(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,
+                      int64_t q_stride_batch, int32_t n_kv_heads, void* workspace, PrepArgs& p,
+                      size_t& shm, dim3& grid) {
+  const int G = n_q_heads / n_kv_heads;
+  const int n_rb = (G + 3) / 4;
+  p = PrepArgs{};
+  p.q = q;
+  p.q_stride_batch = q_stride_batch;
+  p.pit = ctx->t.pit32;
+  p.st = ctx->t.st32;
+  p.ws = (char*)workspace;
+  p.d = ctx->d;
+  p.W = ctx->W;
+  p.nc = dev::n_calls(ctx->cp, !ctx->mse);
+  p.G = G;
+  p.n_kv = n_kv_heads;
+  p.n_rb = n_rb;
+  p.n_q = n_q_heads;
+  p.nv = ctx->n_mono;
+  for (int v = 0; v < ctx->n_mono; ++v) {
+    p.wm2[v] = (float)(-2.0 * ctx->mono_w[v]);
+    p.mask[v] = ctx->mono_mask[v];
+  }
+  p.c0 = (float)ctx->c0;
+  p.n_parts = ctx->mse ? 1 : 2;
+  int nq = 64;
+  while (nq > ctx->Dp / 4) nq >>= 1;
+  p.nq = nq;
+  // q [d][4], outputs [4][Dp], partial sums [4][16][nq]: <= 80 KB at d = 2048
+  shm = sizeof(float) * (4 * ctx->d + 4 * ctx->Dp + 64 * nq);
+  grid = dim3(n_rb * p.n_parts, n_kv_heads, batch);
+}
+
+}  // namespace
+}  // namespace tq

@@ -117,6 +117,38 @@ def test_quantize_bf16_outliers_strided(orc):
         check_quantize(orc, d, b, K[h], pi, s, c, P[h, 123:723], N[h, 123:723])
 
 
+@pytest.mark.parametrize("n_heads,n_tok,b,dtype", [
+    (256, 1, 4, torch.bfloat16),      # one new token per (kv head, layer)
+    (37, 3, 3, torch.float32),        # tiles span up to 22 heads, ragged end
+    (5, 63, 2, torch.bfloat16),
+    (3, 65, 4, torch.float32),        # one tile per head plus a 1-row spill
+    (2, 130, 3, torch.bfloat16),
+])
+def test_quantize_short_heads(orc, n_heads, n_tok, b, dtype):
+    """Many short heads in one call: source rows strided by head and token,
+    records scattered at h * cap + 7 + t of a larger cache."""
+    d = 128
+    say("quantize short heads", n_heads, n_tok, b, dtype)
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    base = workloads.normal((n_tok, n_heads, d + 8), 13, 10, DEV) * 1.5
+    base[0, n_heads // 2] = 0.0                         # a zero vector
+    base = base.to(dtype)
+    x = base[:, :, :d].transpose(0, 1)                  # [head][token][d], strided view
+    cap = n_tok + 11
+    planes, norms = tq.alloc_records(n_heads * cap, d, b)
+    tq.tq_quantize_kv(ctx, x, planes, norms, n_tokens=n_tok, n_heads=n_heads,
+                      x_stride_token=x.stride(1), x_stride_head=x.stride(0),
+                      dst_stride_head=cap, dst_token0=7)
+    torch.cuda.synchronize()
+    P = planes.cpu().numpy().view(np.uint32).reshape(n_heads, cap, -1)
+    N = norms.cpu().numpy().view(np.uint16).reshape(n_heads, cap, 2)
+    assert not P[:, :7].any() and not P[:, 7 + n_tok:].any()
+    assert not N[:, :7].any() and not N[:, 7 + n_tok:].any()
+    xs = x.reshape(n_heads * n_tok, d)
+    check_quantize(orc, d, b, xs, pi, s, c, P[:, 7:7 + n_tok].reshape(n_heads * n_tok, -1),
+                   N[:, 7:7 + n_tok].reshape(n_heads * n_tok, 2))
+
+
 def test_quantize_empty_and_deterministic(orc):
     d, b = 128, 3
     ctx, pi, s, c = ctx_for(orc, d, b)
@@ -228,6 +260,75 @@ def test_prepared_queries_match_one_call(orc):
     assert rel_err_rows(three[:4].cpu().numpy(), ref) < TOL
     with pytest.raises(tq.TqError):
         tq.tq_attn_logits_prepared(ctx, ws2[:64], 1, 8, P, N, 2, n, ss, sl, n, 0.5, two, n)
+
+
+def _step_case(orc, d, b, mse, dtype, n_heads, n_tok, L, n_q, n_kv):
+    if mse:
+        pi = orc.make_rotation(d, 0)[2]
+        c = orc.lloyd_max(d, b)[0].astype(np.float32)
+        ctx, s = tq.tq_ctx_create_mse(d, b, pi, c), None
+    else:
+        ctx, pi, s, c = ctx_for(orc, d, b)
+    kx = (workloads.normal((n_heads, n_tok, d), 14, 10, DEV) * 1.7).to(dtype)
+    vx = (workloads.normal((n_heads, n_tok, d), 14, 11, DEV) * 0.6).to(dtype)
+    q = workloads.normal((L, n_q, d), 14, 12, DEV)
+    cap = n_tok + 5
+    bufs = [tq.alloc_records(n_heads * cap, d, b) for _ in range(4)]
+    ws_bytes = tq.tq_attn_logits_workspace_bytes(ctx, L, n_q, n_kv)
+    ws1, ws2 = tq.workspace(ws_bytes), tq.workspace(ws_bytes)
+    ws1.zero_()
+    ws2.zero_()
+    tq.tq_decode_step_prepare(ctx, kx, vx, *bufs[0], *bufs[1], q, L, n_q, n_q * d, n_kv, ws1,
+                              dst_stride_head=cap, dst_token0=5)
+    tq.tq_quantize_kv(ctx, kx, *bufs[2], dst_stride_head=cap, dst_token0=5)
+    tq.tq_quantize_kv(ctx, vx, *bufs[3], dst_stride_head=cap, dst_token0=5)
+    tq.tq_attn_prepare(ctx, q, L, n_q, n_q * d, n_kv, ws2)
+    torch.cuda.synchronize()
+    for x_, y_ in zip(bufs[0] + bufs[1], bufs[2] + bufs[3]):
+        assert torch.equal(x_, y_)
+    assert torch.equal(ws1, ws2)
+    return ctx, pi, s, c, kx, bufs[0], cap
+
+
+@pytest.mark.parametrize("d,b,mse,dtype,n_heads,n_tok,L,n_q,n_kv", [
+    (128, 4, False, torch.bfloat16, 256, 1, 32, 32, 8),   # one token per (kv head, layer)
+    (128, 3, False, torch.float32, 7, 70, 2, 16, 1),       # several tiles, G = 16
+    (128, 2, True, torch.bfloat16, 24, 3, 3, 8, 8),        # MSE-only records
+    (200, 4, False, torch.float32, 5, 9, 2, 8, 2),          # other d: separate launches
+])
+def test_decode_step_prepare_matches_separate_calls(orc, d, b, mse, dtype, n_heads, n_tok, L,
+                                                    n_q, n_kv):
+    """tq_decode_step_prepare == tq_quantize_kv (K), tq_quantize_kv (V) and
+    tq_attn_prepare, bit for bit; the key records also against the oracle."""
+    say("decode step prepare", d, b, mse, dtype, n_heads, n_tok)
+    ctx, pi, s, c, kx, (kp, kn), cap = _step_case(orc, d, b, mse, dtype, n_heads, n_tok, L,
+                                                  n_q, n_kv)
+    if not mse:
+        P = kp.cpu().numpy().view(np.uint32).reshape(n_heads, cap, -1)[:, 5:5 + n_tok]
+        N = kn.cpu().numpy().view(np.uint16).reshape(n_heads, cap, 2)[:, 5:5 + n_tok]
+        check_quantize(orc, d, b, kx.reshape(n_heads * n_tok, d), pi, s, c,
+                       P.reshape(n_heads * n_tok, -1), N.reshape(n_heads * n_tok, 2))
+
+
+def test_decode_step_prepare_rejects_bad_arguments(orc):
+    d, b = 128, 4
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    kx = torch.zeros((4, 1, d), dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros((1, 8, d), device=DEV)
+    kp, kn = tq.alloc_records(4, d, b)
+    vp, vn = tq.alloc_records(4, d, b)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, 8, 2))
+    with pytest.raises(tq.TqError):      # workspace too small
+        tq.tq_decode_step_prepare(ctx, kx, kx, kp, kn, vp, vn, q, 1, 8, 8 * d, 2, ws[:16],
+                                  dst_stride_head=1)
+    with pytest.raises(tq.TqError):      # n_q not a multiple of n_kv
+        tq.tq_decode_step_prepare(ctx, kx, kx, kp, kn, vp, vn, q, 1, 8, 8 * d, 3, ws,
+                                  dst_stride_head=1)
+    with pytest.raises(tq.TqError):      # NULL value cache
+        tq.tq_decode_step_prepare(ctx, kx, kx, kp, kn, None, vn, q, 1, 8, 8 * d, 2, ws,
+                                  dst_stride_head=1)
+    torch.cuda.synchronize()
+    assert not kp.any() and not kn.any()
 
 
 def test_logits_random_records_and_zero_query(orc):
