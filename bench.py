@@ -6,9 +6,9 @@ channels per KV head scaled by 10, b = 4, logits for one new token).  One
 step runs that layer's hot path for L = 32 independent layer caches (as in a
 32-layer model, so the 704 MB of packed keys and logits per step are well
 beyond the 256 MB Infinity Cache): quantize each layer's new-token K and V
-into its packed cache, rotate/project each layer's 32 query heads, and stream
-all cached keys of every layer into attention logits.  Each stage is one
-launch covering all layers.
+into its packed cache and rotate/project each layer's 32 query heads (one
+launch: tq_decode_step_prepare), then stream all cached keys of every layer
+into attention logits (one launch).
 
 Outside the timed steps: a cache-fill leg times tq_quantize_kv on all K and V
 of the 32 layers (quantize vectors/s), and the CPU oracle is timed on a
@@ -70,23 +70,29 @@ def parse():
 
 
 PROFILE_LOGITS = os.path.join(ROOT, "profiles", "attn_logits_llama8b_decode_32layers.md")
-LOGIT_SOURCE = os.path.join(ROOT, "kv_cache_vector_pi_amd", "csrc", "tq_logits.hip")
+# sources of the logit kernel (hashed together, in this order)
+LOGIT_SOURCES = [os.path.join(ROOT, "kv_cache_vector_pi_amd", "csrc", f)
+                 for f in ("tq_logits.hip", "tq_dev.h")]
 
 
-def profiled_traffic(profile, source):
+def profiled_traffic(profile, sources):
     """HBM bytes per launch from the committed counter summary, or None when
-    the kernel source has changed since the counters were taken."""
+    the kernel sources have changed since the counters were taken."""
     import hashlib
     try:
         text = open(profile).read()
-        src = hashlib.sha256(open(source, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in sources:
+            h.update(open(f, "rb").read())
+        src = h.hexdigest()
     except OSError:
         return None
     vals = {}
     for line in text.splitlines():
         if ":" in line and line.strip().startswith("- `"):
-            k, v = line.strip()[3:].split("`", 1)[0], line.split(":", 1)[1].strip()
-            vals[k] = v.strip("` ")
+            k, v = line.strip()[3:].split("`", 1)[0], line.split(":", 1)[1]
+            parts = v.split("`")
+            vals[k] = parts[1] if len(parts) >= 3 else v.strip()
     if vals.get("kernel_source_sha256") != src:
         return None
     try:
@@ -278,10 +284,10 @@ def main():
                                "layer caches per step",
                    "layers_per_step": L, "cached_tokens": N_TOK, "head_dim": D, "bits": B,
                    "q_heads": N_Q, "kv_heads": N_KV, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,4>",
+        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,false,4>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": profiled_traffic(PROFILE_LOGITS, LOGIT_SOURCE),
+                     "traffic": profiled_traffic(PROFILE_LOGITS, LOGIT_SOURCES),
                      "alg_bytes_per_launch": alg_bytes,
                      "kernel_ms_mean": k_mean_ms, "kernel_ms_median": k_ms},
         "logit_keys_per_s": keys_per_step / (k_mean_ms * 1e-3),
