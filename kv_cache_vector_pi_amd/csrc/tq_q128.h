@@ -151,18 +151,28 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
   // vectors past the end re-read the tile's first row (always valid); the
   // consumer zeroes them, so no lane branches around a load and nothing
   // waits for it
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int v = 4 * wave + 16 * p + (lane >> 4);
-    uint32_t h, t;
-    row_ht(r, v < r.cnt ? v : 0, a, h, t);
-    const int64_t off = (int64_t)h * a.x_stride_head + (int64_t)t * a.x_stride_token +
-                        8 * (lane & 15);
+  auto load = [&](int p, int64_t off) {
     if constexpr (BF16) {
       raw.v[p] = *(const uint4*)((const uint16_t*)a.x + off);
     } else {
       raw.v[2 * p] = *(const uint4*)((const float*)a.x + off);
       raw.v[2 * p + 1] = *(const uint4*)((const float*)a.x + off + 4);
+    }
+  };
+  if (r.one) {        // uniform branch: rows t0 .. t0 + cnt - 1 of head h0
+    const int64_t base = (int64_t)r.h0 * a.x_stride_head + (int64_t)r.t0 * a.x_stride_token;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int v = 4 * wave + 16 * p + (lane >> 4);
+      load(p, base + (int64_t)(v < r.cnt ? v : 0) * a.x_stride_token + 8 * (lane & 15));
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int v = 4 * wave + 16 * p + (lane >> 4);
+      const uint32_t f = r.f0 + (v < r.cnt ? v : 0);
+      const uint32_t h = fast_div(f, a), t = f - h * (uint32_t)a.n_tokens;
+      load(p, (int64_t)h * a.x_stride_head + (int64_t)t * a.x_stride_token + 8 * (lane & 15));
     }
   }
 }
