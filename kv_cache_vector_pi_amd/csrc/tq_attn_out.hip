@@ -6,15 +6,14 @@
 // With v~_t = nu_t (Pi^T c[idx_t] + alpha gamma_t S^T s_t) the output
 //   o = sum_t p_t v~_t = Pi^T a_rot + alpha S^T a_sk,
 //   a_rot = sum_t (p_t nu_t) c[idx_t],   a_sk = sum_t (p_t nu_t gamma_t) s_t,
-// so the token stream accumulates in rotated / sketch space (per coordinate:
-// one centroid lookup and one FMA per query head) and the two d x d
-// transforms run once per query head at the end.
+// so the token stream accumulates in rotated / sketch space and the two
+// d x d transforms run once per query head at the end.
 //
-//  1. vout_accum_kernel: workgroup = (chunk of tokens, kv head and block of 4
-//     query heads, sequence).  The chunk's packed records, norms and weights
-//     are staged in LDS with coalesced loads; each thread owns coordinates
-//     and accumulates both sums for the 4 heads; partial sums per chunk go to
-//     the workspace.
+//  1. vout_accum_kernel: workgroup = (chunk of 256 tokens, kv head and block
+//     of 4 query heads, sequence).  The chunk's weights p nu and p nu gamma
+//     are staged in LDS; dev::vacc_mfma sums the packed bits against them on
+//     the int8 matrix cores (tokens as the contraction); partial sums per
+//     chunk go to the workspace.
 //  2. vout_final_kernel: workgroup = (query head, sequence): sum the chunk
 //     partials, then o_i = sum_j Pi[j][i] a_rot[j] + alpha sum_j S[j][i] a_sk[j].
 // MSE-only records (no QJL stage) have no sketch part: a_sk = 0, and the S^T
@@ -37,41 +36,30 @@ struct VAccArgs {
   const int64_t* seq_start;
   const int32_t* seq_len;
   float* part;              // [batch][n_kv][n_rb][n_chunk][2][4][Dp]
-  int d, W, Dp, G, n_kv, n_rb, n_chunk, chunk;
-  float cent[kMaxK];
+  int d, W, Dp, G, n_kv, n_rb, n_chunk;
+  dev::VaccCoef cf;
 };
 
 inline int n_rb_of(int G) { return (G + 3) / 4; }
 
-// Tokens per chunk: the chunk's records must fit the LDS staging area.
-inline int chunk_of(const tq_ctx* ctx) {
-  const int rec_bytes = ctx->W * ctx->b * 4 + 4 + 32;     // words, norms, 8 weights
-  int ch = 256;
-  while (ch > 16 && (size_t)ch * rec_bytes > 48 * 1024) ch >>= 1;
-  return ch;
-}
+constexpr int kChunk = dev::kVChunk;     // tokens per chunk
 
 template <int NB, bool MSE>
 __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
-  extern __shared__ __align__(16) uint32_t sm[];
-  const int RW = a.W * NB;                       // words per record
-  uint32_t* words = sm;                          // [chunk][RW]
-  float* wts = (float*)(words + a.chunk * RW);   // [chunk][8]: p nu (4 heads), p nu gamma (4)
-
-  __shared__ float ctab[kMaxK];
+  __shared__ __align__(16) char lds[dev::vacc_lds_bytes(NB)];
+  __shared__ __align__(16) float wts[kChunk * 8];   // p nu (4 heads), p nu gamma (4)
   const int tid = threadIdx.x;
-  if (tid < kMaxK) ctab[tid] = a.cent[tid];
   const int chunk_i = blockIdx.x;
   const int h = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
   const int bi = blockIdx.z;
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
-  const int t0 = chunk_i * a.chunk;
-  const int nt = max(0, min(a.chunk, len - t0));
+  const int t0 = chunk_i * kChunk;
+  const int nt = max(0, min(kChunk, len - t0));
+  const int RW = a.W * NB;                       // words per record
 
-  // ---- stage the chunk -------------------------------------------------------
+  // ---- stage the chunk's weights ------------------------------------------------
   const int64_t rec0 = (int64_t)h * a.values_stride_head + start + t0;
-  for (int i = tid; i < nt * RW; i += 256) words[i] = a.planes[rec0 * RW + i];
   for (int i = tid; i < nt * 8; i += 256) {
     const int t = i >> 3, k = i & 7, hh = k & 3;
     const int g = 4 * rb + hh;
@@ -87,7 +75,7 @@ __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   // ---- accumulate and write the chunk partials ---------------------------------
   float* dst = a.part +
       ((((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk + chunk_i) * 8 * (int64_t)a.Dp;
-  dev::vacc_block<NB, MSE>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)sm, dst);
+  dev::vacc_mfma<NB, MSE>(a.planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp);
 }
 
 struct VFinArgs {
@@ -134,7 +122,7 @@ __global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
 size_t vout_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads, int32_t max_seq_len) {
   const int G = n_q_heads / n_kv_heads;
-  const int ch = chunk_of(ctx);
+  const int ch = kChunk;
   const int64_t n_chunk = std::max<int64_t>(1, ((int64_t)max_seq_len + ch - 1) / ch);
   return (size_t)batch * n_kv_heads * n_rb_of(G) * n_chunk * 8 * ctx->Dp * sizeof(float);
 }
@@ -161,13 +149,10 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
   a.G = G;
   a.n_kv = n_kv_heads;
   a.n_rb = n_rb_of(G);
-  a.chunk = chunk_of(ctx);
-  a.n_chunk = std::max(1, (max_seq_len + a.chunk - 1) / a.chunk);
-  for (int k = 0; k < kMaxK; ++k) a.cent[k] = k < ctx->K ? ctx->cent[k] : 0.f;
-  const int NL = std::min(ctx->Dp, 256), TT = 256 / NL;
-  const size_t stage = (size_t)a.chunk * (ctx->W * ctx->b + 8) * 4;
-  const size_t red = TT > 1 ? (size_t)TT * 8 * NL * 4 : 0;
-  const size_t shm = std::max(stage, red);
+  a.n_chunk = std::max(1, (max_seq_len + kChunk - 1) / kChunk);
+  if (!dev::make_vacc_coef(ctx->mono_mask, ctx->mono_w, ctx->n_mono, ctx->c0, ctx->cp, a.cf))
+    return hipErrorInvalidValue;
+  const size_t shm = 0;
   const dim3 grid(a.n_chunk, n_kv_heads * a.n_rb, batch);
   if (ctx->mse) {
     switch (ctx->b) {

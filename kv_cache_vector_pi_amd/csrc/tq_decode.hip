@@ -11,8 +11,9 @@
 //  2. decode_chunk_kernel, per (chunk, kv head and block of 4 query heads,
 //     sequence): the chunk's logits on the int8 MFMAs into LDS, the chunk's
 //     softmax statistics (max m, sum l of exp(logit - m)), then the value
-//     accumulation of dev::vacc_block with weights exp(logit - m) nu (and
-//     times gamma for the sketch part) -- partial sums and (m, l) per chunk;
+//     accumulation of dev::vacc_mfma (int8 MFMAs, tokens as the contraction)
+//     with weights exp(logit - m) nu (and times gamma for the sketch part) --
+//     partial sums and (m, l) per chunk;
 //  3. decode_final_kernel, per (query head, sequence): rescale the chunks by
 //     exp(m_c - M), divide by L = sum_c l_c exp(m_c - M), and apply Pi^T and
 //     S^T once.
@@ -40,18 +41,13 @@ struct DecArgs {
   const int32_t* seq_len;
   float* part;                  // [batch][n_kv][n_rb][n_chunk][8][Dp]
   float* stats;                 // [batch][n_kv][n_rb][n_chunk][4][2]  (m, l)
-  int d, W, Dp, G, n_kv, n_rb, n_chunk, chunk;
+  int d, W, Dp, G, n_kv, n_rb, n_chunk;
   float scale, alpha;
   int mask[kMaxVec];
-  float cent[kMaxK];
+  dev::VaccCoef cf;
 };
 
-inline int dec_chunk(const tq_ctx* ctx) {
-  const int rec_bytes = ctx->W * ctx->b * 4 + 4 + 32 + 16;   // words, norms, weights, logits
-  int ch = 256;
-  while (ch > 16 && (size_t)ch * rec_bytes > 48 * 1024) ch >>= 1;
-  return ch;
-}
+constexpr int kChunk = dev::kVChunk;     // tokens per chunk
 
 __device__ inline float wmax(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -67,18 +63,15 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;          // code planes
   constexpr int NV = 1 << (CP - 1);
   constexpr int NC = 2 * NV + (MSE ? 0 : 2);
-  extern __shared__ __align__(16) uint32_t sm[];
-  const int CH = a.chunk;
+  constexpr int CH = kChunk;
+  __shared__ __align__(16) char lds[dev::vacc_lds_bytes(NB)];
+  __shared__ __align__(16) float lg[4 * CH];           // logits, then softmax numerators
+  __shared__ __align__(16) float wts[CH * 8];          // p nu (4 heads), p nu gamma (4)
   const int RW = a.W * NB;
-  float* lg = (float*)sm;                              // [4][CH] logits, then weights
-  uint32_t* words = sm + 4 * CH;                       // [CH][RW] value records
-  float* wts = (float*)(words + CH * RW);              // [CH][8]
-  __shared__ float ctab[kMaxK];
   __shared__ float st_m[4], st_l[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
-  if (tid < kMaxK) ctab[tid] = a.cent[tid];
   const int chunk_i = blockIdx.x;
   const int h = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
   const int bi = blockIdx.z;
@@ -131,8 +124,6 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     const float logit = a.scale * nu * (MSE ? mse : fmaf(a.alpha * ga, qjl, mse));
     lg[g * CH + tl] = (valid && head_ok) ? logit : -INFINITY;
   }
-  // stage the chunk's value records meanwhile
-  for (int i = tid; i < nt * RW; i += 256) words[i] = a.v_planes[rec0 * RW + i];
   __syncthreads();
 
   // ---- 2. softmax statistics of the chunk: wave hh handles query head hh ----
@@ -172,8 +163,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     a.stats[cidx * 8 + 2 * tid] = st_m[tid];
     a.stats[cidx * 8 + 2 * tid + 1] = st_l[tid];
   }
-  // the token-group scratch of vacc_block aliases the staged records
-  dev::vacc_block<NB, MSE>(words, wts, ctab, nt, RW, a.d, a.Dp, (float*)words, dst);
+  dev::vacc_mfma<NB, MSE>(a.v_planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp);
 }
 
 struct DecFinArgs {
@@ -249,7 +239,7 @@ DecLayout dec_layout(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads, int32_
   DecLayout L{};
   const int G = n_q_heads / n_kv_heads;
   L.n_rb = (G + 3) / 4;
-  L.chunk = dec_chunk(ctx);
+  L.chunk = kChunk;
   L.n_chunk = std::max(1, (max_seq_len + L.chunk - 1) / L.chunk);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nblk = (size_t)batch * n_kv_heads * L.n_rb * L.n_chunk;
@@ -298,16 +288,12 @@ hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, 
   a.n_kv = n_kv_heads;
   a.n_rb = L.n_rb;
   a.n_chunk = L.n_chunk;
-  a.chunk = L.chunk;
   a.scale = scale;
   a.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   for (int v = 0; v < kMaxVec; ++v) a.mask[v] = v < ctx->n_mono ? ctx->mono_mask[v] : 0;
-  for (int k = 0; k < kMaxK; ++k) a.cent[k] = k < ctx->K ? ctx->cent[k] : 0.f;
-  const int CH = L.chunk, RW = ctx->W * ctx->b;
-  const int NL = std::min(ctx->Dp, 256), TT = 256 / NL;
-  const size_t stage = (size_t)4 * CH * 4 + (size_t)CH * RW * 4 + (size_t)CH * 8 * 4;
-  const size_t red = (size_t)4 * CH * 4 + (size_t)TT * 8 * NL * 4;
-  const size_t shm = std::max(stage, red);
+  if (!dev::make_vacc_coef(ctx->mono_mask, ctx->mono_w, ctx->n_mono, ctx->c0, ctx->cp, a.cf))
+    return hipErrorInvalidValue;
+  const size_t shm = 0;
   const dim3 grid(L.n_chunk, n_kv_heads * L.n_rb, batch);
   if (ctx->mse) {
     switch (ctx->b) {

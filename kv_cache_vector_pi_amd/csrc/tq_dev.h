@@ -55,87 +55,246 @@ __device__ inline float limbs_to_float(const v4i& c) {
   return fmaf((float)c[3], 16777216.f, fmaf((float)c[2], 65536.f, fmaf((float)c[1], 256.f, (float)c[0])));
 }
 
-// Block-wide value accumulation over nt staged tokens (256 threads, every
-// thread calls it): for the 4 query heads hh of the block
-//   dst[hh][j]     = sum_t wts[t][hh]     * c[idx_tj]
-//   dst[4 + hh][j] = sum_t wts[t][4 + hh] * s_tj        (s = +-1)
-// for j < Dp (coordinates j >= d hold the contributions of zero bits and are
-// ignored by the consumers).  MSE records (NB code planes, no sign plane)
-// leave dst[4 + hh] zero.  words: LDS [nt][RW] packed records (RW = W*NB),
-// wts: LDS [nt][8], ctab: LDS centroids, red: LDS scratch of
-// max(1, 256 / Dp) * 8 * Dp floats that may alias `words` (a barrier separates
-// the reads from the reuse).  Threads own coordinates lc + 256k of token group
-// tg (tokens tg, tg + TT, ...).
-template <int NB, bool MSE>
-__device__ void vacc_block(const uint32_t* words, const float* wts, const float* ctab, int nt,
-                           int RW, int d, int Dp, float* red, float* dst) {
-  const int tid = threadIdx.x;
-  const int NL = min(Dp, 256);
-  const int TT = 256 / NL;
-  const int lc = tid % NL, tg = tid / NL;
-  constexpr int kMaxCpt = 8;                     // Dp <= 2048
-  const int cpt = (Dp + 255) / 256;
-  float ar[kMaxCpt][4], as[kMaxCpt][4];
+// Odd-sized subsets of the cp code planes (Walsh expansion of a symmetric
+// codebook), in the order the context lists them: masks 1 / 1, 2 / 1, 2, 4, 7.
+template <int CP>
+__device__ constexpr int walsh_mask(int v) {
+  return CP == 1 ? 1 : (CP == 2 ? (v == 0 ? 1 : 2) : (v == 0 ? 1 : v == 1 ? 2 : v == 2 ? 4 : 7));
+}
+
+// rint(Q / 2^k) for k >= 1 (half away from -inf), Q for k == 0
+__device__ inline int shift_round(int Q, int k) {
+  return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
+}
+
+// ---- 32 x 32 bit transpose in registers ------------------------------------
+// Within each half of the wave (lanes 0-31 and 32-63): on entry lane l holds
+// the word of row l; on exit lane l holds column l, i.e. bit b of its word is
+// bit l of the entry word of lane b.  Five exchange stages (partner lane
+// l ^ j, j = 16, 8, 4, 2, 1): the lower lane of a pair keeps the bits b with
+// b & j == 0 and takes the partner's bits shifted up by j, the upper lane the
+// reverse; a rotate and a bitfield insert per stage, with the per-lane mask
+// and rotate amount precomputed (TransposeLanes).
+struct TransposeLanes {
+  uint32_t mk[5], sh[5];
+  __device__ explicit TransposeLanes(int lane) {
+    const uint32_t m0[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
 #pragma unroll
-  for (int k = 0; k < kMaxCpt; ++k)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) ar[k][hh] = as[k][hh] = 0.f;
-  if (tg < TT) {
-    for (int t = tg; t < nt; t += TT) {
-      const uint32_t* rw = words + t * RW;
-      const float4 w1 = *(const float4*)(wts + 8 * t);
-      const float4 w2 = *(const float4*)(wts + 8 * t + 4);
-#pragma unroll
-      for (int k = 0; k < kMaxCpt; ++k) {
-        if (k >= cpt) break;
-        const int j = lc + 256 * k;
-        if (j >= d) continue;
-        const uint32_t* gw = rw + (j >> 5) * NB;
-        const int bit = j & 31;
-        uint32_t idx = 0;
-#pragma unroll
-        for (int q = 0; q < (MSE ? NB : NB - 1); ++q) idx |= __builtin_amdgcn_ubfe(gw[q], bit, 1) << q;
-        const float c = ctab[idx];
-        ar[k][0] = fmaf(w1.x, c, ar[k][0]);
-        ar[k][1] = fmaf(w1.y, c, ar[k][1]);
-        ar[k][2] = fmaf(w1.z, c, ar[k][2]);
-        ar[k][3] = fmaf(w1.w, c, ar[k][3]);
-        if constexpr (MSE) continue;
-        // +1.0 for a set sign bit, -1.0 otherwise
-        const float sg =
-            __uint_as_float(0xbf800000u ^ (__builtin_amdgcn_ubfe(gw[NB - 1], bit, 1) << 31));
-        as[k][0] = fmaf(w2.x, sg, as[k][0]);
-        as[k][1] = fmaf(w2.y, sg, as[k][1]);
-        as[k][2] = fmaf(w2.z, sg, as[k][2]);
-        as[k][3] = fmaf(w2.w, sg, as[k][3]);
-      }
+    for (int s = 0; s < 5; ++s) {
+      const int j = 16 >> s;
+      const bool lower = (lane & j) == 0;
+      mk[s] = lower ? m0[s] : ~m0[s];
+      sh[s] = lower ? 32 - j : j;        // rotate right: left by j for the lower lane
     }
   }
-  __syncthreads();          // staging area may be reused for the token-group sums
-  if (TT > 1) {
-    if (tg < TT)
+};
+__device__ inline uint32_t xpose_step(uint32_t x, uint32_t p, uint32_t mk, uint32_t sh) {
+  const uint32_t r = __builtin_amdgcn_alignbit(p, p, sh);
+  return (x & mk) | (r & ~mk);
+}
+__device__ inline uint32_t transpose32(uint32_t x, const TransposeLanes& t) {
+  x = xpose_step(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (16 << 10) | 0x1F), t.mk[0], t.sh[0]);
+  x = xpose_step(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false), t.mk[1], t.sh[1]);
+  x = xpose_step(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, (4 << 10) | 0x1F), t.mk[2], t.sh[2]);
+  x = xpose_step(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false), t.mk[3], t.sh[3]);
+  x = xpose_step(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false), t.mk[4], t.sh[4]);
+  return x;
+}
+
+// ---- value accumulation on the int8 matrix cores -----------------------------
+// For the 4 query heads hh of the block and a chunk of nt <= kVChunk tokens:
+//   dst[hh][j]     = sum_t wts[t][hh]     * c[idx_tj]
+//   dst[4 + hh][j] = sum_t wts[t][4 + hh] * s_tj        (s = +-1)
+// for j < Dp (coordinates j >= d have zero bits).  MSE records (NB code
+// planes, no sign plane) leave dst[4 + hh] zero.
+//
+// Same algebra as the logit kernel with tokens as the contraction: c[idx] =
+// c_0 + sum_m wm2[m] u_m (u_m the XOR of the code planes in Walsh subset m)
+// and s = 2 beta - 1 (beta the sign bit), so both sums reduce to
+// sum_t w_t * bit_tj, an int8 MFMA (v_mfma_i32_16x16x64_i8) with
+//   A (16 x 64 tokens): 4 heads x 4 balanced int8 limbs of the fixed-point
+//     weights w_t 2^e, one scale e per head and part for the whole chunk;
+//   B (64 tokens x 16 coordinates): bits, as int8 lanes of a word whose bit b
+//     is token b's bit (plane words transposed in registers, 32 x 32 at a
+//     time), masked in place as 0 or 2^k with the 2^k folded into A.
+// Per 128-token block and 32-coordinate word: 2 NB transposes, one
+// v_permlane16_swap per plane to gather 4 token groups x 16 coordinates per
+// operand, then (NV + 1) x 2 MFMAs per 16 coordinates.  Lane (g, n) of an
+// accumulator holds head g's 4 limbs at coordinate n.
+//
+// The chunk's records are staged from global memory in slices of 4 words
+// (wave w takes word w of a slice), plane-major in LDS; the A operands are
+// built once per chunk.  All 256 threads call it.
+constexpr int kVChunk = 256;                       // tokens per chunk
+constexpr int kVAopsBytes = kVChunk / 128 * 4 * 64 * 16;   // A operands: 8 KB
+__host__ __device__ constexpr int vacc_words_bytes(int NB) { return 4 * NB * kVChunk * 4; }
+__host__ __device__ constexpr int vacc_lds_bytes(int NB) { return kVAopsBytes + vacc_words_bytes(NB); }
+
+template <int NB>
+__device__ inline void load_words(const uint32_t* p, uint32_t (&w)[NB]) {
+  if constexpr (NB == 4) {
+    const uint4 v = *(const uint4*)p;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (NB == 2) {
+    const uint2 v = *(const uint2*)p;
+    w[0] = v.x; w[1] = v.y;
+  } else {
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        red[(tg * 8 + hh) * NL + lc] = ar[0][hh];
-        red[(tg * 8 + 4 + hh) * NL + lc] = as[0][hh];
+    for (int i = 0; i < NB; ++i) w[i] = p[i];
+  }
+}
+
+// Codebook in Walsh form: c[idx] = c0 + sum_m wm2[m] u_m (wm2 = -2 w_m).
+struct VaccCoef {
+  float wm2[4];
+  float c0;
+};
+
+// From the context's Walsh expansion (monomials in the order 1 / 1, 2 /
+// 1, 2, 4, 7); false if the masks differ from the ones walsh_mask encodes.
+inline bool make_vacc_coef(const int32_t* mono_mask, const double* mono_w, int n_mono, double c0,
+                           int cp, VaccCoef& cf) {
+  static const int kMasks[3][4] = {{1, 0, 0, 0}, {1, 2, 0, 0}, {1, 2, 4, 7}};
+  if (cp < 1 || cp > 3 || n_mono != (1 << (cp - 1))) return false;
+  for (int v = 0; v < 4; ++v) {
+    if (v < n_mono && mono_mask[v] != kMasks[cp - 1][v]) return false;
+    cf.wm2[v] = v < n_mono ? (float)(-2.0 * mono_w[v]) : 0.f;
+  }
+  cf.c0 = (float)c0;
+  return true;
+}
+
+// planes: global records of the chunk (token t at planes + t * W * NB);
+// wts: LDS [kVChunk][8] (read for t < nt only); lds: vacc_lds_bytes(NB)
+// bytes, 16-aligned.  Callers synchronise before reusing wts or lds.
+template <int NB, bool MSE>
+__device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wts,
+                          const VaccCoef cf, char* lds, float* dst, int Dp) {
+  constexpr int CP = MSE ? NB : NB - 1;       // code planes
+  constexpr int NV = 1 << (CP - 1);           // Walsh subsets
+  constexpr int NP = MSE ? 1 : 2;             // weight parts: code, sign
+  __shared__ int s_e[8];                      // fixed-point exponent per (part, head)
+  __shared__ float s_sum[8];                  // sum of the weights per (part, head)
+  v4i* aops = (v4i*)lds;                      // [block][part][half][64 lanes]
+  uint32_t* wordsT = (uint32_t*)(lds + kVAopsBytes);   // [4 words][NB planes][kVChunk]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int RW = W * NB;
+
+  // 1. scale and sum per (part, head): wave w takes combos 2w, 2w + 1
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int combo = 2 * wave + q, part = combo >> 2, hh = combo & 3;
+    float mx = 0.f, sm = 0.f;
+    if (part < NP)
+      for (int t = lane; t < nt; t += 64) {
+        const float w = wts[8 * t + 4 * part + hh];
+        mx = fmaxf(mx, fabsf(w));
+        sm += w;
       }
-    __syncthreads();
-    for (int i = tid; i < 8 * NL; i += 256) {
-      float s = 0.f;
-      for (int g = 0; g < TT; ++g) s += red[g * 8 * NL + i];
-      dst[(i / NL) * Dp + i % NL] = s;           // TT > 1 only when Dp <= 128: NL == Dp
+    for (int o = 32; o > 0; o >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o));
+      sm += __shfl_xor(sm, o);
     }
-  } else if (tg < TT) {
+    if (lane == 0) {
+      int e = 0;
+      if (mx > 0.f) { int ex; frexpf(mx, &ex); e = min(30 - ex, 120); }
+      s_e[combo] = e;
+      s_sum[combo] = sm;
+    }
+  }
+  __syncthreads();
+  // 2. A operands: weight of token t (block b, position tb): token group
+  //    tb / 32 sits in lane group [0, 2, 1, 3][tb / 32] (the order the
+  //    permlane16 swap leaves), bit tb % 32 = 8 e + 4 h + i is byte e of
+  //    register i of half h, shift k = 4 h + i.
+  for (int it = tid; it < kVChunk * 4 * NP; it += 256) {
+    const int t = it % kVChunk, hh = (it / kVChunk) & 3, part = it / (4 * kVChunk);
+    const int combo = 4 * part + hh;
+    const int Q = t < nt ? (int)rintf(ldexpf(wts[8 * t + combo], s_e[combo])) : 0;
+    const int b = t >> 7, tb = t & 127, grp = tb >> 5, bit = tb & 31;
+    const int g = (grp == 1) ? 2 : (grp == 2 ? 1 : grp);
+    const int eb = bit >> 3, h = (bit >> 2) & 1, i = bit & 3, k = 4 * h + i;
+    const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+    char* base = (char*)(aops + ((b * 2 + part) * 2 + h) * 64) + 4 * i + eb;
 #pragma unroll
-    for (int k = 0; k < kMaxCpt; ++k) {
-      if (k >= cpt) break;
-      const int j = lc + 256 * k;
-      if (j >= Dp) continue;
+    for (int L = 0; L < 4; ++L) {
+      const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
+      base[(16 * g + 4 * hh + L) * 16] = (char)(digit ^ 0x80u);
+    }
+  }
+  const TransposeLanes tl(lane);
+  const int gq = lane >> 4, n = lane & 15;
+  // 3. slices of 4 words
+  for (int w0 = 0; w0 < W; w0 += 4) {
+    __syncthreads();            // A operands written / previous slice consumed
+    for (int it = tid; it < 4 * kVChunk; it += 256) {
+      const int wl = it / kVChunk, t = it % kVChunk, w = w0 + wl;
+      uint32_t v[NB];
 #pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        dst[hh * Dp + j] = ar[k][hh];
-        dst[(4 + hh) * Dp + j] = as[k][hh];
+      for (int p = 0; p < NB; ++p) v[p] = 0u;
+      if (w < W && t < nt) load_words<NB>(planes + (int64_t)t * RW + w * NB, v);
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wordsT[(wl * NB + p) * kVChunk + t] = v[p];
+    }
+    __syncthreads();
+    const int w = w0 + wave;
+    if (w >= W) continue;
+    v4i G[2][NV], S[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      S[cb] = (v4i){0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < NV; ++m) G[cb][m] = (v4i){0, 0, 0, 0};
+    }
+    for (int b = 0; b * 128 < nt; ++b) {
+      uint32_t X0[NB], X1[NB];
+#pragma unroll
+      for (int p = 0; p < NB; ++p) {
+        const uint32_t* row = wordsT + (wave * NB + p) * kVChunk + 128 * b;
+        const uint32_t t1 = transpose32(row[lane], tl);
+        const uint32_t t2 = transpose32(row[64 + lane], tl);
+        const auto r = __builtin_amdgcn_permlane16_swap(t1, t2, false, false);
+        X0[p] = r[0];           // coordinates 32w + n, token groups 0, 2, 1, 3
+        X1[p] = r[1];           // coordinates 32w + 16 + n
       }
+      const v4i* ab = aops + b * 4 * 64;
+      v4i Ac[2], As[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Ac[h] = ab[h * 64 + lane];
+        if constexpr (!MSE) As[h] = ab[(2 + h) * 64 + lane];
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const uint32_t* X = cb ? X1 : X0;
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+          uint32_t u = 0u;
+#pragma unroll
+          for (int p = 0; p < CP; ++p)
+            if ((walsh_mask<CP>(m) >> p) & 1) u ^= X[p];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[h], bit_lanes(u, h), G[cb][m], 0, 0, 0);
+        }
+        if constexpr (!MSE) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[h], bit_lanes(X[NB - 1], h), S[cb], 0, 0, 0);
+        }
+      }
+    }
+    // lane (g, n): head g at coordinate 32w + 16cb + n
+    const float sc0 = ldexpf(1.f, -s_e[gq]);
+    const float sc1 = MSE ? 0.f : ldexpf(2.f, -s_e[4 + gq]);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float code = 0.f;
+#pragma unroll
+      for (int m = 0; m < NV; ++m) code = fmaf(cf.wm2[m], limbs_to_float(G[cb][m]), code);
+      const int j = 32 * w + 16 * cb + n;
+      dst[gq * Dp + j] = fmaf(code, sc0, cf.c0 * s_sum[gq]);
+      dst[(4 + gq) * Dp + j] = MSE ? 0.f : fmaf(limbs_to_float(S[cb]), sc1, -s_sum[4 + gq]);
     }
   }
 }

@@ -43,6 +43,7 @@ using dev::n_ws;
 using dev::rb_bytes;
 using dev::load_group;
 using dev::bit_lanes;
+using dev::walsh_mask;
 
 __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
   prep_block(a, blockIdx.x, blockIdx.y, blockIdx.z);
@@ -147,13 +148,6 @@ __global__ void __launch_bounds__(256) attn_logits_kernel(AttnArgs a) {
       }
     }
   }
-}
-
-// Odd-sized subsets of the code planes (Walsh expansion of a symmetric
-// codebook), in the order the context lists them: masks 1, 2, 4, 7.
-template <int CP>
-__device__ constexpr int walsh_mask(int v) {
-  return CP == 1 ? 1 : (CP == 2 ? (v == 0 ? 1 : 2) : (v == 0 ? 1 : v == 1 ? 2 : v == 2 ? 4 : 7));
 }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

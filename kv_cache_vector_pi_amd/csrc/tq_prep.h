@@ -37,10 +37,6 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-// rint(Q / 2^k) for k >= 1 (half away from -inf), Q for k == 0
-__device__ inline int shift_round(int Q, int k) {
-  return k == 0 ? Q : ((Q + (1 << (k - 1))) >> k);
-}
 
 // Query preparation: one block per (row block of 4 q heads and part, kv
 // head, batch).  Part 0 computes Pi q and the A operands of the code calls,
@@ -191,7 +187,7 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
       for (int el = 0; el < 4; ++el) {
         const int j = 32 * w + 8 * el + k;
         const int Q = (w < a.W && j < a.d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
-        const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+        const int Ap = (k < 7) ? dev::shift_round(Q, k) : -dev::shift_round(Q, 7);
         const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
         word |= (digit ^ 0x80u) << (8 * el);
       }
