@@ -9,11 +9,12 @@
 // so the token stream accumulates in rotated / sketch space and the two
 // d x d transforms run once per query head at the end.
 //
-//  1. vout_accum_kernel: workgroup = (chunk of 256 tokens, kv head and block
-//     of 4 query heads, sequence).  The chunk's weights p nu and p nu gamma
-//     are staged in LDS; dev::vacc_mfma sums the packed bits against them on
-//     the int8 matrix cores (tokens as the contraction); partial sums per
-//     chunk go to the workspace.
+//  1. vout_accum_kernel: workgroup = (chunk of 1024 tokens, kv head and
+//     block of 4 query heads, sequence), in 4 steps of 256 tokens: the
+//     step's weights p nu and p nu gamma are staged in LDS, and
+//     dev::vacc_mfma sums the packed bits against them on the int8 matrix
+//     cores (tokens as the contraction) into the chunk's partial sums in the
+//     workspace.
 //  2. vout_final_kernel: workgroup = (query head, sequence): sum the chunk
 //     partials, then o_i = sum_j Pi[j][i] a_rot[j] + alpha sum_j S[j][i] a_sk[j].
 // MSE-only records (no QJL stage) have no sketch part: a_sk = 0, and the S^T
@@ -42,40 +43,58 @@ struct VAccArgs {
 
 inline int n_rb_of(int G) { return (G + 3) / 4; }
 
-constexpr int kChunk = dev::kVChunk;     // tokens per chunk
+constexpr int kSub = 1;                          // 256-token steps per chunk
+constexpr int kChunk = dev::kVChunk * kSub;      // tokens per chunk (one partial)
 
 template <int NB, bool MSE>
 __global__ void __launch_bounds__(256) vout_accum_kernel(VAccArgs a) {
   __shared__ __align__(16) char lds[dev::vacc_lds_bytes(NB)];
-  __shared__ __align__(16) float wts[kChunk * 8];   // p nu (4 heads), p nu gamma (4)
+  __shared__ __align__(16) float wts[dev::kVChunk * 8];   // p nu (4 heads), p nu gamma (4)
   const int tid = threadIdx.x;
   const int chunk_i = blockIdx.x;
   const int h = blockIdx.y / a.n_rb, rb = blockIdx.y % a.n_rb;
   const int bi = blockIdx.z;
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
-  const int t0 = chunk_i * kChunk;
-  const int nt = max(0, min(kChunk, len - t0));
   const int RW = a.W * NB;                       // words per record
-
-  // ---- stage the chunk's weights ------------------------------------------------
-  const int64_t rec0 = (int64_t)h * a.values_stride_head + start + t0;
-  for (int i = tid; i < nt * 8; i += 256) {
-    const int t = i >> 3, k = i & 7, hh = k & 3;
-    const int g = 4 * rb + hh;
-    const uint32_t nr = a.norms[rec0 + t];
-    const float nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
-    float w = 0.f;
-    if (g < a.G) w = a.p[(int64_t)(h * a.G + g) * a.p_stride_head + start + t0 + t] * nu;
-    if (k >= 4) w *= __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
-    wts[i] = w;
-  }
-  __syncthreads();
-
-  // ---- accumulate and write the chunk partials ---------------------------------
   float* dst = a.part +
       ((((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk + chunk_i) * 8 * (int64_t)a.Dp;
-  dev::vacc_mfma<NB, MSE>(a.planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp);
+
+  for (int step = 0; step < kSub; ++step) {
+    const int t0 = chunk_i * kChunk + step * dev::kVChunk;
+    const int nt = max(0, min(dev::kVChunk, len - t0));
+    if (step > 0 && nt == 0) break;              // uniform; step 0 always writes the partial
+    if (step > 0) __syncthreads();               // the previous step is done with wts and lds
+    // ---- stage the step's weights (thread t: token t), with the first slice
+    //      of the records loaded behind them --------------------------------------
+    const int64_t rec0 = (int64_t)h * a.values_stride_head + start + t0;
+    static_assert(dev::kVChunk == 256, "one token per thread");
+    const int t = tid;
+    uint32_t nr = 0u;
+    float pw[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < nt) {
+      nr = a.norms[rec0 + t];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+        if (4 * rb + hh < a.G)
+          pw[hh] = a.p[(int64_t)(h * a.G + 4 * rb + hh) * a.p_stride_head + start + t0 + t];
+    }
+    dev::VaccSlice<NB> first;
+    dev::vacc_load_slice<NB>(a.planes + rec0 * RW, nt, a.W, 0, first);
+    {
+      const float nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
+      const float ga = __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
+      float4 w1, w2;
+      w1.x = pw[0] * nu; w1.y = pw[1] * nu; w1.z = pw[2] * nu; w1.w = pw[3] * nu;
+      w2.x = w1.x * ga; w2.y = w1.y * ga; w2.z = w1.z * ga; w2.w = w1.w * ga;
+      *(float4*)&wts[8 * t] = w1;
+      *(float4*)&wts[8 * t + 4] = w2;
+    }
+    __syncthreads();
+    // ---- accumulate into the chunk's partial sums ----------------------------------
+    dev::vacc_mfma<NB, MSE>(a.planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp, first,
+                            step > 0);
+  }
 }
 
 struct VFinArgs {
@@ -93,28 +112,13 @@ __global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
   extern __shared__ float fsm[];
   float* arot = fsm;               // [Dp]
   float* ask = fsm + a.Dp;         // [Dp]
-  const int tid = threadIdx.x;
+  __shared__ float red[512];
   const int hq = blockIdx.x, bi = blockIdx.y;
   const int h = hq / a.G, g = hq % a.G, rb = g / 4, hh = g % 4;
   const float* src = a.part + (((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk * 8 * (int64_t)a.Dp;
-  for (int j = tid; j < a.Dp; j += 256) {
-    float s1 = 0.f, s2 = 0.f;
-    for (int c = 0; c < a.n_chunk; ++c) {
-      s1 += src[((int64_t)c * 8 + hh) * a.Dp + j];
-      s2 += src[((int64_t)c * 8 + 4 + hh) * a.Dp + j];
-    }
-    arot[j] = s1;
-    ask[j] = s2;
-  }
-  __syncthreads();
-  for (int i = tid; i < a.d; i += 256) {
-    float o1 = 0.f, o2 = 0.f;
-    for (int j = 0; j < a.d; ++j) {
-      o1 = fmaf(a.pi32[(int64_t)j * a.d + i], arot[j], o1);
-      if (a.qjl) o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
-    }
-    a.out[(int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d + i] = fmaf(a.alpha, o2, o1);
-  }
+  dev::sum_chunk_partials(src, a.n_chunk, hh, 4 + hh, a.Dp, nullptr, 1.f, red, arot, ask);
+  dev::apply_transforms(a.pi32, a.s32, a.d, a.qjl != 0, a.alpha, arot, ask, red,
+                        a.out + (int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d);
 }
 
 }  // namespace

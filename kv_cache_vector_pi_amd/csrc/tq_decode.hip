@@ -81,6 +81,10 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
   const int nt = max(0, min(CH, len - t0));
   const int64_t rec0 = (int64_t)h * a.kv_stride_head + start + t0;
 
+  // the first slice of the value records, loaded while the logits compute
+  dev::VaccSlice<NB> first;
+  dev::vacc_load_slice<NB>(a.v_planes + rec0 * RW, nt, a.W, 0, first);
+
   // ---- 1. logits of the chunk (tiles of 16 tokens, one per wave at a time) ----
   const int nws = dev::n_ws(a.W);
   const size_t rbb = dev::rb_bytes(a.W, NC);
@@ -163,7 +167,7 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     a.stats[cidx * 8 + 2 * tid] = st_m[tid];
     a.stats[cidx * 8 + 2 * tid + 1] = st_l[tid];
   }
-  dev::vacc_mfma<NB, MSE>(a.v_planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp);
+  dev::vacc_mfma<NB, MSE>(a.v_planes + rec0 * RW, nt, a.W, wts, a.cf, lds, dst, a.Dp, first);
 }
 
 struct DecFinArgs {
@@ -208,25 +212,12 @@ __global__ void __launch_bounds__(256) decode_final_kernel(DecFinArgs a) {
   __syncthreads();
   const float L = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int j = tid; j < a.Dp; j += 256) {
-    float s1 = 0.f, s2 = 0.f;
-    for (int c = 0; c < a.n_chunk; ++c) {
-      const float* pc = a.part + (c0 + c) * 8 * (size_t)a.Dp;
-      s1 = fmaf(fac[c], pc[hh * a.Dp + j], s1);
-      s2 = fmaf(fac[c], pc[(4 + hh) * a.Dp + j], s2);
-    }
-    arot[j] = s1 * inv;
-    ask[j] = s2 * inv;
-  }
   __syncthreads();
-  for (int i = tid; i < a.d; i += 256) {
-    float o1 = 0.f, o2 = 0.f;
-    for (int j = 0; j < a.d; ++j) {
-      o1 = fmaf(a.pi32[(int64_t)j * a.d + i], arot[j], o1);
-      if (a.qjl) o2 = fmaf(a.s32[(int64_t)j * a.d + i], ask[j], o2);
-    }
-    a.out[(int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d + i] = fmaf(a.alpha, o2, o1);
-  }
+  __shared__ float red2[512];
+  dev::sum_chunk_partials(a.part + c0 * 8 * (size_t)a.Dp, a.n_chunk, hh, 4 + hh, a.Dp, fac, inv,
+                          red2, arot, ask);
+  dev::apply_transforms(a.pi32, a.s32, a.d, a.qjl != 0, a.alpha, arot, ask, red2,
+                        a.out + (int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d);
 }
 
 struct DecLayout {

@@ -164,12 +164,37 @@ inline bool make_vacc_coef(const int32_t* mono_mask, const double* mono_w, int n
   return true;
 }
 
-// planes: global records of the chunk (token t at planes + t * W * NB);
-// wts: LDS [kVChunk][8] (read for t < nt only); lds: vacc_lds_bytes(NB)
-// bytes, 16-aligned.  Callers synchronise before reusing wts or lds.
+// One slice (4 words) of the chunk's records in registers: thread tid holds
+// items tid + 256 q (q < 4) = (word it / kVChunk of the slice, token
+// it % kVChunk); zero beyond nt and W.  Loaded ahead of use, so that the
+// loads are in flight while other work runs.
+template <int NB>
+struct VaccSlice {
+  uint32_t v[4][NB];
+};
+template <int NB>
+__device__ inline void vacc_load_slice(const uint32_t* planes, int nt, int W, int w0,
+                                       VaccSlice<NB>& sl) {
+  const int RW = W * NB;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int it = (int)threadIdx.x + 256 * q;
+    const int wl = it / kVChunk, t = it % kVChunk, w = w0 + wl;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) sl.v[q][p] = 0u;
+    if (w < W && t < nt) load_words<NB>(planes + (int64_t)t * RW + w * NB, sl.v[q]);
+  }
+}
+
+// planes: global records of the chunk (token t at planes + t * W * NB), of
+// which the caller has loaded slice 0 into `first` (vacc_load_slice with
+// w0 = 0); wts: LDS [kVChunk][8] (read for t < nt only); lds:
+// vacc_lds_bytes(NB) bytes, 16-aligned.  Callers synchronise before reusing
+// wts or lds.
 template <int NB, bool MSE>
 __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wts,
-                          const VaccCoef cf, char* lds, float* dst, int Dp) {
+                          const VaccCoef cf, char* lds, float* dst, int Dp,
+                          const VaccSlice<NB>& first, bool accumulate = false) {
   constexpr int CP = MSE ? NB : NB - 1;       // code planes
   constexpr int NV = 1 << (CP - 1);           // Walsh subsets
   constexpr int NP = MSE ? 1 : 2;             // weight parts: code, sign
@@ -206,37 +231,54 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
   // 2. A operands: weight of token t (block b, position tb): token group
   //    tb / 32 sits in lane group [0, 2, 1, 3][tb / 32] (the order the
   //    permlane16 swap leaves), bit tb % 32 = 8 e + 4 h + i is byte e of
-  //    register i of half h, shift k = 4 h + i.
-  for (int it = tid; it < kVChunk * 4 * NP; it += 256) {
-    const int t = it % kVChunk, hh = (it / kVChunk) & 3, part = it / (4 * kVChunk);
-    const int combo = 4 * part + hh;
-    const int Q = t < nt ? (int)rintf(ldexpf(wts[8 * t + combo], s_e[combo])) : 0;
-    const int b = t >> 7, tb = t & 127, grp = tb >> 5, bit = tb & 31;
-    const int g = (grp == 1) ? 2 : (grp == 2 ? 1 : grp);
-    const int eb = bit >> 3, h = (bit >> 2) & 1, i = bit & 3, k = 4 * h + i;
-    const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
-    char* base = (char*)(aops + ((b * 2 + part) * 2 + h) * 64) + 4 * i + eb;
+  //    register i of half h, shift k = 4 h + i.  An item is the 4 tokens
+  //    e = 0..3 of one (block, part, head, group, h, i): their limb words
+  //    (A' + 0x80808080) ^ 0x80808080 are byte-transposed so that each
+  //    register dword (one limb of the 4 tokens) is one LDS write.
+  for (int it = tid; it < (kVChunk / 32) * 4 * 8 * NP; it += 256) {
+    const int hi = it & 7, h = hi >> 2, i = hi & 3;       // (h, i) fastest: distinct dwords
+    const int rest = it >> 3;
+    const int hh = rest & 3, r2 = rest >> 2;
+    const int tg = r2 % (kVChunk / 32), part = r2 / (kVChunk / 32);   // 32-token group
+    const int combo = 4 * part + hh, e2 = s_e[combo], k = 4 * h + i;
+    uint32_t D[4];
 #pragma unroll
-    for (int L = 0; L < 4; ++L) {
-      const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
-      base[(16 * g + 4 * hh + L) * 16] = (char)(digit ^ 0x80u);
+    for (int e = 0; e < 4; ++e) {
+      const int t = 32 * tg + 8 * e + 4 * h + i;
+      const int Q = t < nt ? (int)rintf(ldexpf(wts[8 * t + combo], e2)) : 0;
+      const int Ap = (k < 7) ? shift_round(Q, k) : -shift_round(Q, 7);
+      D[e] = ((uint32_t)Ap + 0x80808080u) ^ 0x80808080u;
     }
+    // 4 x 4 byte transpose: O[L] byte e = D[e] byte L
+    const uint32_t t0 = __builtin_amdgcn_perm(D[1], D[0], 0x05010400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(D[1], D[0], 0x07030602u);
+    const uint32_t t2 = __builtin_amdgcn_perm(D[3], D[2], 0x05010400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(D[3], D[2], 0x07030602u);
+    const uint32_t O[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u),
+                           __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                           __builtin_amdgcn_perm(t3, t1, 0x05040100u),
+                           __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+    const int b = tg >> 2, grp = tg & 3;
+    const int g = (grp == 1) ? 2 : (grp == 2 ? 1 : grp);
+    uint32_t* base = (uint32_t*)(aops + ((b * 2 + part) * 2 + h) * 64) + i;
+#pragma unroll
+    for (int L = 0; L < 4; ++L) base[(16 * g + 4 * hh + L) * 4] = O[L];
   }
   const TransposeLanes tl(lane);
   const int gq = lane >> 4, n = lane & 15;
-  // 3. slices of 4 words
+  // 3. slices of 4 words; the next slice is loaded while this one computes
+  VaccSlice<NB> sl = first;
   for (int w0 = 0; w0 < W; w0 += 4) {
     __syncthreads();            // A operands written / previous slice consumed
-    for (int it = tid; it < 4 * kVChunk; it += 256) {
-      const int wl = it / kVChunk, t = it % kVChunk, w = w0 + wl;
-      uint32_t v[NB];
 #pragma unroll
-      for (int p = 0; p < NB; ++p) v[p] = 0u;
-      if (w < W && t < nt) load_words<NB>(planes + (int64_t)t * RW + w * NB, v);
+    for (int q = 0; q < 4; ++q) {
+      const int it = tid + 256 * q;
+      const int wl = it / kVChunk, t = it % kVChunk;
 #pragma unroll
-      for (int p = 0; p < NB; ++p) wordsT[(wl * NB + p) * kVChunk + t] = v[p];
+      for (int p = 0; p < NB; ++p) wordsT[(wl * NB + p) * kVChunk + t] = sl.v[q][p];
     }
     __syncthreads();
+    if (w0 + 4 < W) vacc_load_slice<NB>(planes, nt, W, w0 + 4, sl);
     const int w = w0 + wave;
     if (w >= W) continue;
     v4i G[2][NV], S[2];
@@ -293,8 +335,116 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
 #pragma unroll
       for (int m = 0; m < NV; ++m) code = fmaf(cf.wm2[m], limbs_to_float(G[cb][m]), code);
       const int j = 32 * w + 16 * cb + n;
-      dst[gq * Dp + j] = fmaf(code, sc0, cf.c0 * s_sum[gq]);
-      dst[(4 + gq) * Dp + j] = MSE ? 0.f : fmaf(limbs_to_float(S[cb]), sc1, -s_sum[4 + gq]);
+      float v0 = fmaf(code, sc0, cf.c0 * s_sum[gq]);
+      float v1 = MSE ? 0.f : fmaf(limbs_to_float(S[cb]), sc1, -s_sum[4 + gq]);
+      if (accumulate) {         // this block's own partial from an earlier call
+        v0 += dst[gq * Dp + j];
+        v1 += dst[(4 + gq) * Dp + j];
+      }
+      dst[gq * Dp + j] = v0;
+      dst[(4 + gq) * Dp + j] = v1;
+    }
+  }
+}
+
+// ---- finishing a query head: chunk partials -> output -----------------------
+// Block-wide (256 threads).  Threads split as NL = min(n, 256) lanes over the
+// outputs x 256 / NL groups over the summed index; the groups' partial sums
+// meet in LDS `red` (>= 2 * 256 floats).  Four independent accumulators per
+// thread keep several loads in flight.
+
+// arot[j] = sc * sum_c f_c part_c[r0][j],  ask[j] = sc * sum_c f_c part_c[r1][j]
+// for j < Dp, chunk c's rows at part + c * 8 * Dp; f_c = fac[c] (LDS) or 1.
+__device__ inline void sum_chunk_partials(const float* part, int n_chunk, int r0, int r1, int Dp,
+                                          const float* fac, float sc, float* red, float* arot,
+                                          float* ask) {
+  const int tid = threadIdx.x;
+  const int NL = min(Dp, 256), TT = 256 / NL;
+  const int lj = tid % NL, tg = tid / NL;
+  for (int j0 = 0; j0 < Dp; j0 += NL) {
+    const int j = j0 + lj;
+    float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
+    if (tg < TT && j < Dp) {
+      int c = tg;
+      for (; c + 3 * TT < n_chunk; c += 4 * TT) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float* pc = part + (int64_t)(c + u * TT) * 8 * Dp;
+          const float f = fac ? fac[c + u * TT] : 1.f;
+          a1[u] = fmaf(f, pc[r0 * Dp + j], a1[u]);
+          a2[u] = fmaf(f, pc[r1 * Dp + j], a2[u]);
+        }
+      }
+      for (; c < n_chunk; c += TT) {
+        const float* pc = part + (int64_t)c * 8 * Dp;
+        const float f = fac ? fac[c] : 1.f;
+        a1[0] = fmaf(f, pc[r0 * Dp + j], a1[0]);
+        a2[0] = fmaf(f, pc[r1 * Dp + j], a2[0]);
+      }
+    }
+    const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
+    const float s2 = (a2[0] + a2[1]) + (a2[2] + a2[3]);
+    if (TT == 1) {
+      if (tg == 0 && j < Dp) {      // threads past NL (256 % NL != 0) only idle
+        arot[j] = s1 * sc;
+        ask[j] = s2 * sc;
+      }
+    } else {
+      red[tid] = s1;
+      red[256 + tid] = s2;
+      __syncthreads();
+      if (tid < NL) {
+        float t1 = 0.f, t2 = 0.f;
+        for (int q = 0; q < TT; ++q) {
+          t1 += red[q * NL + tid];
+          t2 += red[256 + q * NL + tid];
+        }
+        arot[j] = t1 * sc;
+        ask[j] = t2 * sc;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// out[i] = sum_j Pi[j][i] arot[j] + alpha sum_j S[j][i] ask[j]  (i < d; the
+// second sum only when qjl), with Pi and S row-major fp32 [d][d].
+__device__ inline void apply_transforms(const float* pi32, const float* s32, int d, bool qjl,
+                                        float alpha, const float* arot, const float* ask,
+                                        float* red, float* out) {
+  const int tid = threadIdx.x;
+  const int NI = min(d, 256), TT = 256 / NI;
+  const int li = tid % NI, tg = tid / NI;
+  for (int i0 = 0; i0 < d; i0 += NI) {
+    const int i = i0 + li;
+    float o1[4] = {0.f, 0.f, 0.f, 0.f}, o2[4] = {0.f, 0.f, 0.f, 0.f};
+    if (tg < TT && i < d) {
+      int j = tg;
+      for (; j + 3 * TT < d; j += 4 * TT) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int jj = j + u * TT;
+          o1[u] = fmaf(pi32[(int64_t)jj * d + i], arot[jj], o1[u]);
+          if (qjl) o2[u] = fmaf(s32[(int64_t)jj * d + i], ask[jj], o2[u]);
+        }
+      }
+      for (; j < d; j += TT) {
+        o1[0] = fmaf(pi32[(int64_t)j * d + i], arot[j], o1[0]);
+        if (qjl) o2[0] = fmaf(s32[(int64_t)j * d + i], ask[j], o2[0]);
+      }
+    }
+    const float v = fmaf(alpha, (o2[0] + o2[1]) + (o2[2] + o2[3]), (o1[0] + o1[1]) + (o1[2] + o1[3]));
+    if (TT == 1) {
+      if (tg == 0 && i < d) out[i] = v;
+    } else {
+      red[tid] = v;
+      __syncthreads();
+      if (tid < NI) {
+        float t = 0.f;
+        for (int q = 0; q < TT; ++q) t += red[q * NI + tid];
+        out[i] = t;
+      }
+      __syncthreads();
     }
   }
 }
