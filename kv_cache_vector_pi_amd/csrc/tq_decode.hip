@@ -91,33 +91,58 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
   const char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * rbb;
   const float4 cst = ((const float4*)(rbase + (size_t)nws * NC * 64 * 16))[g];
   const bool head_ok = 4 * rb + g < a.G;
-  for (int ti = wave; ti < CH / dev::kTile; ti += dev::kWaves) {
-    const int tl = dev::kTile * ti + n;                // token within the chunk
+  // every load of the phase is issued up front: the first word step of the
+  // wave's 4 key tiles with their norms, the operands of that word step, and
+  // the value norm of token tid (used for the weights)
+  constexpr int TPW = CH / dev::kTile / dev::kWaves;   // key tiles per wave
+  uint32_t wd0[TPW][NB], nrm0[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tl = dev::kTile * (wave + dev::kWaves * u) + n;
+    const bool valid = tl < nt;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) wd0[u][p] = 0u;
+    if (valid && g < a.W) dev::load_group<NB>(a.k_planes + ((rec0 + tl) * a.W + g) * NB, wd0[u]);
+    nrm0[u] = valid ? a.k_norms[rec0 + tl] : 0u;
+  }
+  v4i A0[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) A0[c] = ((const v4i*)rbase)[c * 64 + lane];
+  const uint32_t vnr = tid < nt ? a.v_norms[rec0 + tid] : 0u;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tl = dev::kTile * (wave + dev::kWaves * u) + n;   // token within the chunk
     const bool valid = tl < nt;
     const int64_t rec = rec0 + tl;
-    const uint32_t nrm = valid ? a.k_norms[rec] : 0u;
+    const uint32_t nrm = nrm0[u];
     v4i acc_m = {0, 0, 0, 0}, acc_q = {0, 0, 0, 0};
     for (int wsi = 0; wsi < nws; ++wsi) {
       const int w = 4 * wsi + g;
       uint32_t wd[NB];
 #pragma unroll
-      for (int p = 0; p < NB; ++p) wd[p] = 0u;
-      if (valid && w < a.W) dev::load_group<NB>(a.k_planes + (rec * a.W + w) * NB, wd);
+      for (int p = 0; p < NB; ++p) wd[p] = wd0[u][p];
+      if (wsi > 0) {
+#pragma unroll
+        for (int p = 0; p < NB; ++p) wd[p] = 0u;
+        if (valid && w < a.W) dev::load_group<NB>(a.k_planes + (rec * a.W + w) * NB, wd);
+      }
       const v4i* fr = (const v4i*)(rbase + (size_t)wsi * NC * 64 * 16);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        uint32_t u = 0u;
+        uint32_t uw = 0u;
 #pragma unroll
         for (int p = 0; p < CP; ++p)
-          if ((a.mask[v] >> p) & 1) u ^= wd[p];
+          if ((a.mask[v] >> p) & 1) uw ^= wd[p];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
-          acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(fr[(2 * v + half) * 64 + lane],
-                                                        dev::bit_lanes(u, half), acc_m, 0, 0, 0);
+          acc_m = __builtin_amdgcn_mfma_i32_16x16x64_i8(wsi == 0 ? A0[2 * v + half]
+                                                                 : fr[(2 * v + half) * 64 + lane],
+                                                        dev::bit_lanes(uw, half), acc_m, 0, 0, 0);
       }
 #pragma unroll
       for (int half = 0; half < (MSE ? 0 : 2); ++half)
-        acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(fr[(2 * NV + half) * 64 + lane],
+        acc_q = __builtin_amdgcn_mfma_i32_16x16x64_i8(wsi == 0 ? A0[2 * NV + half]
+                                                               : fr[(2 * NV + half) * 64 + lane],
                                                       dev::bit_lanes(wd[NB - 1], half), acc_q,
                                                       0, 0, 0);
     }
@@ -150,13 +175,17 @@ __global__ void __launch_bounds__(256) decode_chunk_kernel(DecArgs a) {
     }
   }
   __syncthreads();
-  // weights: p nu and p nu gamma of the value records
-  for (int i = tid; i < nt * 8; i += 256) {
-    const int t = i >> 3, k = i & 7, hh = k & 3;
-    const uint32_t nr = a.v_norms[rec0 + t];
-    float w = lg[hh * CH + t] * __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
-    if (k >= 4) w *= __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
-    wts[i] = w;
+  // weights of token tid: p nu and p nu gamma of its value record
+  static_assert(CH == 256, "one token per thread");
+  {
+    const float nu = __half2float(__ushort_as_half((unsigned short)(vnr & 0xffffu)));
+    const float ga = __half2float(__ushort_as_half((unsigned short)(vnr >> 16)));
+    float4 w1, w2;
+    w1.x = lg[tid] * nu; w1.y = lg[CH + tid] * nu; w1.z = lg[2 * CH + tid] * nu;
+    w1.w = lg[3 * CH + tid] * nu;
+    w2.x = w1.x * ga; w2.y = w1.y * ga; w2.z = w1.z * ga; w2.w = w1.w * ga;
+    *(float4*)&wts[8 * tid] = w1;
+    *(float4*)&wts[8 * tid + 4] = w2;
   }
   __syncthreads();
 
