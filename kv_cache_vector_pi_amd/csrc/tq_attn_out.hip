@@ -23,6 +23,7 @@
 #include <cmath>
 
 #include "tq_dev.h"
+#include "tq_vacc.h"
 #include "tq_internal.h"
 
 namespace tq {
