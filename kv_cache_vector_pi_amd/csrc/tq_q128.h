@@ -160,11 +160,14 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
     }
   };
   if (r.one) {        // uniform branch: rows t0 .. t0 + cnt - 1 of head h0
+    // row offsets within the tile in 32 bits (the launcher keeps
+    // x_stride_token below 2^25 elements)
     const int64_t base = (int64_t)r.h0 * a.x_stride_head + (int64_t)r.t0 * a.x_stride_token;
+    const int32_t xst = (int32_t)a.x_stride_token;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int v = 4 * wave + 16 * p + (lane >> 4);
-      load(p, base + (int64_t)(v < r.cnt ? v : 0) * a.x_stride_token + 8 * (lane & 15));
+      load(p, base + (int64_t)((v < r.cnt ? v : 0) * xst + 8 * (lane & 15)));
     }
   } else {
 #pragma unroll
@@ -196,7 +199,8 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   __shared__ __align__(16) _Float16 xl_s[BF16 ? 8 : kT * kLdx];
   __shared__ __align__(16) _Float16 rh_s[kT * kLdx];
   __shared__ __align__(16) _Float16 rl_s[kT * kLdx];
-  __shared__ float ysc[2][kT];        // by tile parity
+  __shared__ float ysc[2][kT];        // by tile parity: 2^e / nu (0 for x = 0)
+  __shared__ float sinv[2][kT];       // nu 2^-e (1 for x = 0): thresholds to acc units
   __shared__ uint32_t nu16[2][kT];
   __shared__ float gpart[4][kT];
   // packed records and norms of the tile (the global layout), written out
@@ -269,7 +273,8 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     *(v8h*)(xh_s + v * kLdx + 8 * c) = hi;
     if constexpr (!BF16) *(v8h*)(xl_s + v * kLdx + 8 * c) = lo;
     // the 16 lanes of the row write the same values
-    ysc[pb][v] = (nu > 0.f) ? ldexpf(1.f / nu, ex) : 0.f;
+    ysc[pb][v] = (nu > 0.f) ? ldexpf(__builtin_amdgcn_rcpf(nu), ex) : 0.f;
+    sinv[pb][v] = (nu > 0.f) ? ldexpf(nu, -ex) : 1.f;
     nu16[pb][v] = (uint32_t)__half_as_ushort(__float2half_rn(nu));
   };
 
@@ -302,7 +307,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   auto codes = [&](const v16f& acc, int cb, int pb, auto&& hook) {
     const int v = 32 * cb + col;
     const float sv = ysc[pb][v];
-    const float inv = sv > 0.f ? 1.f / sv : 1.f;
+    const float inv = sinv[pb][v];
     float thr_v[NT > 0 ? NT : 1], cpos_v[KH];
 #pragma unroll
     for (int k = 0; k < NT; ++k) thr_v[k] = a.thr[k] * inv;

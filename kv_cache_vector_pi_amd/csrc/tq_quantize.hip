@@ -498,7 +498,8 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
                            int32_t n_heads, int64_t x_stride_token, int64_t x_stride_head,
                            uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
                            int64_t dst_token0, hipStream_t stream) {
-  if (ctx->d == 128)
+  // the d = 128 kernel computes row offsets within a tile in 32 bits
+  if (ctx->d == 128 && x_stride_token < ((int64_t)1 << 25))
     return launch_quantize128(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
                               planes, norms, dst_stride_head, dst_token0, stream);
   QuantArgs a{};

@@ -68,7 +68,8 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
   if (!quant && !prep) return hipSuccess;
   // One grid needs the d = 128 quantizer and one launch's worth of rows;
   // otherwise the same three jobs run as separate launches.
-  if (ctx->d != 128 || (quant && (int64_t)n_heads * n_tokens > kMaxRows)) {
+  if (ctx->d != 128 || (quant && ((int64_t)n_heads * n_tokens > kMaxRows ||
+                                   x_stride_token >= ((int64_t)1 << 25)))) {
     hipError_t e = hipSuccess;
     if (quant) {
       e = launch_quantize(ctx, k_new, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
