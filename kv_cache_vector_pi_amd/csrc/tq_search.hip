@@ -282,22 +282,32 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
 
-  for (int w = 0; w < a.W; ++w) {
-    __syncthreads();              // previous word's operands fully read
-    // stage the query rows: NA arrays x 128 rows x 32 halves, 16 bytes a thread
-    // x 2 NA
+  // Word w's query rows (NA arrays x 128 rows x 32 halves, 16 bytes a thread
+  // x 2 NA) and record words are loaded into registers one word ahead, so the
+  // loads are in flight while the previous word's MFMAs run.
+  v8h ra[2 * NA];
+  uint32_t wd[NB];
+  auto load_word = [&](int w) {
 #pragma unroll
     for (int j = 0; j < 2 * NA; ++j) {
       const int c = tid + 256 * j;
       const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
-      const v8h v = *(const v8h*)(a.qa[ar] + (q0 + row) * a.Dp + 32 * w + 8 * part);
-      *(v8h*)(&As[ar][row * kLdsRow + 8 * part]) = v;
+      ra[j] = *(const v8h*)(a.qa[ar] + (q0 + row) * a.Dp + 32 * w + 8 * part);
+    }
+#pragma unroll
+    for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
+  };
+  load_word(0);
+  for (int w = 0; w < a.W; ++w) {
+    __syncthreads();              // previous word's operands fully read
+#pragma unroll
+    for (int j = 0; j < 2 * NA; ++j) {
+      const int c = tid + 256 * j;
+      const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
+      *(v8h*)(&As[ar][row * kLdsRow + 8 * part]) = ra[j];
     }
     // decode word w of record dr
     {
-      uint32_t wd[NB];
-#pragma unroll
-      for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
       v8h vh[2], vl[2], vg[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -322,6 +332,7 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
       }
     }
     __syncthreads();
+    if (w + 1 < a.W) load_word(w + 1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       v8h A[2][4], B[2][3];
