@@ -1,4 +1,5 @@
-// Device helpers shared by the logit, value-output and fused decode kernels.
+// Device helpers shared by the logit, query-preparation, value-output and
+// fused decode kernels (the value-side code itself is in tq_vacc.h).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
