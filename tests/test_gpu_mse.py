@@ -174,6 +174,7 @@ def test_mse_attn_output_parity(orc, d, b, n_q, n_kv, lens, signed):
     (128, 3, 16, 1, [1024]),
     (128, 1, 8, 8, [300, 1]),                 # G = 1, a one-token sequence
     (200, 2, 8, 2, [333, 70]),
+    (1536, 3, 4, 1, [140]),                   # 12 word slices
 ])
 def test_mse_attn_decode_parity(orc, d, b, n_q, n_kv, lens):
     say("mse attn decode", d, b, n_q, n_kv, lens)

@@ -378,6 +378,7 @@ def run_vout(ctx, p, P, N, n_kv, vstride, starts, lens, n_q, p_stride):
     (128, 4, 6, 2, [700], False),             # G = 3 (partial row block)
     (200, 4, 8, 2, [333, 70], False),
     (1536, 2, 4, 1, [150], True),
+    (64, 3, 16, 4, [257, 600], False),        # d = 64: two words, idle waves in a slice
 ])
 def test_attn_output_parity(orc, d, b, n_q, n_kv, lens, signed):
     say("attn output", d, b, n_q, n_kv, lens)
@@ -444,6 +445,7 @@ def softmax_rows(x):
     (128, 4, 6, 2, [700]),                    # G = 3
     (200, 4, 8, 2, [333, 70]),
     (1536, 2, 4, 1, [150]),
+    (64, 4, 8, 1, [513, 3]),                  # d = 64, G = 8 (two row blocks)
 ])
 def test_attn_decode_parity(orc, d, b, n_q, n_kv, lens):
     say("attn decode", d, b, n_q, n_kv, lens)
