@@ -183,6 +183,26 @@ TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtyp
                                 int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                                 int64_t dst_stride_head, int64_t dst_token0, void* stream);
 
+/* tq_quantize_kv with a destination per input token (turboquant.net
+ * pseudo-code, "integrate into Transformer attention": each step's new keys
+ * and values are quantized into the cache), for appends that land at
+ * different positions in one call: the new tokens of a batch of sequences
+ * (a chunk each, or one token each in decoding), gathered into one input.
+ * Record (h, t) goes to index h*dst_stride_head + slots[t] of planes and
+ * norms; a token with slots[t] < 0 or slots[t] >= dst_stride_head is skipped
+ * (nothing written: padding rows of a batch).  slots: device int64
+ * [n_tokens], 8-byte aligned; distinct slots give distinct records (two
+ * tokens with one slot race).  Everything else, the results included, as
+ * tq_quantize_kv: a token's record is bit-identical to what tq_quantize_kv
+ * writes for it.
+ * Errors: as tq_quantize_kv; TQ_ERR_INVALID_ARG also for NULL slots with work
+ * to do, dst_stride_head < 1 or misaligned slots. */
+TQ_API tq_status tq_quantize_kv_slots(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                      int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                      int64_t x_stride_head, const int64_t* slots,
+                                      uint32_t* planes, uint16_t* norms,
+                                      int64_t dst_stride_head, void* stream);
+
 /* Dequantize n records (turboquant.net pseudo-code "dequant", with the QJL
  * term so that <q, out_i> equals est(q, record i) for every q):
  *   out_i = nu * (Pi^T c[idx] + alpha * gamma * S^T s).
@@ -250,7 +270,9 @@ TQ_API tq_status tq_attn_logits_prepared(const tq_ctx* ctx, const void* workspac
  * tq_quantize_kv(v_new -> v_planes/v_norms) and tq_attn_prepare(q ->
  * workspace), with bit-identical results.  K and V share dtype, sizes,
  * strides and the destination indexing (record (h, t) at
- * h*dst_stride_head + dst_token0 + t of each cache); the preparation
+ * h*dst_stride_head + dst_token0 + t of each cache, or with dst_slots
+ * non-NULL h*dst_stride_head + dst_slots[t] under the rules of
+ * tq_quantize_kv_slots, dst_token0 then 0); the preparation
  * arguments are those of tq_attn_prepare.  At d = 128 the three jobs run in
  * one grid (the small per-step jobs then cost one launch instead of three);
  * other d run them as three launches.
@@ -263,6 +285,7 @@ TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, co
                                         uint32_t* k_planes, uint16_t* k_norms,
                                         uint32_t* v_planes, uint16_t* v_norms,
                                         int64_t dst_stride_head, int64_t dst_token0,
+                                        const int64_t* dst_slots,
                                         const float* q, int32_t batch, int32_t n_q_heads,
                                         int64_t q_stride_batch, int32_t n_kv_heads,
                                         void* workspace, size_t workspace_bytes, void* stream);

@@ -31,7 +31,7 @@ EXPORTS = [
     "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
     "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
-    "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare",
+    "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare", "tq_quantize_kv_slots",
 ]
 
 
@@ -69,10 +69,11 @@ _sig("tq_ctx_destroy", _i32, [_P])
 _sig("tq_ctx_create_mse", _i32, [_i32, _i32, _P, _P, ctypes.POINTER(_P)])
 _sig("tq_ctx_is_mse", _i32, [_P])
 _sig("tq_decode_step_prepare", _i32, [_P, _P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _P,
-                                      _i64, _i64, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
+                                      _i64, _i64, _P, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
 _sig("tq_ctx_dim", _i32, [_P])
 _sig("tq_ctx_bits", _i32, [_P])
 _sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
+_sig("tq_quantize_kv_slots", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _i64, _P])
 _sig("tq_dequantize", _i32, [_P, _P, _P, _i64, _P, _i64, _P])
 _sig("tq_attn_logits_workspace_bytes", _sz, [_P, _i32, _i32, _i32])
 _sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P, _i32, _f32,
@@ -216,10 +217,10 @@ def alloc_records(n, d, b, device="cuda"):
 
 
 # ---- hot path -------------------------------------------------------------
-def tq_quantize_kv(ctx, x, planes, norms, n_tokens=None, n_heads=None, x_stride_token=None,
-                   x_stride_head=None, dst_stride_head=None, dst_token0=0, stream=None):
-    """Quantize x ([n_heads, n_tokens, d] or [n, d] torch tensor, float32 or
-    bfloat16) into planes/norms (see tq.h for the record indexing)."""
+def _quant_input(x, n_tokens, n_heads, x_stride_token, x_stride_head):
+    """(dtype code, n_tokens, n_heads, token stride, head stride) of a
+    [n_heads, n_tokens, d] or [n, d] float32/bfloat16 tensor; explicit
+    arguments win."""
     import torch
     if x.dtype == torch.bfloat16:
         dt = TQ_BF16
@@ -227,24 +228,38 @@ def tq_quantize_kv(ctx, x, planes, norms, n_tokens=None, n_heads=None, x_stride_
         dt = TQ_F32
     else:
         raise TypeError(f"unsupported dtype {x.dtype}")
-    if x.dim() == 2:
-        x3 = x.unsqueeze(0)
-    else:
-        x3 = x
-    if n_heads is None:
-        n_heads = x3.shape[0]
-    if n_tokens is None:
-        n_tokens = x3.shape[1]
-    if x_stride_token is None:
-        x_stride_token = x3.stride(1)
-    if x_stride_head is None:
-        x_stride_head = x3.stride(0)
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    return (dt, x3.shape[1] if n_tokens is None else n_tokens,
+            x3.shape[0] if n_heads is None else n_heads,
+            x3.stride(1) if x_stride_token is None else x_stride_token,
+            x3.stride(0) if x_stride_head is None else x_stride_head)
+
+
+def tq_quantize_kv(ctx, x, planes, norms, n_tokens=None, n_heads=None, x_stride_token=None,
+                   x_stride_head=None, dst_stride_head=None, dst_token0=0, stream=None):
+    """Quantize x ([n_heads, n_tokens, d] or [n, d] torch tensor, float32 or
+    bfloat16) into planes/norms (see tq.h for the record indexing)."""
+    dt, n_tokens, n_heads, x_stride_token, x_stride_head = _quant_input(
+        x, n_tokens, n_heads, x_stride_token, x_stride_head)
     if dst_stride_head is None:
         dst_stride_head = n_tokens
     st = _lib.tq_quantize_kv(ctx.handle, _ptr(x), dt, n_tokens, n_heads, x_stride_token,
                              x_stride_head, _ptr(planes), _ptr(norms), dst_stride_head,
                              dst_token0, _stream(stream))
     _check(st, "tq_quantize_kv")
+
+
+def tq_quantize_kv_slots(ctx, x, slots, planes, norms, dst_stride_head, n_tokens=None,
+                         n_heads=None, x_stride_token=None, x_stride_head=None, stream=None):
+    """Quantize x ([n_heads, n_tokens, d] or [n, d]) into planes/norms with
+    token t's record of head h at h * dst_stride_head + slots[t] (slots: int64
+    device tensor [n_tokens]; slots outside [0, dst_stride_head) are skipped)."""
+    dt, n_tokens, n_heads, x_stride_token, x_stride_head = _quant_input(
+        x, n_tokens, n_heads, x_stride_token, x_stride_head)
+    st = _lib.tq_quantize_kv_slots(ctx.handle, _ptr(x), dt, n_tokens, n_heads, x_stride_token,
+                                   x_stride_head, _ptr(slots), _ptr(planes), _ptr(norms),
+                                   dst_stride_head, _stream(stream))
+    _check(st, "tq_quantize_kv_slots")
 
 
 def tq_dequantize(ctx, planes, norms, n, out, out_ld=None, stream=None):
@@ -280,10 +295,11 @@ def tq_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, worksp
 
 def tq_decode_step_prepare(ctx, k_new, v_new, k_planes, k_norms, v_planes, v_norms, q, batch,
                            n_q_heads, q_stride_batch, n_kv_heads, workspace, dst_stride_head,
-                           dst_token0=0, stream=None):
+                           dst_token0=0, stream=None, dst_slots=None):
     """Quantize k_new and v_new ([n_heads, n_tokens, d], same dtype, sizes and
     strides) into the two caches and prepare q into workspace, in one launch
-    at d = 128 (see tq.h)."""
+    at d = 128 (see tq.h).  dst_slots: None, or an int64 device tensor
+    [n_tokens] of destination tokens (as tq_quantize_kv_slots)."""
     import torch
     if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or \
             k_new.stride() != v_new.stride():
@@ -299,7 +315,8 @@ def tq_decode_step_prepare(ctx, k_new, v_new, k_planes, k_norms, v_planes, v_nor
     st = _lib.tq_decode_step_prepare(ctx.handle, _ptr(k_new), _ptr(v_new), dt, n_tokens, n_heads,
                                      k_new.stride(1), k_new.stride(0), _ptr(k_planes),
                                      _ptr(k_norms), _ptr(v_planes), _ptr(v_norms),
-                                     dst_stride_head, dst_token0, _ptr(q), batch, n_q_heads,
+                                     dst_stride_head, dst_token0, _ptr(dst_slots), _ptr(q),
+                                     batch, n_q_heads,
                                      q_stride_batch, n_kv_heads, _ptr(workspace), ws_bytes,
                                      _stream(stream))
     _check(st, "tq_decode_step_prepare")

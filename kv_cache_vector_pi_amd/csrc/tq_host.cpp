@@ -453,11 +453,14 @@ static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 namespace {
 
 // Argument checks of one quantize job (fn names the entry point in messages);
-// *empty is set for a no-op job.
+// *empty is set for a no-op job.  With slots (per-token destinations) the
+// records of a head are addressed by slot alone: dst_token0 must be 0 and
+// dst_stride_head, the slot range, at least 1.
 tq_status check_quantize(const char* fn, const tq_ctx* ctx, const void* x, int32_t x_dtype,
                          int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                          int64_t x_stride_head, const uint32_t* planes, const uint16_t* norms,
-                         int64_t dst_stride_head, int64_t dst_token0, bool* empty) {
+                         int64_t dst_stride_head, int64_t dst_token0, const int64_t* slots,
+                         bool* empty) {
   *empty = false;
   if (n_tokens < 0 || n_heads < 0)
     return fail(TQ_ERR_INVALID_ARG, "%s: n_tokens=%lld n_heads=%d", fn, (long long)n_tokens,
@@ -472,6 +475,10 @@ tq_status check_quantize(const char* fn, const tq_ctx* ctx, const void* x, int32
   if (x_stride_token < ctx->d || (n_heads > 1 && x_stride_head < 0) || dst_stride_head < 0 ||
       dst_token0 < 0)
     return fail(TQ_ERR_INVALID_ARG, "%s: bad strides", fn);
+  if (slots && (dst_token0 != 0 || dst_stride_head < 1 || !aligned(slots, 8)))
+    return fail(TQ_ERR_INVALID_ARG,
+                "%s: with slots, dst_token0 must be 0, dst_stride_head >= 1 and slots 8-byte "
+                "aligned", fn);
   const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
   if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(x, 16) ||
       (x_stride_token * esz) % 16 != 0 || (x_stride_head * esz) % 16 != 0)
@@ -513,13 +520,35 @@ TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtyp
   bool empty;
   const tq_status st = check_quantize("tq_quantize_kv", ctx, x, x_dtype, n_tokens, n_heads,
                                       x_stride_token, x_stride_head, planes, norms,
-                                      dst_stride_head, dst_token0, &empty);
+                                      dst_stride_head, dst_token0, nullptr, &empty);
   if (st != TQ_OK) return st;
   if (empty) return ok();
   hipError_t e = tq::launch_quantize(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
                                      x_stride_head, planes, norms, dst_stride_head, dst_token0,
-                                     (hipStream_t)stream);
+                                     nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_quantize_kv: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_quantize_kv_slots(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                      int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                      int64_t x_stride_head, const int64_t* slots,
+                                      uint32_t* planes, uint16_t* norms,
+                                      int64_t dst_stride_head, void* stream) {
+  const char* fn = "tq_quantize_kv_slots";
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+  if (!slots && n_tokens > 0 && n_heads > 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: slots is NULL", fn);
+  bool empty;
+  const tq_status st = check_quantize(fn, ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                      x_stride_head, planes, norms, dst_stride_head, 0, slots,
+                                      &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
+  hipError_t e = tq::launch_quantize(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                     x_stride_head, planes, norms, dst_stride_head, 0, slots,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_kv_slots: launch");
   return ok();
 }
 
@@ -529,6 +558,7 @@ TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, co
                                         uint32_t* k_planes, uint16_t* k_norms,
                                         uint32_t* v_planes, uint16_t* v_norms,
                                         int64_t dst_stride_head, int64_t dst_token0,
+                                        const int64_t* dst_slots,
                                         const float* q, int32_t batch, int32_t n_q_heads,
                                         int64_t q_stride_batch, int32_t n_kv_heads,
                                         void* workspace, size_t workspace_bytes, void* stream) {
@@ -537,10 +567,11 @@ TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, co
   bool no_k, no_v, no_q;
   tq_status st = check_quantize(fn, ctx, k_new, x_dtype, n_tokens, n_heads, x_stride_token,
                                 x_stride_head, k_planes, k_norms, dst_stride_head, dst_token0,
-                                &no_k);
+                                dst_slots, &no_k);
   if (st == TQ_OK)
     st = check_quantize(fn, ctx, v_new, x_dtype, n_tokens, n_heads, x_stride_token,
-                        x_stride_head, v_planes, v_norms, dst_stride_head, dst_token0, &no_v);
+                        x_stride_head, v_planes, v_norms, dst_stride_head, dst_token0,
+                        dst_slots, &no_v);
   if (st == TQ_OK)
     st = check_prepare(fn, ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
                        workspace_bytes, &no_q);
@@ -548,7 +579,8 @@ TQ_API tq_status tq_decode_step_prepare(const tq_ctx* ctx, const void* k_new, co
   if (no_k && no_q) return ok();
   hipError_t e = tq::launch_decode_step_prepare(
       ctx, k_new, v_new, x_dtype, no_k ? 0 : n_tokens, no_k ? 0 : n_heads, x_stride_token,
-      x_stride_head, k_planes, k_norms, v_planes, v_norms, dst_stride_head, dst_token0, q,
+      x_stride_head, k_planes, k_norms, v_planes, v_norms, dst_stride_head, dst_token0,
+      dst_slots, q,
       no_q ? 0 : batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_decode_step_prepare: launch");
   return ok();

@@ -58,19 +58,21 @@ namespace tq {
 hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, int64_t n_tokens,
                            int32_t n_heads, int64_t x_stride_token, int64_t x_stride_head,
                            uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
-                           int64_t dst_token0, hipStream_t stream);
+                           int64_t dst_token0, const int64_t* slots, hipStream_t stream);
 
 hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
-                              int64_t dst_stride_head, int64_t dst_token0, hipStream_t stream);
+                              int64_t dst_stride_head, int64_t dst_token0,
+                              const int64_t* slots, hipStream_t stream);
 
 hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, const void* v_new,
                                       int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
                                       int64_t x_stride_token, int64_t x_stride_head,
                                       uint32_t* k_planes, uint16_t* k_norms, uint32_t* v_planes,
                                       uint16_t* v_norms, int64_t dst_stride_head,
-                                      int64_t dst_token0, const float* q, int32_t batch,
+                                      int64_t dst_token0, const int64_t* slots,
+                                      const float* q, int32_t batch,
                                       int32_t n_q_heads, int64_t q_stride_batch,
                                       int32_t n_kv_heads, void* workspace, hipStream_t stream);
 

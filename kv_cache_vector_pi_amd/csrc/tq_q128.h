@@ -46,6 +46,7 @@ struct Q128Args {
   uint32_t* planes;
   uint32_t* norms;
   int64_t dst_stride_head, dst_token0;
+  const int64_t* slots;              // per-token destination, or null (dst_token0 + t)
   const __half* pi_hi;
   const __half* pi_lo;
   const __half* m_hi;
@@ -426,10 +427,16 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   int par = 0;
   bool have_prev = false;
   TileRows prev{};
+  // record of row v, or -1 for a token whose slot lies outside [0, dst_stride_head)
   auto rec_of = [&](const TileRows& r, int v) -> int64_t {
     uint32_t h, t;
     row_ht(r, v, a, h, t);
-    return (int64_t)h * a.dst_stride_head + a.dst_token0 + t;
+    int64_t s = t;
+    if (a.slots) {
+      s = a.slots[t];
+      if (s < 0 || s >= a.dst_stride_head) return -1;
+    }
+    return (int64_t)h * a.dst_stride_head + a.dst_token0 + s;
   };
   // Copy the staged records and norms of the previous tile (buffer pb) to
   // memory: prev.cnt * NB <= 256 chunks of 16 bytes, one per thread, and the
@@ -438,7 +445,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   // waits for fresh stores.
   auto flush = [&](int pb) {
     if (!have_prev) return;
-    if (prev.one) {
+    if (prev.one && !a.slots) {
       const int64_t rec0 = rec_of(prev, 0);
       if (tid < prev.cnt * NB)
         ((uint4*)(a.planes + rec0 * 4 * NB))[tid] = ((const uint4*)outw[pb])[tid];
@@ -446,10 +453,14 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     } else {
       if (tid < prev.cnt * NB) {
         const int v = tid / NB;
-        ((uint4*)(a.planes + rec_of(prev, v) * 4 * NB))[tid - v * NB] =
-            ((const uint4*)outw[pb])[tid];
+        const int64_t rec = rec_of(prev, v);
+        if (rec >= 0)
+          ((uint4*)(a.planes + rec * 4 * NB))[tid - v * NB] = ((const uint4*)outw[pb])[tid];
       }
-      if (tid < prev.cnt) a.norms[rec_of(prev, tid)] = outn[pb][tid];
+      if (tid < prev.cnt) {
+        const int64_t rec = rec_of(prev, tid);
+        if (rec >= 0) a.norms[rec] = outn[pb][tid];
+      }
     }
   };
   for (; tile < a.n_tiles; tile += stride, par ^= 1) {
@@ -515,11 +526,14 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
 constexpr int64_t kMaxRows = ((int64_t)1 << 32) - 2 * kT;   // 32-bit row indices per launch
 
 // Arguments shared by every launch of one quantize call (hipErrorInvalidValue
-// for n_tokens beyond 32-bit row indices).
+// for n_tokens beyond 32-bit row indices).  slots: null, or the destination
+// token of each input token (device int64 [n_tokens]; record (h, t) at
+// h * dst_stride_head + dst_token0 + slots[t], skipped for a slot outside
+// [0, dst_stride_head)).
 inline hipError_t q128_args(const tq_ctx* ctx, const void* x, int64_t n_tokens,
                             int64_t x_stride_token, int64_t x_stride_head, uint32_t* planes,
                             uint16_t* norms, int64_t dst_stride_head, int64_t dst_token0,
-                            Q128Args& a) {
+                            const int64_t* slots, Q128Args& a) {
   a = Q128Args{};
   a.x = x;
   a.x_stride_token = x_stride_token;
@@ -529,6 +543,7 @@ inline hipError_t q128_args(const tq_ctx* ctx, const void* x, int64_t n_tokens,
   a.norms = (uint32_t*)norms;
   a.dst_stride_head = dst_stride_head;
   a.dst_token0 = dst_token0;
+  a.slots = slots;
   a.pi_hi = ctx->t.pi_hi;
   a.pi_lo = ctx->t.pi_lo;
   a.m_hi = ctx->t.m_hi;

@@ -38,6 +38,7 @@ struct QuantArgs {
   uint32_t* planes;
   uint32_t* norms;
   int64_t dst_stride_head, dst_token0;
+  const int64_t* slots;   // per-token destination, or null (dst_token0 + t)
   const __half* pi_hi;
   const __half* pi_lo;
   const __half* m_hi;
@@ -51,6 +52,17 @@ struct QuantArgs {
 __device__ inline float lane_sum(float v, int width) {
   for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// record of (head h, token t), or -1 for a token whose slot lies outside
+// [0, dst_stride_head)
+__device__ inline int64_t dst_record(const QuantArgs& a, int64_t h, int64_t t) {
+  int64_t s = t;
+  if (a.slots) {
+    s = a.slots[t];
+    if (s < 0 || s >= a.dst_stride_head) return -1;
+  }
+  return h * a.dst_stride_head + a.dst_token0 + s;
 }
 
 __device__ inline v8h lds_v8h(const _Float16* p) { return *(const v8h*)p; }
@@ -379,8 +391,8 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
 #pragma unroll
             for (int p = 0; p < NB; ++p)
               if (g == p) val = codew[wi][cb][p];
-            const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + v;
-            a.planes[(rec * W + w) * NB + g] = val;
+            const int64_t rec = dst_record(a, h, t0 + v);
+            if (rec >= 0) a.planes[(rec * W + w) * NB + g] = val;
           }
         }
       }
@@ -450,8 +462,8 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
 #pragma unroll
             for (int p = 0; p < NB - 1; ++p)
               if (g == p) val = codew[wi][cb][p];
-            const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + v;
-            a.planes[(rec * W + w) * NB + g] = val;
+            const int64_t rec = dst_record(a, h, t0 + v);
+            if (rec >= 0) a.planes[(rec * W + w) * NB + g] = val;
           }
         }
       }
@@ -462,8 +474,8 @@ __global__ void __launch_bounds__(RES ? 256 : 512) quantize_kernel(QuantArgs a) 
         for (int ww = 0; ww < NW; ++ww) s += gpart[ww * T + tid];
       const float gam = sqrtf(s);
       const uint32_t gb = (uint32_t)__half_as_ushort(__float2half_rn(gam));
-      const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + tid;
-      a.norms[rec] = nu16[tid] | (gb << 16);
+      const int64_t rec = dst_record(a, h, t0 + tid);
+      if (rec >= 0) a.norms[rec] = nu16[tid] | (gb << 16);
     }
     __syncthreads();   // LDS is reused by the next tile
   }
@@ -497,11 +509,11 @@ hipError_t launch_nb(const QuantArgs& a, size_t shm, dim3 grid, dim3 block, hipS
 hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, int64_t n_tokens,
                            int32_t n_heads, int64_t x_stride_token, int64_t x_stride_head,
                            uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
-                           int64_t dst_token0, hipStream_t stream) {
+                           int64_t dst_token0, const int64_t* slots, hipStream_t stream) {
   // the d = 128 kernel computes row offsets within a tile in 32 bits
   if (ctx->d == 128 && x_stride_token < ((int64_t)1 << 25))
     return launch_quantize128(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
-                              planes, norms, dst_stride_head, dst_token0, stream);
+                              planes, norms, dst_stride_head, dst_token0, slots, stream);
   QuantArgs a{};
   a.x = x;
   a.x_stride_token = x_stride_token;
@@ -512,6 +524,7 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
   a.norms = (uint32_t*)norms;
   a.dst_stride_head = dst_stride_head;
   a.dst_token0 = dst_token0;
+  a.slots = slots;
   a.pi_hi = ctx->t.pi_hi;
   a.pi_lo = ctx->t.pi_lo;
   a.m_hi = ctx->t.m_hi;

@@ -30,10 +30,11 @@ hipError_t launch128(const Q128Args& a, int n_cu, hipStream_t st) {
 hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
-                              int64_t dst_stride_head, int64_t dst_token0, hipStream_t stream) {
+                              int64_t dst_stride_head, int64_t dst_token0,
+                              const int64_t* slots, hipStream_t stream) {
   Q128Args a;
   const hipError_t ea = q128_args(ctx, x, n_tokens, x_stride_token, x_stride_head, planes, norms,
-                                  dst_stride_head, dst_token0, a);
+                                  dst_stride_head, dst_token0, slots, a);
   if (ea != hipSuccess) return ea;
   const bool bf = x_dtype == TQ_BF16;
   // launch over groups of heads with fewer than kMaxRows rows

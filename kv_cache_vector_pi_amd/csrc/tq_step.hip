@@ -60,7 +60,8 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
                                       int64_t x_stride_token, int64_t x_stride_head,
                                       uint32_t* k_planes, uint16_t* k_norms, uint32_t* v_planes,
                                       uint16_t* v_norms, int64_t dst_stride_head,
-                                      int64_t dst_token0, const float* q, int32_t batch,
+                                      int64_t dst_token0, const int64_t* slots,
+                                      const float* q, int32_t batch,
                                       int32_t n_q_heads, int64_t q_stride_batch,
                                       int32_t n_kv_heads, void* workspace, hipStream_t stream) {
   const bool quant = n_tokens > 0 && n_heads > 0;
@@ -73,11 +74,11 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
     hipError_t e = hipSuccess;
     if (quant) {
       e = launch_quantize(ctx, k_new, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
-                          k_planes, k_norms, dst_stride_head, dst_token0, stream);
+                          k_planes, k_norms, dst_stride_head, dst_token0, slots, stream);
       if (e == hipSuccess)
         e = launch_quantize(ctx, v_new, x_dtype, n_tokens, n_heads, x_stride_token,
                             x_stride_head, v_planes, v_norms, dst_stride_head, dst_token0,
-                            stream);
+                            slots, stream);
     }
     if (e == hipSuccess && prep)
       e = launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
@@ -89,11 +90,11 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
   if (quant) {
     Q128Args base;
     hipError_t e = q128_args(ctx, k_new, n_tokens, x_stride_token, x_stride_head, k_planes,
-                             k_norms, dst_stride_head, dst_token0, base);
+                             k_norms, dst_stride_head, dst_token0, slots, base);
     if (e != hipSuccess) return e;
     a.k = q128_group(base, 0, n_heads, bf);
     e = q128_args(ctx, v_new, n_tokens, x_stride_token, x_stride_head, v_planes, v_norms,
-                  dst_stride_head, dst_token0, base);
+                  dst_stride_head, dst_token0, slots, base);
     if (e != hipSuccess) return e;
     a.v = q128_group(base, 0, n_heads, bf);
     // a persistent loop over tiles: at most one workgroup per CU per job

@@ -152,7 +152,9 @@ def test_hot_path_rejects_null_context(tq):
                             1.0, None, 0, None, 0, None) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_attn_decode_workspace_bytes(None, 1, 32, 8, 100) == 0
     assert L.tq_decode_step_prepare(None, None, None, 1, 1, 256, 128, 128, None, None, None, None,
-                                    4, 0, None, 32, 32, 4096, 8, None, 0, None) == \
+                                    4, 0, None, None, 32, 32, 4096, 8, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_quantize_kv_slots(None, None, 0, 1, 1, 128, 0, None, None, None, 1, None) == \
         tq.TQ_ERR_INVALID_ARG
     assert L.tq_attn_logits_workspace_bytes(None, 1, 32, 8) == 0
     assert L.tq_search_workspace_bytes(None, 1, 1, 10) == 0
