@@ -285,3 +285,62 @@ def topk(scores, k):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+# --- fractional bit widths: two instances over a channel split ------------
+# The pages quote quality at 2.5 and 3.5 bits per channel (zingnex.cn digest,
+# section on theoretical guarantees and experiments; turboquant.net, the KV
+# cache compression benchmark table; admirer.cn article, LongBench paragraph)
+# without saying how a fractional width is formed.  Reading taken here: the
+# channels are split in two contiguous groups, the first d_hi channels at
+# b_hi bits and the other d_lo at b_lo, each group quantized by its own
+# instance (own rotation, projection and codebook of its own dimension), so
+# a record pair costs d_hi b_hi + d_lo b_lo code bits.  The estimate of
+# <q, k> is the sum of the two instances' estimates over their channels (each
+# unbiased, so the sum is), and a dequantized vector is the concatenation.
+# An instance is a tuple (d, b, pi32, s32, cen32); s32 None marks an
+# MSE-only instance (b code planes, cen32 of 2^b centroids).
+def _inst_quantize(inst, x, margins):
+    d, b, pi32, s32, cen32 = inst
+    if s32 is None:
+        return quantize_mse(d, b, pi32, cen32, x, margins=margins)
+    return quantize(d, b, pi32, s32, cen32, x, margins=margins)
+
+
+def split_quantize(hi, lo, x, margins=False):
+    """Rows of x (float64 [n, d_hi + d_lo]) -> (records of the first d_hi
+    channels under `hi`, records of the remaining d_lo channels under `lo`),
+    each as returned by quantize / quantize_mse."""
+    dh, dl = hi[0], lo[0]
+    x = _c(x, np.float64).reshape(-1, dh + dl)
+    return _inst_quantize(hi, x[:, :dh], margins), _inst_quantize(lo, x[:, dh:], margins)
+
+
+def _inst_estimate(inst, q, planes, norms, scale):
+    d, b, pi32, s32, cen32 = inst
+    if s32 is None:
+        return estimate_mse(d, b, pi32, cen32, q, planes, norms, scale=scale)
+    return estimate(d, b, pi32, s32, cen32, q, planes, norms, scale=scale)
+
+
+def split_estimate(hi, lo, q, rec_hi, rec_lo, scale=1.0):
+    """out[a, i] = est_hi(q_a[:d_hi], record i of hi) + est_lo(q_a[d_hi:],
+    record i of lo), each the instance's own estimate, times scale.
+    rec_hi / rec_lo: (planes, norms)."""
+    dh, dl = hi[0], lo[0]
+    q = _c(q, np.float64).reshape(-1, dh + dl)
+    return (_inst_estimate(hi, q[:, :dh], rec_hi[0], rec_hi[1], scale) +
+            _inst_estimate(lo, q[:, dh:], rec_lo[0], rec_lo[1], scale))
+
+
+def _inst_dequantize(inst, planes, norms):
+    d, b, pi32, s32, cen32 = inst
+    if s32 is None:
+        return dequantize_mse(d, b, pi32, cen32, planes, norms)
+    return dequantize(d, b, pi32, s32, cen32, planes, norms)
+
+
+def split_dequantize(hi, lo, rec_hi, rec_lo):
+    """[n, d_hi + d_lo]: the hi instance's reconstruction of the first d_hi
+    channels followed by the lo instance's of the rest."""
+    return np.hstack([_inst_dequantize(hi, *rec_hi), _inst_dequantize(lo, *rec_lo)])
