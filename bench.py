@@ -57,7 +57,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "long", "batched", "search", "attn_out", "decode_fused"])
+                    choices=["decode", "long", "batched", "search", "attn_out", "decode_fused",
+                             "split"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--mse", action="store_true",
@@ -122,7 +123,8 @@ def main():
         sys.exit(2)
     if args.workload != "decode":
         out = {"long": run_long, "batched": run_batched, "search": run_search,
-               "attn_out": run_attn_out, "decode_fused": run_decode_fused}[args.workload](args)
+               "attn_out": run_attn_out, "decode_fused": run_decode_fused,
+               "split": run_split}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     dev = "cuda"
@@ -284,7 +286,7 @@ def main():
                                "layer caches per step",
                    "layers_per_step": L, "cached_tokens": N_TOK, "head_dim": D, "bits": B,
                    "q_heads": N_Q, "kv_heads": N_KV, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,false,4>",
+        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,false,4,0>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic(PROFILE_LOGITS, LOGIT_SOURCES),
@@ -344,6 +346,100 @@ def _line(args, metric, value, unit, workload, extra):
     if getattr(args, "mse", False):
         out["config"] = dict(out["config"], records="MSE-only: b code bits, no QJL stage")
     return out
+
+
+def run_split(args):
+    """Fractional bit widths (two instances over a channel split: channels
+    0..63 at b_hi bits, 64..127 at b_lo) on the Llama-shaped decode layer of
+    the default workload: quantize the 32 layer caches' keys, then the logits
+    of 32 layers x 32 heads against them, at 2.5 (3 + 2) and 3.5 (4 + 3) bits."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    L, DH = args.layers, D // 2
+    n_rec = N_KV * L * N_TOK
+    Kx = torch.empty((N_KV, L * N_TOK, D), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        Kx[:, l * N_TOK:(l + 1) * N_TOK] = workloads.llama(dev, seed=l, n_tok=N_TOK)["K"]
+    torch.cuda.synchronize()
+    q_all = torch.stack([workloads.normal((N_Q, D), l, workloads.STREAM_Q, dev)
+                         for l in range(L)])
+    seq_start = torch.arange(L, dtype=torch.int64, device=dev) * N_TOK
+    seq_len = torch.full((L,), N_TOK, dtype=torch.int32, device=dev)
+    logits = torch.empty((N_Q, L * N_TOK), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    reps = max(10, min(args.steps, 50))
+
+    def inst(b, seed):
+        pi, s = tq.tq_make_rotation(DH, seed)
+        cent, _, _ = tq.tq_lloyd_max(DH, b - 1)
+        return tq.TqContext(DH, b, pi, s, cent)
+
+    def events(fn, n):
+        ts = []
+        for _ in range(n):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sum(ts) / len(ts), sorted(ts)[len(ts) // 2]
+
+    res = {}
+    for bh, bl in ((3, 2), (4, 3)):
+        hi, lo = inst(bh, 1), inst(bl, 2)
+        hp = torch.empty((n_rec, tq.tq_record_words(DH, bh)), dtype=torch.int32, device=dev)
+        lp = torch.empty((n_rec, tq.tq_record_words(DH, bl)), dtype=torch.int32, device=dev)
+        hn = torch.empty((n_rec, 2), dtype=torch.int16, device=dev)
+        ln = torch.empty_like(hn)
+        ws = tq.workspace(tq.tq_split_attn_logits_workspace_bytes(hi, lo, L, N_Q, N_KV), dev)
+
+        def fill():
+            tq.tq_split_quantize_kv(hi, lo, Kx, hp, hn, lp, ln)
+
+        def stream_only():
+            tq.tq_split_attn_logits_prepared(hi, lo, ws, L, N_Q, hp, hn, lp, ln, N_KV, L * N_TOK,
+                                             seq_start, seq_len, N_TOK, scale, logits, L * N_TOK)
+
+        def one_call():
+            tq.tq_split_attn_logits(hi, lo, q_all, L, N_Q, N_Q * D, hp, hn, lp, ln, N_KV,
+                                    L * N_TOK, seq_start, seq_len, N_TOK, scale, logits,
+                                    L * N_TOK, ws)
+
+        fill()
+        tq.tq_split_attn_prepare(hi, lo, q_all, L, N_Q, N_Q * D, N_KV, ws)
+        for _ in range(args.warmup):
+            stream_only()
+            one_call()
+        torch.cuda.synchronize()
+        f_ms, _ = events(fill, 3)
+        s_ms, s_med = events(stream_only, reps)
+        c_ms, _ = events(one_call, reps)
+        rec = (DH * bh // 8 + 4) + (DH * bl // 8 + 4)
+        alg = n_rec * rec + N_Q * L * N_TOK * 4
+        bits = (DH * bh + DH * bl) / D
+        res[f"{bits:g}"] = {
+            "b_hi": bh, "b_lo": bl, "record_pair_bytes": rec,
+            "logits_per_s": N_Q * L * N_TOK / (c_ms * 1e-3), "call_ms_mean": c_ms,
+            "roofline": {"bound": "hbm", "kernel": f"attn_logits_res_kernel<{bh},false,4,{bl}>",
+                         "achieved": alg / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": alg / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "alg_bytes_per_launch": alg,
+                         "kernel_ms_mean": s_ms, "kernel_ms_median": s_med},
+            "quantize_vec_per_s": n_rec / (f_ms * 1e-3), "quantize_ms": f_ms}
+        hi.close()
+        lo.close()
+        del hp, lp, hn, ln, ws
+    return _line(args, "packed-key attention logits/sec at fractional bit widths (channel split)",
+                 res["2.5"]["logits_per_s"], "logits/s",
+                 {"workload": f"llama-3.1-8b decode layer x {L} layer caches (32 q / 8 kv heads, "
+                              f"32768 tokens, d=128): channels 0-63 at b_hi, 64-127 at b_lo; "
+                              f"value = 2.5-bit logits incl. query prep"},
+                 {"dtype": "int8-mfma/fp32", "widths": res})
 
 
 def run_long(args):

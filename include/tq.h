@@ -371,6 +371,96 @@ TQ_API tq_status tq_search_topk(const tq_ctx* ctx, const float* queries, int64_t
                                 int32_t k, int64_t* out_idx, float* out_score,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- fractional bit widths: two instances over a channel split ------------
+ *
+ * The pages quote quality at 2.5 and 3.5 bits per channel (zingnex.cn digest,
+ * section on theoretical guarantees and experiments; turboquant.net, KV cache
+ * compression benchmark table; admirer.cn article, LongBench paragraph) but do
+ * not say how a fractional width is formed.  Reading implemented here: the d
+ * channels of a key/value/query are split in two contiguous groups, channels
+ * [0, d_hi) quantized by instance `hi` (its own d = d_hi, b = b_hi, rotation,
+ * projection and codebook) and channels [d_hi, d_hi + d_lo) by instance `lo`;
+ * a record pair costs d_hi b_hi + d_lo b_lo code bits (64 channels at 3 bits
+ * + 64 at 2 = 2.5 bits per channel at d = 128; 4 + 3 = 3.5).  Which channels
+ * get the wider code is the caller's choice: order them first (a fixed
+ * channel permutation can be folded into the projection weights, since inner
+ * products are invariant under a common permutation).
+ *   estimate(q, k) = est_hi(q[0:d_hi], k_hi) + est_lo(q[d_hi:], k_lo)
+ * (each instance's own estimator, so the sum is unbiased when both are
+ * two-stage); dequantized vectors are the concatenation of the two parts.
+ * Each group's records follow the layout and indexing of its own instance
+ * (two record arrays, same (head, token) indexing).  hi and lo must be both
+ * two-stage or both MSE-only and on one device; any of b_hi >= b_lo or
+ * b_hi < b_lo is allowed.  Errors as the single-instance calls, plus
+ * TQ_ERR_INVALID_ARG for a NULL or mismatched instance. */
+
+/* tq_quantize_kv of x[..][0:d_hi] into (hi_planes, hi_norms) and of
+ * x[..][d_hi:d_hi+d_lo] into (lo_planes, lo_norms); x rows hold d_hi + d_lo
+ * elements (x_stride_token >= d_hi + d_lo; d_hi a multiple of 8 keeps the
+ * second group 16-byte aligned). */
+TQ_API tq_status tq_split_quantize_kv(const tq_ctx* hi, const tq_ctx* lo, const void* x,
+                                      int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
+                                      int64_t x_stride_token, int64_t x_stride_head,
+                                      uint32_t* hi_planes, uint16_t* hi_norms,
+                                      uint32_t* lo_planes, uint16_t* lo_norms,
+                                      int64_t dst_stride_head, int64_t dst_token0, void* stream);
+/* out[i][0:d_hi] and out[i][d_hi:d_hi+d_lo] = the two groups' reconstructions
+ * of record pair i (out_ld >= d_hi + d_lo). */
+TQ_API tq_status tq_split_dequantize(const tq_ctx* hi, const tq_ctx* lo,
+                                     const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                     const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                     int64_t n, float* out, int64_t out_ld, void* stream);
+/* Workspace for tq_split_attn_logits in bytes (0 for invalid sizes). */
+TQ_API size_t tq_split_attn_logits_workspace_bytes(const tq_ctx* hi, const tq_ctx* lo,
+                                                   int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads);
+/* tq_attn_logits over split records: logit = scale * (est_hi + est_lo), with
+ * q [batch][n_q_heads][d_hi + d_lo] (batch stride q_stride_batch), both record
+ * arrays indexed as keys_stride_head / seq_start / seq_len say.  One
+ * preparation launch and one key-stream launch that reads both record arrays.
+ * Errors: as tq_attn_logits; TQ_ERR_UNSUPPORTED unless d_hi, d_lo <= 128 and
+ * n_q_heads / n_kv_heads <= 4. */
+TQ_API tq_status tq_split_attn_logits(const tq_ctx* hi, const tq_ctx* lo, const float* q,
+                                      int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                      const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                      const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                      int32_t n_kv_heads, int64_t keys_stride_head,
+                                      const int64_t* seq_start, const int32_t* seq_len,
+                                      int32_t max_seq_len, float scale, float* logits,
+                                      int64_t logits_stride_head, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+/* The two halves of tq_split_attn_logits (as tq_attn_prepare and
+ * tq_attn_logits_prepared): prepare the queries against both instances into
+ * `workspace`, then stream both record arrays against it (same hi, lo,
+ * batch, n_q_heads and n_kv_heads).  Arguments and errors as for
+ * tq_split_attn_logits. */
+TQ_API tq_status tq_split_attn_prepare(const tq_ctx* hi, const tq_ctx* lo, const float* q,
+                                       int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                       int32_t n_kv_heads, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+TQ_API tq_status tq_split_attn_logits_prepared(
+    const tq_ctx* hi, const tq_ctx* lo, const void* workspace, size_t workspace_bytes,
+    int32_t batch, int32_t n_q_heads, const uint32_t* hi_planes, const uint16_t* hi_norms,
+    const uint32_t* lo_planes, const uint16_t* lo_norms, int32_t n_kv_heads,
+    int64_t keys_stride_head, const int64_t* seq_start, const int32_t* seq_len,
+    int32_t max_seq_len, float scale, float* logits, int64_t logits_stride_head, void* stream);
+/* Workspace for tq_split_attn_output in bytes (0 for invalid sizes). */
+TQ_API size_t tq_split_attn_output_workspace_bytes(const tq_ctx* hi, const tq_ctx* lo,
+                                                   int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads, int32_t max_seq_len);
+/* tq_attn_output over split value records: out[bi][h][0:d_hi] from the hi
+ * records and out[bi][h][d_hi:] from the lo records, weights p as for
+ * tq_attn_output (out row of a head: d_hi + d_lo floats; out_stride_batch >=
+ * n_q_heads (d_hi + d_lo) when batch > 1).  Errors: as tq_attn_output. */
+TQ_API tq_status tq_split_attn_output(const tq_ctx* hi, const tq_ctx* lo, const float* p,
+                                      int64_t p_stride_head, int32_t batch, int32_t n_q_heads,
+                                      const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                      const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                      int32_t n_kv_heads, int64_t values_stride_head,
+                                      const int64_t* seq_start, const int32_t* seq_len,
+                                      int32_t max_seq_len, float* out, int64_t out_stride_batch,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,9 @@ EXPORTS = [
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
     "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
     "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare", "tq_quantize_kv_slots",
+    "tq_split_quantize_kv", "tq_split_dequantize", "tq_split_attn_logits_workspace_bytes",
+    "tq_split_attn_logits", "tq_split_attn_output_workspace_bytes", "tq_split_attn_output",
+    "tq_split_attn_prepare", "tq_split_attn_logits_prepared",
 ]
 
 
@@ -75,6 +78,18 @@ _sig("tq_ctx_bits", _i32, [_P])
 _sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
 _sig("tq_quantize_kv_slots", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _i64, _P])
 _sig("tq_dequantize", _i32, [_P, _P, _P, _i64, _P, _i64, _P])
+_sig("tq_split_quantize_kv", _i32, [_P, _P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _P,
+                                    _i64, _i64, _P])
+_sig("tq_split_dequantize", _i32, [_P, _P, _P, _P, _P, _P, _i64, _P, _i64, _P])
+_sig("tq_split_attn_logits_workspace_bytes", _sz, [_P, _P, _i32, _i32, _i32])
+_sig("tq_split_attn_logits", _i32, [_P, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _i32, _i64, _P,
+                                    _P, _i32, _f32, _P, _i64, _P, _sz, _P])
+_sig("tq_split_attn_prepare", _i32, [_P, _P, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
+_sig("tq_split_attn_logits_prepared", _i32, [_P, _P, _P, _sz, _i32, _i32, _P, _P, _P, _P, _i32,
+                                             _i64, _P, _P, _i32, _f32, _P, _i64, _P])
+_sig("tq_split_attn_output_workspace_bytes", _sz, [_P, _P, _i32, _i32, _i32, _i32])
+_sig("tq_split_attn_output", _i32, [_P, _P, _P, _i64, _i32, _i32, _P, _P, _P, _P, _i32, _i64,
+                                    _P, _P, _i32, _P, _i64, _P, _sz, _P])
 _sig("tq_attn_logits_workspace_bytes", _sz, [_P, _i32, _i32, _i32])
 _sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P, _i32, _f32,
                               _P, _i64, _P, _sz, _P])
@@ -383,3 +398,86 @@ def workspace(nbytes, device="cuda"):
     """A 256-byte aligned uint8 device buffer of at least nbytes."""
     import torch
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ---- fractional bit widths: two instances over a channel split (see tq.h) ----
+def tq_split_quantize_kv(hi, lo, x, hi_planes, hi_norms, lo_planes, lo_norms, n_tokens=None,
+                         n_heads=None, x_stride_token=None, x_stride_head=None,
+                         dst_stride_head=None, dst_token0=0, stream=None):
+    """Quantize channels [0, d_hi) of x ([n_heads, n_tokens, d_hi + d_lo] or
+    [n, d_hi + d_lo]) under `hi` and the rest under `lo`."""
+    dt, n_tokens, n_heads, x_stride_token, x_stride_head = _quant_input(
+        x, n_tokens, n_heads, x_stride_token, x_stride_head)
+    if dst_stride_head is None:
+        dst_stride_head = n_tokens
+    st = _lib.tq_split_quantize_kv(hi.handle, lo.handle, _ptr(x), dt, n_tokens, n_heads,
+                                   x_stride_token, x_stride_head, _ptr(hi_planes),
+                                   _ptr(hi_norms), _ptr(lo_planes), _ptr(lo_norms),
+                                   dst_stride_head, dst_token0, _stream(stream))
+    _check(st, "tq_split_quantize_kv")
+
+
+def tq_split_dequantize(hi, lo, hi_planes, hi_norms, lo_planes, lo_norms, n, out, out_ld=None,
+                        stream=None):
+    if out_ld is None:
+        out_ld = out.stride(0)
+    _check(_lib.tq_split_dequantize(hi.handle, lo.handle, _ptr(hi_planes), _ptr(hi_norms),
+                                    _ptr(lo_planes), _ptr(lo_norms), n, _ptr(out), out_ld,
+                                    _stream(stream)), "tq_split_dequantize")
+
+
+def tq_split_attn_logits_workspace_bytes(hi, lo, batch, n_q_heads, n_kv_heads):
+    return _lib.tq_split_attn_logits_workspace_bytes(hi.handle, lo.handle, batch, n_q_heads,
+                                                     n_kv_heads)
+
+
+def tq_split_attn_logits(hi, lo, q, batch, n_q_heads, q_stride_batch, hi_planes, hi_norms,
+                         lo_planes, lo_norms, n_kv_heads, keys_stride_head, seq_start, seq_len,
+                         max_seq_len, scale, logits, logits_stride_head, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_split_attn_logits(hi.handle, lo.handle, _ptr(q), batch, n_q_heads,
+                                   q_stride_batch, _ptr(hi_planes), _ptr(hi_norms),
+                                   _ptr(lo_planes), _ptr(lo_norms), n_kv_heads, keys_stride_head,
+                                   _ptr(seq_start), _ptr(seq_len), max_seq_len, float(scale),
+                                   _ptr(logits), logits_stride_head, _ptr(workspace), ws_bytes,
+                                   _stream(stream))
+    _check(st, "tq_split_attn_logits")
+
+
+def tq_split_attn_prepare(hi, lo, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
+                          stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.tq_split_attn_prepare(hi.handle, lo.handle, _ptr(q), batch, n_q_heads,
+                                      q_stride_batch, n_kv_heads, _ptr(workspace), ws_bytes,
+                                      _stream(stream)), "tq_split_attn_prepare")
+
+
+def tq_split_attn_logits_prepared(hi, lo, workspace, batch, n_q_heads, hi_planes, hi_norms,
+                                  lo_planes, lo_norms, n_kv_heads, keys_stride_head, seq_start,
+                                  seq_len, max_seq_len, scale, logits, logits_stride_head,
+                                  stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_split_attn_logits_prepared(hi.handle, lo.handle, _ptr(workspace), ws_bytes,
+                                            batch, n_q_heads, _ptr(hi_planes), _ptr(hi_norms),
+                                            _ptr(lo_planes), _ptr(lo_norms), n_kv_heads,
+                                            keys_stride_head, _ptr(seq_start), _ptr(seq_len),
+                                            max_seq_len, float(scale), _ptr(logits),
+                                            logits_stride_head, _stream(stream))
+    _check(st, "tq_split_attn_logits_prepared")
+
+
+def tq_split_attn_output_workspace_bytes(hi, lo, batch, n_q_heads, n_kv_heads, max_seq_len):
+    return _lib.tq_split_attn_output_workspace_bytes(hi.handle, lo.handle, batch, n_q_heads,
+                                                     n_kv_heads, max_seq_len)
+
+
+def tq_split_attn_output(hi, lo, p, p_stride_head, batch, n_q_heads, hi_planes, hi_norms,
+                         lo_planes, lo_norms, n_kv_heads, values_stride_head, seq_start, seq_len,
+                         max_seq_len, out, out_stride_batch, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_split_attn_output(hi.handle, lo.handle, _ptr(p), p_stride_head, batch,
+                                   n_q_heads, _ptr(hi_planes), _ptr(hi_norms), _ptr(lo_planes),
+                                   _ptr(lo_norms), n_kv_heads, values_stride_head,
+                                   _ptr(seq_start), _ptr(seq_len), max_seq_len, _ptr(out),
+                                   out_stride_batch, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "tq_split_attn_output")

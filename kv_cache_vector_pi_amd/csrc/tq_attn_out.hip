@@ -102,8 +102,8 @@ struct VFinArgs {
   const float* part;
   const float* pi32;        // [d][d] row-major
   const float* s32;
-  float* out;               // out[bi * out_stride_batch + hq * d + i]
-  int64_t out_stride_batch;
+  float* out;               // out[bi * out_stride_batch + hq * out_stride_head + i]
+  int64_t out_stride_batch, out_stride_head;
   int d, Dp, G, n_kv, n_rb, n_chunk;
   int qjl;                  // 0: MSE-only records, no sketch part
   float alpha;
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
   const float* src = a.part + (((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk * 8 * (int64_t)a.Dp;
   dev::sum_chunk_partials(src, a.n_chunk, hh, 4 + hh, a.Dp, nullptr, 1.f, red, arot, ask);
   dev::apply_transforms(a.pi32, a.s32, a.d, a.qjl != 0, a.alpha, arot, ask, red,
-                        a.out + (int64_t)bi * a.out_stride_batch + (int64_t)hq * a.d);
+                        a.out + (int64_t)bi * a.out_stride_batch + (int64_t)hq * a.out_stride_head);
 }
 
 }  // namespace
@@ -137,7 +137,8 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
                               const uint16_t* norms, int32_t n_kv_heads,
                               int64_t values_stride_head, const int64_t* seq_start,
                               const int32_t* seq_len, int32_t max_seq_len, float* out,
-                              int64_t out_stride_batch, void* workspace, hipStream_t stream) {
+                              int64_t out_stride_batch, int64_t out_stride_head, void* workspace,
+                              hipStream_t stream) {
   const int G = n_q_heads / n_kv_heads;
   VAccArgs a{};
   a.p = p;
@@ -180,6 +181,7 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
   f.s32 = ctx->t.s32;
   f.out = out;
   f.out_stride_batch = out_stride_batch;
+  f.out_stride_head = out_stride_head;
   f.d = ctx->d;
   f.Dp = ctx->Dp;
   f.G = G;

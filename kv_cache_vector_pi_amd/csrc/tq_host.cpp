@@ -3,6 +3,7 @@
 // validation in front of every kernel launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -735,7 +736,7 @@ TQ_API tq_status tq_attn_output(const tq_ctx* ctx, const float* p, int64_t p_str
                 need);
   hipError_t e = tq::launch_attn_output(ctx, p, p_stride_head, batch, n_q_heads, planes, norms,
                                         n_kv_heads, values_stride_head, seq_start, seq_len,
-                                        max_seq_len, out, out_stride_batch, workspace,
+                                        max_seq_len, out, out_stride_batch, ctx->d, workspace,
                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_attn_output: launch");
   return ok();
@@ -807,6 +808,263 @@ TQ_API tq_status tq_search_topk(const tq_ctx* ctx, const float* queries, int64_t
   hipError_t e = tq::launch_search_topk(ctx, queries, n_queries, planes, norms, n_db, k,
                                         out_idx, out_score, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_search_topk: launch");
+  return ok();
+}
+
+// ---- fractional bit widths: two instances over a channel split ------------
+namespace {
+
+// Both instances present, of one kind (two-stage or MSE-only) and on one device.
+tq_status check_split(const char* fn, const tq_ctx* hi, const tq_ctx* lo) {
+  if (!hi || !lo) return fail(TQ_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+  if (hi->mse != lo->mse)
+    return fail(TQ_ERR_INVALID_ARG, "%s: both instances must be two-stage or both MSE-only", fn);
+  if (hi->device != lo->device)
+    return fail(TQ_ERR_INVALID_ARG, "%s: instances on different devices", fn);
+  return TQ_OK;
+}
+
+}  // namespace
+
+TQ_API tq_status tq_split_quantize_kv(const tq_ctx* hi, const tq_ctx* lo, const void* x,
+                                      int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
+                                      int64_t x_stride_token, int64_t x_stride_head,
+                                      uint32_t* hi_planes, uint16_t* hi_norms,
+                                      uint32_t* lo_planes, uint16_t* lo_norms,
+                                      int64_t dst_stride_head, int64_t dst_token0, void* stream) {
+  const char* fn = "tq_split_quantize_kv";
+  tq_status st = check_split(fn, hi, lo);
+  if (st != TQ_OK) return st;
+  bool empty_hi, empty_lo;
+  if (n_tokens > 0 && n_heads > 0 && x_stride_token < (int64_t)hi->d + lo->d)
+    return fail(TQ_ERR_INVALID_ARG, "%s: x_stride_token < d_hi + d_lo", fn);
+  const size_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  const void* x_lo = x ? (const void*)((const char*)x + (size_t)hi->d * esz) : nullptr;
+  st = check_quantize(fn, hi, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
+                      hi_planes, hi_norms, dst_stride_head, dst_token0, nullptr, &empty_hi);
+  if (st == TQ_OK)
+    st = check_quantize(fn, lo, x_lo, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
+                        lo_planes, lo_norms, dst_stride_head, dst_token0, nullptr, &empty_lo);
+  if (st != TQ_OK) return st;
+  if (empty_hi) return ok();
+  hipError_t e = tq::launch_quantize(hi, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                     x_stride_head, hi_planes, hi_norms, dst_stride_head,
+                                     dst_token0, nullptr, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_quantize(lo, x_lo, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
+                            lo_planes, lo_norms, dst_stride_head, dst_token0, nullptr,
+                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_quantize_kv: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_split_dequantize(const tq_ctx* hi, const tq_ctx* lo,
+                                     const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                     const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                     int64_t n, float* out, int64_t out_ld, void* stream) {
+  const char* fn = "tq_split_dequantize";
+  const tq_status st = check_split(fn, hi, lo);
+  if (st != TQ_OK) return st;
+  if (n < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n=%lld", fn, (long long)n);
+  if (n == 0) return ok();
+  if (!hi_planes || !hi_norms || !lo_planes || !lo_norms || !out)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (out_ld < (int64_t)hi->d + lo->d)
+    return fail(TQ_ERR_INVALID_ARG, "%s: out_ld < d_hi + d_lo", fn);
+  if (!aligned(hi_planes, 16) || !aligned(lo_planes, 16) || !aligned(hi_norms, 4) ||
+      !aligned(lo_norms, 4) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  hipError_t e = tq::launch_dequantize(hi, hi_planes, hi_norms, n, out, out_ld,
+                                       (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_dequantize(lo, lo_planes, lo_norms, n, out + hi->d, out_ld,
+                              (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_dequantize: launch");
+  return ok();
+}
+
+TQ_API size_t tq_split_attn_logits_workspace_bytes(const tq_ctx* hi, const tq_ctx* lo,
+                                                   int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads) {
+  if (!hi || !lo || batch < 0 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads)
+    return 0;
+  return tq::split_attn_workspace_bytes(hi, lo, batch, n_q_heads, n_kv_heads);
+}
+
+namespace {
+
+// Checks shared by the split logit calls (q == nullptr skips the query checks,
+// records == false the record and sequence checks); *empty for no work.
+tq_status check_split_logits(const char* fn, const tq_ctx* hi, const tq_ctx* lo, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t max_seq_len,
+                             const float* q, int64_t q_stride_batch, bool records,
+                             const uint32_t* hi_planes, const uint16_t* hi_norms,
+                             const uint32_t* lo_planes, const uint16_t* lo_norms,
+                             int64_t keys_stride_head, const int64_t* seq_start,
+                             const int32_t* seq_len, float scale, float* logits,
+                             int64_t logits_stride_head, const void* workspace,
+                             size_t workspace_bytes, bool* empty) {
+  *empty = false;
+  tq_status st = check_split(fn, hi, lo);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: batch=%d n_q=%d n_kv=%d max_seq_len=%d", fn, batch,
+                n_q_heads, n_kv_heads, max_seq_len);
+  if (!tq::split_logits_supported(hi, lo, n_q_heads, n_kv_heads))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "%s: needs d <= 128 per instance and at most 4 query heads per kv head", fn);
+  if (batch == 0 || (records && max_seq_len == 0)) {
+    *empty = true;
+    return TQ_OK;
+  }
+  if (!workspace) return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (q) {
+    if (q_stride_batch < (int64_t)n_q_heads * (hi->d + lo->d) && batch > 1)
+      return fail(TQ_ERR_INVALID_ARG, "%s: q_stride_batch too small", fn);
+    if (!aligned(q, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  }
+  if (records) {
+    if (!hi_planes || !hi_norms || !lo_planes || !lo_norms || !seq_start || !seq_len || !logits)
+      return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (keys_stride_head < 0 || logits_stride_head < 0)
+      return fail(TQ_ERR_INVALID_ARG, "%s: negative stride", fn);
+    if (!aligned(hi_planes, 16) || !aligned(lo_planes, 16) || !aligned(hi_norms, 4) ||
+        !aligned(lo_norms, 4))
+      return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  }
+  if (!aligned(workspace, 16)) return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const size_t need = tq::split_attn_workspace_bytes(hi, lo, batch, n_q_heads, n_kv_heads);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  return TQ_OK;
+}
+
+}  // namespace
+
+TQ_API tq_status tq_split_attn_logits(const tq_ctx* hi, const tq_ctx* lo, const float* q,
+                                      int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                      const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                      const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                      int32_t n_kv_heads, int64_t keys_stride_head,
+                                      const int64_t* seq_start, const int32_t* seq_len,
+                                      int32_t max_seq_len, float scale, float* logits,
+                                      int64_t logits_stride_head, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_split_attn_logits";
+  if (!q && hi && lo && batch > 0 && max_seq_len > 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  bool empty;
+  const tq_status st = check_split_logits(
+      fn, hi, lo, batch, n_q_heads, n_kv_heads, max_seq_len, q, q_stride_batch, true, hi_planes,
+      hi_norms, lo_planes, lo_norms, keys_stride_head, seq_start, seq_len, scale, logits,
+      logits_stride_head, workspace, workspace_bytes, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
+  hipError_t e = tq::launch_split_prepare(hi, lo, q, batch, n_q_heads, q_stride_batch,
+                                          n_kv_heads, workspace, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_split_stream(hi, lo, workspace, batch, n_q_heads, hi_planes, hi_norms,
+                                lo_planes, lo_norms, n_kv_heads, keys_stride_head, seq_start,
+                                seq_len, max_seq_len, scale, logits, logits_stride_head,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_attn_logits: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_split_attn_prepare(const tq_ctx* hi, const tq_ctx* lo, const float* q,
+                                       int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                       int32_t n_kv_heads, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_split_attn_prepare";
+  if (!q && hi && lo && batch > 0) return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  bool empty;
+  const tq_status st = check_split_logits(
+      fn, hi, lo, batch, n_q_heads, n_kv_heads, 0, q, q_stride_batch, false, nullptr, nullptr,
+      nullptr, nullptr, 0, nullptr, nullptr, 1.f, nullptr, 0, workspace, workspace_bytes, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
+  hipError_t e = tq::launch_split_prepare(hi, lo, q, batch, n_q_heads, q_stride_batch,
+                                          n_kv_heads, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_attn_prepare: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_split_attn_logits_prepared(
+    const tq_ctx* hi, const tq_ctx* lo, const void* workspace, size_t workspace_bytes,
+    int32_t batch, int32_t n_q_heads, const uint32_t* hi_planes, const uint16_t* hi_norms,
+    const uint32_t* lo_planes, const uint16_t* lo_norms, int32_t n_kv_heads,
+    int64_t keys_stride_head, const int64_t* seq_start, const int32_t* seq_len,
+    int32_t max_seq_len, float scale, float* logits, int64_t logits_stride_head, void* stream) {
+  const char* fn = "tq_split_attn_logits_prepared";
+  bool empty;
+  const tq_status st = check_split_logits(
+      fn, hi, lo, batch, n_q_heads, n_kv_heads, max_seq_len, nullptr, 0, true, hi_planes,
+      hi_norms, lo_planes, lo_norms, keys_stride_head, seq_start, seq_len, scale, logits,
+      logits_stride_head, workspace, workspace_bytes, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
+  hipError_t e = tq::launch_split_stream(hi, lo, workspace, batch, n_q_heads, hi_planes,
+                                         hi_norms, lo_planes, lo_norms, n_kv_heads,
+                                         keys_stride_head, seq_start, seq_len, max_seq_len,
+                                         scale, logits, logits_stride_head, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_attn_logits_prepared: launch");
+  return ok();
+}
+
+TQ_API size_t tq_split_attn_output_workspace_bytes(const tq_ctx* hi, const tq_ctx* lo,
+                                                   int32_t batch, int32_t n_q_heads,
+                                                   int32_t n_kv_heads, int32_t max_seq_len) {
+  if (!hi || !lo || batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads)
+    return 0;
+  // the two instances run one after the other on the stream and reuse it
+  return std::max(tq::vout_workspace_bytes(hi, batch, n_q_heads, n_kv_heads, max_seq_len),
+                  tq::vout_workspace_bytes(lo, batch, n_q_heads, n_kv_heads, max_seq_len));
+}
+
+TQ_API tq_status tq_split_attn_output(const tq_ctx* hi, const tq_ctx* lo, const float* p,
+                                      int64_t p_stride_head, int32_t batch, int32_t n_q_heads,
+                                      const uint32_t* hi_planes, const uint16_t* hi_norms,
+                                      const uint32_t* lo_planes, const uint16_t* lo_norms,
+                                      int32_t n_kv_heads, int64_t values_stride_head,
+                                      const int64_t* seq_start, const int32_t* seq_len,
+                                      int32_t max_seq_len, float* out, int64_t out_stride_batch,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_split_attn_output";
+  const tq_status st = check_split(fn, hi, lo);
+  if (st != TQ_OK) return st;
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: batch=%d n_q=%d n_kv=%d max_seq_len=%d", fn, batch,
+                n_q_heads, n_kv_heads, max_seq_len);
+  if (batch == 0) return ok();
+  if (!p || !hi_planes || !hi_norms || !lo_planes || !lo_norms || !seq_start || !seq_len ||
+      !out || !workspace)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  const int64_t d = (int64_t)hi->d + lo->d;
+  if (p_stride_head < 0 || values_stride_head < 0 ||
+      (batch > 1 && out_stride_batch < (int64_t)n_q_heads * d))
+    return fail(TQ_ERR_INVALID_ARG, "%s: bad stride", fn);
+  if (!aligned(hi_planes, 16) || !aligned(lo_planes, 16) || !aligned(hi_norms, 4) ||
+      !aligned(lo_norms, 4) || !aligned(workspace, 16) || !aligned(p, 4) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  const size_t need =
+      tq_split_attn_output_workspace_bytes(hi, lo, batch, n_q_heads, n_kv_heads, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_INVALID_ARG, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, need);
+  // channels [0, d_hi) of every head from the first instance, the rest from
+  // the second: head stride d, channel offset d_hi
+  hipError_t e = tq::launch_attn_output(hi, p, p_stride_head, batch, n_q_heads, hi_planes,
+                                        hi_norms, n_kv_heads, values_stride_head, seq_start,
+                                        seq_len, max_seq_len, out, out_stride_batch, d, workspace,
+                                        (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_attn_output(lo, p, p_stride_head, batch, n_q_heads, lo_planes, lo_norms,
+                               n_kv_heads, values_stride_head, seq_start, seq_len, max_seq_len,
+                               out + hi->d, out_stride_batch, d, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_split_attn_output: launch");
   return ok();
 }
 

@@ -100,7 +100,24 @@ hipError_t launch_attn_output(const tq_ctx* ctx, const float* p, int64_t p_strid
                               const uint16_t* norms, int32_t n_kv_heads,
                               int64_t values_stride_head, const int64_t* seq_start,
                               const int32_t* seq_len, int32_t max_seq_len, float* out,
-                              int64_t out_stride_batch, void* workspace, hipStream_t stream);
+                              int64_t out_stride_batch, int64_t out_stride_head, void* workspace,
+                              hipStream_t stream);
+// Channel-split records (two instances c1, c2 over channels [0, d1) and
+// [d1, d1 + d2)): logits as one preparation launch and one stream launch.
+size_t split_attn_workspace_bytes(const tq_ctx* c1, const tq_ctx* c2, int32_t batch,
+                                  int32_t n_q_heads, int32_t n_kv_heads);
+bool split_logits_supported(const tq_ctx* c1, const tq_ctx* c2, int32_t n_q_heads,
+                            int32_t n_kv_heads);
+hipError_t launch_split_prepare(const tq_ctx* c1, const tq_ctx* c2, const float* q,
+                                int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                int32_t n_kv_heads, void* workspace, hipStream_t stream);
+hipError_t launch_split_stream(const tq_ctx* c1, const tq_ctx* c2, const void* workspace,
+                               int32_t batch, int32_t n_q_heads, const uint32_t* planes1,
+                               const uint16_t* norms1, const uint32_t* planes2,
+                               const uint16_t* norms2, int32_t n_kv_heads,
+                               int64_t keys_stride_head, const int64_t* seq_start,
+                               const int32_t* seq_len, int32_t max_seq_len, float scale,
+                               float* logits, int64_t logits_stride_head, hipStream_t stream);
 size_t decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                               int32_t n_kv_heads, int32_t max_seq_len);
 hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,

@@ -60,6 +60,13 @@ struct AttnArgs {
   int W, G, n_kv, n_rb, tiles_per_wave;
   float scale, alpha;
   int mask[kMaxVec];
+  struct {                    // second record set of channel-split records
+    const char* ws;
+    const uint32_t* planes;
+    const uint32_t* norms;
+    int W;
+    float alpha;
+  } set2;
 };
 
 // Logit stream.  grid = (token chunks, kv heads, batch); each wave owns
@@ -180,12 +187,22 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // loads in flight while its MFMAs run.  Records and norms are read through
 // buffer resources bounded to the wave's token range, so loads past the end
 // of the sequence (and of word groups beyond d) return zeros without branches.
-template <int NB, bool MSE, int U>
+//
+// NB2 > 0: channel-split records (fractional bit widths, two instances over
+// the first and the remaining channels).  A second record set (a.set2, NB2
+// words per group, its own prepared operands) is streamed alongside the
+// first; each token's logit is the sum of the two instances' estimates.
+template <int NB, bool MSE, int U, int NB2>
 __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
+  constexpr bool SPLIT = NB2 > 0;
   constexpr int CP = MSE ? NB : NB - 1;
   constexpr int NV = 1 << (CP - 1);
   constexpr int NC = 2 * NV + (MSE ? 0 : 2);
+  constexpr int NBs = SPLIT ? NB2 : NB;                // second set (unused if none)
+  constexpr int CP2 = MSE ? NBs : NBs - 1;
+  constexpr int NV2 = 1 << (CP2 - 1);
+  constexpr int NC2 = SPLIT ? 2 * NV2 + (MSE ? 0 : 2) : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int g = lane >> 4, n = lane & 15;
@@ -195,10 +212,14 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const int chunk = a.tiles_per_wave * kTile;
   const size_t rbb = (size_t)NC * 64 * 16 + 64;
   const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
+  const size_t rbb2 = (size_t)NC2 * 64 * 16 + 64;
+  const char* wsb2 = a.set2.ws + ((size_t)bi * a.n_kv + h) * rbb2;
   // the 4 waves share (sequence, kv head): the prepared operands are read
   // from memory once per workgroup
-  __shared__ v4i Asm[NC * 64];
+  __shared__ v4i Asm[(NC + (SPLIT ? NC2 : 0)) * 64];
   for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
+  if constexpr (SPLIT)
+    for (int i = threadIdx.x; i < NC2 * 64; i += 256) Asm[NC * 64 + i] = ((const v4i*)wsb2)[i];
   __syncthreads();
   const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
   if (t_begin >= len) return;
@@ -210,6 +231,14 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const rsrc_t rn = make_rsrc(a.norms + rec_first, (uint32_t)n_tok * 4u);
   // word group g of this lane's token; groups beyond d read out of range (0)
   const uint32_t goff = g < a.W ? (uint32_t)(g * NB * 4) : 0x80000000u;
+  const uint32_t rec_bytes2 = SPLIT ? (uint32_t)(a.set2.W * NB2 * 4) : 0u;
+  rsrc_t rp2 = rp, rn2 = rn;
+  uint32_t goff2 = 0u;
+  if constexpr (SPLIT) {
+    rp2 = make_rsrc(a.set2.planes + rec_first * a.set2.W * NB2, (uint32_t)n_tok * rec_bytes2);
+    rn2 = make_rsrc(a.set2.norms + rec_first, (uint32_t)n_tok * 4u);
+    goff2 = g < a.set2.W ? (uint32_t)(g * NB2 * 4) : 0x80000000u;
+  }
   // stores: lane half hf (0/1) writes 32 consecutive tokens of head gs + hf
   // (gs = 0 for the first store of a tile pair, 2 for the second)
   const int hf = lane >> 5, ts = lane & 31;
@@ -219,18 +248,32 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   // source lanes (head g, token n) of the values this lane stores
   const int src_a = 16 * hf + (ts & 15), src_b = 32 + src_a;
 
-  v4i A[NC];
+  v4i A[NC], A2[NC2];
 #pragma unroll
   for (int c = 0; c < NC; ++c) A[c] = Asm[c * 64 + lane];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int c = 0; c < NC2; ++c) A2[c] = Asm[(NC + c) * 64 + lane];
+  }
   // per-head constants with the logit scale and the QJL factor folded in:
   // logit = nu * (vm X + Z + gamma (vq Y + W))
   const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
   const float cX = a.scale * cst.x, cZ = a.scale * cst.z;
   const float cY = a.scale * a.alpha * cst.y, cW = a.scale * a.alpha * cst.w;
+  float cX2 = 0.f, cZ2 = 0.f, cY2 = 0.f, cW2 = 0.f;
+  if constexpr (SPLIT) {
+    const float4 c2 = ((const float4*)(wsb2 + (size_t)NC2 * 64 * 16))[g];
+    cX2 = a.scale * c2.x;
+    cZ2 = a.scale * c2.z;
+    cY2 = a.scale * a.set2.alpha * c2.y;
+    cW2 = a.scale * a.set2.alpha * c2.w;
+  }
 
   struct Grp {
     uint32_t wd[U][NB];
     uint32_t nr[U];
+    uint32_t wd2[U][NBs];
+    uint32_t nr2[U];
   };
   // tl: local index (from t_begin) of the group's first token
   auto load = [&](Grp& gr, int tl) {
@@ -239,6 +282,10 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
       const uint32_t t = (uint32_t)(tl + kTile * u + n);
       buf_group<NB>(rp, t * rec_bytes + goff, gr.wd[u]);
       gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4u, 0, 0);
+      if constexpr (SPLIT) {
+        buf_group<NB2>(rp2, t * rec_bytes2 + goff2, gr.wd2[u]);
+        gr.nr2[u] = __builtin_amdgcn_raw_buffer_load_b32(rn2, t * 4u, 0, 0);
+      }
     }
   };
   // limbs -> float: |limb accumulators| < 2^21.1 (at most 16 NV K-slots per
@@ -247,11 +294,11 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
     const int lo = c[0] + (c[1] << 8), hi = c[2] + (c[3] << 8);
     return fmaf((float)hi, 65536.f, (float)lo);
   };
-  auto logit = [&](v4i am, v4i aq, uint32_t nrm) {
-    const float ms = fmaf(limbs(am), cX, cZ);
+  auto logit = [&](v4i am, v4i aq, uint32_t nrm, float x, float z, float y, float w) {
+    const float ms = fmaf(limbs(am), x, z);
     const float nu = __half2float(__ushort_as_half((unsigned short)(nrm & 0xffffu)));
     if constexpr (MSE) return nu * ms;
-    const float qs = fmaf(limbs(aq), cY, cW);
+    const float qs = fmaf(limbs(aq), y, w);
     const float ga = __half2float(__ushort_as_half((unsigned short)(nrm >> 16)));
     return nu * fmaf(ga, qs, ms);
   };
@@ -267,35 +314,51 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
       if (head_b) __builtin_nontemporal_store(ts < 16 ? b0 : b1, &out_b[t_begin + tloc]);
     }
   };
-  // two tiles at a time: their MFMA chains interleave, hiding each other's
-  // dependent-issue latency
+  // the MFMA chains of one record set (B words per group) for a tile pair,
+  // interleaved so each hides the other's dependent-issue latency
+  auto dots = [&](auto nb_c, const v4i* Aop, const uint32_t* w0, const uint32_t* w1, v4i& am0,
+                  v4i& aq0, v4i& am1, v4i& aq1) {
+    constexpr int B = decltype(nb_c)::value;
+    constexpr int cp = MSE ? B : B - 1;
+    constexpr int nv = 1 << (cp - 1);
+#pragma unroll
+    for (int v = 0; v < nv; ++v) {
+      uint32_t u0 = 0u, u1 = 0u;
+#pragma unroll
+      for (int p = 0; p < cp; ++p)
+        if ((walsh_mask<cp>(v) >> p) & 1) {
+          u0 ^= w0[p];
+          u1 ^= w1[p];
+        }
+      am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v], bit_lanes(u0, 0), am0, 0, 0, 0);
+      am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v], bit_lanes(u1, 0), am1, 0, 0, 0);
+      am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v + 1], bit_lanes(u0, 1), am0, 0, 0, 0);
+      am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v + 1], bit_lanes(u1, 1), am1, 0, 0, 0);
+    }
+    if constexpr (!MSE) {
+      const uint32_t s0 = w0[B - 1], s1 = w1[B - 1];
+      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv], bit_lanes(s0, 0), aq0, 0, 0, 0);
+      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv], bit_lanes(s1, 0), aq1, 0, 0, 0);
+      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
+      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
+    }
+  };
   auto compute = [&](const Grp& gr, int tl) {
 #pragma unroll
     for (int u = 0; u < U; u += 2) {
       if (tl + kTile * u >= n_tok) break;
       v4i am0 = {0, 0, 0, 0}, aq0 = {0, 0, 0, 0}, am1 = {0, 0, 0, 0}, aq1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        uint32_t u0 = 0u, u1 = 0u;
-#pragma unroll
-        for (int p = 0; p < CP; ++p)
-          if ((walsh_mask<CP>(v) >> p) & 1) {
-            u0 ^= gr.wd[u][p];
-            u1 ^= gr.wd[u + 1][p];
-          }
-        am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(u0, 0), am0, 0, 0, 0);
-        am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v], bit_lanes(u1, 0), am1, 0, 0, 0);
-        am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u0, 1), am0, 0, 0, 0);
-        am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * v + 1], bit_lanes(u1, 1), am1, 0, 0, 0);
+      dots(std::integral_constant<int, NB>{}, A, gr.wd[u], gr.wd[u + 1], am0, aq0, am1, aq1);
+      float v0 = logit(am0, aq0, gr.nr[u], cX, cZ, cY, cW);
+      float v1 = logit(am1, aq1, gr.nr[u + 1], cX, cZ, cY, cW);
+      if constexpr (SPLIT) {
+        v4i bm0 = {0, 0, 0, 0}, bq0 = {0, 0, 0, 0}, bm1 = {0, 0, 0, 0}, bq1 = {0, 0, 0, 0};
+        dots(std::integral_constant<int, NBs>{}, A2, gr.wd2[u], gr.wd2[u + 1], bm0, bq0, bm1,
+             bq1);
+        v0 += logit(bm0, bq0, gr.nr2[u], cX2, cZ2, cY2, cW2);
+        v1 += logit(bm1, bq1, gr.nr2[u + 1], cX2, cZ2, cY2, cW2);
       }
-      if constexpr (!MSE) {
-        const uint32_t s0 = gr.wd[u][NB - 1], s1 = gr.wd[u + 1][NB - 1];
-        aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s0, 0), aq0, 0, 0, 0);
-        aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV], bit_lanes(s1, 0), aq1, 0, 0, 0);
-        aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
-        aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[2 * NV + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
-      }
-      finish2(logit(am0, aq0, gr.nr[u]), logit(am1, aq1, gr.nr[u + 1]), tl + kTile * u);
+      finish2(v0, v1, tl + kTile * u);
     }
   };
   Grp g0, g1;
@@ -340,14 +403,14 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
   return hipGetLastError();
 }
 
-hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
-                              int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
-                              int32_t n_kv_heads, int64_t keys_stride_head,
-                              const int64_t* seq_start, const int32_t* seq_len,
-                              int32_t max_seq_len, float scale, float* logits,
-                              int64_t logits_stride_head, hipStream_t stream) {
+namespace {
+
+// Fill the arguments of one record set's stream (everything but the grid).
+AttnArgs stream_args(const tq_ctx* ctx, const void* workspace, int32_t n_q_heads,
+                     const uint32_t* planes, const uint16_t* norms, int32_t n_kv_heads,
+                     int64_t keys_stride_head, const int64_t* seq_start, const int32_t* seq_len,
+                     float scale, float* logits, int64_t logits_stride_head) {
   const int G = n_q_heads / n_kv_heads;
-  const int n_rb = (G + 3) / 4;
   AttnArgs a{};
   a.ws = (const char*)workspace;
   a.planes = planes;
@@ -360,58 +423,195 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
   a.W = ctx->W;
   a.G = G;
   a.n_kv = n_kv_heads;
-  a.n_rb = n_rb;
+  a.n_rb = (G + 3) / 4;
   a.scale = scale;
   a.alpha = (float)(std::sqrt(M_PI / 2.0) / ctx->d);
   for (int v = 0; v < ctx->n_mono; ++v) a.mask[v] = ctx->mono_mask[v];
-  // the resident kernel hard-codes the Walsh subsets 1 / 1,2 / 1,2,4,7
+  return a;
+}
+
+// The resident kernel applies: d <= 128, G <= 4 and the Walsh subsets it
+// hard-codes (1 / 1,2 / 1,2,4,7).
+bool resident_ok(const tq_ctx* ctx, int n_rb) {
   static const int kMasks[3][4] = {{1, 0, 0, 0}, {1, 2, 0, 0}, {1, 2, 4, 7}};
   bool masks_ok = true;
   for (int v = 0; v < ctx->n_mono; ++v) masks_ok &= ctx->mono_mask[v] == kMasks[ctx->cp - 1][v];
-  const bool res = (ctx->W <= 4) && (n_rb == 1) && masks_ok;
-  // Grid: one round of resident waves over all tiles (each wave takes a
-  // contiguous chunk of one sequence), so no partial second round is left.
-  // Variants by code planes 1..3, two-stage then MSE-only.
-  static const int nb_res[2][3] = {
-      {resident_blocks_per_cu(attn_logits_res_kernel<2, false, 4>),
-       resident_blocks_per_cu(attn_logits_res_kernel<3, false, 4>),
-       resident_blocks_per_cu(attn_logits_res_kernel<4, false, 4>)},
-      {resident_blocks_per_cu(attn_logits_res_kernel<1, true, 4>),
-       resident_blocks_per_cu(attn_logits_res_kernel<2, true, 4>),
-       resident_blocks_per_cu(attn_logits_res_kernel<3, true, 4>)}};
-  const int nb = res ? nb_res[ctx->mse][ctx->cp - 1] : 4;
+  return ctx->W <= 4 && n_rb == 1 && masks_ok;
+}
+
+// Grid of a stream with nb resident blocks per CU: one round of resident
+// waves over all tiles (each wave takes a contiguous chunk of one sequence),
+// so no partial second round is left.  Short chunks (about 8 rounds of
+// resident waves) keep many independent read/write streams in flight, which
+// measured best on the mixed record-read / logit-write traffic; at least 8
+// tiles per wave.
+dim3 stream_grid(int n_cu, int nb, int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
+                 int& tiles_per_wave) {
   const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
   const int64_t tiles_total = (int64_t)batch * n_kv_heads * tiles_seq;
-  // short chunks (about 8 rounds of resident waves) keep many independent
-  // read/write streams in flight, which measured best on the mixed
-  // record-read / logit-write traffic; at least 8 tiles per wave
-  const int64_t resident_waves = (int64_t)ctx->n_cu * nb * kWaves;
+  const int64_t resident_waves = (int64_t)n_cu * nb * kWaves;
   int64_t tpw = (tiles_total + 8 * resident_waves - 1) / (8 * resident_waves);
   tpw = std::max<int64_t>(8, std::min<int64_t>(256, tpw));
-  a.tiles_per_wave = (int)tpw;
+  tiles_per_wave = (int)tpw;
   const int64_t tok_per_block = (int64_t)kWaves * tpw * kTile;
-  const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
-                  batch);
-#define TQ_LOGITS(NB, MSE)                                                                     \
-  do {                                                                                         \
-    if (res) hipLaunchKernelGGL((attn_logits_res_kernel<NB, MSE, 4>), grid, dim3(256), 0, stream, a); \
-    else hipLaunchKernelGGL((attn_logits_kernel<NB, MSE, false>), grid, dim3(256), 0, stream, a);     \
-  } while (0)
+  return dim3((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads, batch);
+}
+
+template <int NB, bool MSE, int NB2>
+hipError_t launch_res(const AttnArgs& a, int n_cu, int32_t batch, int32_t n_kv_heads,
+                      int32_t max_seq_len, hipStream_t stream) {
+  static const int nb = resident_blocks_per_cu(attn_logits_res_kernel<NB, MSE, 4, NB2>);
+  AttnArgs b = a;
+  const dim3 grid = stream_grid(n_cu, nb, batch, n_kv_heads, max_seq_len, b.tiles_per_wave);
+  hipLaunchKernelGGL((attn_logits_res_kernel<NB, MSE, 4, NB2>), grid, dim3(256), 0, stream, b);
+  return hipGetLastError();
+}
+
+template <int NB, bool MSE>
+hipError_t launch_general(const AttnArgs& a, int n_cu, int32_t batch, int32_t n_kv_heads,
+                          int32_t max_seq_len, hipStream_t stream) {
+  AttnArgs b = a;
+  const dim3 grid = stream_grid(n_cu, 4, batch, n_kv_heads, max_seq_len, b.tiles_per_wave);
+  hipLaunchKernelGGL((attn_logits_kernel<NB, MSE, false>), grid, dim3(256), 0, stream, b);
+  return hipGetLastError();
+}
+
+// Channel-split preparation: the queries' first d1 channels against the first
+// instance and the rest against the second, as disjoint workgroups of one grid.
+struct SplitPrepArgs {
+  PrepArgs p1, p2;
+  uint32_t n1;                    // workgroups of the first preparation
+  uint32_t x1, y1, x2, y2;        // the two preparations' grids (x, y); z = batch
+};
+
+__global__ void __launch_bounds__(256) split_prep_kernel(SplitPrepArgs a) {
+  uint32_t b = blockIdx.x;
+  if (b < a.n1) {
+    const uint32_t byz = b / a.x1;
+    prep_block(a.p1, (int)(b % a.x1), (int)(byz % a.y1), (int)(byz / a.y1));
+  } else {
+    b -= a.n1;
+    const uint32_t byz = b / a.x2;
+    prep_block(a.p2, (int)(b % a.x2), (int)(byz % a.y2), (int)(byz / a.y2));
+  }
+}
+
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+}  // namespace
+
+hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
+                              int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
+                              int32_t n_kv_heads, int64_t keys_stride_head,
+                              const int64_t* seq_start, const int32_t* seq_len,
+                              int32_t max_seq_len, float scale, float* logits,
+                              int64_t logits_stride_head, hipStream_t stream) {
+  const AttnArgs a = stream_args(ctx, workspace, n_q_heads, planes, norms, n_kv_heads,
+                                 keys_stride_head, seq_start, seq_len, scale, logits,
+                                 logits_stride_head);
+  const bool res = resident_ok(ctx, a.n_rb);
+  const int n_cu = ctx->n_cu;
+#define TQ_LOGITS(NB, MSE)                                                           \
+  return res ? launch_res<NB, MSE, 0>(a, n_cu, batch, n_kv_heads, max_seq_len, stream) \
+             : launch_general<NB, MSE>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
   if (ctx->mse) {
     switch (ctx->b) {
-      case 1: TQ_LOGITS(1, true); break;
-      case 2: TQ_LOGITS(2, true); break;
-      default: TQ_LOGITS(3, true); break;
-    }
-  } else {
-    switch (ctx->b) {
-      case 2: TQ_LOGITS(2, false); break;
-      case 3: TQ_LOGITS(3, false); break;
-      default: TQ_LOGITS(4, false); break;
+      case 1: TQ_LOGITS(1, true);
+      case 2: TQ_LOGITS(2, true);
+      default: TQ_LOGITS(3, true);
     }
   }
+  switch (ctx->b) {
+    case 2: TQ_LOGITS(2, false);
+    case 3: TQ_LOGITS(3, false);
+    default: TQ_LOGITS(4, false);
+  }
 #undef TQ_LOGITS
+}
+
+size_t split_attn_workspace_bytes(const tq_ctx* c1, const tq_ctx* c2, int32_t batch,
+                                  int32_t n_q_heads, int32_t n_kv_heads) {
+  return align16(attn_workspace_bytes(c1, batch, n_q_heads, n_kv_heads)) +
+         attn_workspace_bytes(c2, batch, n_q_heads, n_kv_heads);
+}
+
+bool split_logits_supported(const tq_ctx* c1, const tq_ctx* c2, int32_t n_q_heads,
+                            int32_t n_kv_heads) {
+  const int n_rb = (n_q_heads / n_kv_heads + 3) / 4;
+  return c1->mse == c2->mse && resident_ok(c1, n_rb) && resident_ok(c2, n_rb);
+}
+
+hipError_t launch_split_prepare(const tq_ctx* c1, const tq_ctx* c2, const float* q,
+                                int32_t batch, int32_t n_q_heads, int64_t q_stride_batch,
+                                int32_t n_kv_heads, void* workspace, hipStream_t stream) {
+  char* ws1 = (char*)workspace;
+  char* ws2 = ws1 + align16(attn_workspace_bytes(c1, batch, n_q_heads, n_kv_heads));
+  // q channels [0, d1) against the first instance, [d1, d1 + d2) against the
+  // second, head stride d1 + d2
+  SplitPrepArgs sp{};
+  size_t shm1, shm2;
+  dim3 g1, g2;
+  prep_args(c1, q, batch, n_q_heads, q_stride_batch, n_kv_heads, ws1, sp.p1, shm1, g1);
+  prep_args(c2, q + c1->d, batch, n_q_heads, q_stride_batch, n_kv_heads, ws2, sp.p2, shm2, g2);
+  sp.p1.q_stride_head = sp.p2.q_stride_head = c1->d + c2->d;
+  sp.n1 = g1.x * g1.y * g1.z;
+  sp.x1 = g1.x;
+  sp.y1 = g1.y;
+  sp.x2 = g2.x;
+  sp.y2 = g2.y;
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)split_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(split_prep_kernel, dim3(sp.n1 + g2.x * g2.y * g2.z), dim3(256),
+                     std::max(shm1, shm2), stream, sp);
   return hipGetLastError();
+}
+
+hipError_t launch_split_stream(const tq_ctx* c1, const tq_ctx* c2, const void* workspace,
+                               int32_t batch, int32_t n_q_heads, const uint32_t* planes1,
+                               const uint16_t* norms1, const uint32_t* planes2,
+                               const uint16_t* norms2, int32_t n_kv_heads,
+                               int64_t keys_stride_head, const int64_t* seq_start,
+                               const int32_t* seq_len, int32_t max_seq_len, float scale,
+                               float* logits, int64_t logits_stride_head, hipStream_t stream) {
+  const char* ws1 = (const char*)workspace;
+  const char* ws2 = ws1 + align16(attn_workspace_bytes(c1, batch, n_q_heads, n_kv_heads));
+  // one stream over both record sets; the set with more words per group is
+  // the kernel's first
+  const bool swap = c2->b > c1->b;
+  const tq_ctx* ca = swap ? c2 : c1;
+  const tq_ctx* cb = swap ? c1 : c2;
+  AttnArgs a = stream_args(ca, swap ? ws2 : ws1, n_q_heads, swap ? planes2 : planes1,
+                           swap ? norms2 : norms1, n_kv_heads, keys_stride_head, seq_start,
+                           seq_len, scale, logits, logits_stride_head);
+  a.set2.ws = swap ? ws1 : ws2;
+  a.set2.planes = swap ? planes1 : planes2;
+  a.set2.norms = (const uint32_t*)(swap ? norms1 : norms2);
+  a.set2.W = cb->W;
+  a.set2.alpha = (float)(std::sqrt(M_PI / 2.0) / cb->d);
+  const int n_cu = ca->n_cu;
+#define TQ_SPLIT(NB, MSE, NB2) \
+  return launch_res<NB, MSE, NB2>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
+  const int key = 10 * ca->b + cb->b;
+  if (ca->mse) {
+    switch (key) {
+      case 11: TQ_SPLIT(1, true, 1);
+      case 21: TQ_SPLIT(2, true, 1);
+      case 22: TQ_SPLIT(2, true, 2);
+      case 31: TQ_SPLIT(3, true, 1);
+      case 32: TQ_SPLIT(3, true, 2);
+      default: TQ_SPLIT(3, true, 3);
+    }
+  }
+  switch (key) {
+    case 22: TQ_SPLIT(2, false, 2);
+    case 32: TQ_SPLIT(3, false, 2);
+    case 33: TQ_SPLIT(3, false, 3);
+    case 42: TQ_SPLIT(4, false, 2);
+    case 43: TQ_SPLIT(4, false, 3);
+    default: TQ_SPLIT(4, false, 4);
+  }
+#undef TQ_SPLIT
 }
 
 }  // namespace tq

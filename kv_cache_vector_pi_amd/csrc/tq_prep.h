@@ -14,8 +14,8 @@ namespace tq {
 namespace {
 
 struct PrepArgs {
-  const float* q;          // [batch][n_q][d], batch stride q_stride_batch
-  int64_t q_stride_batch;
+  const float* q;          // q[bi * q_stride_batch + head * q_stride_head + j]
+  int64_t q_stride_batch, q_stride_head;
   const float* pit;        // [d][d] Pi^T
   const float* st;         // [d][d] S^T
   char* ws;
@@ -66,7 +66,8 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
     const int hh = it / a.d, j = it - hh * a.d;
     const int slot = 4 * rb + hh;
     qv[4 * j + hh] = slot < a.G
-        ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.d + j] : 0.f;
+        ? a.q[(int64_t)bi * a.q_stride_batch + (int64_t)(h * a.G + slot) * a.q_stride_head + j]
+        : 0.f;
   }
   __syncthreads();
   {
@@ -210,6 +211,7 @@ inline void prep_args(const tq_ctx* ctx, const float* q, int32_t batch, int32_t 
   p = PrepArgs{};
   p.q = q;
   p.q_stride_batch = q_stride_batch;
+  p.q_stride_head = ctx->d;
   p.pit = ctx->t.pit32;
   p.st = ctx->t.st32;
   p.ws = (char*)workspace;

@@ -156,6 +156,22 @@ def test_hot_path_rejects_null_context(tq):
         tq.TQ_ERR_INVALID_ARG
     assert L.tq_quantize_kv_slots(None, None, 0, 1, 1, 128, 0, None, None, None, 1, None) == \
         tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_quantize_kv(None, None, None, 0, 1, 1, 128, 0, None, None, None, None, 1, 0,
+                                  None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_dequantize(None, None, None, None, None, None, 1, None, 128, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_attn_logits(None, None, None, 1, 32, 4096, None, None, None, None, 8, 0,
+                                  None, None, 1, 1.0, None, 0, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_attn_output(None, None, None, 0, 1, 32, None, None, None, None, 8, 0, None,
+                                  None, 1, None, 0, None, 0, None) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_attn_prepare(None, None, None, 1, 32, 4096, 8, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_attn_logits_prepared(None, None, None, 0, 1, 32, None, None, None, None, 8,
+                                           0, None, None, 1, 1.0, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_split_attn_logits_workspace_bytes(None, None, 1, 32, 8) == 0
+    assert L.tq_split_attn_output_workspace_bytes(None, None, 1, 32, 8, 100) == 0
     assert L.tq_attn_logits_workspace_bytes(None, 1, 32, 8) == 0
     assert L.tq_search_workspace_bytes(None, 1, 1, 10) == 0
     assert L.tq_ctx_dim(None) == 0 and L.tq_ctx_bits(None) == 0
