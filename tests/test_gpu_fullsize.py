@@ -7,7 +7,10 @@ oracle computes one by one:
     the cache fill, the new-token quantize into the caches, the prepared
     queries and one logit launch over all layers;
   * batched decode: 16 ragged sequences (4096..8192 tokens), b = 3, prefix and
-    512-token chunk quantized per sequence, one logit launch;
+    512-token chunk quantized per sequence, one logit launch; the chunks also
+    as one slot-mapped call;
+  * fractional widths (channels 0..63 at 3 or 4 bits, 64..127 at 2 or 3) over
+    the 32 Llama-shaped layer caches;
   * long context: 8 KV heads x 131072 tokens, b in {2, 3, 4};
   * vector search: 1e6 unit vectors at d = 1536 and 200, b in {2, 4}, top-10
     of 1000 queries (the oracle ranks a subset of queries over the whole
@@ -142,6 +145,94 @@ def test_batched_ragged_decode(orc):
         got = logits[hq, a:a + lens[bi]].cpu().numpy()[None]
         assert rel_err_rows(got, ref) < TOL, (bi, hq, rel_err_rows(got, ref))
     ctx.close()
+
+
+def test_batched_chunks_slot_mapped(orc):
+    """The batched workload's chunk appends as bench.py times them: the 16
+    sequences' 512-token chunks gathered into one input and written by one
+    tq_quantize_kv_slots call; the whole cache equals the per-sequence
+    tq_quantize_kv calls bit for bit, and sampled chunk records match the
+    oracle."""
+    d, b = 128, 3
+    say("batched chunks, slot-mapped")
+    ctx, pi, s, c = make_ctx(orc, d, b)
+    wl = workloads.batched(DEV)
+    lens, chunk, n_kv = wl["lens"], wl["chunk"], wl["n_kv"]
+    total = sum(lens)
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    rw = tq.tq_record_words(d, b)
+    kp = torch.zeros((n_kv * total, rw), dtype=torch.int32, device=DEV)
+    kn = torch.zeros((n_kv * total, 2), dtype=torch.int16, device=DEV)
+    ref_p, ref_n = torch.zeros_like(kp), torch.zeros_like(kn)
+    K = wl["K"]
+    for i in range(len(lens)):
+        a = int(offs[i]) + lens[i] - chunk
+        tq.tq_quantize_kv(ctx, K[:, a:a + chunk], ref_p, ref_n, dst_stride_head=total,
+                          dst_token0=a)
+    idx = torch.cat([torch.arange(int(o) + n - chunk, int(o) + n) for o, n in zip(offs, lens)])
+    idx = idx.to(DEV)
+    Kn = K[:, idx].contiguous()
+    tq.tq_quantize_kv_slots(ctx, Kn, idx, kp, kn, total)
+    torch.cuda.synchronize()
+    assert torch.equal(kp, ref_p) and torch.equal(kn, ref_n)
+    rng = np.random.default_rng(4)
+    pick = rng.choice(n_kv * idx.numel(), 1024, replace=False)
+    h, t = pick // idx.numel(), pick % idx.numel()
+    rows = h * total + idx.cpu().numpy()[t]
+    x = Kn[torch.as_tensor(h, device=DEV), torch.as_tensor(t, device=DEV)].double().cpu().numpy()
+    P, N = np_records(kp, kn, rows)
+    check_records(orc, d, b, pi, s, c, x, P, N)
+    ctx.close()
+
+
+@pytest.mark.parametrize("bh,bl", [(3, 2), (4, 3)])
+def test_llama_split_32_layers(orc, bh, bl):
+    """Fractional widths as bench.py --workload split runs them: channels
+    0..63 at bh bits and 64..127 at bl over the 32 Llama-shaped layer caches;
+    sampled record pairs against the oracle's split quantization, and whole
+    logit rows of one prepared launch over all layers against its split
+    estimate."""
+    d, dh, n_kv, n_q, n_tok, L = 128, 64, 8, 32, 32768, 32
+    say("llama split", bh, bl)
+    insts = []
+    for bb, seed in ((bh, 1), (bl, 2)):
+        pi64, s64, pi32, s32 = orc.make_rotation(dh, seed)
+        cen = orc.lloyd_max(dh, bb - 1)[0].astype(np.float32)
+        insts.append((tq.TqContext(dh, bb, pi32, s32, cen), (dh, bb, pi32, s32, cen)))
+    (hi, ohi), (lo, olo) = insts
+    n_rec = n_kv * L * n_tok
+    hp = torch.zeros((n_rec, tq.tq_record_words(dh, bh)), dtype=torch.int32, device=DEV)
+    lp = torch.zeros((n_rec, tq.tq_record_words(dh, bl)), dtype=torch.int32, device=DEV)
+    hn = torch.zeros((n_rec, 2), dtype=torch.int16, device=DEV)
+    ln = torch.zeros_like(hn)
+    Kx = torch.empty((n_kv, L * n_tok, d), dtype=torch.bfloat16, device=DEV)
+    for l in range(L):
+        Kx[:, l * n_tok:(l + 1) * n_tok] = workloads.llama(DEV, seed=l, n_tok=n_tok)["K"]
+    q_all = torch.stack([workloads.normal((n_q, d), l, workloads.STREAM_Q, DEV) for l in range(L)])
+    tq.tq_split_quantize_kv(hi, lo, Kx, hp, hn, lp, ln)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(5).choice(n_rec, 1024, replace=False)
+    x = Kx.view(-1, d)[torch.as_tensor(rows, device=DEV)].double().cpu().numpy()
+    check_records(orc, dh, bh, *ohi[2:], x[:, :dh], *np_records(hp, hn, rows))
+    check_records(orc, dh, bl, *olo[2:], x[:, dh:], *np_records(lp, ln, rows))
+    ws = tq.workspace(tq.tq_split_attn_logits_workspace_bytes(hi, lo, L, n_q, n_kv), DEV)
+    seq_start = torch.arange(L, dtype=torch.int64, device=DEV) * n_tok
+    seq_len = torch.full((L,), n_tok, dtype=torch.int32, device=DEV)
+    logits = torch.empty((n_q, L * n_tok), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    tq.tq_split_attn_prepare(hi, lo, q_all, L, n_q, n_q * d, n_kv, ws)
+    tq.tq_split_attn_logits_prepared(hi, lo, ws, L, n_q, hp, hn, lp, ln, n_kv, L * n_tok,
+                                     seq_start, seq_len, n_tok, scale, logits, L * n_tok)
+    torch.cuda.synchronize()
+    for (l, hq) in [(0, 0), (9, 14), (31, 31)]:
+        h = hq // (n_q // n_kv)
+        r = np.arange((h * L + l) * n_tok, (h * L + l + 1) * n_tok)
+        ref = orc.split_estimate(ohi, olo, q_all[l, hq:hq + 1].double().cpu().numpy(),
+                                 np_records(hp, hn, r), np_records(lp, ln, r), scale=scale)
+        got = logits[hq, l * n_tok:(l + 1) * n_tok].cpu().numpy()[None]
+        assert rel_err_rows(got, ref) < TOL, (l, hq, rel_err_rows(got, ref))
+    hi.close()
+    lo.close()
 
 
 @pytest.mark.parametrize("b", [2, 3, 4])
