@@ -25,10 +25,17 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-fvisibility=
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-source flags.  The value-accumulation kernels keep their int8 MFMA
+# accumulators in VGPRs: in AGPRs every chunk paid a zeroing write and a
+# read-back per accumulator register.
+EXTRA = {"tq_attn_out.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "tq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

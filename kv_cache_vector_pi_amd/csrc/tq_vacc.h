@@ -223,13 +223,12 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
     const int w = w0 + wave;
     if (w >= W) continue;
     v4i G[2][NV], S[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      S[cb] = (v4i){0, 0, 0, 0};
-#pragma unroll
-      for (int m = 0; m < NV; ++m) G[cb][m] = (v4i){0, 0, 0, 0};
-    }
-    for (int b = 0; b * 128 < nt; ++b) {
+    // one 128-token block; the first starts the accumulators from an inline
+    // zero operand instead of zeroed registers (a chunk with no tokens has
+    // zero bits and weights, so running it is harmless)
+    auto block = [&](int b, auto first_c) {
+      constexpr bool FIRST = decltype(first_c)::value;
+      const v4i zero = {0, 0, 0, 0};
       uint32_t X0[NB], X1[NB];
 #pragma unroll
       for (int p = 0; p < NB; ++p) {
@@ -256,16 +255,22 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
 #pragma unroll
           for (int p = 0; p < CP; ++p)
             if ((walsh_mask<CP>(m) >> p) & 1) u ^= X[p];
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[h], bit_lanes(u, h), G[cb][m], 0, 0, 0);
+          G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[0], bit_lanes(u, 0),
+                                                           FIRST ? zero : G[cb][m], 0, 0, 0);
+          G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[1], bit_lanes(u, 1), G[cb][m], 0, 0, 0);
         }
         if constexpr (!MSE) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[h], bit_lanes(X[NB - 1], h), S[cb], 0, 0, 0);
+          S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[0], bit_lanes(X[NB - 1], 0),
+                                                        FIRST ? zero : S[cb], 0, 0, 0);
+          S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[1], bit_lanes(X[NB - 1], 1), S[cb], 0, 0, 0);
         }
       }
+    };
+    block(0, std::true_type{});
+    for (int b = 1; b * 128 < nt; ++b) block(b, std::false_type{});
+    if constexpr (MSE) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) S[cb] = (v4i){0, 0, 0, 0};
     }
     // lane (g, n): head g at coordinate 32w + 16cb + n
     const float sc0 = ldexpf(1.f, -s_e[gq]);
