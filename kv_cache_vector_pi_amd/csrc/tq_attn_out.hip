@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(256) vout_final_kernel(VFinArgs a) {
   extern __shared__ float fsm[];
   float* arot = fsm;               // [Dp]
   float* ask = fsm + a.Dp;         // [Dp]
-  __shared__ float red[512];
+  __shared__ __align__(16) float red[2048];
   const int hq = blockIdx.x, bi = blockIdx.y;
   const int h = hq / a.G, g = hq % a.G, rb = g / 4, hh = g % 4;
   const float* src = a.part + (((int64_t)bi * a.n_kv + h) * a.n_rb + rb) * a.n_chunk * 8 * (int64_t)a.Dp;

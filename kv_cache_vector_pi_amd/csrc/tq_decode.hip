@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(256) decode_final_kernel(DecFinArgs a) {
   const float L = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = L > 0.f ? 1.f / L : 0.f;
   __syncthreads();
-  __shared__ float red2[512];
+  __shared__ __align__(16) float red2[2048];
   dev::sum_chunk_partials(a.part + c0 * 8 * (size_t)a.Dp, a.n_chunk, hh, 4 + hh, a.Dp, fac, inv,
                           red2, arot, ask);
   dev::apply_transforms(a.pi32, a.s32, a.d, a.qjl != 0, a.alpha, arot, ask, red2,

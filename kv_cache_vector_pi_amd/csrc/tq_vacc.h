@@ -294,60 +294,73 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
 }
 
 // ---- finishing a query head: chunk partials -> output -----------------------
-// Block-wide (256 threads).  Threads split as NL = min(n, 256) lanes over the
-// outputs x 256 / NL groups over the summed index; the groups' partial sums
-// meet in LDS `red` (>= 2 * 256 floats).  Four independent accumulators per
-// thread keep several loads in flight.
+// Block-wide (256 threads).  Threads split as NL = min(Dp / 4, 256) lanes over
+// float4 groups of the outputs x 256 / NL groups over the chunks; the chunk
+// groups' partial sums meet in LDS `red` (>= 2048 floats).  Each thread keeps
+// 4 chunk steps x 2 rows of float4 loads in flight: the reduction reads the
+// whole partial array once and is bound by how many loads are outstanding.
 
 // arot[j] = sc * sum_c f_c part_c[r0][j],  ask[j] = sc * sum_c f_c part_c[r1][j]
-// for j < Dp, chunk c's rows at part + c * 8 * Dp; f_c = fac[c] (LDS) or 1.
+// for j < Dp, chunk c's rows at part + c * 8 * Dp (16-byte aligned, Dp a
+// multiple of 4); f_c = fac[c] (LDS) or 1.
 __device__ inline void sum_chunk_partials(const float* part, int n_chunk, int r0, int r1, int Dp,
                                           const float* fac, float sc, float* red, float* arot,
                                           float* ask) {
   const int tid = threadIdx.x;
-  const int NL = min(Dp, 256), TT = 256 / NL;
+  const int D4 = Dp / 4;
+  const int NL = min(D4, 256), TT = 256 / NL;
   const int lj = tid % NL, tg = tid / NL;
-  for (int j0 = 0; j0 < Dp; j0 += NL) {
-    const int j = j0 + lj;
-    float a1[4] = {0.f, 0.f, 0.f, 0.f}, a2[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tg < TT && j < Dp) {
+  float4* red4 = (float4*)red;                  // [2][TT][NL]
+  auto fma4 = [](float f, float4 v, float4 acc) {
+    return make_float4(fmaf(f, v.x, acc.x), fmaf(f, v.y, acc.y), fmaf(f, v.z, acc.z),
+                       fmaf(f, v.w, acc.w));
+  };
+  auto add4 = [](float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  };
+  for (int j0 = 0; j0 < D4; j0 += NL) {
+    const int j4 = j0 + lj;
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 a1[4] = {z4, z4, z4, z4}, a2[4] = {z4, z4, z4, z4};
+    if (tg < TT && j4 < D4) {
+      const float4* p1 = (const float4*)(part + r0 * Dp) + j4;
+      const float4* p2 = (const float4*)(part + r1 * Dp) + j4;
+      const int64_t cs = 2 * Dp;                 // float4s per chunk (8 rows)
       int c = tg;
       for (; c + 3 * TT < n_chunk; c += 4 * TT) {
+        float4 v1[4], v2[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float* pc = part + (int64_t)(c + u * TT) * 8 * Dp;
+          v1[u] = p1[(int64_t)(c + u * TT) * cs];
+          v2[u] = p2[(int64_t)(c + u * TT) * cs];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
           const float f = fac ? fac[c + u * TT] : 1.f;
-          a1[u] = fmaf(f, pc[r0 * Dp + j], a1[u]);
-          a2[u] = fmaf(f, pc[r1 * Dp + j], a2[u]);
+          a1[u] = fma4(f, v1[u], a1[u]);
+          a2[u] = fma4(f, v2[u], a2[u]);
         }
       }
       for (; c < n_chunk; c += TT) {
-        const float* pc = part + (int64_t)c * 8 * Dp;
         const float f = fac ? fac[c] : 1.f;
-        a1[0] = fmaf(f, pc[r0 * Dp + j], a1[0]);
-        a2[0] = fmaf(f, pc[r1 * Dp + j], a2[0]);
+        a1[0] = fma4(f, p1[(int64_t)c * cs], a1[0]);
+        a2[0] = fma4(f, p2[(int64_t)c * cs], a2[0]);
       }
     }
-    const float s1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
-    const float s2 = (a2[0] + a2[1]) + (a2[2] + a2[3]);
-    if (TT == 1) {
-      if (tg == 0 && j < Dp) {      // threads past NL (256 % NL != 0) only idle
-        arot[j] = s1 * sc;
-        ask[j] = s2 * sc;
+    if (tg < TT) {          // threads past TT * NL (256 % NL != 0) only idle
+      red4[tg * NL + lj] = add4(add4(a1[0], a1[1]), add4(a1[2], a1[3]));
+      red4[(TT + tg) * NL + lj] = add4(add4(a2[0], a2[1]), add4(a2[2], a2[3]));
+    }
+    __syncthreads();
+    if (tid < NL && j0 + tid < D4) {
+      float4 t1 = z4, t2 = z4;
+      for (int q = 0; q < TT; ++q) {
+        t1 = add4(t1, red4[q * NL + tid]);
+        t2 = add4(t2, red4[(TT + q) * NL + tid]);
       }
-    } else {
-      red[tid] = s1;
-      red[256 + tid] = s2;
-      __syncthreads();
-      if (tid < NL) {
-        float t1 = 0.f, t2 = 0.f;
-        for (int q = 0; q < TT; ++q) {
-          t1 += red[q * NL + tid];
-          t2 += red[256 + q * NL + tid];
-        }
-        arot[j] = t1 * sc;
-        ask[j] = t2 * sc;
-      }
+      const int j = 4 * (j0 + tid);
+      arot[j] = t1.x * sc; arot[j + 1] = t1.y * sc; arot[j + 2] = t1.z * sc; arot[j + 3] = t1.w * sc;
+      ask[j] = t2.x * sc; ask[j + 1] = t2.y * sc; ask[j + 2] = t2.z * sc; ask[j + 3] = t2.w * sc;
     }
     __syncthreads();
   }
