@@ -289,7 +289,7 @@ hipError_t launch_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch, 
   const DecLayout L = dec_layout(ctx, batch, n_q_heads, n_kv_heads, max_seq_len);
   char* ws = (char*)workspace;
   hipError_t e = launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
-                                     ws + L.prep, stream);
+                                     ws + L.prep, false, stream);
   if (e != hipSuccess) return e;
   DecArgs a{};
   a.ws = ws + L.prep;

@@ -635,7 +635,8 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
                 need);
   if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits: scale not finite");
   hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
-                                         workspace, (hipStream_t)stream);
+                                         workspace, tq::logits_fold(ctx, n_q_heads, n_kv_heads),
+                                         (hipStream_t)stream);
   if (e == hipSuccess)
     e = tq::launch_attn_stream(ctx, workspace, batch, n_q_heads, planes, norms, n_kv_heads,
                                keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
@@ -654,7 +655,8 @@ TQ_API tq_status tq_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batc
   if (st != TQ_OK) return st;
   if (empty) return ok();
   hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
-                                         workspace, (hipStream_t)stream);
+                                         workspace, tq::logits_fold(ctx, n_q_heads, n_kv_heads),
+                                         (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_attn_prepare: launch");
   return ok();
 }

@@ -78,9 +78,14 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
 
 size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads);
+// fold: prepare the folded operand layout that the logit stream uses when
+// logits_fold() holds (the fused decode kernel reads the unfolded one)
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
                                int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
-                               void* workspace, hipStream_t stream);
+                               void* workspace, bool fold, hipStream_t stream);
+// whether tq_attn_logits' stream reads a folded preparation (d <= 64 on the
+// resident kernel)
+bool logits_fold(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads);
 hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
                               int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
                               int32_t n_kv_heads, int64_t keys_stride_head,

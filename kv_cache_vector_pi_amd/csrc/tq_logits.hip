@@ -192,17 +192,24 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // the first and the remaining channels).  A second record set (a.set2, NB2
 // words per group, its own prepared operands) is streamed alongside the
 // first; each token's logit is the sum of the two instances' estimates.
-template <int NB, bool MSE, int U, int NB2>
+//
+// FOLD (every set with W <= 2): the lane groups that would hold words 2 and 3
+// hold the upper 16 bits of words 0 and 1 instead (lane group g: word g & 1,
+// shifts 4 (g >> 1) .. +3), so one MFMA covers all 64 coordinates and each
+// Walsh subset (and the sign plane) takes one call instead of two; the query
+// operands are prepared in the same folded layout.
+template <int NB, bool MSE, int U, int NB2, bool FOLD>
 __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
   constexpr bool SPLIT = NB2 > 0;
+  constexpr int HALVES = FOLD ? 1 : 2;                 // MFMA calls per bit set
   constexpr int CP = MSE ? NB : NB - 1;
   constexpr int NV = 1 << (CP - 1);
-  constexpr int NC = 2 * NV + (MSE ? 0 : 2);
+  constexpr int NC = HALVES * (NV + (MSE ? 0 : 1));
   constexpr int NBs = SPLIT ? NB2 : NB;                // second set (unused if none)
   constexpr int CP2 = MSE ? NBs : NBs - 1;
   constexpr int NV2 = 1 << (CP2 - 1);
-  constexpr int NC2 = SPLIT ? 2 * NV2 + (MSE ? 0 : 2) : 1;
+  constexpr int NC2 = SPLIT ? HALVES * (NV2 + (MSE ? 0 : 1)) : 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int g = lane >> 4, n = lane & 15;
@@ -229,16 +236,34 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const uint32_t rec_bytes = (uint32_t)(a.W * NB * 4);
   const rsrc_t rp = make_rsrc(a.planes + rec_first * a.W * NB, (uint32_t)n_tok * rec_bytes);
   const rsrc_t rn = make_rsrc(a.norms + rec_first, (uint32_t)n_tok * 4u);
-  // word group g of this lane's token; groups beyond d read out of range (0)
-  const uint32_t goff = g < a.W ? (uint32_t)(g * NB * 4) : 0x80000000u;
+  // word group of this lane's token (g, or g & 1 folded); groups beyond d read
+  // out of range (0)
+  const int wg = FOLD ? (g & 1) : g;
+  const uint32_t goff = wg < a.W ? (uint32_t)(wg * NB * 4) : 0x80000000u;
   const uint32_t rec_bytes2 = SPLIT ? (uint32_t)(a.set2.W * NB2 * 4) : 0u;
   rsrc_t rp2 = rp, rn2 = rn;
   uint32_t goff2 = 0u;
   if constexpr (SPLIT) {
     rp2 = make_rsrc(a.set2.planes + rec_first * a.set2.W * NB2, (uint32_t)n_tok * rec_bytes2);
     rn2 = make_rsrc(a.set2.norms + rec_first, (uint32_t)n_tok * 4u);
-    goff2 = g < a.set2.W ? (uint32_t)(g * NB2 * 4) : 0x80000000u;
+    goff2 = wg < a.set2.W ? (uint32_t)(wg * NB2 * 4) : 0x80000000u;
   }
+  // folded bit masks: shifts 4 (g >> 1) + i of every byte
+  uint32_t fmk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fmk[i] = 0x01010101u << (4 * (g >> 1) + i);
+  auto bits = [&](uint32_t u, int half) -> v4i {
+    if constexpr (FOLD) {
+      v4i r;
+      r[0] = (int)(u & fmk[0]);
+      r[1] = (int)(u & fmk[1]);
+      r[2] = (int)(u & fmk[2]);
+      r[3] = (int)(u & fmk[3]);
+      return r;
+    } else {
+      return bit_lanes(u, half);
+    }
+  };
   // stores: lane half hf (0/1) writes 32 consecutive tokens of head gs + hf
   // (gs = 0 for the first store of a tile pair, 2 for the second)
   const int hf = lane >> 5, ts = lane & 31;
@@ -330,17 +355,21 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
           u0 ^= w0[p];
           u1 ^= w1[p];
         }
-      am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v], bit_lanes(u0, 0), am0, 0, 0, 0);
-      am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v], bit_lanes(u1, 0), am1, 0, 0, 0);
-      am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v + 1], bit_lanes(u0, 1), am0, 0, 0, 0);
-      am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * v + 1], bit_lanes(u1, 1), am1, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h) {
+        const v4i Ah = Aop[HALVES * v + h];
+        am0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ah, bits(u0, h), am0, 0, 0, 0);
+        am1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ah, bits(u1, h), am1, 0, 0, 0);
+      }
     }
     if constexpr (!MSE) {
       const uint32_t s0 = w0[B - 1], s1 = w1[B - 1];
-      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv], bit_lanes(s0, 0), aq0, 0, 0, 0);
-      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv], bit_lanes(s1, 0), aq1, 0, 0, 0);
-      aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv + 1], bit_lanes(s0, 1), aq0, 0, 0, 0);
-      aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop[2 * nv + 1], bit_lanes(s1, 1), aq1, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < HALVES; ++h) {
+        const v4i Ah = Aop[HALVES * nv + h];
+        aq0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ah, bits(s0, h), aq0, 0, 0, 0);
+        aq1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ah, bits(s1, h), aq1, 0, 0, 0);
+      }
     }
   };
   auto compute = [&](const Grp& gr, int tl) {
@@ -390,11 +419,11 @@ size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
 
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
                                int32_t n_q_heads, int64_t q_stride_batch, int32_t n_kv_heads,
-                               void* workspace, hipStream_t stream) {
+                               void* workspace, bool fold, hipStream_t stream) {
   PrepArgs p;
   size_t shm;
   dim3 grid;
-  prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, p, shm, grid);
+  prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, p, shm, grid, fold);
   // raise the dynamic-LDS limit once (never inside a sequence a caller may capture)
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)attn_prep_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
@@ -457,13 +486,14 @@ dim3 stream_grid(int n_cu, int nb, int32_t batch, int32_t n_kv_heads, int32_t ma
   return dim3((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads, batch);
 }
 
-template <int NB, bool MSE, int NB2>
+template <int NB, bool MSE, int NB2, bool FOLD>
 hipError_t launch_res(const AttnArgs& a, int n_cu, int32_t batch, int32_t n_kv_heads,
                       int32_t max_seq_len, hipStream_t stream) {
-  static const int nb = resident_blocks_per_cu(attn_logits_res_kernel<NB, MSE, 4, NB2>);
+  static const int nb = resident_blocks_per_cu(attn_logits_res_kernel<NB, MSE, 4, NB2, FOLD>);
   AttnArgs b = a;
   const dim3 grid = stream_grid(n_cu, nb, batch, n_kv_heads, max_seq_len, b.tiles_per_wave);
-  hipLaunchKernelGGL((attn_logits_res_kernel<NB, MSE, 4, NB2>), grid, dim3(256), 0, stream, b);
+  hipLaunchKernelGGL((attn_logits_res_kernel<NB, MSE, 4, NB2, FOLD>), grid, dim3(256), 0, stream,
+                     b);
   return hipGetLastError();
 }
 
@@ -510,10 +540,12 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
                                  keys_stride_head, seq_start, seq_len, scale, logits,
                                  logits_stride_head);
   const bool res = resident_ok(ctx, a.n_rb);
+  const bool fold = res && ctx->W <= 2;        // as logits_fold()
   const int n_cu = ctx->n_cu;
-#define TQ_LOGITS(NB, MSE)                                                           \
-  return res ? launch_res<NB, MSE, 0>(a, n_cu, batch, n_kv_heads, max_seq_len, stream) \
-             : launch_general<NB, MSE>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
+#define TQ_LOGITS(NB, MSE)                                                                 \
+  return !res ? launch_general<NB, MSE>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)   \
+         : fold ? launch_res<NB, MSE, 0, true>(a, n_cu, batch, n_kv_heads, max_seq_len, stream) \
+                : launch_res<NB, MSE, 0, false>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
   if (ctx->mse) {
     switch (ctx->b) {
       case 1: TQ_LOGITS(1, true);
@@ -527,6 +559,10 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
     default: TQ_LOGITS(4, false);
   }
 #undef TQ_LOGITS
+}
+
+bool logits_fold(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads) {
+  return ctx->W <= 2 && resident_ok(ctx, (n_q_heads / n_kv_heads + 3) / 4);
 }
 
 size_t split_attn_workspace_bytes(const tq_ctx* c1, const tq_ctx* c2, int32_t batch,
@@ -551,8 +587,10 @@ hipError_t launch_split_prepare(const tq_ctx* c1, const tq_ctx* c2, const float*
   SplitPrepArgs sp{};
   size_t shm1, shm2;
   dim3 g1, g2;
-  prep_args(c1, q, batch, n_q_heads, q_stride_batch, n_kv_heads, ws1, sp.p1, shm1, g1);
-  prep_args(c2, q + c1->d, batch, n_q_heads, q_stride_batch, n_kv_heads, ws2, sp.p2, shm2, g2);
+  const bool fold = c1->W <= 2 && c2->W <= 2;   // as the split stream
+  prep_args(c1, q, batch, n_q_heads, q_stride_batch, n_kv_heads, ws1, sp.p1, shm1, g1, fold);
+  prep_args(c2, q + c1->d, batch, n_q_heads, q_stride_batch, n_kv_heads, ws2, sp.p2, shm2, g2,
+            fold);
   sp.p1.q_stride_head = sp.p2.q_stride_head = c1->d + c2->d;
   sp.n1 = g1.x * g1.y * g1.z;
   sp.x1 = g1.x;
@@ -590,8 +628,10 @@ hipError_t launch_split_stream(const tq_ctx* c1, const tq_ctx* c2, const void* w
   a.set2.W = cb->W;
   a.set2.alpha = (float)(std::sqrt(M_PI / 2.0) / cb->d);
   const int n_cu = ca->n_cu;
-#define TQ_SPLIT(NB, MSE, NB2) \
-  return launch_res<NB, MSE, NB2>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
+  const bool fold = c1->W <= 2 && c2->W <= 2;   // as the split preparation
+#define TQ_SPLIT(NB, MSE, NB2)                                                                 \
+  return fold ? launch_res<NB, MSE, NB2, true>(a, n_cu, batch, n_kv_heads, max_seq_len, stream) \
+              : launch_res<NB, MSE, NB2, false>(a, n_cu, batch, n_kv_heads, max_seq_len, stream)
   const int key = 10 * ca->b + cb->b;
   if (ca->mse) {
     switch (key) {

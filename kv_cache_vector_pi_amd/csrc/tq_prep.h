@@ -20,6 +20,8 @@ struct PrepArgs {
   const float* st;         // [d][d] S^T
   char* ws;
   int d, W, nc, G, n_kv, n_rb, n_q;     // nc: MFMA calls per word step
+  int fold;                // W <= 2 folded layout: lane group g holds word g & 1,
+                           // bits 16 (g >> 1) .. +15, so one call per subset
   int n_parts;                          // 2: code and sign parts, 1: MSE-only records
   int nq;                               // output quads per chunk (power of two <= 64)
   float wm2[kMaxVec];      // -2 * w_m of the odd Walsh subsets
@@ -161,7 +163,10 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
   }
   __syncthreads();
   const int nws = dev::n_ws(a.W);
-  const int c_begin = part ? 2 * a.nv : 0, n_c = part ? a.nc - 2 * a.nv : 2 * a.nv;
+  // calls of this part: a code call per Walsh subset and half (one per subset
+  // when folded), then the sign calls
+  const int code_calls = a.fold ? a.nv : 2 * a.nv;
+  const int c_begin = part ? code_calls : 0, n_c = part ? a.nc - code_calls : code_calls;
   // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
   // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
   // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
@@ -174,9 +179,11 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
     const int rest = it >> 4;
     const int cl = rest % n_c, wsi = (rest / n_c) % nws, hh = rest / (n_c * nws);
     const int c = c_begin + cl;
-    const int w = 4 * wsi + g;
-    const int kbase = part ? 4 * cl : 4 * (c % 2);
-    const float wv = part ? 2.f : a.wm2[c / 2];
+    // word and shift base of lane group g: unfolded, word 4 wsi + g and the
+    // call's half; folded, word g & 1 and half g >> 1
+    const int w = a.fold ? (g & 1) : 4 * wsi + g;
+    const int kbase = a.fold ? 4 * (g >> 1) : (part ? 4 * cl : 4 * (c % 2));
+    const float wv = part ? 2.f : a.wm2[a.fold ? c : c / 2];
     const float* src = out + hh * Dp;
     const int e = qfix_e[hh];
     uint32_t outw[4];
@@ -205,7 +212,7 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
 // sets of n_q_heads heads against n_kv_heads key heads into `workspace`.
 inline void prep_args(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,
                       int64_t q_stride_batch, int32_t n_kv_heads, void* workspace, PrepArgs& p,
-                      size_t& shm, dim3& grid) {
+                      size_t& shm, dim3& grid, bool fold = false) {
   const int G = n_q_heads / n_kv_heads;
   const int n_rb = (G + 3) / 4;
   p = PrepArgs{};
@@ -217,7 +224,8 @@ inline void prep_args(const tq_ctx* ctx, const float* q, int32_t batch, int32_t 
   p.ws = (char*)workspace;
   p.d = ctx->d;
   p.W = ctx->W;
-  p.nc = dev::n_calls(ctx->cp, !ctx->mse);
+  p.fold = fold ? 1 : 0;
+  p.nc = fold ? (1 << (ctx->cp - 1)) + (ctx->mse ? 0 : 1) : dev::n_calls(ctx->cp, !ctx->mse);
   p.G = G;
   p.n_kv = n_kv_heads;
   p.n_rb = n_rb;

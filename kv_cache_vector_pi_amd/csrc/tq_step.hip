@@ -82,7 +82,7 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
     }
     if (e == hipSuccess && prep)
       e = launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
-                              stream);
+                              logits_fold(ctx, n_q_heads, n_kv_heads), stream);
     return e;
   }
   const bool bf = x_dtype == TQ_BF16;
@@ -104,7 +104,8 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
   unsigned n_prep = 0;
   if (prep) {
     dim3 pg;
-    prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, a.p, shm, pg);
+    prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace, a.p, shm, pg,
+              logits_fold(ctx, n_q_heads, n_kv_heads));
     a.prep_x = pg.x;
     a.prep_y = pg.y;
     n_prep = pg.x * pg.y * pg.z;

@@ -102,6 +102,8 @@ def test_mse_dequantize_parity(orc, d, b, n):
     (128, 2, 6, 2, [129]),                    # G = 3
     (200, 3, 8, 2, [333, 70]),                # generic kernel
     (1536, 1, 4, 1, [100]),
+    (64, 3, 8, 2, [300, 77]),                 # d <= 64: folded operands
+    (32, 2, 4, 4, [129]),                     # one word, folded, G = 1
 ])
 def test_mse_logits_parity(orc, d, b, n_q, n_kv, lens):
     say("mse logits", d, b, n_q, n_kv, lens)

@@ -204,6 +204,10 @@ def run_logits(ctx, q, planes, norms, n_kv, keys_stride_head, starts, lens, scal
     (128, 4, 6, 2, [129]),                    # G = 3 (partial row block)
     (200, 4, 8, 2, [333, 70]),
     (1536, 2, 4, 1, [100]),
+    (64, 4, 32, 8, [1000, 37, 513]),          # d <= 64: folded operands, GQA 4
+    (64, 3, 8, 4, [300, 1]),                  # folded, G = 2
+    (32, 2, 12, 4, [257]),                    # one word, folded, G = 3
+    (64, 2, 40, 4, [200]),                    # G = 10: general kernel, unfolded
 ])
 def test_logits_parity_oracle_records(orc, d, b, n_q, n_kv, lens):
     say("logits", d, b, n_q, n_kv, lens)
@@ -230,10 +234,10 @@ def test_logits_parity_oracle_records(orc, d, b, n_q, n_kv, lens):
             assert rel_err_rows(g, ref) < TOL, (bi, h, rel_err_rows(g, ref))
 
 
-def test_prepared_queries_match_one_call(orc):
+@pytest.mark.parametrize("d,b", [(128, 4), (64, 3)])
+def test_prepared_queries_match_one_call(orc, d, b):
     """tq_attn_prepare + tq_attn_logits_prepared == tq_attn_logits, and one
-    prepared workspace serves two caches."""
-    d, b = 128, 4
+    prepared workspace serves two caches (d = 64: folded operands)."""
     ctx, pi, s, c = ctx_for(orc, d, b)
     n = 700
     P, N = workloads.random_records(2 * n, tq.tq_record_words(d, b), 5, DEV)
@@ -295,6 +299,7 @@ def _step_case(orc, d, b, mse, dtype, n_heads, n_tok, L, n_q, n_kv):
     (128, 3, False, torch.float32, 7, 70, 2, 16, 1),       # several tiles, G = 16
     (128, 2, True, torch.bfloat16, 24, 3, 3, 8, 8),        # MSE-only records
     (200, 4, False, torch.float32, 5, 9, 2, 8, 2),          # other d: separate launches
+    (64, 3, False, torch.bfloat16, 16, 2, 4, 8, 2),         # d = 64: folded preparation
 ])
 def test_decode_step_prepare_matches_separate_calls(orc, d, b, mse, dtype, n_heads, n_tok, L,
                                                     n_q, n_kv):
@@ -446,6 +451,7 @@ def softmax_rows(x):
     (200, 4, 8, 2, [333, 70]),
     (1536, 2, 4, 1, [150]),
     (64, 4, 8, 1, [513, 3]),                  # d = 64, G = 8 (two row blocks)
+    (64, 3, 8, 2, [300, 700]),                # d = 64, G = 4 (unfolded preparation)
 ])
 def test_attn_decode_parity(orc, d, b, n_q, n_kv, lens):
     say("attn decode", d, b, n_q, n_kv, lens)
