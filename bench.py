@@ -371,6 +371,12 @@ def run_split(args):
     logits = torch.empty((N_Q, L * N_TOK), dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(D)
     reps = max(10, min(args.steps, 50))
+    # attention weights for the value side (the packed keys stand in for
+    # values: same record format and size)
+    g = workloads.gen(0, workloads.STREAM_Q, dev)
+    pw = torch.softmax(torch.randn((N_Q, L * N_TOK), generator=g, device=dev).view(N_Q, L, N_TOK),
+                       dim=2).view(N_Q, L * N_TOK).contiguous()
+    out = torch.empty((L, N_Q, D), device=dev)
 
     def inst(b, seed):
         pi, s = tq.tq_make_rotation(DH, seed)
@@ -431,6 +437,15 @@ def run_split(args):
             one_call()
         torch.cuda.synchronize()
         c_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ows = tq.workspace(tq.tq_split_attn_output_workspace_bytes(hi, lo, L, N_Q, N_KV, N_TOK),
+                           dev)
+
+        def vout():
+            tq.tq_split_attn_output(hi, lo, pw, L * N_TOK, L, N_Q, hp, hn, lp, ln, N_KV,
+                                    L * N_TOK, seq_start, seq_len, N_TOK, out, N_Q * D, ows)
+
+        vout()
+        o_ms, o_med = events(vout, reps)
         rec = (DH * bh // 8 + 4) + (DH * bl // 8 + 4)
         alg = n_rec * rec + N_Q * L * N_TOK * 4
         bits = (DH * bh + DH * bl) / D
@@ -442,10 +457,13 @@ def run_split(args):
                          "unit": "GB/s", "frac": alg / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": None, "alg_bytes_per_launch": alg,
                          "kernel_ms_mean": s_ms, "kernel_ms_median": s_med},
-            "quantize_vec_per_s": n_rec / (f_ms * 1e-3), "quantize_ms": f_ms}
+            "quantize_vec_per_s": n_rec / (f_ms * 1e-3), "quantize_ms": f_ms,
+            "attn_output": {"ms_mean": o_ms, "ms_median": o_med,
+                            "GB_per_s": alg / (o_ms * 1e-3) / 1e9,
+                            "hbm_frac": alg / (o_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
         hi.close()
         lo.close()
-        del hp, lp, hn, ln, ws
+        del hp, lp, hn, ln, ws, ows
     return _line(args, "packed-key attention logits/sec at fractional bit widths (channel split)",
                  res["2.5"]["logits_per_s"], "logits/s",
                  {"workload": f"llama-3.1-8b decode layer x {L} layer caches (32 q / 8 kv heads, "

@@ -209,6 +209,8 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
   const int gq = lane >> 4, n = lane & 15;
   // 3. slices of 4 words; the next slice is loaded while this one computes
   VaccSlice<NB> sl = first;
+  const int nsplit = W <= 2 ? 2 : 1;          // waves per word (token halves)
+  __shared__ float xch[2][2][2][64];          // [word][cb][code, sign][lane]
   for (int w0 = 0; w0 < W; w0 += 4) {
     __syncthreads();            // A operands written / previous slice consumed
 #pragma unroll
@@ -220,75 +222,101 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
     }
     __syncthreads();
     if (w0 + 4 < W) vacc_load_slice<NB>(planes, nt, W, w0 + 4, sl);
-    const int w = w0 + wave;
-    if (w >= W) continue;
-    v4i G[2][NV], S[2];
-    // one 128-token block; the first starts the accumulators from an inline
-    // zero operand instead of zeroed registers (a chunk with no tokens has
-    // zero bits and weights, so running it is harmless)
-    auto block = [&](int b, auto first_c) {
-      constexpr bool FIRST = decltype(first_c)::value;
-      const v4i zero = {0, 0, 0, 0};
-      uint32_t X0[NB], X1[NB];
+    // word of this wave; with at most two words per record the other waves
+    // are not idle: a second wave per word takes tokens 128..255 and the two
+    // partial sums meet in LDS (nsplit = 2)
+    const int wl = nsplit == 2 ? wave % W : wave;       // word within the slice
+    const int bh = nsplit == 2 ? wave / W : 0;          // first 128-token block
+    const int w = w0 + wl;
+    const bool active = w < W && bh < nsplit;
+    float pc[2] = {0.f, 0.f}, ps[2] = {0.f, 0.f};       // scaled code / sign sums
+    if (active) {
+      v4i G[2][NV], S[2];
+      // one 128-token block; the first starts the accumulators from an inline
+      // zero operand instead of zeroed registers (a block with no tokens has
+      // zero bits and weights, so running it is harmless)
+      auto block = [&](int b, auto first_c) {
+        constexpr bool FIRST = decltype(first_c)::value;
+        const v4i zero = {0, 0, 0, 0};
+        uint32_t X0[NB], X1[NB];
 #pragma unroll
-      for (int p = 0; p < NB; ++p) {
-        const uint32_t* row = wordsT + (wave * NB + p) * kVChunk + 128 * b;
-        const uint32_t t1 = transpose32(row[lane], tl);
-        const uint32_t t2 = transpose32(row[64 + lane], tl);
-        const auto r = __builtin_amdgcn_permlane16_swap(t1, t2, false, false);
-        X0[p] = r[0];           // coordinates 32w + n, token groups 0, 2, 1, 3
-        X1[p] = r[1];           // coordinates 32w + 16 + n
-      }
-      const v4i* ab = aops + b * 4 * 64;
-      v4i Ac[2], As[2];
+        for (int p = 0; p < NB; ++p) {
+          const uint32_t* row = wordsT + (wl * NB + p) * kVChunk + 128 * b;
+          const uint32_t t1 = transpose32(row[lane], tl);
+          const uint32_t t2 = transpose32(row[64 + lane], tl);
+          const auto r = __builtin_amdgcn_permlane16_swap(t1, t2, false, false);
+          X0[p] = r[0];           // coordinates 32w + n, token groups 0, 2, 1, 3
+          X1[p] = r[1];           // coordinates 32w + 16 + n
+        }
+        const v4i* ab = aops + b * 4 * 64;
+        v4i Ac[2], As[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        Ac[h] = ab[h * 64 + lane];
-        if constexpr (!MSE) As[h] = ab[(2 + h) * 64 + lane];
-      }
+        for (int h = 0; h < 2; ++h) {
+          Ac[h] = ab[h * 64 + lane];
+          if constexpr (!MSE) As[h] = ab[(2 + h) * 64 + lane];
+        }
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const uint32_t* X = cb ? X1 : X0;
+#pragma unroll
+          for (int m = 0; m < NV; ++m) {
+            uint32_t u = 0u;
+#pragma unroll
+            for (int p = 0; p < CP; ++p)
+              if ((walsh_mask<CP>(m) >> p) & 1) u ^= X[p];
+            G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[0], bit_lanes(u, 0),
+                                                             FIRST ? zero : G[cb][m], 0, 0, 0);
+            G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[1], bit_lanes(u, 1), G[cb][m], 0, 0, 0);
+          }
+          if constexpr (!MSE) {
+            S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[0], bit_lanes(X[NB - 1], 0),
+                                                          FIRST ? zero : S[cb], 0, 0, 0);
+            S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[1], bit_lanes(X[NB - 1], 1), S[cb], 0, 0, 0);
+          }
+        }
+      };
+      block(bh, std::true_type{});
+      for (int b = bh + nsplit; b * 128 < nt; b += nsplit) block(b, std::false_type{});
+      // lane (g, n): head g at coordinate 32w + 16cb + n
+      const float sc0 = ldexpf(1.f, -s_e[gq]);
+      const float sc1 = MSE ? 0.f : ldexpf(2.f, -s_e[4 + gq]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const uint32_t* X = cb ? X1 : X0;
+        float code = 0.f;
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-          uint32_t u = 0u;
-#pragma unroll
-          for (int p = 0; p < CP; ++p)
-            if ((walsh_mask<CP>(m) >> p) & 1) u ^= X[p];
-          G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[0], bit_lanes(u, 0),
-                                                           FIRST ? zero : G[cb][m], 0, 0, 0);
-          G[cb][m] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ac[1], bit_lanes(u, 1), G[cb][m], 0, 0, 0);
-        }
-        if constexpr (!MSE) {
-          S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[0], bit_lanes(X[NB - 1], 0),
-                                                        FIRST ? zero : S[cb], 0, 0, 0);
-          S[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[1], bit_lanes(X[NB - 1], 1), S[cb], 0, 0, 0);
-        }
+        for (int m = 0; m < NV; ++m) code = fmaf(cf.wm2[m], limbs_to_float(G[cb][m]), code);
+        pc[cb] = code * sc0;
+        if constexpr (!MSE) ps[cb] = limbs_to_float(S[cb]) * sc1;
       }
-    };
-    block(0, std::true_type{});
-    for (int b = 1; b * 128 < nt; ++b) block(b, std::false_type{});
-    if constexpr (MSE) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) S[cb] = (v4i){0, 0, 0, 0};
     }
-    // lane (g, n): head g at coordinate 32w + 16cb + n
-    const float sc0 = ldexpf(1.f, -s_e[gq]);
-    const float sc1 = MSE ? 0.f : ldexpf(2.f, -s_e[4 + gq]);
+    if (nsplit == 2) {                    // uniform: W is the same for the block
+      if (active && bh == 1)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float code = 0.f;
+        for (int cb = 0; cb < 2; ++cb) {
+          xch[wl][cb][0][lane] = pc[cb];
+          xch[wl][cb][1][lane] = ps[cb];
+        }
+      __syncthreads();
+      if (active && bh == 0)
 #pragma unroll
-      for (int m = 0; m < NV; ++m) code = fmaf(cf.wm2[m], limbs_to_float(G[cb][m]), code);
-      const int j = 32 * w + 16 * cb + n;
-      float v0 = fmaf(code, sc0, cf.c0 * s_sum[gq]);
-      float v1 = MSE ? 0.f : fmaf(limbs_to_float(S[cb]), sc1, -s_sum[4 + gq]);
-      if (accumulate) {         // this block's own partial from an earlier call
-        v0 += dst[gq * Dp + j];
-        v1 += dst[(4 + gq) * Dp + j];
+        for (int cb = 0; cb < 2; ++cb) {
+          pc[cb] += xch[wl][cb][0][lane];
+          ps[cb] += xch[wl][cb][1][lane];
+        }
+    }
+    if (active && bh == 0) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int j = 32 * w + 16 * cb + n;
+        float v0 = pc[cb] + cf.c0 * s_sum[gq];
+        float v1 = MSE ? 0.f : ps[cb] - s_sum[4 + gq];
+        if (accumulate) {         // this block's own partial from an earlier call
+          v0 += dst[gq * Dp + j];
+          v1 += dst[(4 + gq) * Dp + j];
+        }
+        dst[gq * Dp + j] = v0;
+        dst[(4 + gq) * Dp + j] = v1;
       }
-      dst[gq * Dp + j] = v0;
-      dst[(4 + gq) * Dp + j] = v1;
     }
   }
 }
