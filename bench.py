@@ -286,7 +286,7 @@ def main():
                                "layer caches per step",
                    "layers_per_step": L, "cached_tokens": N_TOK, "head_dim": D, "bits": B,
                    "q_heads": N_Q, "kv_heads": N_KV, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,false,4,0>",
+        "roofline": {"bound": "hbm", "kernel": "attn_logits_res_kernel<4,false,4,0,false>",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic(PROFILE_LOGITS, LOGIT_SOURCES),
@@ -452,7 +452,7 @@ def run_split(args):
         res[f"{bits:g}"] = {
             "b_hi": bh, "b_lo": bl, "record_pair_bytes": rec,
             "logits_per_s": N_Q * L * N_TOK / (c_ms * 1e-3), "call_ms_mean": c_ms,
-            "roofline": {"bound": "hbm", "kernel": f"attn_logits_res_kernel<{bh},false,4,{bl}>",
+            "roofline": {"bound": "hbm", "kernel": f"attn_logits_res_kernel<{bh},false,4,{bl},true>",
                          "achieved": alg / (s_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": alg / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": None, "alg_bytes_per_launch": alg,
