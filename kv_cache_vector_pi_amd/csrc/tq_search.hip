@@ -254,8 +254,12 @@ struct SearchArgs {
 template <int NB, bool MSE>
 __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;         // code planes
-  constexpr int NA = MSE ? 2 : 4;               // staged query arrays
-  __shared__ __align__(16) _Float16 As[4][kQT * kLdsRow];
+  // staged query arrays: QR hi, QR lo and (alpha QP) hi.  The sketch term
+  // alpha gamma <QP, s> is a small part of a score, so its fp16 rounding of
+  // QP (2^-12 relative) stays ~1e-4 of the scores' rms; (alpha QP) lo is not
+  // used.  The code term keeps hi/lo products (2^-22).
+  constexpr int NA = MSE ? 2 : 3;
+  __shared__ __align__(16) _Float16 As[NA][kQT * kLdsRow];
   __shared__ __align__(16) _Float16 Bs[3][kRT * kLdsRow];
   __shared__ float thr_s[kQT];
   __shared__ uint32_t ctab_s[kMaxK];
@@ -335,7 +339,7 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
     if (w + 1 < a.W) load_word(w + 1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      v8h A[2][4], B[2][3];
+      v8h A[2][NA], B[2][3];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int off = (64 * wq + 32 * qb + col) * kLdsRow + 16 * kk + 8 * hh;
@@ -356,10 +360,8 @@ __global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
-          if constexpr (!MSE) {
+          if constexpr (!MSE)
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][3], B[rb][2], c, 0, 0, 0);
-          }
           acc[qb][rb] = c;
         }
     }
