@@ -395,44 +395,68 @@ __device__ inline void sum_chunk_partials(const float* part, int n_chunk, int r0
 }
 
 // out[i] = sum_j Pi[j][i] arot[j] + alpha sum_j S[j][i] ask[j]  (i < d; the
-// second sum only when qjl), with Pi and S row-major fp32 [d][d].
+// second sum only when qjl), with Pi and S row-major fp32 [d][d].  Threads
+// split as NI = min(d / 4, 256) lanes over float4 groups of outputs x 256 / NI
+// groups over j (4 independent float4 row loads per matrix in flight), met in
+// LDS `red` (>= 2048 floats); d is a multiple of 8, so 4 | d, rows are 16-byte
+// aligned.
 __device__ inline void apply_transforms(const float* pi32, const float* s32, int d, bool qjl,
                                         float alpha, const float* arot, const float* ask,
                                         float* red, float* out) {
   const int tid = threadIdx.x;
-  const int NI = min(d, 256), TT = 256 / NI;
+  const int D4 = d / 4;
+  const int NI = min(D4, 256), TT = 256 / NI;
   const int li = tid % NI, tg = tid / NI;
-  for (int i0 = 0; i0 < d; i0 += NI) {
-    const int i = i0 + li;
-    float o1[4] = {0.f, 0.f, 0.f, 0.f}, o2[4] = {0.f, 0.f, 0.f, 0.f};
-    if (tg < TT && i < d) {
+  float4* red4 = (float4*)red;                  // [TT][NI]
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fma4 = [](float f, float4 v, float4 acc) {
+    return make_float4(fmaf(f, v.x, acc.x), fmaf(f, v.y, acc.y), fmaf(f, v.z, acc.z),
+                       fmaf(f, v.w, acc.w));
+  };
+  auto add4 = [](float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  };
+  for (int i0 = 0; i0 < D4; i0 += NI) {
+    const int i4 = i0 + li;
+    float4 o1[4] = {z4, z4, z4, z4}, o2[4] = {z4, z4, z4, z4};
+    if (tg < TT && i4 < D4) {
+      const float4* P = (const float4*)pi32 + i4;
+      const float4* S = (const float4*)s32 + i4;
       int j = tg;
       for (; j + 3 * TT < d; j += 4 * TT) {
+        float4 vp[4], vs[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int jj = j + u * TT;
-          o1[u] = fmaf(pi32[(int64_t)jj * d + i], arot[jj], o1[u]);
-          if (qjl) o2[u] = fmaf(s32[(int64_t)jj * d + i], ask[jj], o2[u]);
+          vp[u] = P[(int64_t)(j + u * TT) * D4];
+          if (qjl) vs[u] = S[(int64_t)(j + u * TT) * D4];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          o1[u] = fma4(arot[j + u * TT], vp[u], o1[u]);
+          if (qjl) o2[u] = fma4(ask[j + u * TT], vs[u], o2[u]);
         }
       }
       for (; j < d; j += TT) {
-        o1[0] = fmaf(pi32[(int64_t)j * d + i], arot[j], o1[0]);
-        if (qjl) o2[0] = fmaf(s32[(int64_t)j * d + i], ask[j], o2[0]);
+        o1[0] = fma4(arot[j], P[(int64_t)j * D4], o1[0]);
+        if (qjl) o2[0] = fma4(ask[j], S[(int64_t)j * D4], o2[0]);
       }
     }
-    const float v = fmaf(alpha, (o2[0] + o2[1]) + (o2[2] + o2[3]), (o1[0] + o1[1]) + (o1[2] + o1[3]));
-    if (TT == 1) {
-      if (tg == 0 && i < d) out[i] = v;
-    } else {
-      red[tid] = v;
-      __syncthreads();
-      if (tid < NI) {
-        float t = 0.f;
-        for (int q = 0; q < TT; ++q) t += red[q * NI + tid];
-        out[i] = t;
-      }
-      __syncthreads();
+    const float4 s1 = add4(add4(o1[0], o1[1]), add4(o1[2], o1[3]));
+    const float4 s2 = add4(add4(o2[0], o2[1]), add4(o2[2], o2[3]));
+    const float4 v = make_float4(fmaf(alpha, s2.x, s1.x), fmaf(alpha, s2.y, s1.y),
+                                 fmaf(alpha, s2.z, s1.z), fmaf(alpha, s2.w, s1.w));
+    if (tg < TT) red4[tg * NI + li] = v;   // threads past TT * NI only idle
+    __syncthreads();
+    if (tid < NI && i0 + tid < D4) {
+      float4 t = z4;
+      for (int q = 0; q < TT; ++q) t = add4(t, red4[q * NI + tid]);
+      const int i = 4 * (i0 + tid);
+      out[i] = t.x;
+      out[i + 1] = t.y;
+      out[i + 2] = t.z;
+      out[i + 3] = t.w;
     }
+    __syncthreads();
   }
 }
 
