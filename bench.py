@@ -741,9 +741,12 @@ def run_search(args):
     for b in _bits(args, [2, 4], [2, 3]):
         ctx = _common(args, d, b)
         planes, norms = tq.alloc_records(n_db, d, b, dev)
+        # blocked products with a workspace at large d (none needed at d = 200)
+        qws_bytes = tq.tq_quantize_workspace_bytes(ctx, n_db)
+        qws = tq.workspace(qws_bytes, dev) if qws_bytes else None
 
         def quant():
-            tq.tq_quantize_kv(ctx, db, planes, norms)
+            tq.tq_quantize_kv_ws(ctx, db, planes, norms, qws)
 
         for _ in range(max(1, args.warmup)):
             quant()

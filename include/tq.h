@@ -183,6 +183,28 @@ TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtyp
                                 int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                                 int64_t dst_stride_head, int64_t dst_token0, void* stream);
 
+/* tq_quantize_kv with a caller workspace, for large head dimensions.  For d
+ * above 480 (32-coordinate words >= 16) the quantization runs as two blocked
+ * matrix products (Y = Pi x, then Z = M r) over tiles of 128 vectors, the
+ * residual r kept in `workspace` between them; the tables are then read once
+ * per 128 vectors instead of once per 16.  Arguments, record indexing and
+ * results as tq_quantize_kv (codes and signs equal up to accumulation-order
+ * rounding at decision boundaries, within the parity margins).  Rows are
+ * processed in chunks of as many 128-row tiles as the workspace holds.
+ * workspace: device memory, 256-byte aligned, at least
+ * tq_quantize_workspace_bytes(ctx, 1) bytes (one tile); the bytes for n_rows
+ * rows at once (capped at 65536 rows) are tq_quantize_workspace_bytes(ctx,
+ * n_rows).  Smaller d: the tq_quantize_kv path, workspace unused (may be
+ * NULL).
+ * Errors: as tq_quantize_kv; TQ_ERR_INVALID_ARG also for a missing, too small
+ * or misaligned workspace when d needs one. */
+TQ_API size_t tq_quantize_workspace_bytes(const tq_ctx* ctx, int64_t n_rows);
+TQ_API tq_status tq_quantize_kv_ws(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                   int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                   int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                                   int64_t dst_stride_head, int64_t dst_token0, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* tq_quantize_kv with a destination per input token (turboquant.net
  * pseudo-code, "integrate into Transformer attention": each step's new keys
  * and values are quantized into the cache), for appends that land at

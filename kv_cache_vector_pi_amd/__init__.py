@@ -34,7 +34,8 @@ EXPORTS = [
     "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare", "tq_quantize_kv_slots",
     "tq_split_quantize_kv", "tq_split_dequantize", "tq_split_attn_logits_workspace_bytes",
     "tq_split_attn_logits", "tq_split_attn_output_workspace_bytes", "tq_split_attn_output",
-    "tq_split_attn_prepare", "tq_split_attn_logits_prepared",
+    "tq_split_attn_prepare", "tq_split_attn_logits_prepared", "tq_quantize_workspace_bytes",
+    "tq_quantize_kv_ws",
 ]
 
 
@@ -76,6 +77,9 @@ _sig("tq_decode_step_prepare", _i32, [_P, _P, _P, _i32, _i64, _i32, _i64, _i64, 
 _sig("tq_ctx_dim", _i32, [_P])
 _sig("tq_ctx_bits", _i32, [_P])
 _sig("tq_quantize_kv", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P])
+_sig("tq_quantize_workspace_bytes", _sz, [_P, _i64])
+_sig("tq_quantize_kv_ws", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _i64, _i64, _P,
+                                 _sz, _P])
 _sig("tq_quantize_kv_slots", _i32, [_P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _i64, _P])
 _sig("tq_dequantize", _i32, [_P, _P, _P, _i64, _P, _i64, _P])
 _sig("tq_split_quantize_kv", _i32, [_P, _P, _P, _i32, _i64, _i32, _i64, _i64, _P, _P, _P, _P,
@@ -262,6 +266,25 @@ def tq_quantize_kv(ctx, x, planes, norms, n_tokens=None, n_heads=None, x_stride_
                              x_stride_head, _ptr(planes), _ptr(norms), dst_stride_head,
                              dst_token0, _stream(stream))
     _check(st, "tq_quantize_kv")
+
+
+def tq_quantize_workspace_bytes(ctx, n_rows):
+    return _lib.tq_quantize_workspace_bytes(ctx.handle, n_rows)
+
+
+def tq_quantize_kv_ws(ctx, x, planes, norms, workspace, n_tokens=None, n_heads=None,
+                      x_stride_token=None, x_stride_head=None, dst_stride_head=None,
+                      dst_token0=0, stream=None):
+    """tq_quantize_kv with a workspace (blocked products at large d; see tq.h)."""
+    dt, n_tokens, n_heads, x_stride_token, x_stride_head = _quant_input(
+        x, n_tokens, n_heads, x_stride_token, x_stride_head)
+    if dst_stride_head is None:
+        dst_stride_head = n_tokens
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.tq_quantize_kv_ws(ctx.handle, _ptr(x), dt, n_tokens, n_heads, x_stride_token,
+                                x_stride_head, _ptr(planes), _ptr(norms), dst_stride_head,
+                                dst_token0, _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "tq_quantize_kv_ws")
 
 
 def tq_quantize_kv_slots(ctx, x, slots, planes, norms, dst_stride_head, n_tokens=None,

@@ -15,6 +15,7 @@ LIB = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["tq_host.cpp", "tq_logits.hip", "tq_quantize.hip", "tq_quantize128.hip",
+           "tq_quantize_big.hip",
            "tq_search.hip", "tq_attn_out.hip",
            "tq_decode.hip", "tq_step.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")

@@ -531,6 +531,43 @@ TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtyp
   return ok();
 }
 
+TQ_API size_t tq_quantize_workspace_bytes(const tq_ctx* ctx, int64_t n_rows) {
+  if (!ctx || n_rows < 0) return 0;
+  return tq::quantize_big_workspace_bytes(ctx, n_rows);
+}
+
+TQ_API tq_status tq_quantize_kv_ws(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                   int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                   int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                                   int64_t dst_stride_head, int64_t dst_token0, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const char* fn = "tq_quantize_kv_ws";
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+  bool empty;
+  const tq_status st = check_quantize(fn, ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                      x_stride_head, planes, norms, dst_stride_head, dst_token0,
+                                      nullptr, &empty);
+  if (st != TQ_OK) return st;
+  if (empty) return ok();
+  hipError_t e;
+  if (tq::quantize_big_applies(ctx)) {
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < tq::quantize_big_workspace_bytes(ctx, 1))
+      return fail(TQ_ERR_INVALID_ARG,
+                  "%s: workspace must be 256-byte aligned and hold at least %zu bytes", fn,
+                  tq::quantize_big_workspace_bytes(ctx, 1));
+    e = tq::launch_quantize_big(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                x_stride_head, planes, norms, dst_stride_head, dst_token0,
+                                workspace, workspace_bytes, (hipStream_t)stream);
+  } else {
+    e = tq::launch_quantize(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
+                            planes, norms, dst_stride_head, dst_token0, nullptr,
+                            (hipStream_t)stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "tq_quantize_kv_ws: launch");
+  return ok();
+}
+
 TQ_API tq_status tq_quantize_kv_slots(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                                       int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                                       int64_t x_stride_head, const int64_t* slots,

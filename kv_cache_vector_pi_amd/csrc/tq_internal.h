@@ -60,6 +60,15 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
                            uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
                            int64_t dst_token0, const int64_t* slots, hipStream_t stream);
 
+// Large head dimensions (Dp >= 512): blocked products with a workspace.
+bool quantize_big_applies(const tq_ctx* ctx);
+size_t quantize_big_workspace_bytes(const tq_ctx* ctx, int64_t n_rows);
+hipError_t launch_quantize_big(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                               int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                               int64_t dst_stride_head, int64_t dst_token0, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,

@@ -352,7 +352,9 @@ def test_vector_search_1m(orc, d, b):
     db, qs = wl["db"], wl["queries"]
     n_db, n_q = db.shape[0], qs.shape[0]
     planes, norms = tq.alloc_records(n_db, d, b, DEV)
-    tq.tq_quantize_kv(ctx, db, planes, norms)
+    # as bench.py: the workspace form (blocked products at d = 1536)
+    nb = tq.tq_quantize_workspace_bytes(ctx, n_db)
+    tq.tq_quantize_kv_ws(ctx, db, planes, norms, tq.workspace(nb, DEV) if nb else None)
     torch.cuda.synchronize()
     rng = np.random.default_rng(4)
     rows = rng.choice(n_db, 256, replace=False)

@@ -170,6 +170,9 @@ def test_hot_path_rejects_null_context(tq):
     assert L.tq_split_attn_logits_prepared(None, None, None, 0, 1, 32, None, None, None, None, 8,
                                            0, None, None, 1, 1.0, None, 0, None) == \
         tq.TQ_ERR_INVALID_ARG
+    assert L.tq_quantize_kv_ws(None, None, 0, 1, 1, 128, 0, None, None, 1, 0, None, 0, None) == \
+        tq.TQ_ERR_INVALID_ARG
+    assert L.tq_quantize_workspace_bytes(None, 100) == 0
     assert L.tq_split_attn_logits_workspace_bytes(None, None, 1, 32, 8) == 0
     assert L.tq_split_attn_output_workspace_bytes(None, None, 1, 32, 8, 100) == 0
     assert L.tq_attn_logits_workspace_bytes(None, 1, 32, 8) == 0
