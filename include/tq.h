@@ -185,12 +185,12 @@ TQ_API tq_status tq_quantize_kv(const tq_ctx* ctx, const void* x, int32_t x_dtyp
 
 /* tq_quantize_kv with a caller workspace, for large head dimensions.  For d
  * above 480 (32-coordinate words >= 16) the quantization runs as two blocked
- * matrix products (Y = Pi x, then Z = M r) over tiles of 128 vectors, the
+ * matrix products (Y = Pi x, then Z = M r) over tiles of 256 vectors, the
  * residual r kept in `workspace` between them; the tables are then read once
- * per 128 vectors instead of once per 16.  Arguments, record indexing and
+ * per 256 vectors instead of once per 16.  Arguments, record indexing and
  * results as tq_quantize_kv (codes and signs equal up to accumulation-order
  * rounding at decision boundaries, within the parity margins).  Rows are
- * processed in chunks of as many 128-row tiles as the workspace holds.
+ * processed in chunks of as many 256-row tiles as the workspace holds.
  * workspace: device memory, 256-byte aligned, at least
  * tq_quantize_workspace_bytes(ctx, 1) bytes (one tile); the bytes for n_rows
  * rows at once (capped at 65536 rows) are tq_quantize_workspace_bytes(ctx,

@@ -8,10 +8,10 @@
 // vectors re-read all of Pi and M (19 MB at d = 1536) from L2 / MALL.  Here:
 //
 //  1. norm kernel: nu = ||x||, the power-of-two scale 2^-e of each row.
-//  2. Y kernel: a workgroup owns 128 vectors x 4 words (128 coordinates, one
+//  2. Y kernel: a workgroup owns 256 vectors x 4 words (128 coordinates, one
 //     word per wave) and loops over K in blocks of 32 coordinates: the x block
 //     (scaled, fp16 hi/lo) is staged in LDS and shared by the 4 waves, each
-//     wave streams its 32 rows of Pi.  Pi is read once per 128 vectors instead
+//     wave streams its 32 rows of Pi.  Pi is read once per 256 vectors instead
 //     of once per 16.  Epilogue: codes (written into the records), the
 //     residual r = y - c[idx] as fp16 hi/lo into the workspace, and the
 //     per-word partial sums of r^2.
@@ -30,7 +30,8 @@
 namespace tq {
 namespace {
 
-constexpr int kBM = 128;     // vectors per tile: 4 column blocks of 32
+constexpr int kBM = 256;     // vectors per tile: 8 column blocks of 32
+constexpr int kCB = kBM / 32;
 constexpr int kLdk = 40;     // LDS row stride of a 32-coordinate block, in halves
 
 struct BigArgs {
@@ -51,7 +52,23 @@ struct BigArgs {
   _Float16* r_hi;            // [n_rows][Dp]
   _Float16* r_lo;
   float* g2;                 // [n_rows][W] partial sums of r^2 (unit space)
+  int nvb, nwb;              // vector blocks (kBM rows) and word blocks (4 words)
 };
+
+// The Y and Z grids are 1-D: workgroup L runs on XCD L mod 8 (round-robin
+// dispatch), and XCD x takes the vector blocks vb = 8 tx + x in order, each
+// with all of its word blocks in turn.  The workgroups that share a block of
+// x then run together on one XCD and read it from that XCD's L2; the table
+// comes from the MALL.  In x-fastest 2-D order every x tile was fetched from
+// memory once per word block (12 times at d = 1536), which cost 25% more
+// time.  False for the padding workgroups (vb >= nvb), which exit at once.
+__device__ inline bool big_tile(const BigArgs& a, int& vb, int& wb) {
+  const int L = (int)blockIdx.x, s = L >> 3;
+  const int tx = s / a.nwb;
+  wb = s - tx * a.nwb;
+  vb = 8 * tx + (L & 7);
+  return vb < a.nvb;
+}
 
 __device__ inline void row_of(const BigArgs& a, int64_t f, int64_t& xoff, int64_t& rec) {
   const int64_t h = f / a.n_tokens, t = f - h * a.n_tokens;
@@ -110,63 +127,82 @@ __global__ void __launch_bounds__(256) bigq_norm_kernel(BigArgs a) {
 // (this wave's word), columns = vectors 32 cb .. 32 cb + 31 of the tile.
 // Lane (col, hh) holds rows 8 (i / 4) + 4 hh + i % 4 of column col.
 // ZSRC: B operand from the workspace residual (fp16 hi/lo) instead of x.
+// One LDS buffer per block of 32 coordinates: two barriers per block, the
+// next block's x (or r) and table fragments load into registers meanwhile.
 template <bool BF16, bool ZSRC>
 __device__ __forceinline__ void big_product(const BigArgs& a, int vb0, int w, bool wok,
-                                            const float4* scs, _Float16 (*bh)[kBM * kLdk],
-                                            _Float16 (*bl)[kBM * kLdk], v16f (&acc)[4]) {
+                                            const float4* scs, _Float16* bh, _Float16* bl,
+                                            v16f (&acc)[kCB]) {
   constexpr bool LO = ZSRC || !BF16;       // B has a lo part: 3 passes
+  constexpr int NP = kBM / 128;            // staged vectors per thread
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = lane & 31, hh = lane >> 5;
-  // staging role: vector sv of the tile, coordinates 16 sh .. 16 sh + 15 of a block
-  const int sv = tid >> 1, sh = tid & 1;
-  const bool svok = vb0 + sv < a.n_rows;
-  int64_t sxoff = 0, srec = 0;
-  if (!ZSRC && svok) row_of(a, a.f0 + vb0 + sv, sxoff, srec);
-  const float ssc = scs[sv].x;
-  const int64_t rbase = (int64_t)(vb0 + sv) * a.Dp;
-  // x (or r) of one block in registers: 16 elements
-  float xr[16];
-  v8h rh2[2], rl2[2];
+  // staging role: vectors tid / 2 + 128 p of the tile, coordinates
+  // 16 sh .. 16 sh + 15 of a block
+  const int sh = tid & 1;
+  bool svok[NP];
+  int64_t sxoff[NP], rbase[NP];
+  float ssc[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int sv = (tid >> 1) + 128 * p;
+    svok[p] = vb0 + sv < a.n_rows;
+    sxoff[p] = 0;
+    int64_t srec;
+    if (!ZSRC && svok[p]) row_of(a, a.f0 + vb0 + sv, sxoff[p], srec);
+    ssc[p] = scs[sv].x;
+    rbase[p] = (int64_t)(vb0 + sv) * a.Dp;
+  }
+  // x (or r) of one block in registers: 16 elements per staged vector
+  float xr[NP][16];
+  v8h rh2[NP][2], rl2[NP][2];
   auto fetch = [&](int kb) {
     const int k0 = 32 * kb + 16 * sh;
-    if constexpr (ZSRC) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        rh2[c] = svok ? *(const v8h*)(a.r_hi + rbase + k0 + 8 * c) : (v8h){};
-        rl2[c] = svok ? *(const v8h*)(a.r_lo + rbase + k0 + 8 * c) : (v8h){};
-      }
-    } else {
+    for (int p = 0; p < NP; ++p) {
+      if constexpr (ZSRC) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (svok && k0 + 8 * c < a.d) load8<BF16>(a.x, sxoff + k0 + 8 * c, v);
+        for (int c = 0; c < 2; ++c) {
+          rh2[p][c] = svok[p] ? *(const v8h*)(a.r_hi + rbase[p] + k0 + 8 * c) : (v8h){};
+          rl2[p][c] = svok[p] ? *(const v8h*)(a.r_lo + rbase[p] + k0 + 8 * c) : (v8h){};
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xr[8 * c + e] = v[e];
+        for (int c = 0; c < 2; ++c) {
+          float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (svok[p] && k0 + 8 * c < a.d) load8<BF16>(a.x, sxoff[p] + k0 + 8 * c, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[p][8 * c + e] = v[e];
+        }
       }
     }
   };
-  auto stage = [&](int buf) {
-    _Float16* dh = bh[buf] + sv * kLdk + 16 * sh;
-    _Float16* dl = bl[buf] + sv * kLdk + 16 * sh;
-    if constexpr (ZSRC) {
-      *(v8h*)dh = rh2[0];
-      *(v8h*)(dh + 8) = rh2[1];
-      *(v8h*)dl = rl2[0];
-      *(v8h*)(dl + 8) = rl2[1];
-    } else {
-      v8h hi[2], lo[2];
+  auto stage = [&]() {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float xs = xr[e] * ssc;
-        const _Float16 hv = (_Float16)xs;
-        hi[e >> 3][e & 7] = hv;
-        lo[e >> 3][e & 7] = (_Float16)(xs - (float)hv);
-      }
-      *(v8h*)dh = hi[0];
-      *(v8h*)(dh + 8) = hi[1];
-      if constexpr (LO) {
-        *(v8h*)dl = lo[0];
-        *(v8h*)(dl + 8) = lo[1];
+    for (int p = 0; p < NP; ++p) {
+      const int sv = (tid >> 1) + 128 * p;
+      _Float16* dh = bh + sv * kLdk + 16 * sh;
+      _Float16* dl = bl + sv * kLdk + 16 * sh;
+      if constexpr (ZSRC) {
+        *(v8h*)dh = rh2[p][0];
+        *(v8h*)(dh + 8) = rh2[p][1];
+        *(v8h*)dl = rl2[p][0];
+        *(v8h*)(dl + 8) = rl2[p][1];
+      } else {
+        v8h hi[2], lo[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float xs = xr[p][e] * ssc[p];
+          const _Float16 hv = (_Float16)xs;
+          hi[e >> 3][e & 7] = hv;
+          lo[e >> 3][e & 7] = (_Float16)(xs - (float)hv);
+        }
+        *(v8h*)dh = hi[0];
+        *(v8h*)(dh + 8) = hi[1];
+        if constexpr (LO) {
+          *(v8h*)dl = lo[0];
+          *(v8h*)(dl + 8) = lo[1];
+        }
       }
     }
   };
@@ -182,14 +218,14 @@ __device__ __forceinline__ void big_product(const BigArgs& a, int vb0, int w, bo
     }
   };
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = (v16f){};
+  for (int cb = 0; cb < kCB; ++cb) acc[cb] = (v16f){};
   const int nkb = a.W;                       // Dp = 32 W: blocks of 32 coordinates
   fetch(0);
   load_t(0);
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    stage(buf);
-    __syncthreads();      // block kb staged; block kb - 2's buffer no longer read
+    if (kb > 0) __syncthreads();      // every wave has read block kb - 1
+    stage();
+    __syncthreads();                  // block kb staged
     const v8h ch[2] = {th[0], th[1]}, cl[2] = {tl[0], tl[1]};
     if (kb + 1 < nkb) {
       fetch(kb + 1);      // next block in flight during the MFMAs
@@ -199,14 +235,14 @@ __device__ __forceinline__ void big_product(const BigArgs& a, int vb0, int w, bo
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < kCB; ++cb) {
           const int off = (32 * cb + col) * kLdk + 16 * ks + 8 * hh;
-          const v8h xh = *(const v8h*)(bh[buf] + off);
+          const v8h xh = *(const v8h*)(bh + off);
           v16f c = acc[cb];
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ch[ks], xh, c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(cl[ks], xh, c, 0, 0, 0);
           if constexpr (LO) {
-            const v8h xl = *(const v8h*)(bl[buf] + off);
+            const v8h xl = *(const v8h*)(bl + off);
             c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ch[ks], xl, c, 0, 0, 0);
           }
           acc[cb] = c;
@@ -220,23 +256,25 @@ template <int NB, bool BF16, bool MSE>
 __global__ void __launch_bounds__(256, 2) bigq_y_kernel(BigArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;
   constexpr int K = 1 << CP;
-  __shared__ __align__(16) _Float16 bh[2][kBM * kLdk];
-  __shared__ __align__(16) _Float16 bl[2][kBM * kLdk];
+  __shared__ __align__(16) _Float16 bh[kBM * kLdk];
+  __shared__ __align__(16) _Float16 bl[kBM * kLdk];
   __shared__ float4 scs[kBM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int vb0 = blockIdx.x * kBM;
-  const int w = blockIdx.y * 4 + wave;
+  int vb, wb;
+  if (!big_tile(a, vb, wb)) return;               // uniform over the workgroup
+  const int vb0 = vb * kBM;
+  const int w = wb * 4 + wave;
   const bool wok = w < a.W;
-  if (tid < kBM)
-    scs[tid] = vb0 + tid < a.n_rows ? a.sc[vb0 + tid] : make_float4(1.f, 0.f, 0.f, 0.f);
+  for (int t = tid; t < kBM; t += 256)
+    scs[t] = vb0 + t < a.n_rows ? a.sc[vb0 + t] : make_float4(1.f, 0.f, 0.f, 0.f);
   __syncthreads();
-  v16f acc[4];
+  v16f acc[kCB];
   big_product<BF16, false>(a, vb0, w, wok, scs, bh, bl, acc);
   if (!wok) return;
   const int jb = 32 * w;                           // first coordinate of the word
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const int v = vb0 + 32 * cb + col;             // chunk-local row
     const bool vok = v < a.n_rows;
     const float s = scs[32 * cb + col].y;          // 2^e / nu (0: x = 0)
@@ -301,35 +339,37 @@ __global__ void __launch_bounds__(256, 2) bigq_y_kernel(BigArgs a) {
 // ---- 3. Z = M r, signs, norms ---------------------------------------------
 template <int NB>
 __global__ void __launch_bounds__(256, 2) bigq_z_kernel(BigArgs a) {
-  __shared__ __align__(16) _Float16 bh[2][kBM * kLdk];
-  __shared__ __align__(16) _Float16 bl[2][kBM * kLdk];
+  __shared__ __align__(16) _Float16 bh[kBM * kLdk];
+  __shared__ __align__(16) _Float16 bl[kBM * kLdk];
   __shared__ float4 scs[kBM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int vb0 = blockIdx.x * kBM;
-  const int w = blockIdx.y * 4 + wave;
+  int vb, wb;
+  if (!big_tile(a, vb, wb)) return;               // uniform over the workgroup
+  const int vb0 = vb * kBM;
+  const int w = wb * 4 + wave;
   const bool wok = w < a.W;
-  if (tid < kBM)
-    scs[tid] = vb0 + tid < a.n_rows ? a.sc[vb0 + tid] : make_float4(1.f, 0.f, 0.f, 0.f);
+  for (int t = tid; t < kBM; t += 256)
+    scs[t] = vb0 + t < a.n_rows ? a.sc[vb0 + t] : make_float4(1.f, 0.f, 0.f, 0.f);
   __syncthreads();
   // norms of the tile's vectors: gamma = ||r|| from the per-word partial sums
-  if (blockIdx.y == 0 && tid < kBM && vb0 + tid < a.n_rows) {
-    const int v = vb0 + tid;
+  for (int t = tid; wb == 0 && t < kBM && vb0 + t < a.n_rows; t += 256) {
+    const int v = vb0 + t;
     float s2 = 0.f;
     for (int ww = 0; ww < a.W; ++ww) s2 += a.g2[(int64_t)v * a.W + ww];
-    const float4 sc = scs[tid];
+    const float4 sc = scs[t];
     const float gam = sc.y == 0.f ? 0.f : sqrtf(s2);
     int64_t xoff, rec;
     row_of(a, a.f0 + v, xoff, rec);
     a.norms[rec] = __float_as_uint(sc.w) | ((uint32_t)__half_as_ushort(__float2half_rn(gam)) << 16);
   }
-  v16f acc[4];
+  v16f acc[kCB];
   big_product<false, true>(a, vb0, w, wok, scs, bh, bl, acc);
   if (!wok) return;
   const int jb = 32 * w;
   const uint32_t dmask = a.d - jb >= 32 ? 0xffffffffu : ((1u << (a.d - jb)) - 1u);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < kCB; ++cb) {
     const int v = vb0 + 32 * cb + col;
     uint32_t sb = 0u;
 #pragma unroll
@@ -367,17 +407,18 @@ size_t big_bytes(const tq_ctx* ctx, int64_t rows) {
 
 template <int NB, bool BF16, bool MSE>
 hipError_t launch_big_chunk(BigArgs a, const tq_ctx* ctx, hipStream_t st) {
-  const unsigned nvb = (unsigned)((a.n_rows + kBM - 1) / kBM);
-  const unsigned nwb = (unsigned)((a.W + 3) / 4);
+  a.nvb = (a.n_rows + kBM - 1) / kBM;
+  a.nwb = (a.W + 3) / 4;
+  const dim3 grid((unsigned)(8 * ((a.nvb + 7) / 8) * a.nwb));
   hipLaunchKernelGGL((bigq_norm_kernel<BF16, MSE>), dim3((unsigned)((a.n_rows + 3) / 4)),
                      dim3(256), 0, st, a);
   a.ta_hi = ctx->t.pi_hi;
   a.ta_lo = ctx->t.pi_lo;
-  hipLaunchKernelGGL((bigq_y_kernel<NB, BF16, MSE>), dim3(nvb, nwb), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((bigq_y_kernel<NB, BF16, MSE>), grid, dim3(256), 0, st, a);
   if constexpr (!MSE) {
     a.ta_hi = ctx->t.m_hi;
     a.ta_lo = ctx->t.m_lo;
-    hipLaunchKernelGGL((bigq_z_kernel<NB>), dim3(nvb, nwb), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bigq_z_kernel<NB>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -397,7 +438,7 @@ hipError_t launch_quantize_big(const tq_ctx* ctx, const void* x, int32_t x_dtype
                                int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                                int64_t dst_stride_head, int64_t dst_token0, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  // rows per chunk: the most whole 128-row tiles whose workspace fits
+  // rows per chunk: the most whole kBM-row tiles whose workspace fits
   const BigLayout L1 = big_layout(ctx, 1);
   int64_t chunk = std::min<int64_t>((int64_t)(workspace_bytes / L1.per_row) / kBM * kBM, 65536);
   while (chunk >= kBM && big_bytes(ctx, chunk) > workspace_bytes) chunk -= kBM;
