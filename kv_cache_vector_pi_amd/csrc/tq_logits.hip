@@ -163,21 +163,26 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            0x00020000);
 }
 
+// Cache policy of the record loads: nontemporal.  Each record is read once per
+// launch; on the 32-layer stream (570 MB of records) this measured 2-4% faster
+// than the default policy.
+constexpr int kNT = 2;
+
 template <int NB>
 __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
   if constexpr (NB == 4) {
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNT);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else if constexpr (NB == 3) {
     typedef int v3i __attribute__((ext_vector_type(3)));
-    const v3i v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    const v3i v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, kNT);
     w[0] = v[0]; w[1] = v[1]; w[2] = v[2];
   } else if constexpr (NB == 2) {
     typedef int v2i __attribute__((ext_vector_type(2)));
-    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNT);
     w[0] = v[0]; w[1] = v[1];
   } else {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNT);
   }
 }
 
@@ -306,10 +311,10 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
     for (int u = 0; u < U; ++u) {
       const uint32_t t = (uint32_t)(tl + kTile * u + n);
       buf_group<NB>(rp, t * rec_bytes + goff, gr.wd[u]);
-      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4u, 0, 0);
+      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4u, 0, kNT);
       if constexpr (SPLIT) {
         buf_group<NB2>(rp2, t * rec_bytes2 + goff2, gr.wd2[u]);
-        gr.nr2[u] = __builtin_amdgcn_raw_buffer_load_b32(rn2, t * 4u, 0, 0);
+        gr.nr2[u] = __builtin_amdgcn_raw_buffer_load_b32(rn2, t * 4u, 0, kNT);
       }
     }
   };
