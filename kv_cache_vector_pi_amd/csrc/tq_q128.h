@@ -89,6 +89,19 @@ __device__ inline uint32_t shift_in(uint32_t acc, uint64_t mask) {
   return out;
 }
 
+// Low fp16 parts of a residual pair: fp16(r - hi) for (r0, hi0) and (r1, hi1),
+// hi0 / hi1 the low / high half of h01.  v_fma_mix forms r * 1 - hi in fp32
+// and rounds once to fp16; r - hi is exact in fp32 (hi is r rounded to
+// fp16), so this is the plain conversion of (r - (float)hi) in one
+// instruction per element instead of three.
+__device__ inline uint32_t lo_pair(float r0, float r1, uint32_t h01) {
+  uint32_t out;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(out) : "v"(r0), "v"(h01));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "+v"(out) : "v"(r1), "v"(h01));
+  return out;
+}
+
 // Combine a value with the one in lane l ^ 32 (v_permlane32_swap: with both
 // operands v it returns v[l mod 32] and v[32 + l mod 32] in every lane l).
 __device__ inline uint32_t halves_or(uint32_t v) {
@@ -348,17 +361,17 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     // residual -> LDS as hi/lo fp16 (rows 8j + 4hh .. +3 hold 4 consecutive i)
 #pragma unroll
     for (int j = 0; j < (MSE ? 0 : 4); ++j) {
-      v4h rh, rl;
+      typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+      v4h rh;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float r = rr[4 * j + e];
-        const _Float16 hv = (_Float16)r;
-        rh[e] = hv;
-        rl[e] = (_Float16)(r - (float)hv);
-      }
+      for (int e = 0; e < 4; ++e) rh[e] = (_Float16)rr[4 * j + e];
+      const u2v hb = __builtin_bit_cast(u2v, rh);
+      u2v lb;
+      lb[0] = lo_pair(rr[4 * j], rr[4 * j + 1], hb[0]);
+      lb[1] = lo_pair(rr[4 * j + 2], rr[4 * j + 3], hb[1]);
       const int off = v * kLdx + 32 * wave + 8 * j + 4 * hh;
       *(v4h*)(rh_s + off) = rh;
-      *(v4h*)(rl_s + off) = rl;
+      *(u2v*)(rl_s + off) = lb;
     }
 #pragma unroll
     for (int p = 0; p < CP; ++p) codew[cb][p] = halves_or(spread16(bacc[p], hh));
