@@ -46,7 +46,7 @@ using dev::bit_lanes;
 using dev::walsh_mask;
 
 __global__ void __launch_bounds__(256) attn_prep_kernel(PrepArgs a) {
-  prep_block(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  prep_block<true>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 struct AttnArgs {

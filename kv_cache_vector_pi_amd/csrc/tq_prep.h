@@ -6,6 +6,7 @@
 #pragma once
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "tq_dev.h"
 #include "tq_internal.h"
@@ -51,6 +52,10 @@ __device__ inline float wave_max(float v) {
 // the exact lane order the logit kernels consume.  Slots beyond the GQA
 // group size get zero weights.
 // The work of block (bx, by, bz) of that grid (the kernel body: 256 threads).
+// PREFETCH: load the first batch of table rows before staging the queries
+// (the standalone preparation kernels, where the table reads are cold; the
+// fused decode-step kernel measured no gain and keeps its registers).
+template <bool PREFETCH = false>
 __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, int bz) {
   extern __shared__ float sm[];
   const int Dp = 32 * a.W;
@@ -63,6 +68,19 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
   const int rb = bx / a.n_parts, part = bx - rb * a.n_parts;
   const int h = by, bi = bz;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* tab = part ? a.st : a.pit;
+  const int quad = tid & (nq - 1), jg = tid / nq;    // nq: a power of two <= 64
+  const int jl = (a.d + nj - 1) / nj;
+  const int ja = min(a.d, jg * jl), jb = min(a.d, ja + jl);
+  // PREFETCH: the first batch of this thread's table rows (output chunk 0) is
+  // loaded before the queries are staged, so the two memory round trips
+  // overlap; the accumulation order below is the same either way.
+  float4 t0[PREFETCH ? 16 : 1];
+  const bool pre = PREFETCH && 4 * quad < a.d && ja + 16 <= jb;
+  if constexpr (PREFETCH) if (pre) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) t0[u] = *(const float4*)(tab + 4 * quad + (int64_t)(ja + u) * a.d);
+  }
 
   for (int it = tid; it < 4 * a.d; it += 256) {
     const int hh = it / a.d, j = it - hh * a.d;
@@ -73,11 +91,10 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
   }
   __syncthreads();
   {
-    const float* tab = part ? a.st : a.pit;
-    const int quad = tid & (nq - 1), jg = tid / nq;    // nq: a power of two <= 64
-    const int jl = (a.d + nj - 1) / nj;
-    const int ja = min(a.d, jg * jl), jb = min(a.d, ja + jl);
-    for (int o0 = 0; o0 < Dp; o0 += 4 * nq) {
+    // one chunk of 4 nq outputs; PRE: the first chunk, which starts from the
+    // prefetched rows (a separate instance, so they are dead afterwards)
+    auto chunk = [&](int o0, auto pre_tag) {
+      constexpr bool PRE = decltype(pre_tag)::value;
       const int r = o0 + 4 * quad;                     // multiple of 4; r < d => r + 3 < d
       float acc[4][4];
 #pragma unroll
@@ -94,6 +111,13 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
         };
         const float* tr = tab + r;
         int j = ja;
+        if constexpr (PRE && PREFETCH) {
+          if (pre) {                                   // the prefetched first batch
+#pragma unroll
+            for (int u = 0; u < 16; ++u) fma16(t0[u], *(const float4*)&qv[4 * (ja + u)]);
+            j = ja + 16;
+          }
+        }
         for (; j + 16 <= jb; j += 16) {                // 16 independent row loads in flight
           float4 t[16];
 #pragma unroll
@@ -123,7 +147,13 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
         if (o < Dp) out[(k >> 2) * Dp + o] = v;
       }
       __syncthreads();
+    };
+    int o0 = 0;
+    if constexpr (PREFETCH) {
+      chunk(0, std::true_type{});
+      o0 = 4 * nq;
     }
+    for (; o0 < Dp; o0 += 4 * nq) chunk(o0, std::false_type{});
   }
   // wave hh: max |out| and sum of out for slot hh -> scale and offsets
   char* rbase = a.ws + (((size_t)bi * a.n_kv + h) * a.n_rb + rb) * dev::rb_bytes(a.W, a.nc);
