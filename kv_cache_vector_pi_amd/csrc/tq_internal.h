@@ -75,6 +75,18 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t dst_stride_head, int64_t dst_token0,
                               const int64_t* slots, hipStream_t stream);
 
+// d = 64 as token pairs through the d = 128 kernel: when it applies (even
+// token count, even first record index and head stride, no slots), and the
+// launch.
+bool quantize64_pairs_apply(const tq_ctx* ctx, int64_t n_tokens, int32_t n_heads,
+                            int64_t x_stride_token, int64_t dst_stride_head, int64_t dst_token0,
+                            const int64_t* slots);
+hipError_t launch_quantize64_pairs(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                   int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                   int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                                   int64_t dst_stride_head, int64_t dst_token0,
+                                   hipStream_t stream);
+
 hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, const void* v_new,
                                       int32_t x_dtype, int64_t n_tokens, int32_t n_heads,
                                       int64_t x_stride_token, int64_t x_stride_head,

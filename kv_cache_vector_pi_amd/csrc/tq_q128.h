@@ -22,6 +22,13 @@
 //  * Tiles run over the flattened (head, token) rows of a launch, so many
 //    short heads (one new token per head and layer in decoding) share a
 //    tile; a tile inside one head reads and writes contiguous rows.
+//  * Head dimension 64 (template D = 64) runs the same code on token pairs: a
+//    tile row is two consecutive tokens of one head (coordinates 0..63 the
+//    first, 64..127 the second), waves 0-1 take the first token's two words
+//    and waves 2-3 the second's, each against the 64 x 64 tables over its
+//    token's 64 coordinates (half the MFMAs and table registers).  The pair's
+//    four record groups are exactly the two tokens' records back to back, so
+//    the staging and stores are unchanged; norms and scales are per token.
 #pragma once
 #include <algorithm>
 #include <cmath>
@@ -122,6 +129,14 @@ __device__ inline float row16_sum(float x) {
   return x;
 }
 
+// Sum over each group of 8 lanes (the first three steps of row16_sum).
+__device__ inline float row8_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+  return x;
+}
+
 template <bool BF16>
 struct RawX {
   uint4 v[BF16 ? 4 : 8];
@@ -156,11 +171,15 @@ __device__ inline void row_ht(const TileRows& r, int v, const Q128Args& a, uint3
   }
 }
 
-// Loads of one 64-vector tile: pass p covers vector 4*wave + 16*p + lane/16,
-// 8-element chunk lane%16.  Vectors past the end of the launch read as zero.
-template <bool BF16>
+// Loads of one 64-row tile: pass p covers row 4*wave + 16*p + lane/16,
+// 8-element chunk lane%16 (D = 64: token (lane%16)/8 of the row's pair, chunk
+// lane%8).  Rows past the end of the launch read as zero.
+template <bool BF16, int D>
 __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t tile, int wave,
                                  int lane) {
+  constexpr int TPV = 128 / D;                       // tokens per row
+  const int tp = D == 64 ? (lane & 15) >> 3 : 0;     // token of the pair
+  const int cc = D == 64 ? (lane & 7) : (lane & 15); // 8-element chunk of the token
   const TileRows r = tile_rows(tile, a);
   // vectors past the end re-read the tile's first row (always valid); the
   // consumer zeroes them, so no lane branches around a load and nothing
@@ -175,13 +194,14 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
   };
   if (r.one) {        // uniform branch: rows t0 .. t0 + cnt - 1 of head h0
     // row offsets within the tile in 32 bits (the launcher keeps
-    // x_stride_token below 2^25 elements)
-    const int64_t base = (int64_t)r.h0 * a.x_stride_head + (int64_t)r.t0 * a.x_stride_token;
+    // x_stride_token below 2^25 elements, 2^24 for D = 64)
+    const int64_t base =
+        (int64_t)r.h0 * a.x_stride_head + (int64_t)TPV * r.t0 * a.x_stride_token;
     const int32_t xst = (int32_t)a.x_stride_token;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int v = 4 * wave + 16 * p + (lane >> 4);
-      load(p, base + (int64_t)((v < r.cnt ? v : 0) * xst + 8 * (lane & 15)));
+      load(p, base + (int64_t)((TPV * (v < r.cnt ? v : 0) + tp) * xst + 8 * cc));
     }
   } else {
 #pragma unroll
@@ -189,7 +209,7 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
       const int v = 4 * wave + 16 * p + (lane >> 4);
       const uint32_t f = r.f0 + (v < r.cnt ? v : 0);
       const uint32_t h = fast_div(f, a), t = f - h * (uint32_t)a.n_tokens;
-      load(p, (int64_t)h * a.x_stride_head + (int64_t)t * a.x_stride_token + 8 * (lane & 15));
+      load(p, (int64_t)h * a.x_stride_head + ((int64_t)TPV * t + tp) * a.x_stride_token + 8 * cc);
     }
   }
 }
@@ -199,13 +219,17 @@ __device__ inline void load_tile(RawX<BF16>& raw, const Q128Args& a, uint32_t ti
 // The tiles tile0, tile0 + stride, ... of a launch, by one 256-thread
 // workgroup (the kernel body; launch bounds: 256 threads, 2 workgroups per CU,
 // 3 for MSE-only records).
-template <int NB, bool BF16, bool MSE>
+template <int NB, bool BF16, bool MSE, int D = 128>
 __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, uint32_t stride) {
+  static_assert(D == 128 || D == 64, "head dimension 128, or 64 as token pairs");
+  constexpr int TPV = 128 / D;            // tokens per tile row
+  constexpr int KS = D / 16;              // K steps of one product
   constexpr int CP = MSE ? NB : NB - 1;   // code planes
   constexpr int K = 1 << CP;
   constexpr int KH = K / 2;           // positive centroids
   constexpr int NT = KH - 1;          // positive thresholds
   constexpr int YP = BF16 ? 2 : 3;    // MFMA passes per K step of Y
+  constexpr int ZN = KS * 3;          // MFMAs of Z = M r per 32-vector block
   // x (scaled, fp16 hi/lo) and the residual (hi/lo) in separate buffers, so
   // a tile needs two barriers: x of the next tile is written while the
   // residual of this one is still being read.
@@ -213,23 +237,28 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   __shared__ __align__(16) _Float16 xl_s[BF16 ? 8 : kT * kLdx];
   __shared__ __align__(16) _Float16 rh_s[kT * kLdx];
   __shared__ __align__(16) _Float16 rl_s[kT * kLdx];
-  __shared__ float ysc[2][kT];        // by tile parity: 2^e / nu (0 for x = 0)
-  __shared__ float sinv[2][kT];       // nu 2^-e (1 for x = 0): thresholds to acc units
-  __shared__ uint32_t nu16[2][kT];
+  // per token (row v, token k of the row at TPV * v + k), by tile parity
+  __shared__ float ysc[2][TPV * kT];  // 2^e / nu (0 for x = 0)
+  __shared__ float sinv[2][TPV * kT]; // nu 2^-e (1 for x = 0): thresholds to acc units
+  __shared__ uint32_t nu16[2][TPV * kT];
   __shared__ float gpart[4][kT];
   // packed records and norms of the tile (the global layout), written out
   // one tile later with contiguous stores
   __shared__ __align__(16) uint32_t outw[2][kT * 4 * NB];
-  __shared__ __align__(16) uint32_t outn[2][kT];
+  __shared__ __align__(16) uint32_t outn[2][TPV * kT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
+  // D = 64: this wave's token of the pair, and where its coordinates start
+  const int half = D == 64 ? wave >> 1 : 0;
+  const int kofs = 64 * half;
 
-  // Pi / M rows 32*wave + col, K slots 16*ks + 8*hh .. +8
-  v8h Ph[8], Pl[8], Mh[8], Ml[8];
+  // Pi / M rows 32*wave + col (D = 64: 32*(wave&1) + col of the 64 x 64
+  // tables), K slots 16*ks + 8*hh .. +8
+  v8h Ph[KS], Pl[KS], Mh[KS], Ml[KS];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const int off = (32 * wave + col) * 128 + 16 * ks + 8 * hh;
+  for (int ks = 0; ks < KS; ++ks) {
+    const int off = (32 * (D == 64 ? (wave & 1) : wave) + col) * D + 16 * ks + 8 * hh;
     Ph[ks] = *(const v8h*)(a.pi_hi + off);
     Pl[ks] = *(const v8h*)(a.pi_lo + off);
     Mh[ks] = *(const v8h*)(a.m_hi + off);
@@ -271,7 +300,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(xv[e], xv[e], ss);
     }
-    ss = row16_sum(ss);
+    ss = D == 64 ? row8_sum(ss) : row16_sum(ss);
     const float nu = sqrtf(ss);
     int ex = 0;
     if (nu > 0.f) frexpf(nu, &ex);
@@ -286,10 +315,11 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     }
     *(v8h*)(xh_s + v * kLdx + 8 * c) = hi;
     if constexpr (!BF16) *(v8h*)(xl_s + v * kLdx + 8 * c) = lo;
-    // the 16 lanes of the row write the same values
-    ysc[pb][v] = (nu > 0.f) ? ldexpf(__builtin_amdgcn_rcpf(nu), ex) : 0.f;
-    sinv[pb][v] = (nu > 0.f) ? ldexpf(nu, -ex) : 1.f;
-    nu16[pb][v] = (uint32_t)__half_as_ushort(__float2half_rn(nu));
+    // the 16 lanes of the row (8 of each token for D = 64) write the same values
+    const int vk = TPV * v + (D == 64 ? c >> 3 : 0);
+    ysc[pb][vk] = (nu > 0.f) ? ldexpf(__builtin_amdgcn_rcpf(nu), ex) : 0.f;
+    sinv[pb][vk] = (nu > 0.f) ? ldexpf(nu, -ex) : 1.f;
+    nu16[pb][vk] = (uint32_t)__half_as_ushort(__float2half_rn(nu));
   };
 
   // ---- MFMA m (0 .. 8*YP-1) of Y = Pi x_s for the 32 vectors of block cb ---
@@ -297,7 +327,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   auto y_mfma = [&](v16f& acc, int cb, int m) {
     const int ks = m / YP, ps = m % YP;
     if (ps == 0) {
-      const int off = (32 * cb + col) * kLdx + 16 * ks + 8 * hh;
+      const int off = (32 * cb + col) * kLdx + kofs + 16 * ks + 8 * hh;
       xf_h = *(const v8h*)(xh_s + off);
       if constexpr (!BF16) xf_l = *(const v8h*)(xl_s + off);
     }
@@ -320,8 +350,8 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   uint32_t codew[2][3];
   auto codes = [&](const v16f& acc, int cb, int pb, auto&& hook) {
     const int v = 32 * cb + col;
-    const float sv = ysc[pb][v];
-    const float inv = sinv[pb][v];
+    const float sv = ysc[pb][TPV * v + half];
+    const float inv = sinv[pb][TPV * v + half];
     float thr_v[NT > 0 ? NT : 1], cpos_v[KH];
 #pragma unroll
     for (int k = 0; k < NT; ++k) thr_v[k] = a.thr[k] * inv;
@@ -384,7 +414,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   auto z_mfma = [&](v16f& z, int cb, int m) {
     const int ks = m / 3, ps = m % 3;
     if (ps == 0) {
-      const int off = (32 * cb + col) * kLdx + 16 * ks + 8 * hh;
+      const int off = (32 * cb + col) * kLdx + kofs + 16 * ks + 8 * hh;
       rf_h = *(const v8h*)(rh_s + off);
       rf_l = *(const v8h*)(rl_s + off);
     }
@@ -413,7 +443,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     }
     uint32_t sw = halves_or(spread16(sb, hh));
     const int v = 32 * cb + col;
-    if (ysc[pb][v] == 0.f) sw = 0xffffffffu;       // ||x|| = 0: r = 0, all signs +1
+    if (ysc[pb][TPV * v + half] == 0.f) sw = 0xffffffffu;   // ||x|| = 0: r = 0, all signs +1
     // group `wave` of record v; each lane half writes the words it owns
     // (a word both halves write gets the same value from both)
     uint32_t* dst = outw[pb] + (v * 4 + wave) * NB;
@@ -431,7 +461,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   uint32_t tile = tile0;
   if (tile >= a.n_tiles) return;
   // prologue: x of the first tile
-  load_tile<BF16>(raw, a, tile, wave, lane);
+  load_tile<BF16, D>(raw, a, tile, wave, lane);
   {
     const int cnt0 = tile_cnt(tile);
 #pragma unroll
@@ -449,7 +479,7 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
       s = a.slots[t];
       if (s < 0 || s >= a.dst_stride_head) return -1;
     }
-    return (int64_t)h * a.dst_stride_head + a.dst_token0 + s;
+    return (int64_t)h * a.dst_stride_head + a.dst_token0 + TPV * s;   // first token of the row
   };
   // Copy the staged records and norms of the previous tile (buffer pb) to
   // memory: prev.cnt * NB <= 256 chunks of 16 bytes, one per thread, and the
@@ -459,20 +489,21 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
   auto flush = [&](int pb) {
     if (!have_prev) return;
     if (prev.one && !a.slots) {
+      // a row's 4 record groups are its TPV records, back to back
       const int64_t rec0 = rec_of(prev, 0);
       if (tid < prev.cnt * NB)
-        ((uint4*)(a.planes + rec0 * 4 * NB))[tid] = ((const uint4*)outw[pb])[tid];
-      if (tid < prev.cnt) a.norms[rec0 + tid] = outn[pb][tid];
+        ((uint4*)(a.planes + rec0 * (D / 32) * NB))[tid] = ((const uint4*)outw[pb])[tid];
+      if (tid < TPV * prev.cnt) a.norms[rec0 + tid] = outn[pb][tid];
     } else {
       if (tid < prev.cnt * NB) {
         const int v = tid / NB;
         const int64_t rec = rec_of(prev, v);
         if (rec >= 0)
-          ((uint4*)(a.planes + rec * 4 * NB))[tid - v * NB] = ((const uint4*)outw[pb])[tid];
+          ((uint4*)(a.planes + rec * (D / 32) * NB))[tid - v * NB] = ((const uint4*)outw[pb])[tid];
       }
-      if (tid < prev.cnt) {
-        const int64_t rec = rec_of(prev, tid);
-        if (rec >= 0) a.norms[rec] = outn[pb][tid];
+      if (tid < TPV * prev.cnt) {
+        const int64_t rec = rec_of(prev, tid / TPV);
+        if (rec >= 0) a.norms[rec + tid % TPV] = outn[pb][tid];
       }
     }
   };
@@ -485,15 +516,15 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     // every wave has finished the previous tile and x of this one is in LDS:
     // write the previous records, then prefetch the next tile
     flush(par ^ 1);
-    if (BF16 && has_next) load_tile<BF16>(raw, a, next, wave, lane);
+    if (BF16 && has_next) load_tile<BF16, D>(raw, a, next, wave, lane);
 
     // Y of block 0, then the codes of block 0 with Y of block 1 interleaved
     v16f acc0 = {}, acc1 = {};
 #pragma unroll
-    for (int m = 0; m < 8 * YP; ++m) y_mfma(acc0, 0, m);
+    for (int m = 0; m < KS * YP; ++m) y_mfma(acc0, 0, m);
     codes(acc0, 0, par, [&](int e) {
 #pragma unroll
-      for (int m = e * YP / 2; m < (e + 1) * YP / 2; ++m) y_mfma(acc1, 1, m);
+      for (int m = e * KS * YP / 16; m < (e + 1) * KS * YP / 16; ++m) y_mfma(acc1, 1, m);
     });
     codes(acc1, 1, par, none);
     __syncthreads();
@@ -503,27 +534,30 @@ __device__ __forceinline__ void q128_tiles(const Q128Args& a, uint32_t tile0, ui
     // signs of block 0
     v16f z0 = {}, z1 = {};
     const int cnt_n = has_next ? tile_cnt(next) : 0;
-    if (!BF16 && has_next) load_tile<BF16>(raw, a, next, wave, lane);    // fp32: no prefetch
+    if (!BF16 && has_next) load_tile<BF16, D>(raw, a, next, wave, lane);    // fp32: no prefetch
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if constexpr (!MSE)
 #pragma unroll
-        for (int m = 6 * p; m < 6 * p + 3; ++m) z_mfma(z0, 0, m);
+        for (int m = p * ZN / 4; m < p * ZN / 4 + ZN / 8; ++m) z_mfma(z0, 0, m);
       x_pass(p, cnt_n, par ^ 1);
       if constexpr (!MSE)
 #pragma unroll
-        for (int m = 6 * p + 3; m < 6 * p + 6; ++m) z_mfma(z0, 0, m);
+        for (int m = p * ZN / 4 + ZN / 8; m < (p + 1) * ZN / 4; ++m) z_mfma(z0, 0, m);
     }
     signs(z0, 0, par, [&](int e) {
-      if (!MSE && e < 12) {
+      if (!MSE && e < ZN / 2) {
 #pragma unroll
         for (int m = 2 * e; m < 2 * e + 2; ++m) z_mfma(z1, 1, m);
       }
     });
     signs(z1, 1, par, none);
 
-    if (tid < cnt) {
-      const float sq = MSE ? 0.f : (gpart[0][tid] + gpart[1][tid]) + (gpart[2][tid] + gpart[3][tid]);
+    if (tid < TPV * cnt) {            // token tid % TPV of row tid / TPV
+      const int v = tid / TPV, k = tid % TPV;
+      const float sq = MSE ? 0.f
+                     : D == 64 ? gpart[2 * k][v] + gpart[2 * k + 1][v]
+                               : (gpart[0][v] + gpart[1][v]) + (gpart[2][v] + gpart[3][v]);
       const float gam = (MSE || ysc[par][tid] == 0.f) ? 0.f : sqrtf(sq);
       const uint32_t gb = (uint32_t)__half_as_ushort(__float2half_rn(gam));
       outn[par][tid] = nu16[par][tid] | (gb << 16);

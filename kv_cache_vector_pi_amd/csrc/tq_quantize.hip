@@ -514,6 +514,12 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
   if (ctx->d == 128 && x_stride_token < ((int64_t)1 << 25))
     return launch_quantize128(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
                               planes, norms, dst_stride_head, dst_token0, slots, stream);
+  // d = 64: the same kernel on token pairs, where they line up
+  if (quantize64_pairs_apply(ctx, n_tokens, n_heads, x_stride_token, dst_stride_head, dst_token0,
+                             slots))
+    return launch_quantize64_pairs(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
+                                   x_stride_head, planes, norms, dst_stride_head, dst_token0,
+                                   stream);
   QuantArgs a{};
   a.x = x;
   a.x_stride_token = x_stride_token;

@@ -1,28 +1,65 @@
-// Quantization for head_dim 128: the kernel and its launcher (the method
-// and its organisation are described in tq_q128.h).
+// Quantization for head_dim 128, and 64 as token pairs: the kernel and its
+// launchers (the method and its organisation are described in tq_q128.h).
 #include "tq_q128.h"
 
 namespace tq {
 namespace {
 
-template <int NB, bool BF16, bool MSE>
+template <int NB, bool BF16, bool MSE, int D>
 __global__ void __launch_bounds__(256, MSE ? 3 : 2) quantize128_kernel(Q128Args a) {
-  q128_tiles<NB, BF16, MSE>(a, blockIdx.x, gridDim.x);
+  q128_tiles<NB, BF16, MSE, D>(a, blockIdx.x, gridDim.x);
 }
 
-template <int NB, bool BF16, bool MSE>
+template <int NB, bool BF16, bool MSE, int D>
 hipError_t launch128(const Q128Args& a, int n_cu, hipStream_t st) {
   static int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize128_kernel<NB, BF16, MSE>, 256, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, quantize128_kernel<NB, BF16, MSE, D>, 256,
+                                                     0) != hipSuccess ||
         nb < 1)
       nb = 1;
     return nb;
   }();
   const int64_t grid = std::min<int64_t>((int64_t)a.n_tiles, (int64_t)n_cu * per_cu);
-  hipLaunchKernelGGL((quantize128_kernel<NB, BF16, MSE>), dim3((unsigned)grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((quantize128_kernel<NB, BF16, MSE, D>), dim3((unsigned)grid), dim3(256), 0, st,
+                     a);
   return hipGetLastError();
+}
+
+// rows: tokens (D = 128) or token pairs (D = 64) per head
+template <int D>
+hipError_t launch_rows(const tq_ctx* ctx, const void* x, int32_t x_dtype, int64_t rows,
+                       int32_t n_heads, int64_t x_stride_token, int64_t x_stride_head,
+                       uint32_t* planes, uint16_t* norms, int64_t dst_stride_head,
+                       int64_t dst_token0, const int64_t* slots, hipStream_t stream) {
+  Q128Args a;
+  const hipError_t ea = q128_args(ctx, x, rows, x_stride_token, x_stride_head, planes, norms,
+                                  dst_stride_head, dst_token0, slots, a);
+  if (ea != hipSuccess) return ea;
+  const bool bf = x_dtype == TQ_BF16;
+  // launch over groups of heads with fewer than kMaxRows rows
+  const int64_t heads_per_launch = std::max<int64_t>(1, kMaxRows / rows);
+  for (int64_t h0 = 0; h0 < n_heads; h0 += heads_per_launch) {
+    const int64_t nh = std::min<int64_t>(heads_per_launch, n_heads - h0);
+    const Q128Args ah = q128_group(a, h0, nh, bf);
+    hipError_t e;
+    const int n_cu = ctx->n_cu;
+    if (ctx->mse) {
+      switch (ctx->b) {
+        case 1: e = bf ? launch128<1, true, true, D>(ah, n_cu, stream) : launch128<1, false, true, D>(ah, n_cu, stream); break;
+        case 2: e = bf ? launch128<2, true, true, D>(ah, n_cu, stream) : launch128<2, false, true, D>(ah, n_cu, stream); break;
+        default: e = bf ? launch128<3, true, true, D>(ah, n_cu, stream) : launch128<3, false, true, D>(ah, n_cu, stream); break;
+      }
+    } else {
+      switch (ctx->b) {
+        case 2: e = bf ? launch128<2, true, false, D>(ah, n_cu, stream) : launch128<2, false, false, D>(ah, n_cu, stream); break;
+        case 3: e = bf ? launch128<3, true, false, D>(ah, n_cu, stream) : launch128<3, false, false, D>(ah, n_cu, stream); break;
+        default: e = bf ? launch128<4, true, false, D>(ah, n_cu, stream) : launch128<4, false, false, D>(ah, n_cu, stream); break;
+      }
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -32,34 +69,26 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                               int64_t dst_stride_head, int64_t dst_token0,
                               const int64_t* slots, hipStream_t stream) {
-  Q128Args a;
-  const hipError_t ea = q128_args(ctx, x, n_tokens, x_stride_token, x_stride_head, planes, norms,
-                                  dst_stride_head, dst_token0, slots, a);
-  if (ea != hipSuccess) return ea;
-  const bool bf = x_dtype == TQ_BF16;
-  // launch over groups of heads with fewer than kMaxRows rows
-  const int64_t heads_per_launch = std::max<int64_t>(1, kMaxRows / n_tokens);
-  for (int64_t h0 = 0; h0 < n_heads; h0 += heads_per_launch) {
-    const int64_t nh = std::min<int64_t>(heads_per_launch, n_heads - h0);
-    const Q128Args ah = q128_group(a, h0, nh, bf);
-    hipError_t e;
-    const int n_cu = ctx->n_cu;
-    if (ctx->mse) {
-      switch (ctx->b) {
-        case 1: e = bf ? launch128<1, true, true>(ah, n_cu, stream) : launch128<1, false, true>(ah, n_cu, stream); break;
-        case 2: e = bf ? launch128<2, true, true>(ah, n_cu, stream) : launch128<2, false, true>(ah, n_cu, stream); break;
-        default: e = bf ? launch128<3, true, true>(ah, n_cu, stream) : launch128<3, false, true>(ah, n_cu, stream); break;
-      }
-    } else {
-      switch (ctx->b) {
-        case 2: e = bf ? launch128<2, true, false>(ah, n_cu, stream) : launch128<2, false, false>(ah, n_cu, stream); break;
-        case 3: e = bf ? launch128<3, true, false>(ah, n_cu, stream) : launch128<3, false, false>(ah, n_cu, stream); break;
-        default: e = bf ? launch128<4, true, false>(ah, n_cu, stream) : launch128<4, false, false>(ah, n_cu, stream); break;
-      }
-    }
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return launch_rows<128>(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
+                          planes, norms, dst_stride_head, dst_token0, slots, stream);
+}
+
+bool quantize64_pairs_apply(const tq_ctx* ctx, int64_t n_tokens, int32_t n_heads,
+                            int64_t x_stride_token, int64_t dst_stride_head, int64_t dst_token0,
+                            const int64_t* slots) {
+  // pairs of consecutive tokens of one head, whose two records start at an
+  // even index (16-byte aligned pair records for any b), 32-bit row offsets
+  return ctx->d == 64 && !slots && n_tokens > 0 && n_tokens % 2 == 0 && dst_token0 % 2 == 0 &&
+         (n_heads == 1 || dst_stride_head % 2 == 0) && x_stride_token < ((int64_t)1 << 24);
+}
+
+hipError_t launch_quantize64_pairs(const tq_ctx* ctx, const void* x, int32_t x_dtype,
+                                   int64_t n_tokens, int32_t n_heads, int64_t x_stride_token,
+                                   int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
+                                   int64_t dst_stride_head, int64_t dst_token0,
+                                   hipStream_t stream) {
+  return launch_rows<64>(ctx, x, x_dtype, n_tokens / 2, n_heads, x_stride_token, x_stride_head,
+                         planes, norms, dst_stride_head, dst_token0, nullptr, stream);
 }
 
 }  // namespace tq

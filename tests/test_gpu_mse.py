@@ -51,6 +51,7 @@ def to_dev(planes, norms):
     (128, 3, torch.float32, 257),
     (200, 2, torch.float32, 300),         # generic kernel, padded last word
     (64, 1, torch.float32, 77),
+    (64, 2, torch.bfloat16, 200),         # d = 64 token pairs (d = 128 kernel)
     (1536, 3, torch.float32, 33),
     (1536, 1, torch.bfloat16, 40),
 ])

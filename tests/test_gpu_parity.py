@@ -84,7 +84,9 @@ def check_quantize(orc, d, b, x, pi, s, c, planes, norms, rows=None):
     (128, 4, torch.float32, 64),
     (200, 2, torch.float32, 300),
     (200, 4, torch.float32, 130),
-    (64, 3, torch.float32, 77),
+    (64, 3, torch.float32, 77),           # odd count: the generic kernel
+    (64, 4, torch.bfloat16, 1000),        # token pairs through the d = 128 kernel
+    (64, 2, torch.float32, 258),
     (1536, 2, torch.float32, 40),
     (1536, 4, torch.float32, 33),
 ])
@@ -147,6 +149,38 @@ def test_quantize_short_heads(orc, n_heads, n_tok, b, dtype):
     xs = x.reshape(n_heads * n_tok, d)
     check_quantize(orc, d, b, xs, pi, s, c, P[:, 7:7 + n_tok].reshape(n_heads * n_tok, -1),
                    N[:, 7:7 + n_tok].reshape(n_heads * n_tok, 2))
+
+
+@pytest.mark.parametrize("n_heads,n_tok,b,dtype,cap,t0", [
+    (40, 2, 4, torch.bfloat16, 2, 0),       # one pair per head: tiles across heads
+    (3, 130, 3, torch.float32, 140, 6),      # pairs inside heads, offset and strided cache
+    (2, 96, 2, torch.bfloat16, 100, 2),
+])
+def test_quantize_d64_pairs(orc, n_heads, n_tok, b, dtype, cap, t0):
+    """d = 64 through the d = 128 kernel on token pairs: records against the
+    oracle, each token's norms its own, records at h * cap + t0 + t, and
+    neighbouring records untouched."""
+    say("d64 pairs", n_heads, n_tok, b, dtype, cap, t0)
+    d = 64
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    x = (workloads.normal((n_heads, n_tok, d), 61, 10, DEV) * 3.0)
+    x[0, 1] = 0.0                           # second token of a pair is zero
+    x[n_heads - 1, n_tok - 2] *= 1e-3      # first token of the last pair is small
+    x = x.to(dtype)
+    P, N = tq.alloc_records(n_heads * cap, d, b)
+    P.fill_(0x5A5A5A5A)
+    N.fill_(0x3C3C)
+    tq.tq_quantize_kv(ctx, x, P, N, dst_stride_head=cap, dst_token0=t0)
+    torch.cuda.synchronize()
+    W = tq.tq_words_per_plane(d)
+    gp = P.cpu().numpy().view(np.uint32).reshape(n_heads, cap, W * b)
+    gn = N.cpu().numpy().view(np.uint16).reshape(n_heads, cap, 2)
+    assert np.all(gp[:, :t0] == 0x5A5A5A5A) and np.all(gp[:, t0 + n_tok:] == 0x5A5A5A5A)
+    assert np.all(gn[:, :t0] == 0x3C3C) and np.all(gn[:, t0 + n_tok:] == 0x3C3C)
+    rows = gp[:, t0:t0 + n_tok].reshape(n_heads * n_tok, -1)
+    nrm = gn[:, t0:t0 + n_tok].reshape(n_heads * n_tok, 2)
+    check_quantize(orc, d, b, x.reshape(-1, d), pi, s, c, rows, nrm)
+    assert np.all(nrm[1] == 0)              # the zero token: nu = gamma = 0
 
 
 def test_quantize_empty_and_deterministic(orc):
