@@ -75,9 +75,10 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t dst_stride_head, int64_t dst_token0,
                               const int64_t* slots, hipStream_t stream);
 
-// d = 64 as token pairs through the d = 128 kernel: when it applies (even
-// token count, even first record index and head stride, no slots), and the
-// launch.
+// d = 64 as token pairs through the d = 128 kernel: when it applies (no
+// slots, at least one pair per head; for odd b, even first record index and
+// head stride), and the launch of the pairs (an odd last token per head is
+// left to the caller).
 bool quantize64_pairs_apply(const tq_ctx* ctx, int64_t n_tokens, int32_t n_heads,
                             int64_t x_stride_token, int64_t dst_stride_head, int64_t dst_token0,
                             const int64_t* slots);

@@ -514,12 +514,19 @@ hipError_t launch_quantize(const tq_ctx* ctx, const void* x, int32_t x_dtype, in
   if (ctx->d == 128 && x_stride_token < ((int64_t)1 << 25))
     return launch_quantize128(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
                               planes, norms, dst_stride_head, dst_token0, slots, stream);
-  // d = 64: the same kernel on token pairs, where they line up
+  // d = 64: the same kernel on token pairs, where they line up; an odd last
+  // token of each head goes through the generic kernel below
   if (quantize64_pairs_apply(ctx, n_tokens, n_heads, x_stride_token, dst_stride_head, dst_token0,
-                             slots))
-    return launch_quantize64_pairs(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token,
-                                   x_stride_head, planes, norms, dst_stride_head, dst_token0,
-                                   stream);
+                             slots)) {
+    const hipError_t e = launch_quantize64_pairs(ctx, x, x_dtype, n_tokens, n_heads,
+                                                 x_stride_token, x_stride_head, planes, norms,
+                                                 dst_stride_head, dst_token0, stream);
+    if (e != hipSuccess || n_tokens % 2 == 0) return e;
+    const size_t esz = x_dtype == TQ_BF16 ? 2 : 4;
+    x = (const char*)x + (size_t)(n_tokens - 1) * x_stride_token * esz;
+    dst_token0 += n_tokens - 1;
+    n_tokens = 1;
+  }
   QuantArgs a{};
   a.x = x;
   a.x_stride_token = x_stride_token;

@@ -76,10 +76,11 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
 bool quantize64_pairs_apply(const tq_ctx* ctx, int64_t n_tokens, int32_t n_heads,
                             int64_t x_stride_token, int64_t dst_stride_head, int64_t dst_token0,
                             const int64_t* slots) {
-  // pairs of consecutive tokens of one head, whose two records start at an
-  // even index (16-byte aligned pair records for any b), 32-bit row offsets
-  return ctx->d == 64 && !slots && n_tokens > 0 && n_tokens % 2 == 0 && dst_token0 % 2 == 0 &&
-         (n_heads == 1 || dst_stride_head % 2 == 0) && x_stride_token < ((int64_t)1 << 24);
+  // pairs of consecutive tokens of one head (at least one per head), 32-bit
+  // row offsets, and 16-byte aligned pair records: a d = 64 record is 8 b
+  // bytes, so any index serves for even b and an even one for odd b
+  return ctx->d == 64 && !slots && n_tokens >= 2 && x_stride_token < ((int64_t)1 << 24) &&
+         (ctx->b % 2 == 0 || (dst_token0 % 2 == 0 && (n_heads == 1 || dst_stride_head % 2 == 0)));
 }
 
 hipError_t launch_quantize64_pairs(const tq_ctx* ctx, const void* x, int32_t x_dtype,
@@ -87,6 +88,8 @@ hipError_t launch_quantize64_pairs(const tq_ctx* ctx, const void* x, int32_t x_d
                                    int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                                    int64_t dst_stride_head, int64_t dst_token0,
                                    hipStream_t stream) {
+  // the first 2 floor(n_tokens / 2) tokens of each head; an odd last token is
+  // the caller's
   return launch_rows<64>(ctx, x, x_dtype, n_tokens / 2, n_heads, x_stride_token, x_stride_head,
                          planes, norms, dst_stride_head, dst_token0, nullptr, stream);
 }

@@ -155,6 +155,9 @@ def test_quantize_short_heads(orc, n_heads, n_tok, b, dtype):
     (40, 2, 4, torch.bfloat16, 2, 0),       # one pair per head: tiles across heads
     (3, 130, 3, torch.float32, 140, 6),      # pairs inside heads, offset and strided cache
     (2, 96, 2, torch.bfloat16, 100, 2),
+    (2, 131, 4, torch.bfloat16, 140, 3),     # odd count: pairs + the generic last token; odd index, even b
+    (3, 7, 3, torch.float32, 10, 2),         # odd count, odd b
+    (2, 9, 3, torch.bfloat16, 11, 1),        # odd b at odd indices: the generic kernel
 ])
 def test_quantize_d64_pairs(orc, n_heads, n_tok, b, dtype, cap, t0):
     """d = 64 through the d = 128 kernel on token pairs: records against the
@@ -165,7 +168,7 @@ def test_quantize_d64_pairs(orc, n_heads, n_tok, b, dtype, cap, t0):
     ctx, pi, s, c = ctx_for(orc, d, b)
     x = (workloads.normal((n_heads, n_tok, d), 61, 10, DEV) * 3.0)
     x[0, 1] = 0.0                           # second token of a pair is zero
-    x[n_heads - 1, n_tok - 2] *= 1e-3      # first token of the last pair is small
+    x[n_heads - 1, n_tok - 2] *= 1e-3      # a small token near the end
     x = x.to(dtype)
     P, N = tq.alloc_records(n_heads * cap, d, b)
     P.fill_(0x5A5A5A5A)
