@@ -23,7 +23,7 @@
  *       PolarQuant (rotation, Beta coordinates, Lloyd-Max), on QJL (one sign
  *       bit, unbiased inner products) and on the two-stage b-1 + 1 bit split.
  *
- * Readings where the pages are silent (each one is listed in the design doc):
+ * Readings where the pages are silent:
  *  - the random generator (the pages use numpy's randn, which is not
  *    reproduced): SplitMix64 over a per-(seed, stream) key, Box-Muller;
  *  - Pi is the Q factor with the signs fixed so that R has a positive
@@ -33,7 +33,7 @@
  *    ||x|| is stored as fp16 next to ||r||;
  *  - sign(0) = +1; ties in the nearest-centroid search go to the lower index;
  *  - the QJL scale is alpha = sqrt(pi/2)/m, which makes the estimator
- *    unbiased over S (derivation in the design doc);
+ *    unbiased over S: for s ~ N(0, I), E[sign(s.r) s.q] = sqrt(2/pi) <r, q> / ||r||;
  *  - a zero vector stores nu = 0, gamma = 0, codes of y = 0, all signs +1.
  *
  * Canonical packed record (the format both sides read and write):
