@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "long", "batched", "search", "attn_out", "decode_fused",
-                             "split"])
+                             "split", "dequant"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--mse", action="store_true",
@@ -124,7 +124,7 @@ def main():
     if args.workload != "decode":
         out = {"long": run_long, "batched": run_batched, "search": run_search,
                "attn_out": run_attn_out, "decode_fused": run_decode_fused,
-               "split": run_split}[args.workload](args)
+               "split": run_split, "dequant": run_dequant}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     dev = "cuda"
@@ -346,6 +346,57 @@ def _line(args, metric, value, unit, workload, extra):
     if getattr(args, "mse", False):
         out["config"] = dict(out["config"], records="MSE-only: b code bits, no QJL stage")
     return out
+
+
+def run_dequant(args):
+    """tq_dequantize over one Llama-shaped layer's keys (8 KV heads x 32768
+    tokens, d = 128, b = 4: 262,144 records to fp32 vectors), and over the tiny
+    configuration (1024 keys, d = 128, b = 3).  Calls back to back between two
+    events on the launch stream."""
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    import workloads
+    dev, d = "cuda", 128
+    stream = torch.cuda.current_stream()
+    reps = max(10, min(args.steps, 50))
+    mse = getattr(args, "mse", False)
+    res = {}
+    for name, b, x in (("llama_layer", 3 if mse else 4, workloads.llama(dev, seed=0)["K"]),
+                       ("tiny", 2 if mse else 3, workloads.tiny(dev)["K"])):
+        x = x.reshape(-1, d).contiguous()
+        n = x.shape[0]
+        ctx = _common(args, d, b)
+        planes, norms = tq.alloc_records(n, d, b, dev)
+        tq.tq_quantize_kv(ctx, x, planes, norms)
+        out = torch.empty((n, d), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            tq.tq_dequantize(ctx, planes, norms, n, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tq.tq_dequantize(ctx, planes, norms, n, out)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rb = b * d // 8 + 4
+        alg_bytes = n * (rb + 4 * d)                 # packed record in, fp32 vector out
+        alg_flops = n * 4 * d * d                    # Pi^T c[idx] and S^T s: 2 d^2 each
+        res[name] = {"n": n, "b": b, "ms_per_call": ms, "vec_per_s": n / (ms * 1e-3),
+                     "GB_per_s": alg_bytes / (ms * 1e-3) / 1e9,
+                     "TFLOP_per_s": alg_flops / (ms * 1e-3) / 1e12}
+        del ctx
+    big = res["llama_layer"]
+    return _line(args, "dequantize: vectors/s from packed records", big["vec_per_s"], "vectors/s",
+                 {"workload": "dequantize one Llama-shaped layer's keys (8 KV heads x 32768 tokens, "
+                              "d=128, b=%d) to fp32; tiny: 1024 keys, b=%d" %
+                              (big["b"], res["tiny"]["b"])},
+                 {"dtype": "fp16-mfma/fp32", "per_config": res,
+                  "roofline": {"bound": "hbm", "kernel": "decoded_gemm_kernel",
+                               "achieved": big["GB_per_s"], "peak": 8000.0, "unit": "GB/s",
+                               "frac": big["GB_per_s"] / 8000.0, "traffic": None,
+                               "mfma_TFLOP_per_s_algorithmic": big["TFLOP_per_s"],
+                               "mfma_frac_algorithmic": big["TFLOP_per_s"] / 2500.0}})
 
 
 def run_split(args):

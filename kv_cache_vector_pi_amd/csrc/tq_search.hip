@@ -166,17 +166,35 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
     am[cb] = (v4f){0.f, 0.f, 0.f, 0.f};
     aq[cb] = (v4f){0.f, 0.f, 0.f, 0.f};
   }
+  // The next word's record words and A fragments load into registers while
+  // this word's MFMAs run.
+  uint32_t wn[NB];
+  v8h rhn, rln, phn = {}, pln = {};
+  auto load_word = [&](int ks) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p) wn[p] = 0u;
+    if (dlive) {
+      const uint32_t* src = a.planes + ((a.rec0 + drec) * a.W + ks) * NB;
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wn[p] = src[p];
+    }
+    const int64_t aoff = row * a.Dp + 32 * ks + 8 * g;
+    rhn = *(const v8h*)(a.qr_hi + aoff);
+    rln = *(const v8h*)(a.qr_lo + aoff);
+    if constexpr (!MSE) {
+      phn = *(const v8h*)(a.qp_hi + aoff);
+      pln = *(const v8h*)(a.qp_lo + aoff);
+    }
+  };
+  load_word(0);
   for (int ks = 0; ks < a.W; ++ks) {
+    uint32_t wd[NB];
+#pragma unroll
+    for (int p = 0; p < NB; ++p) wd[p] = wn[p];
+    const v8h rh = rhn, rl = rln;
+    const v8h ph = phn, pl = pln;
     // decode word ks of record dr, coordinates 8dq .. 8dq+7
     {
-      uint32_t wd[NB];
-#pragma unroll
-      for (int p = 0; p < NB; ++p) wd[p] = 0u;
-      if (dlive) {
-        const uint32_t* src = a.planes + ((a.rec0 + drec) * a.W + ks) * NB;
-#pragma unroll
-        for (int p = 0; p < NB; ++p) wd[p] = src[p];
-      }
       v8h vh, vl, vs;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -193,9 +211,7 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
       if constexpr (!MSE) *(v8h*)(ds + dr * kLdsRow + 8 * dq) = vs;
     }
     __syncthreads();
-    const int64_t aoff = row * a.Dp + 32 * ks + 8 * g;
-    const v8h rh = *(const v8h*)(a.qr_hi + aoff);
-    const v8h rl = *(const v8h*)(a.qr_lo + aoff);
+    if (ks + 1 < a.W) load_word(ks + 1);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const int off = (16 * cb + n) * kLdsRow + 8 * g;
@@ -206,8 +222,6 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
       am[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rh, bl, am[cb], 0, 0, 0);
     }
     if constexpr (!MSE) {
-      const v8h ph = *(const v8h*)(a.qp_hi + aoff);
-      const v8h pl = *(const v8h*)(a.qp_lo + aoff);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const v8h bs = *(const v8h*)(ds + (16 * cb + n) * kLdsRow + 8 * g);
@@ -217,22 +231,31 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
   }
-  // epilogue: lane holds rows 4g+i of the wave's 16-row block, record 16cb+n
+  // epilogue: lane holds rows 4g+i of the wave's 16-row block, record 16cb+n.
+  // The tile is staged in LDS as [record][row] and written one record row at
+  // a time, consecutive threads on consecutive outputs (a lane's own values
+  // sit 16 records apart, one float each).
+  __shared__ float ot[kRecTile * (kRowsTile + 1)];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    const int64_t rec = rt * kRecTile + 16 * cb + n;
-    if (rec >= a.n_rec) continue;
-    const uint32_t nr = a.norms[a.rec0 + rec];
-    const float nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
-    const float ga = __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
-    const float ag = a.alpha * ga;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = qt * kRowsTile + 16 * wave + 4 * g + i;
-      if (r >= a.n_rows) continue;
-      const float v = nu * fmaf(ag, aq[cb][i], am[cb][i]);
-      a.out[(a.rec0 + rec) * a.out_ld + r] = v;
+    const int rl = 16 * cb + n;
+    const int64_t rec = rt * kRecTile + rl;
+    float nu = 0.f, ag = 0.f;
+    if (rec < a.n_rec) {
+      const uint32_t nr = a.norms[a.rec0 + rec];
+      nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
+      ag = a.alpha * __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ot[rl * (kRowsTile + 1) + 16 * wave + 4 * g + i] = nu * fmaf(ag, aq[cb][i], am[cb][i]);
+  }
+  __syncthreads();
+  for (int k = tid; k < kRecTile * kRowsTile; k += 256) {
+    const int rl = k / kRowsTile, rr = k - rl * kRowsTile;
+    const int64_t rec = rt * kRecTile + rl;
+    const int64_t r = qt * kRowsTile + rr;
+    if (rec < a.n_rec && r < a.n_rows) a.out[(a.rec0 + rec) * a.out_ld + r] = ot[rl * (kRowsTile + 1) + rr];
   }
 }
 

@@ -387,3 +387,26 @@ def test_vector_search_1m(orc, d, b):
             if row[idx] > kth + 2 * TOL * rms:
                 assert idx in gi[a]
     ctx.close()
+
+
+def test_dequantize_llama_layer(orc):
+    """tq_dequantize as bench.py --workload dequant runs it: one Llama-shaped
+    layer's keys (262,144 records, d = 128, b = 4) in one call, sampled rows
+    against the oracle's dequantization of the same records."""
+    d, b = 128, 4
+    say("dequantize llama layer")
+    ctx, pi, s, c = make_ctx(orc, d, b)
+    x = workloads.llama(DEV, seed=0)["K"].reshape(-1, d).contiguous()
+    n = x.shape[0]
+    planes, norms = tq.alloc_records(n, d, b)
+    tq.tq_quantize_kv(ctx, x, planes, norms)
+    out = torch.full((n, d), float("nan"), device=DEV)
+    tq.tq_dequantize(ctx, planes, norms, n, out)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 64, n),
+                                     np.random.default_rng(7).integers(0, n, 300)]))
+    P, N = np_records(planes, norms, rows)
+    ref = orc.dequantize(d, b, pi, s, c, P, N)
+    got = out[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    assert rel_err_rows(got, ref) < TOL
+    assert torch.isfinite(out).all()
