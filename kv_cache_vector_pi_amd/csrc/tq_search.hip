@@ -142,6 +142,7 @@ struct GemmArgs {
   // output: out[rec * out_ld + row]
   float* out;
   int64_t out_ld;
+  int out_vec4;          // out 16-byte aligned and out_ld % 4 == 0 (dequant128_kernel)
 };
 
 // MSE: records of NB code planes without the QJL stage (no sketch term).
@@ -256,6 +257,157 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
     const int64_t rec = rt * kRecTile + rl;
     const int64_t r = qt * kRowsTile + rr;
     if (rec < a.n_rec && r < a.n_rows) a.out[(a.rec0 + rec) * a.out_ld + r] = ot[rl * (kRowsTile + 1) + rr];
+  }
+}
+
+// ---- dequantization at d = 128 ------------------------------------------------
+// Wave w computes output rows 32w .. 32w + 31 (v_mfma_f32_32x32x16_f16): its
+// rows of Pi^T and S^T, hi and lo fp16, stay in registers for the whole
+// persistent loop.  A tile of 64 records is decoded once into LDS -- centroid
+// hi and lo parts and the signs as +-1 -- the codebook looked up in LDS; then
+// am = Pi^T c (3 passes) and aq = S^T s (2 passes), and the output
+// nu (am + alpha gamma aq) is staged in LDS (over the decoded tile) and
+// written one record row at a time.  The next tile's record words load during
+// the MFMAs.
+constexpr int kDqT = 64;      // records per tile
+constexpr int kDqLd = 136;    // LDS row stride of a decoded record, in halves
+constexpr int kDqOut = 132;   // LDS row stride of a staged output record, in floats
+
+template <int NB, bool MSE>
+__global__ void __launch_bounds__(256, 2) dequant128_kernel(GemmArgs a) {
+  constexpr int CP = MSE ? NB : NB - 1;
+  __shared__ __align__(16) _Float16 bufs[3 * kDqT * kDqLd];
+  __shared__ uint32_t ctab_s[kMaxK];
+  __shared__ float nu_s[kDqT], ag_s[kDqT];
+  _Float16* bch = bufs;
+  _Float16* bcl = bufs + kDqT * kDqLd;
+  _Float16* bsg = bufs + 2 * kDqT * kDqLd;
+  float* ot = (float*)bufs;          // [kDqT][kDqOut] floats, over bch and bcl
+  static_assert(kDqT * kDqOut * 4 <= 2 * kDqT * kDqLd * 2, "output staging fits");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  if (tid < kMaxK)
+    ctab_s[tid] = (uint32_t)__builtin_bit_cast(uint16_t, a.c_hi[tid]) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, a.c_lo[tid]) << 16);
+  // Pi^T / S^T rows 32 wave + col, K slots 16 ks + 8 hh .. +8
+  v8h Th[8], Tl[8], Sh[8], Sl[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int off = (32 * wave + col) * 128 + 16 * ks + 8 * hh;
+    Th[ks] = *(const v8h*)(a.qr_hi + off);
+    Tl[ks] = *(const v8h*)(a.qr_lo + off);
+    if constexpr (!MSE) {
+      Sh[ks] = *(const v8h*)(a.qp_hi + off);
+      Sl[ks] = *(const v8h*)(a.qp_lo + off);
+    }
+  }
+  // decode role: record tid / 4 of the tile, word tid % 4 (coordinates 32 w ..)
+  const int dr = tid >> 2, dw = tid & 3;
+  const int64_t n_tiles = (a.n_rec + kDqT - 1) / kDqT;
+  uint32_t wn[NB];
+  auto load_words = [&](int64_t tile) {
+    const int64_t rec = tile * kDqT + dr;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) wn[p] = 0u;
+    if (tile < n_tiles && rec < a.n_rec) {
+      const uint32_t* src = a.planes + ((a.rec0 + rec) * 4 + dw) * NB;
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wn[p] = src[p];
+    }
+  };
+  int64_t tile = blockIdx.x;
+  load_words(tile);
+  __syncthreads();                          // ctab_s written
+  for (; tile < n_tiles; tile += gridDim.x) {
+    const int64_t r0 = tile * kDqT;
+    // ---- decode: 32 coordinates of one record word per thread ----------------
+    {
+      uint32_t wd[NB];
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wd[p] = wn[p];
+#pragma unroll
+      for (int c8 = 0; c8 < 4; ++c8) {
+        v8h vh, vl, vs;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int bit = 8 * c8 + e;
+          uint32_t idx = 0;
+#pragma unroll
+          for (int p = 0; p < CP; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
+          const uint32_t hl = ctab_s[idx];
+          vh[e] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
+          vl[e] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
+          if constexpr (!MSE) vs[e] = ((wd[NB - 1] >> bit) & 1u) ? (_Float16)1.0f : (_Float16)-1.0f;
+        }
+        const int off = dr * kDqLd + 32 * dw + 8 * c8;
+        *(v8h*)(bch + off) = vh;
+        *(v8h*)(bcl + off) = vl;
+        if constexpr (!MSE) *(v8h*)(bsg + off) = vs;
+      }
+      if (tid < kDqT) {
+        const int64_t rec = r0 + tid;
+        float nu = 0.f, ag = 0.f;
+        if (rec < a.n_rec) {
+          const uint32_t nr = a.norms[a.rec0 + rec];
+          nu = __half2float(__ushort_as_half((unsigned short)(nr & 0xffffu)));
+          ag = a.alpha * __half2float(__ushort_as_half((unsigned short)(nr >> 16)));
+        }
+        nu_s[tid] = nu;
+        ag_s[tid] = ag;
+      }
+    }
+    __syncthreads();
+    load_words(tile + gridDim.x);          // the next tile's words, in flight during the MFMAs
+    // ---- products: two 32-record blocks --------------------------------------
+    v16f am[2], aq[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      am[cb] = (v16f){};
+      aq[cb] = (v16f){};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = (32 * cb + col) * kDqLd + 16 * ks + 8 * hh;
+        const v8h bh = *(const v8h*)(bch + off);
+        const v8h bl = *(const v8h*)(bcl + off);
+        am[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Th[ks], bh, am[cb], 0, 0, 0);
+        am[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Tl[ks], bh, am[cb], 0, 0, 0);
+        am[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Th[ks], bl, am[cb], 0, 0, 0);
+        if constexpr (!MSE) {
+          const v8h bs = *(const v8h*)(bsg + off);
+          aq[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Sh[ks], bs, aq[cb], 0, 0, 0);
+          aq[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(Sl[ks], bs, aq[cb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();                        // every wave is done with the decoded tile
+    // element i of block cb: row 32 wave + 8 (i / 4) + 4 hh + i % 4, record 32 cb + col
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int rl = 32 * cb + col;
+      const float nu = nu_s[rl], ag = ag_s[rl];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * wave + 8 * (i >> 2) + 4 * hh + (i & 3);
+        ot[rl * kDqOut + row] = nu * fmaf(ag, aq[cb][i], am[cb][i]);
+      }
+    }
+    __syncthreads();
+    if (a.out_vec4) {
+      for (int k = tid; k < kDqT * 32; k += 256) {
+        const int rl = k >> 5, r4 = k & 31;
+        const int64_t rec = r0 + rl;
+        if (rec < a.n_rec)
+          *(float4*)(a.out + (a.rec0 + rec) * a.out_ld + 4 * r4) =
+              *(const float4*)(ot + rl * kDqOut + 4 * r4);
+      }
+    } else {
+      for (int k = tid; k < kDqT * 128; k += 256) {
+        const int rl = k >> 7, row = k & 127;
+        const int64_t rec = r0 + rl;
+        if (rec < a.n_rec) a.out[(a.rec0 + rec) * a.out_ld + row] = ot[rl * kDqOut + row];
+      }
+    }
+    __syncthreads();                        // the staging area is the next tile's decode buffer
   }
 }
 
@@ -671,6 +823,39 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   return hipSuccess;
 }
 
+namespace {
+template <int NB, bool MSE>
+hipError_t launch_dq128(const GemmArgs& g, int n_cu, hipStream_t st) {
+  static int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, dequant128_kernel<NB, MSE>, 256, 0) !=
+            hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb;
+  }();
+  const int64_t n_tiles = (g.n_rec + kDqT - 1) / kDqT;
+  const int64_t grid = std::min<int64_t>(n_tiles, (int64_t)n_cu * per_cu);
+  hipLaunchKernelGGL((dequant128_kernel<NB, MSE>), dim3((unsigned)grid), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant128(const tq_ctx* ctx, const GemmArgs& g, hipStream_t st) {
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: return launch_dq128<1, true>(g, ctx->n_cu, st);
+      case 2: return launch_dq128<2, true>(g, ctx->n_cu, st);
+      default: return launch_dq128<3, true>(g, ctx->n_cu, st);
+    }
+  }
+  switch (ctx->b) {
+    case 2: return launch_dq128<2, false>(g, ctx->n_cu, st);
+    case 3: return launch_dq128<3, false>(g, ctx->n_cu, st);
+    default: return launch_dq128<4, false>(g, ctx->n_cu, st);
+  }
+}
+}  // namespace
+
 hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const uint16_t* norms,
                              int64_t n, float* out, int64_t out_ld, hipStream_t stream) {
   GemmArgs g{};
@@ -689,6 +874,12 @@ hipError_t launch_dequantize(const tq_ctx* ctx, const uint32_t* planes, const ui
   fill_centroid_split(ctx, g);
   g.out = out;
   g.out_ld = out_ld;
+  // d = 128 with enough records to fill the chip: the register-resident form
+  // (each workgroup loads 128 KB of tables, which a few tiles do not repay)
+  if (ctx->d == 128 && n >= (int64_t)kDqT * ctx->n_cu) {
+    g.out_vec4 = (out_ld % 4 == 0 && ((uintptr_t)out & 15) == 0) ? 1 : 0;
+    return launch_dequant128(ctx, g, stream);
+  }
   const dim3 grid((unsigned)((n + kRecTile - 1) / kRecTile),
                   (unsigned)((ctx->Dp + kRowsTile - 1) / kRowsTile));
   return launch_gemm<1>(ctx, g, grid, stream);

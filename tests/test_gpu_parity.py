@@ -557,6 +557,47 @@ def test_dequantize_parity(orc, d, b, n):
     assert rel_err_rows(got[:, :d], ref) < TOL
 
 
+@pytest.mark.parametrize("b,mse,n,pad", [
+    (4, False, 16384 + 37, 0),      # register-resident d = 128 form, ragged last tile
+    (3, False, 20000, 3),           # out_ld = d + 3: scalar stores
+    (2, True, 17001, 0),            # MSE-only records
+])
+def test_dequantize_d128_resident(orc, b, mse, n, pad):
+    """tq_dequantize at d = 128 with enough records for the register-resident
+    kernel: sampled rows (first and last tiles, random rows) against the
+    oracle's dequantization of the same records; padding columns untouched."""
+    say("dequantize d128 resident", b, mse, n, pad)
+    d = 128
+    if mse:
+        pi = orc.make_rotation(d, 0)[2]
+        c = orc.lloyd_max(d, b)[0].astype(np.float32)
+        ctx = tq.tq_ctx_create_mse(d, b, pi, c)
+        s = None
+    else:
+        ctx, pi, s, c = ctx_for(orc, d, b)
+    x = workloads.normal((n, d), 8, 10, DEV) * 1.7
+    x[3] = 0.0
+    P, N = tq.alloc_records(n, d, b)
+    tq.tq_quantize_kv(ctx, x, P, N)
+    out = torch.full((n, d + pad), float("nan"), device=DEV)
+    tq.tq_dequantize(ctx, P, N, n, out, out_ld=d + pad)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(70), np.arange(n - 70, n),
+                                     np.random.default_rng(9).integers(0, n, 200)]))
+    idx = torch.as_tensor(rows, device=DEV)
+    rp = P[idx].cpu().numpy().view(np.uint32)
+    rn = N[idx].cpu().numpy().view(np.uint16)
+    if mse:
+        ref = orc.dequantize_mse(d, b, pi, c, rp, rn)
+    else:
+        ref = orc.dequantize(d, b, pi, s, c, rp, rn)
+    got = out[idx].cpu().numpy()
+    assert rel_err_rows(got[:, :d], ref) < TOL
+    if pad:
+        assert np.all(np.isnan(out[:, d:].cpu().numpy()))
+    assert torch.isfinite(out[:, :d]).all()
+
+
 # -------------------------------------------------------------------- search
 def topk_ok(gi, gs, ref_scores, k, tol=TOL):
     """GPU (idx, score) rows vs exact oracle scores: every returned index is
