@@ -266,9 +266,10 @@ __global__ void __launch_bounds__(256) decoded_gemm_kernel(GemmArgs a) {
 // persistent loop.  A tile of 64 records is decoded once into LDS -- centroid
 // hi and lo parts and the signs as +-1 -- the codebook looked up in LDS; then
 // am = Pi^T c (3 passes) and aq = S^T s (2 passes), and the output
-// nu (am + alpha gamma aq) is staged in LDS (over the decoded tile) and
-// written one record row at a time.  The next tile's record words load during
-// the MFMAs.
+// nu (am + alpha gamma aq) is stored from the accumulators as float4 runs of
+// four rows (or, for an unaligned output stride, staged in LDS over the
+// decoded tile and written one record row at a time).  The next tile's
+// record words load during the MFMAs.
 constexpr int kDqT = 64;      // records per tile
 constexpr int kDqLd = 136;    // LDS row stride of a decoded record, in halves
 constexpr int kDqOut = 132;   // LDS row stride of a staged output record, in floats
@@ -379,35 +380,45 @@ __global__ void __launch_bounds__(256, 2) dequant128_kernel(GemmArgs a) {
         }
       }
     }
-    __syncthreads();                        // every wave is done with the decoded tile
     // element i of block cb: row 32 wave + 8 (i / 4) + 4 hh + i % 4, record 32 cb + col
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int rl = 32 * cb + col;
-      const float nu = nu_s[rl], ag = ag_s[rl];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 32 * wave + 8 * (i >> 2) + 4 * hh + (i & 3);
-        ot[rl * kDqOut + row] = nu * fmaf(ag, aq[cb][i], am[cb][i]);
-      }
-    }
-    __syncthreads();
     if (a.out_vec4) {
-      for (int k = tid; k < kDqT * 32; k += 256) {
-        const int rl = k >> 5, r4 = k & 31;
+      // four consecutive rows per (lane, i / 4): float4 stores straight from
+      // the accumulators, 32 contiguous bytes per record and instruction
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int rl = 32 * cb + col;
         const int64_t rec = r0 + rl;
-        if (rec < a.n_rec)
-          *(float4*)(a.out + (a.rec0 + rec) * a.out_ld + 4 * r4) =
-              *(const float4*)(ot + rl * kDqOut + 4 * r4);
+        const float nu = nu_s[rl], ag = ag_s[rl];
+        if (rec < a.n_rec) {
+          float* dst = a.out + (a.rec0 + rec) * a.out_ld + 32 * wave + 4 * hh;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(float4*)(dst + 8 * j) = make_float4(nu * fmaf(ag, aq[cb][4 * j], am[cb][4 * j]),
+                                                  nu * fmaf(ag, aq[cb][4 * j + 1], am[cb][4 * j + 1]),
+                                                  nu * fmaf(ag, aq[cb][4 * j + 2], am[cb][4 * j + 2]),
+                                                  nu * fmaf(ag, aq[cb][4 * j + 3], am[cb][4 * j + 3]));
+        }
       }
     } else {
+      __syncthreads();                      // every wave is done with the decoded tile
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int rl = 32 * cb + col;
+        const float nu = nu_s[rl], ag = ag_s[rl];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 32 * wave + 8 * (i >> 2) + 4 * hh + (i & 3);
+          ot[rl * kDqOut + row] = nu * fmaf(ag, aq[cb][i], am[cb][i]);
+        }
+      }
+      __syncthreads();
       for (int k = tid; k < kDqT * 128; k += 256) {
         const int rl = k >> 7, row = k & 127;
         const int64_t rec = r0 + rl;
         if (rec < a.n_rec) a.out[(a.rec0 + rec) * a.out_ld + row] = ot[rl * kDqOut + row];
       }
     }
-    __syncthreads();                        // the staging area is the next tile's decode buffer
+    __syncthreads();                        // the decode buffers (and staging) are free again
   }
 }
 
