@@ -350,9 +350,10 @@ def _line(args, metric, value, unit, workload, extra):
 
 def run_dequant(args):
     """tq_dequantize over one Llama-shaped layer's keys (8 KV heads x 32768
-    tokens, d = 128, b = 4: 262,144 records to fp32 vectors), and over the tiny
-    configuration (1024 keys, d = 128, b = 3).  Calls back to back between two
-    events on the launch stream."""
+    tokens, d = 128, b = 4: 262,144 records to fp32 vectors), and the tiny
+    configuration (1024 keys, d = 128, b = 3): its dequantize, quantize and
+    16 x 1024 logits.  Calls back to back between two events on the launch
+    stream."""
     import torch
     import kv_cache_vector_pi_amd as tq
     import workloads
@@ -385,6 +386,31 @@ def run_dequant(args):
         res[name] = {"n": n, "b": b, "ms_per_call": ms, "vec_per_s": n / (ms * 1e-3),
                      "GB_per_s": alg_bytes / (ms * 1e-3) / 1e9,
                      "TFLOP_per_s": alg_flops / (ms * 1e-3) / 1e12}
+        if name == "tiny":
+            # the rest of the tiny configuration: quantize the 1024 keys, and the
+            # 16 x 1024 logits of its queries (one KV head, G = 16)
+            q = workloads.tiny(dev)["Q"]
+            ss = torch.zeros(1, dtype=torch.int64, device=dev)
+            sl = torch.full((1,), n, dtype=torch.int32, device=dev)
+            lg = torch.empty((16, n), dtype=torch.float32, device=dev)
+            ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 1, 16, 1), dev)
+
+            def step_q():
+                tq.tq_quantize_kv(ctx, x, planes, norms)
+
+            def step_l():
+                tq.tq_attn_logits(ctx, q, 1, 16, 16 * d, planes, norms, 1, n, ss, sl, n,
+                                  1.0 / math.sqrt(d), lg, n, ws)
+            for fn, key in ((step_q, "quantize_ms_per_call"), (step_l, "logits_ms_per_call")):
+                for _ in range(args.warmup):
+                    fn()
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                e1.synchronize()
+                res[name][key] = e0.elapsed_time(e1) / reps
         del ctx
     big = res["llama_layer"]
     return _line(args, "dequantize: vectors/s from packed records", big["vec_per_s"], "vectors/s",
