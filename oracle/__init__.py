@@ -57,6 +57,8 @@ def lib():
         L.orc_unpack_record.argtypes = [i32, i32, P, P, P]
         L.orc_quantize.restype = None
         L.orc_quantize.argtypes = [i32, i32, P, P, P, i64, P, i64, P, P, P, P, P, P, P]
+        L.orc_qjl_given_codes.restype = None
+        L.orc_qjl_given_codes.argtypes = [i32, i32, P, P, P, i64, P, i64, P, P, P, P, P]
         L.orc_dequantize.restype = None
         L.orc_dequantize.argtypes = [i32, i32, P, P, P, i64, P, P, P, i64]
         L.orc_estimate.restype = None
@@ -199,6 +201,25 @@ def quantize(d, b, pi32, s32, cen32, x, margins=False):
                        _p(_c(cen32, np.float32)), n, _p(x), d, _p(planes), _p(norms),
                        _p(cm), _p(sm), _p(nu), _p(ga), _p(y))
     return out
+
+
+def qjl_given_codes(d, b, pi32, s32, cen32, x, idx):
+    """The QJL stage for given codes idx (int [n, d]) instead of the nearest
+    centroids: returns dict with planes (the given codes and the signs of
+    S (x/||x|| - Pi^T c[idx])), norms (uint16 [n, 2]), sign_margin ([n, d])
+    and gamma ([n], unrounded)."""
+    x = _c(x, np.float64).reshape(-1, d)
+    idx = _c(idx, np.int32).reshape(-1, d)
+    n = x.shape[0]
+    assert idx.shape[0] == n
+    planes = np.empty((n, record_words(d, b)), np.uint32)
+    norms = np.empty((n, 2), np.uint16)
+    sm = np.empty((n, d))
+    ga = np.empty(n)
+    lib().orc_qjl_given_codes(d, b, _p(_c(pi32, np.float32)), _p(_c(s32, np.float32)),
+                              _p(_c(cen32, np.float32)), n, _p(x), d, _p(idx), _p(planes),
+                              _p(norms), _p(sm), _p(ga))
+    return {"planes": planes, "norms": norms, "sign_margin": sm, "gamma": ga}
 
 
 def quantize_mse(d, b, pi32, cen32, x, margins=False):

@@ -482,6 +482,58 @@ ORC_API void orc_quantize(int32_t d, int32_t b, const float* pi, const float* s,
 }
 
 /* ------------------------------------------------------------------------ */
+/* The second stage for codes chosen elsewhere ([P1] two-stage section and
+ * [P3] QJL paragraph: 1-bit signs of the sketch of the residual that the
+ * codes leave; [P2] "potential challenges": its norm as one fp16 scalar):
+ *   nu = ||x||, xh = x / nu, r = xh - Pi^T c[idx], gamma = ||r||,
+ *   z = S r, s_i = +1 iff z_i >= 0,
+ * with idx[n*d] given rather than the nearest centroids.  Used to check the
+ * signs and gamma of a vector whose codes differ from orc_quantize's only at
+ * coordinates on a decision boundary: the residual depends on the codes.
+ * Outputs: packed records (the given codes and these signs), fp16 norms,
+ * sign_margin[n*d] = |z_i| and the unrounded gamma (both optional).
+ * A zero vector gets r = 0: gamma = 0 and all signs +1. */
+ORC_API void orc_qjl_given_codes(int32_t d, int32_t b, const float* pi, const float* s,
+                                 const float* cen, int64_t n, const double* x, int64_t ld,
+                                 const int32_t* idx_in, uint32_t* planes, uint16_t* norms,
+                                 double* sign_margin, double* gamma_out) {
+    int W = (d + 31) / 32;
+#pragma omp parallel
+    {
+        double* xh = (double*)malloc(sizeof(double) * d);
+        double* r = (double*)malloc(sizeof(double) * d);
+        int32_t* sg = (int32_t*)malloc(sizeof(int32_t) * d);
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < n; ++i) {
+            const double* xi = x + i * ld;
+            const int32_t* idx = idx_in + i * (int64_t)d;
+            double nu2 = 0.0;
+            for (int j = 0; j < d; ++j) nu2 += xi[j] * xi[j];
+            double nu = sqrt(nu2);
+            for (int j = 0; j < d; ++j) xh[j] = (nu > 0.0) ? xi[j] / nu : 0.0;
+            double g2 = 0.0;
+            for (int j = 0; j < d; ++j) {
+                double back = 0.0;
+                for (int jr = 0; jr < d; ++jr) back += (double)pi[(int64_t)jr * d + j] * (double)cen[idx[jr]];
+                r[j] = (nu > 0.0) ? xh[j] - back : 0.0;
+                g2 += r[j] * r[j];
+            }
+            for (int ir = 0; ir < d; ++ir) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) acc += (double)s[(int64_t)ir * d + j] * r[j];
+                sg[ir] = (acc >= 0.0) ? 1 : -1;
+                if (sign_margin) sign_margin[i * d + ir] = fabs(acc);
+            }
+            orc_pack_record(d, b, idx, sg, planes + i * (int64_t)W * b);
+            norms[2 * i] = orc_f16_from_double(nu);
+            norms[2 * i + 1] = orc_f16_from_double(sqrt(g2));
+            if (gamma_out) gamma_out[i] = sqrt(g2);
+        }
+        free(xh); free(r); free(sg);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantize ([P2] pseudo-code "dequant": y = centroids[idx], x = Pi^T y),
  * with the QJL term included so that <q, xt> equals the estimator below:
  *   xt = nu16 * (Pi^T c[idx] + alpha * gamma16 * S^T s),  alpha = sqrt(pi/2)/d.
