@@ -44,6 +44,18 @@
  *  32w..32w+31 (bit j%32 <-> coordinate j), word b-1 = QJL signs (1 <-> +1).
  *  Bits of coordinates >= d are 0.  norms: uint16 [n_records][2] holding the
  *  fp16 bit patterns of (nu, gamma).  A record is b*d bits + 4 bytes.
+ *  The b words of a word group are adjacent (rather than each plane being
+ *  contiguous over W words) so that one 16-byte load brings every plane of
+ *  32 coordinates at b = 4; the two norms share one 4-byte slot so one load
+ *  brings both.  Planes and norms are passed as two pointers, not a struct.
+ *
+ * Device arrays (seq_start, seq_len, slots) are never read on the host: their
+ * contents are not validated, and the caller keeps the logit ranges of
+ * different sequences disjoint.  Entry points that need scratch memory
+ * (prepared queries, chunk partials, search candidates, blocked-quantize
+ * residuals) take a caller workspace sized by the matching *_workspace_bytes
+ * call; tq_attn_logits also takes max_seq_len (an upper bound of seq_len)
+ * to size its grid without reading seq_len.
  *
  * Device pointers must come from the HIP device the context was created on;
  * `stream` is a hipStream_t (NULL = default stream).  Calls are asynchronous:

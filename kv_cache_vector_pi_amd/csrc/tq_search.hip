@@ -21,7 +21,12 @@
 // after each chunk of records folds them into the running top-k (score
 // descending, index ascending) and raises the threshold.
 //
-// Dequantization keeps the two-accumulator form on 16x16x32 tiles.
+// Dequantization has two kernels, picked by tq_dequantize: at d = 128 with
+// at least 64 records per compute unit, dequant128_kernel keeps each wave's
+// 32 rows of Pi^T and S^T in registers for a persistent loop over 64-record
+// tiles (32x32x16 MFMAs, output straight from the accumulators); every other
+// d, and smaller calls, run decoded_gemm_kernel in its two-accumulator form
+// on 16x16x32 tiles (the rows of Pi^T and S^T as the "queries").
 #include <algorithm>
 #include <cmath>
 

@@ -32,7 +32,7 @@ if not torch.cuda.is_available():
 
 import kv_cache_vector_pi_amd as tq  # noqa: E402
 import workloads  # noqa: E402
-from helpers import TOL, check_records, oracle_tables, rel_err_rows  # noqa: E402
+from helpers import TOL, check_records, oracle_tables, rel_err_rows, topk_order_ok  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -344,8 +344,12 @@ def test_llama_decode_fused(orc):
 
 @pytest.mark.parametrize("d,b", [(1536, 2), (1536, 4), (200, 2), (200, 4)])
 def test_vector_search_1m(orc, d, b):
+    """Top-10 of 1000 queries over 1e6 records as bench.py times it.  Every
+    query: each returned (index, score) pair against the oracle's estimate of
+    that one record, and the (score desc, index asc) order.  A deterministic
+    subset of 20 queries: the whole ranking against the oracle's scores of the
+    full database (staged parity on the GPU's records)."""
     k = 10
-    n_check = 2 if d > 512 else 3          # the oracle ranks the whole database per query
     say("search 1e6", d, b)
     ctx, pi, s, c = make_ctx(orc, d, b)
     wl = workloads.search(DEV, d)
@@ -367,18 +371,34 @@ def test_vector_search_1m(orc, d, b):
     tq.tq_search_topk(ctx, qs, n_q, planes, norms, n_db, k, oi, osc, ws)
     torch.cuda.synchronize()
     gi, gs = oi.cpu().numpy(), osc.cpu().numpy()
-    assert np.all(np.diff(gs, axis=1) <= 0)
+    assert np.all((gi >= 0) & (gi < n_db))
+    assert all(len(set(r.tolist())) == k for r in gi)
+    assert topk_order_ok(gi, gs)
+    qd = qs.double().cpu().numpy()
+    # every query: the returned pairs against the oracle's scores of those records
+    # (a row's rms over the database from a random sample of 4096 records)
+    uniq, inv = np.unique(gi, return_inverse=True)
+    inv = inv.reshape(gi.shape)
+    samp = rng.choice(n_db, 4096, replace=False)
+    UP, UN = np_records(planes, norms, np.concatenate([uniq, samp]))
+    nu_ = uniq.size
+    for a0 in range(0, n_q, 250):
+        sc = orc.estimate(d, b, pi, s, c, qd[a0:a0 + 250], UP, UN)
+        for a in range(a0, min(a0 + 250, n_q)):
+            ref = sc[a - a0, inv[a]]
+            rms = np.sqrt(np.mean(sc[a - a0, nu_:] ** 2))
+            assert np.all(np.abs(gs[a] - ref) <= TOL * np.maximum(np.abs(ref), rms)), a
+    # 20 queries: the ranking over the whole database
     allP = planes.cpu().numpy().view(np.uint32)
     allN = norms.cpu().numpy().view(np.uint16)
-    picks = [0, 517, n_q - 1][:n_check]
-    ref = orc.estimate(d, b, pi, s, c, qs[picks].double().cpu().numpy(), allP, allN)
+    picks = np.linspace(0, n_q - 1, 20).round().astype(int)
+    ref = orc.estimate(d, b, pi, s, c, qd[picks], allP, allN)
     del allP, allN
     for j, a in enumerate(picks):
         row = ref[j]
         rms = np.sqrt(np.mean(row ** 2))
         order = np.lexsort((np.arange(row.size), -row))
         kth = row[order[k - 1]]
-        assert len(set(gi[a].tolist())) == k
         for t in range(k):
             idx = gi[a, t]
             assert abs(gs[a, t] - row[idx]) <= TOL * max(abs(row[idx]), rms)

@@ -15,7 +15,7 @@ if not torch.cuda.is_available():
 
 import kv_cache_vector_pi_amd as tq  # noqa: E402
 import workloads  # noqa: E402
-from helpers import CODE_MARGIN, f16_ulp_diff, oracle_tables  # noqa: E402
+from helpers import check_records_mse, f16_ulp_diff, oracle_tables  # noqa: E402
 from test_gpu_parity import check_quantize  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -74,12 +74,7 @@ def test_quantize_ws_parity(orc, d, b, mse, dtype, n):
     xd = x.double().cpu().numpy()
     gp, gn = np_rec(P, N)
     if mse:
-        ref = orc.quantize_mse(d, b, pi, c, xd, margins=True)
-        gi = orc.unpack_codes_mse(d, b, gp)
-        ri = orc.unpack_codes_mse(d, b, ref["planes"])
-        assert not np.any((gi != ri) & (ref["code_margin"] >= CODE_MARGIN))
-        assert f16_ulp_diff(gn[:, 0], ref["norms"][:, 0]).max() <= 1
-        assert np.all(gn[:, 1] == 0)
+        check_records_mse(orc, d, b, pi, c, xd, gp, gn)
     else:
         check_quantize(orc, d, b, x.float(), pi, s, c, gp, gn)
     assert np.all(gn[7] == 0)

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
 
 import kv_cache_vector_pi_amd as tq  # noqa: E402
 import workloads  # noqa: E402
-from helpers import CODE_MARGIN, TOL, f16_ulp_diff, rel_err_rows  # noqa: E402
+from helpers import TOL, check_records_mse, f16_ulp_diff, rel_err_rows  # noqa: E402
 from test_gpu_parity import check_quantize  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -78,14 +78,9 @@ def test_split_quantize_parity(orc, dh, bh, dl, bl, mse, dtype, n_heads, n_tok):
     torch.cuda.synchronize()
     xd = x.reshape(n, dh + dl).double().cpu()
     if mse:
-        rh, rl = orc.split_quantize(ohi, olo, xd.numpy(), margins=True)
-        for (P, N), r, (d, b) in (((hp, hn), rh, (dh, bh)), ((lp, ln), rl, (dl, bl))):
-            gp, gn = np_rec(P, N)
-            gi = orc.unpack_codes_mse(d, b, gp)
-            ri = orc.unpack_codes_mse(d, b, r["planes"])
-            assert not np.any((gi != ri) & (r["code_margin"] >= CODE_MARGIN))
-            assert f16_ulp_diff(gn[:, 0], r["norms"][:, 0]).max() <= 1
-            assert np.all(gn[:, 1] == 0)
+        xn = xd.numpy()
+        check_records_mse(orc, dh, bh, ohi[2], ohi[4], xn[:, :dh], *np_rec(hp, hn))
+        check_records_mse(orc, dl, bl, olo[2], olo[4], xn[:, dh:], *np_rec(lp, ln))
     else:
         check_quantize(orc, dh, bh, xd[:, :dh], *ohi[2:], *np_rec(hp, hn))
         check_quantize(orc, dl, bl, xd[:, dh:], *olo[2:], *np_rec(lp, ln))
