@@ -33,6 +33,20 @@ tq_status hip_fail(hipError_t e, const char* what) {
   return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// bf16 bits of a finite float, rounded to nearest even, and back
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_value(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
 // ---------------------------------------------------------------------------
 // Seeded Gaussians.  SplitMix64 (Steele, Lea & Flood 2014) used as a
 // counter-based generator: output i of state s is mix(s + (i+1)*golden).
@@ -374,13 +388,26 @@ tq_status create_ctx(int32_t d, int32_t b, const float* pi, const float* s,
         h16[4 * dpp + 3 * rpp + (size_t)j * Dp + i] = sl;
       }
   }
+  // bf16 hi and mid parts of Pi (the raw-bf16 products of the d = 128
+  // quantizer): hi = bf16(Pi), mid = bf16(Pi - hi), both rounded to nearest
+  // even; Pi - hi is exact in fp32
+  std::vector<uint16_t> b16(2 * dpp, 0);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const float p = pi[(size_t)i * d + j];
+      const uint16_t hb = bf16_rne(p);
+      const float hv = bf16_value(hb);
+      b16[(size_t)i * Dp + j] = hb;
+      b16[dpp + (size_t)i * Dp + j] = bf16_rne(p - hv);
+    }
   const size_t bytes16 = (4 * dpp + 4 * rpp) * sizeof(__half);
   const size_t bytes32 = 4 * dd * sizeof(float);
+  const size_t bytesb = 2 * dpp * sizeof(uint16_t);
   void* blk = nullptr;
-  e = hipMalloc(&blk, bytes16 + bytes32);
+  e = hipMalloc(&blk, bytes16 + bytes32 + bytesb);
   if (e != hipSuccess) {
     delete ctx;
-    return fail(TQ_ERR_ALLOC, "tq_ctx_create: hipMalloc(%zu): %s", bytes16 + bytes32,
+    return fail(TQ_ERR_ALLOC, "tq_ctx_create: hipMalloc(%zu): %s", bytes16 + bytes32 + bytesb,
                 hipGetErrorString(e));
   }
   char* p = (char*)blk;
@@ -398,6 +425,8 @@ tq_status create_ctx(int32_t d, int32_t b, const float* pi, const float* s,
   e = hipMemcpy(p, h16.data(), bytes16, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(p + bytes16, t32.data(), 4 * dd * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(p + bytes16 + bytes32, b16.data(), bytesb, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(blk);
     delete ctx;
@@ -417,6 +446,8 @@ tq_status create_ctx(int32_t d, int32_t b, const float* pi, const float* s,
   ctx->t.st32 = (const float*)(p + bytes16) + dd;
   ctx->t.pi32 = (const float*)(p + bytes16) + 2 * dd;
   ctx->t.s32 = (const float*)(p + bytes16) + 3 * dd;
+  ctx->t.pib_hi = (const uint16_t*)(p + bytes16 + bytes32);
+  ctx->t.pib_mid = ctx->t.pib_hi + dpp;
   *out = ctx;
   return ok();
 }

@@ -21,6 +21,8 @@ struct DevTables {
   const __half* pi_lo;   // [Dp][Dp] fp16 of (Pi - pi_hi)
   const __half* m_hi;    // [Dp][Dp] M = S Pi^T (formed in double), hi part
   const __half* m_lo;    // [Dp][Dp] lo part
+  const uint16_t* pib_hi;   // [Dp][Dp] bf16 bits of Pi (round to nearest even)
+  const uint16_t* pib_mid;  // [Dp][Dp] bf16 bits of Pi - pib_hi
   const __half* pit_hi;  // [Rp][Dp] Pi^T hi/lo (rows padded to a multiple of 64)
   const __half* pit_lo;
   const __half* st_hi;   // [Rp][Dp] S^T hi/lo

@@ -137,6 +137,14 @@ __device__ inline float row8_sum(float x) {
   return x;
 }
 
+// Maximum over each group of 8 lanes (the row8_sum pattern with max).
+__device__ inline uint32_t row8_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true));
+  return x;
+}
+
 template <bool BF16>
 struct RawX {
   uint4 v[BF16 ? 4 : 8];

@@ -1,6 +1,10 @@
-// Quantization for head_dim 128, and 64 as token pairs: the kernel and its
-// launchers (the method and its organisation are described in tq_q128.h).
+// Quantization for head_dim 128, and 64 as token pairs: the kernels and their
+// launchers (the method and the organisation of each kernel are described
+// in tq_q128.h and tq_q128s.h).  bf16 input at d = 128 with a token count
+// that is a multiple of 32 (and no slot map) runs the pipelined kernel of
+// tq_q128s.h; everything else runs q128_tiles.
 #include "tq_q128.h"
+#include "tq_q128s.h"
 
 namespace tq {
 namespace {
@@ -24,6 +28,58 @@ hipError_t launch128(const Q128Args& a, int n_cu, hipStream_t st) {
   hipLaunchKernelGGL((quantize128_kernel<NB, BF16, MSE, D>), dim3((unsigned)grid), dim3(256), 0, st,
                      a);
   return hipGetLastError();
+}
+
+template <int NB, bool MSE>
+__global__ void __launch_bounds__(512, 4) quantize128s_kernel(Q128SArgs a) {
+  q128s_body<NB, MSE>(a);
+}
+
+template <int NB, bool MSE>
+hipError_t launch128s(const Q128SArgs& a, int n_cu, hipStream_t st) {
+  const uint32_t grid = std::min<uint32_t>(a.n_blocks, (uint32_t)n_cu * 2);
+  hipLaunchKernelGGL((quantize128s_kernel<NB, MSE>), dim3(grid), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+// bf16 at d = 128, n_tokens a multiple of 32, no slots: the pipelined kernel
+hipError_t launch_stream128(const tq_ctx* ctx, const void* x, int64_t n_tokens, int32_t n_heads,
+                            int64_t x_stride_token, int64_t x_stride_head, uint32_t* planes,
+                            uint16_t* norms, int64_t dst_stride_head, int64_t dst_token0,
+                            hipStream_t stream) {
+  Q128SArgs a{};
+  a.x = (const uint16_t*)x;
+  a.x_stride_token = x_stride_token;
+  a.x_stride_head = x_stride_head;
+  a.n_tokens = (uint32_t)n_tokens;
+  a.blk_per_head = (uint32_t)(n_tokens / kSB);
+  a.n_blocks = (uint32_t)((int64_t)n_heads * (n_tokens / kSB));
+  a.planes = planes;
+  a.norms = (uint32_t*)norms;
+  a.dst_stride_head = dst_stride_head;
+  a.dst_token0 = dst_token0;
+  a.pib_hi = ctx->t.pib_hi;
+  a.pib_mid = ctx->t.pib_mid;
+  a.m_hi = ctx->t.m_hi;
+  a.m_lo = ctx->t.m_lo;
+  const int KH = ctx->K / 2;
+  for (int k = 0; k < 4; ++k) {
+    a.thr[k] = (k < KH - 1) ? ctx->mid[KH + k] : 0.f;
+    a.cpos[k] = (k < KH) ? ctx->cent[KH + k] : 0.f;
+  }
+  const int n_cu = ctx->n_cu;
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: return launch128s<1, true>(a, n_cu, stream);
+      case 2: return launch128s<2, true>(a, n_cu, stream);
+      default: return launch128s<3, true>(a, n_cu, stream);
+    }
+  }
+  switch (ctx->b) {
+    case 2: return launch128s<2, false>(a, n_cu, stream);
+    case 3: return launch128s<3, false>(a, n_cu, stream);
+    default: return launch128s<4, false>(a, n_cu, stream);
+  }
 }
 
 // rows: tokens (D = 128) or token pairs (D = 64) per head
@@ -69,6 +125,10 @@ hipError_t launch_quantize128(const tq_ctx* ctx, const void* x, int32_t x_dtype,
                               int64_t x_stride_head, uint32_t* planes, uint16_t* norms,
                               int64_t dst_stride_head, int64_t dst_token0,
                               const int64_t* slots, hipStream_t stream) {
+  if (x_dtype == TQ_BF16 && !slots && n_tokens % kSB == 0 &&
+      (int64_t)n_heads * (n_tokens / kSB) < ((int64_t)1 << 32))
+    return launch_stream128(ctx, x, n_tokens, n_heads, x_stride_token, x_stride_head, planes,
+                            norms, dst_stride_head, dst_token0, stream);
   return launch_rows<128>(ctx, x, x_dtype, n_tokens, n_heads, x_stride_token, x_stride_head,
                           planes, norms, dst_stride_head, dst_token0, slots, stream);
 }

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
 
 import kv_cache_vector_pi_amd as tq  # noqa: E402
 import workloads  # noqa: E402
-from helpers import (TOL, check_records, clear_padding, oracle_tables,  # noqa: E402
+from helpers import (TOL, check_records, check_records_mse, clear_padding, oracle_tables,  # noqa: E402
                      rel_err_rows, topk_order_ok)
 
 pytestmark = pytest.mark.gpu
@@ -756,3 +756,77 @@ def test_repeat_calls_bit_identical(orc):
     assert torch.equal(o1, o2)
     assert torch.equal(d1, d2)
     assert torch.equal(s1[0], s2[0]) and torch.equal(s1[1], s2[1])
+
+
+# -------------------------------- d = 128 bf16 cache fills (pipelined kernel)
+def _stream_case(n_heads, n_tok, seed):
+    """[n_heads][n_tok][136] bf16 source (x = first 128 columns, strided
+    rows) with special vectors: zero, tiny (norm ~2^-75), huge (norm ~2^75),
+    one loud channel, and a vector of bf16 subnormals."""
+    base = workloads.normal((n_heads, n_tok, 136), seed, 10, DEV) * 1.4
+    x = base[:, :, :128]
+    if n_tok >= 8:
+        x[0, 1] = 0.0
+        x[0, 2] *= 2.0 ** -80
+        x[n_heads - 1, n_tok - 1] *= 2.0 ** 70
+        x[n_heads - 1, 3, 5] = 3.0e4
+        x[n_heads // 2, 4] *= 2.0 ** -130
+    return base.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("b,mse,n_heads,n_tok,cap,t0", [
+    (4, False, 1, 32, 32, 0),          # one block
+    (3, False, 2, 96, 100, 3),         # a few blocks, records offset in a larger cache
+    (2, False, 3, 4096, 4096, 0),      # several blocks per workgroup
+    (4, False, 40, 2048, 2050, 1),     # 2560 blocks over 512 workgroups: ragged last round
+    (1, True, 2, 160, 170, 5),         # MSE-only records
+    (2, True, 5, 1024, 1024, 0),
+    (3, True, 3, 2048, 2048, 0),
+])
+def test_quantize_stream_parity(orc, b, mse, n_heads, n_tok, cap, t0):
+    """bf16 fills at d = 128 with a token count that is a multiple of 32:
+    strided source rows and heads, records at h * cap + t0 + t of a larger
+    cache (neighbours untouched), special vectors; records against the
+    oracle (every row up to 8192 rows, else a sample plus every special row)."""
+    say("quantize stream", b, mse, n_heads, n_tok, cap, t0)
+    d = 128
+    if mse:
+        pi = orc.make_rotation(d, 0)[2]
+        c = orc.lloyd_max(d, b)[0].astype(np.float32)
+        ctx, s = tq.tq_ctx_create_mse(d, b, pi, c), None
+    else:
+        ctx, pi, s, c = ctx_for(orc, d, b)
+    src = _stream_case(n_heads, n_tok, 30 + b)
+    x = src[:, :, :d]
+    P, N = tq.alloc_records(n_heads * cap, d, b)
+    P.fill_(0x5A5A5A5A)
+    N.fill_(0x3C3C)
+    tq.tq_quantize_kv(ctx, x, P, N, n_tokens=n_tok, n_heads=n_heads,
+                      x_stride_token=x.stride(1), x_stride_head=x.stride(0),
+                      dst_stride_head=cap, dst_token0=t0)
+    torch.cuda.synchronize()
+    W = tq.tq_words_per_plane(d)
+    gp = P.cpu().numpy().view(np.uint32).reshape(n_heads, cap, W * b)
+    gn = N.cpu().numpy().view(np.uint16).reshape(n_heads, cap, 2)
+    assert np.all(gp[:, :t0] == 0x5A5A5A5A) and np.all(gp[:, t0 + n_tok:] == 0x5A5A5A5A)
+    assert np.all(gn[:, :t0] == 0x3C3C) and np.all(gn[:, t0 + n_tok:] == 0x3C3C)
+    rows = gp[:, t0:t0 + n_tok].reshape(n_heads * n_tok, -1)
+    nrm = gn[:, t0:t0 + n_tok].reshape(n_heads * n_tok, 2)
+    xd = x.reshape(-1, d).double().cpu().numpy()
+    n = n_heads * n_tok
+    if n > 8192:
+        special = [1, 2, 4, (n_heads // 2) * n_tok + 4, (n_heads - 1) * n_tok + 3, n - 1]
+        pick = np.unique(np.concatenate([
+            np.random.default_rng(5).choice(n, 4096, replace=False), special,
+            np.arange(64), np.arange(n - 64, n)]))
+    else:
+        pick = np.arange(n)
+    if mse:
+        stats = check_records_mse(orc, d, b, pi, c, xd[pick], rows[pick], nrm[pick])
+    else:
+        stats = check_records(orc, d, b, pi, s, c, xd[pick], rows[pick], nrm[pick])
+    say("ok", stats)
+    if n_tok >= 8:
+        assert np.all(nrm[1] == 0)              # the zero vector: nu = gamma = 0
+    if mse:
+        ctx.close()
