@@ -4,17 +4,17 @@
 // fp16 from the "potential challenges" section), with a different schedule.
 //
 //  * Blocks of 32 vectors (all in one head: the caller's token count is a
-//    multiple of 32) flow through a software pipeline.  In step j a wave
-//      - issues the copy of block j+5 from HBM straight into LDS
-//        (global_load_lds_dwordx4: no registers held while in flight),
-//      - computes the norms of block j+2 from LDS,
-//      - decides the codes of block j from Y(j) (computed in step j-1) and
-//        writes its residual to LDS,
-//      - runs the MFMAs of Z(j-1) = M r(j-1) and Y(j+1) = Pi x(j+1) between
-//        the code decisions, so the matrix cores work while the vector
-//        units decide codes,
-//      - takes the signs of Z(j-1) and stores block j-1's records,
-//    then waits for block j+3's copy and meets the other waves at one barrier.
+//    multiple of 32) flow through a software pipeline run by two roles of
+//    four waves each, which meet at one barrier per step.  In step j
+//      - the code waves decide the codes of block j from Y(j) (computed at
+//        the end of step j-1), write its residual to LDS, then run the MFMAs
+//        of Y(j+1) = Pi x(j+1);
+//      - the sketch waves run the MFMAs of Z(j-1) = M r(j-1) (while the code
+//        waves' vector units decide codes), take the signs and store block
+//        j-1's records and norms, issue the copy of block j+5 from HBM
+//        straight into LDS (global_load_lds_dwordx4: no registers held while
+//        in flight), compute the norms of block j+2 from LDS, and wait for
+//        block j+3's copy.
 //  * Y = Pi x runs on v_mfma_f32_32x32x16_bf16 straight on the raw bf16
 //    input, with Pi split into two bf16 parts (hi + mid, |Pi - hi - mid| <=
 //    2^-18 |Pi| elementwise), so no conversion of x is needed: the rotated
@@ -32,12 +32,13 @@
 //  * x rows land in LDS 256 bytes apart with their 16-byte chunks permuted
 //    (chunk c of row r at slot c ^ (r & 7)), so the MFMA operand reads of 8
 //    rows at one chunk hit distinct banks.
-//  * Wave w owns output coordinates 32w..32w+31; its slices of Pi (bf16 hi,
-//    mid) and M (fp16 hi, lo) stay in registers for the whole call.  Every
-//    wave stores its record words and (redundantly, identical values) the
-//    block's norms with all 64 lanes active, so each step issues a fixed
-//    number of memory instructions and the wait for a copy in flight can
-//    name its exact count.
+//  * Code wave w and sketch wave 4 + w own output coordinates 32w..32w+31;
+//    their slices of Pi (bf16 hi, mid) and of M (fp16 hi, lo) stay in
+//    registers for the whole call.  Every sketch wave stores its record
+//    words and (redundantly, identical values) the block's norms with all 64
+//    lanes active, so each step issues a fixed number of memory
+//    instructions and the wait for a copy in flight can name its exact
+//    count.
 #pragma once
 #include "tq_q128.h"
 
@@ -56,6 +57,7 @@ struct Q128SArgs {
   uint32_t n_tokens;                 // per head, a multiple of 32
   uint32_t n_blocks;                 // n_heads * n_tokens / 32
   uint32_t blk_per_head;             // n_tokens / 32
+  uint32_t div_m, div_s1, div_s2;    // block / blk_per_head by multiply-shift
   uint32_t* planes;
   uint32_t* norms;
   int64_t dst_stride_head, dst_token0;
@@ -66,6 +68,12 @@ struct Q128SArgs {
   float thr[4];                      // positive thresholds t_{K/2} .. t_{K-2}
   float cpos[4];                     // positive centroids c_{K/2} .. c_{K-1}
 };
+
+// n / blk_per_head (multiply-shift, as fast_div)
+__device__ inline uint32_t head_of(uint32_t n, const Q128SArgs& a) {
+  const uint32_t t = __umulhi(n, a.div_m);
+  return (t + ((n - t) >> a.div_s1)) >> a.div_s2;
+}
 
 // LDS byte address of a shared-memory object
 __device__ inline uint32_t lds_addr(const void* p) {
@@ -138,7 +146,7 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
   // with the row's chunk (slot ^ (row & 7))
   auto copy_block = [&](int j) {
     const uint32_t blk = g + (uint32_t)j * G;
-    const uint32_t h = blk / a.blk_per_head;
+    const uint32_t h = head_of(blk, a);
     const uint32_t t0 = (blk - h * a.blk_per_head) * kSB;
     const uint16_t* base = a.x + (int64_t)h * a.x_stride_head + (int64_t)t0 * a.x_stride_token;
     const int buf = j % kSD;
@@ -226,18 +234,29 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
       Ph[ks] = *(const v8bf*)(a.pib_hi + off);
       Pm[ks] = *(const v8bf*)(a.pib_mid + off);
     }
-    // Y(j): 16 MFMAs on block j's raw rows (chunk c of row r at slot c ^ (r & 7))
-    // (hi and mid products in two accumulators: two independent MFMA chains
-    // instead of one dependent chain of 16)
+    // Y(j): 16 MFMAs on block j's raw rows (chunk c of row r at slot c ^ (r & 7)),
+    // hi and mid products in two accumulators (two independent MFMA
+    // chains), the operand read of step ks + 1 issued before the MFMAs of
+    // step ks
     auto y_block = [&](v16f& acc, int j) {
       const uint16_t* xr = &xb[j % kSD][col * 128];
       v16f a1 = {}, a2 = {};
+      v8bf xf = *(const v8bf*)(xr + 8 * (hh ^ (col & 7)));
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const v8bf xf = *(const v8bf*)(xr + 8 * ((2 * ks + hh) ^ (col & 7)));
+        v8bf xn = xf;
+        if (ks < 7) xn = *(const v8bf*)(xr + 8 * ((2 * ks + 2 + hh) ^ (col & 7)));
         a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph[ks], xf, a1, 0, 0, 0);
         a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pm[ks], xf, a2, 0, 0, 0);
+        xf = xn;
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < 6; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       acc = a1 + a2;
     };
     // Codes of block j from acc = Y(j).  Element i of a lane is coordinate
@@ -328,23 +347,36 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): tables in before the copies start
-    // Z(j) = M r(j): 24 MFMAs on the residual's fp16 hi and lo parts
-    // (the hi x hi and hi x lo products in one accumulator and lo x hi in a
-    // second: two independent MFMA chains)
+    // Z(j) = M r(j): 24 MFMAs on the residual's fp16 hi and lo parts, in one
+    // accumulator (a second would not fit the register budget; the other
+    // waves' work fills the chain's gaps), with the operand reads of step
+    // ks + 1 issued before the MFMAs of step ks
     auto z_block = [&](v16f& z, int j) {
       z = v16f{};
       if constexpr (!MSE) {
-        v16f z2 = {};
+        const _Float16* rh = rh_s[j & 1] + col * kSR + 8 * hh;
+        const _Float16* rl = rl_s[j & 1] + col * kSR + 8 * hh;
+        v8h h0 = *(const v8h*)rh, l0 = *(const v8h*)rl;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const int off = col * kSR + 16 * ks + 8 * hh;
-          const v8h rf_h = *(const v8h*)(rh_s[j & 1] + off);
-          const v8h rf_l = *(const v8h*)(rl_s[j & 1] + off);
-          z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Mh[ks], rf_h, z, 0, 0, 0);
-          z2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ml[ks], rf_h, z2, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Mh[ks], rf_l, z, 0, 0, 0);
+          v8h h1 = h0, l1 = l0;
+          if (ks < 7) {
+            h1 = *(const v8h*)(rh + 16 * (ks + 1));
+            l1 = *(const v8h*)(rl + 16 * (ks + 1));
+          }
+          z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Mh[ks], h0, z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ml[ks], h0, z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_32x32x16_f16(Mh[ks], l0, z, 0, 0, 0);
+          h0 = h1;
+          l0 = l1;
         }
-        z += z2;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
       }
     };
     // signs of Z(j) and the stores of block j's record group grp and norms;
@@ -359,7 +391,7 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
         sw = halves_or(spread16(sb, hh));
       }
       const uint32_t blk = g + (uint32_t)j * G;
-      const uint32_t h = blk / a.blk_per_head;
+      const uint32_t h = head_of(blk, a);
       const uint32_t t0 = (blk - h * a.blk_per_head) * kSB;
       const int64_t rec = (int64_t)h * a.dst_stride_head + a.dst_token0 + t0 + col;
       uint32_t* gw = a.planes + (rec * 4 + grp) * NB;     // group grp of record col
@@ -398,21 +430,23 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
     __syncthreads();
     __syncthreads();            // the code waves' Y(0) is done with buffer 0
     for (int j = 0; j <= nb; ++j) {
-      if (j + kSD < nb) copy_block(j + kSD);
-      if (j + 2 < nb) norms_block(j + 2);
+      // Z first: its MFMAs run while the code waves decide codes
       if (j >= 1) {
         v16f z;
         z_block(z, j - 1);
         finish(z, j - 1);
       }
-      // block j + 3 must have landed before its norms in the next step:
-      // copies issued after it (2 per block, blocks j+4 .. min(j+kSD, nb-1))
-      // and stores (2 per step with j' >= 1, from the step that issued it on)
+      if (j + kSD < nb) copy_block(j + kSD);
+      if (j + 2 < nb) norms_block(j + 2);
+      // block j + 3 must have landed before its norms in the next step.
+      // Issued after it: copies of blocks j+4 .. min(j+kSD, nb-1) (2 each),
+      // and the stores of steps max(1, s+1) .. j (2 each), s the step that
+      // issued it (its own stores precede the copy; s < 0: the prologue)
       if (j + 3 < nb) {
-        const int issued_at = j + 3 - kSD;                 // < 0: the prologue
+        const int issued_at = j + 3 - kSD;
         const int last_copy = (j + kSD < nb ? j + kSD : nb - 1);
         int after = 2 * (last_copy - (j + 3));
-        const int from = issued_at < 0 ? 0 : issued_at;
+        const int from = issued_at < 0 ? 1 : issued_at + 1;
         for (int s = (from < 1 ? 1 : from); s <= j; ++s) after += 2;
         wait_vmcnt(after);
       }

@@ -53,6 +53,7 @@ hipError_t launch_stream128(const tq_ctx* ctx, const void* x, int64_t n_tokens, 
   a.x_stride_head = x_stride_head;
   a.n_tokens = (uint32_t)n_tokens;
   a.blk_per_head = (uint32_t)(n_tokens / kSB);
+  make_div(a.blk_per_head, a.div_m, a.div_s1, a.div_s2);
   a.n_blocks = (uint32_t)((int64_t)n_heads * (n_tokens / kSB));
   a.planes = planes;
   a.norms = (uint32_t*)norms;
