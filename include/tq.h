@@ -278,6 +278,26 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
                                 int64_t logits_stride_head, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* tq_attn_logits for callers that cannot allocate or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, launches and results, with the
+ * prepared query operands in a static device array of
+ * TQ_NOALLOC_SCRATCH_BYTES (4 MiB) that the library holds on each GPU until
+ * the process ends.  Allocates nothing.  A call whose prepared queries
+ * (tq_attn_logits_workspace_bytes of the same sizes) exceed that size returns
+ * TQ_ERR_INVALID_ARG.  Every call on one GPU shares the array, which keeps
+ * the last call's contents: calls that overlap on one GPU (other streams,
+ * other threads) race.  The context must come from tq_ctx_create on the
+ * device the call runs on (context creation looks the array up). */
+#define TQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+TQ_API tq_status tq_attn_logits_noalloc(const tq_ctx* ctx, const float* q, int32_t batch,
+                                        int32_t n_q_heads, int64_t q_stride_batch,
+                                        const uint32_t* planes, const uint16_t* norms,
+                                        int32_t n_kv_heads, int64_t keys_stride_head,
+                                        const int64_t* seq_start, const int32_t* seq_len,
+                                        int32_t max_seq_len, float scale, float* logits,
+                                        int64_t logits_stride_head, void* stream);
+
 /* The two halves of tq_attn_logits, for callers that reuse prepared queries
  * (several caches or chunks scored against the same queries) or time the key
  * stream on its own.  tq_attn_prepare rotates and projects the queries (Pi q,

@@ -28,7 +28,7 @@ EXPORTS = [
     "tq_status_string", "tq_last_error", "tq_words_per_plane", "tq_record_words",
     "tq_make_rotation", "tq_lloyd_max", "tq_ctx_create", "tq_ctx_destroy", "tq_ctx_dim",
     "tq_ctx_bits", "tq_quantize_kv", "tq_dequantize", "tq_attn_logits_workspace_bytes",
-    "tq_attn_logits", "tq_attn_prepare", "tq_attn_logits_prepared",
+    "tq_attn_logits", "tq_attn_logits_noalloc", "tq_attn_prepare", "tq_attn_logits_prepared",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_attn_output_workspace_bytes",
     "tq_attn_output", "tq_attn_decode_workspace_bytes", "tq_attn_decode",
     "tq_ctx_create_mse", "tq_ctx_is_mse", "tq_decode_step_prepare", "tq_quantize_kv_slots",
@@ -98,6 +98,8 @@ _sig("tq_attn_logits_workspace_bytes", _sz, [_P, _i32, _i32, _i32])
 _sig("tq_attn_logits", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P, _i32, _f32,
                               _P, _i64, _P, _sz, _P])
 _sig("tq_attn_prepare", _i32, [_P, _P, _i32, _i32, _i64, _i32, _P, _sz, _P])
+_sig("tq_attn_logits_noalloc", _i32, [_P, _P, _i32, _i32, _i64, _P, _P, _i32, _i64, _P, _P,
+                                     _i32, _f32, _P, _i64, _P])
 _sig("tq_attn_logits_prepared", _i32, [_P, _P, _sz, _i32, _i32, _P, _P, _i32, _i64, _P, _P, _i32,
                                        _f32, _P, _i64, _P])
 _sig("tq_attn_output_workspace_bytes", _sz, [_P, _i32, _i32, _i32, _i32])
@@ -321,6 +323,16 @@ def tq_attn_logits(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv
                              _ptr(logits), logits_stride_head, _ptr(workspace), ws_bytes,
                              _stream(stream))
     _check(st, "tq_attn_logits")
+
+
+def tq_attn_logits_noalloc(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv_heads,
+                           keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                           logits_stride_head, stream=None):
+    st = _lib.tq_attn_logits_noalloc(ctx.handle, _ptr(q), batch, n_q_heads, q_stride_batch,
+                                     _ptr(planes), _ptr(norms), n_kv_heads, keys_stride_head,
+                                     _ptr(seq_start), _ptr(seq_len), max_seq_len, float(scale),
+                                     _ptr(logits), logits_stride_head, _stream(stream))
+    _check(st, "tq_attn_logits_noalloc")
 
 
 def tq_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,

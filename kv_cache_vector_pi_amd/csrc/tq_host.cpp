@@ -351,6 +351,12 @@ tq_status create_ctx(int32_t d, int32_t b, const float* pi, const float* s,
     return hip_fail(e, "tq_ctx_create: device query");
   }
   if (ctx->n_cu < 1) ctx->n_cu = 1;
+  // the static scratch of tq_attn_logits_noalloc: its address on this device
+  e = tq::noalloc_scratch(ctx->device, nullptr);
+  if (e != hipSuccess) {
+    delete ctx;
+    return hip_fail(e, "tq_ctx_create: scratch symbol");
+  }
   const int Dp = ctx->Dp;
   const int Rp = (Dp + 63) / 64 * 64;
   const size_t dpp = (size_t)Dp * Dp;
@@ -710,6 +716,48 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
                                keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
                                logits_stride_head, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "tq_attn_logits: launch");
+  return ok();
+}
+
+TQ_API tq_status tq_attn_logits_noalloc(const tq_ctx* ctx, const float* q, int32_t batch,
+                                        int32_t n_q_heads, int64_t q_stride_batch,
+                                        const uint32_t* planes, const uint16_t* norms,
+                                        int32_t n_kv_heads, int64_t keys_stride_head,
+                                        const int64_t* seq_start, const int32_t* seq_len,
+                                        int32_t max_seq_len, float scale, float* logits,
+                                        int64_t logits_stride_head, void* stream) {
+  static const char* fn = "tq_attn_logits_noalloc";
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "%s: ctx is NULL", fn);
+  if (batch < 0 || max_seq_len < 0 || n_kv_heads < 1 || n_q_heads < 1 ||
+      n_q_heads % n_kv_heads != 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: batch=%d n_q=%d n_kv=%d max_seq_len=%d", fn, batch,
+                n_q_heads, n_kv_heads, max_seq_len);
+  if (batch == 0 || max_seq_len == 0) return ok();
+  if (!q || !planes || !norms || !seq_start || !seq_len || !logits)
+    return fail(TQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (q_stride_batch < (int64_t)n_q_heads * ctx->d && batch > 1)
+    return fail(TQ_ERR_INVALID_ARG, "%s: q_stride_batch too small", fn);
+  if (keys_stride_head < 0 || logits_stride_head < 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: negative stride", fn);
+  if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(q, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
+  if (need > (size_t)TQ_NOALLOC_SCRATCH_BYTES)
+    return fail(TQ_ERR_INVALID_ARG,
+                "%s: %zu bytes of prepared queries exceed the static scratch (%zu bytes); "
+                "use tq_attn_logits with a workspace", fn, need,
+                (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  hipError_t e = tq::noalloc_scratch(ctx->device, &ws);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_logits_noalloc: scratch symbol");
+  e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, ws,
+                              tq::logits_fold(ctx, n_q_heads, n_kv_heads), (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = tq::launch_attn_stream(ctx, ws, batch, n_q_heads, planes, norms, n_kv_heads,
+                               keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                               logits_stride_head, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "tq_attn_logits_noalloc: launch");
   return ok();
 }
 

@@ -102,6 +102,10 @@ hipError_t launch_decode_step_prepare(const tq_ctx* ctx, const void* k_new, cons
 
 size_t attn_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t n_q_heads,
                             int32_t n_kv_heads);
+// Device address of the static scratch of tq_attn_logits_noalloc on `device`
+// (looked up on the first call for a device, which must then be current;
+// context creation makes that call).
+hipError_t noalloc_scratch(int device, void** out);
 // fold: prepare the folded operand layout that the logit stream uses when
 // logits_fold() holds (the fused decode kernel reads the unfolded one)
 hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,

@@ -27,6 +27,7 @@
 //    (head, token) pair and finishes the logit on its own.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "tq_dev.h"
 #include "tq_internal.h"
@@ -657,6 +658,36 @@ hipError_t launch_split_stream(const tq_ctx* c1, const tq_ctx* c2, const void* w
     default: TQ_SPLIT(4, false, 4);
   }
 #undef TQ_SPLIT
+}
+
+// ---- static scratch of tq_attn_logits_noalloc ------------------------------
+// The prepared query operands of the entry point that allocates nothing live
+// in this file-scope device array instead of a caller workspace.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code the array's name is only a stand-in: its device address is looked up
+// once per device (hipGetSymbolAddress, at context creation with that device
+// current) and only that address is ever passed to a kernel.  Calls that
+// overlap on one GPU share the array and race.
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t noalloc_scratch(int device, void** out) {
+  if (device < 0 || device >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  if (out) *out = g_scratch_ptr[device];
+  return hipSuccess;
 }
 
 }  // namespace tq

@@ -128,6 +128,16 @@ static void validation() {
   EXPECT(tq_attn_logits(&ctx, x, 1, 4, 512, planes, norms, 1, 4, starts, lens, 4, 1.f, logits,
                         8, ws, sizeof(ws), nullptr) == TQ_ERR_HIP);
 
+  // the entry point without a workspace: too much prepared-query data for
+  // the static scratch, then (scratch lookup unavailable here) a HIP error
+  EXPECT(tq_attn_logits_noalloc(&ctx, x, 2000, 4, 512, planes, norms, 1, 4, starts, lens, 4, 1.f,
+                                logits, 8, nullptr) == TQ_ERR_INVALID_ARG);
+  EXPECT(std::strstr(tq_last_error(), "static scratch") != nullptr);
+  EXPECT(tq_attn_logits_noalloc(&ctx, x, 1, 4, 512, planes, norms, 3, 4, starts, lens, 4, 1.f,
+                                logits, 8, nullptr) == TQ_ERR_INVALID_ARG);
+  EXPECT(tq_attn_logits_noalloc(&ctx, x, 1, 4, 512, planes, norms, 1, 4, starts, lens, 4, 1.f,
+                                logits, 8, nullptr) == TQ_ERR_HIP);
+
   // search: k out of range, too small a workspace, then the launcher
   EXPECT(tq_search_topk(&ctx, x, 1, planes, norms, 4, 0, oidx, oscore, ws, sizeof(ws),
                         nullptr) == TQ_ERR_INVALID_ARG);

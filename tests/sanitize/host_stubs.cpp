@@ -41,7 +41,10 @@ hipError_t launch_decode_step_prepare(const tq_ctx*, const void*, const void*, i
                                       int32_t, int32_t, int64_t, int32_t, void*, hipStream_t) {
   return hipErrorNotSupported;
 }
-size_t attn_workspace_bytes(const tq_ctx*, int32_t, int32_t, int32_t) { return kStubBytes; }
+size_t attn_workspace_bytes(const tq_ctx*, int32_t batch, int32_t, int32_t n_kv) {
+  return kStubBytes * (size_t)(batch > 0 ? batch : 0) * (size_t)(n_kv > 0 ? n_kv : 0);
+}
+hipError_t noalloc_scratch(int, void**) { return hipErrorNotSupported; }
 hipError_t launch_attn_prepare(const tq_ctx*, const float*, int32_t, int32_t, int64_t, int32_t,
                                void*, bool, hipStream_t) {
   return hipErrorNotSupported;
