@@ -265,7 +265,11 @@ TQ_API size_t tq_attn_logits_workspace_bytes(const tq_ctx* ctx, int32_t batch,
  *   sized from it; the caller guarantees 0 <= seq_len[bi] <= max_seq_len and
  *   that the addressed records exist).
  * workspace: device memory of at least tq_attn_logits_workspace_bytes(),
- *   16-byte aligned; it is overwritten.
+ *   16-byte aligned; it may be overwritten.  With d <= 128 and at most 4
+ *   query heads per kv head the call is one launch that prepares the query
+ *   operands on chip and leaves the workspace untouched (same results as
+ *   tq_attn_prepare + tq_attn_logits_prepared, bit for bit); otherwise the
+ *   prepared operands go through the workspace.
  * Errors: TQ_ERR_INVALID_ARG for NULL pointers with work to do, batch < 0,
  * n_kv_heads < 1, n_q_heads % n_kv_heads != 0, a too small workspace,
  * misaligned planes/workspace.  batch == 0 or max_seq_len == 0 is a no-op. */
@@ -280,15 +284,18 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
 
 /* tq_attn_logits for callers that cannot allocate or pass a workspace (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
- * allocation): the same computation, launches and results, with the
- * prepared query operands in a static device array of
- * TQ_NOALLOC_SCRATCH_BYTES (4 MiB) that the library holds on each GPU until
- * the process ends.  Allocates nothing.  A call whose prepared queries
- * (tq_attn_logits_workspace_bytes of the same sizes) exceed that size returns
- * TQ_ERR_INVALID_ARG.  Every call on one GPU shares the array, which keeps
- * the last call's contents: calls that overlap on one GPU (other streams,
- * other threads) race.  The context must come from tq_ctx_create on the
- * device the call runs on (context creation looks the array up). */
+ * allocation): the same computation, launches and results.  Where
+ * tq_attn_logits is one launch (d <= 128, at most 4 query heads per kv
+ * head) it needs no memory beyond its arguments; otherwise the prepared
+ * query operands go to a static device array of TQ_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) that the library holds on each GPU until the process ends.
+ * Allocates nothing.  On that two-launch path a call whose prepared queries
+ * (tq_attn_logits_workspace_bytes of the same sizes) exceed the array
+ * returns TQ_ERR_INVALID_ARG; every call on one GPU shares the array, which
+ * keeps the last call's contents, so such calls that overlap on one GPU
+ * (other streams, other threads) race.  The context must come from
+ * tq_ctx_create on the device the call runs on (context creation looks the
+ * array up). */
 #define TQ_NOALLOC_SCRATCH_BYTES (4u << 20)
 TQ_API tq_status tq_attn_logits_noalloc(const tq_ctx* ctx, const float* q, int32_t batch,
                                         int32_t n_q_heads, int64_t q_stride_batch,

@@ -708,9 +708,17 @@ TQ_API tq_status tq_attn_logits(const tq_ctx* ctx, const float* q, int32_t batch
     return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits: workspace %zu < %zu bytes", workspace_bytes,
                 need);
   if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "tq_attn_logits: scale not finite");
-  hipError_t e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads,
-                                         workspace, tq::logits_fold(ctx, n_q_heads, n_kv_heads),
-                                         (hipStream_t)stream);
+  // one launch where the resident stream applies (the workspace stays unused)
+  hipError_t e;
+  if (tq::attn_one_applies(ctx, n_q_heads, n_kv_heads)) {
+    e = tq::launch_attn_one(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv_heads,
+                            keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                            logits_stride_head, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tq_attn_logits: launch");
+    return ok();
+  }
+  e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, workspace,
+                              tq::logits_fold(ctx, n_q_heads, n_kv_heads), (hipStream_t)stream);
   if (e == hipSuccess)
     e = tq::launch_attn_stream(ctx, workspace, batch, n_q_heads, planes, norms, n_kv_heads,
                                keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
@@ -742,6 +750,16 @@ TQ_API tq_status tq_attn_logits_noalloc(const tq_ctx* ctx, const float* q, int32
   if (!aligned(planes, 16) || !aligned(norms, 4) || !aligned(q, 4))
     return fail(TQ_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
   if (!std::isfinite(scale)) return fail(TQ_ERR_INVALID_ARG, "%s: scale not finite", fn);
+  // one launch where the resident stream applies: no scratch at all
+  hipError_t e;
+  if (tq::attn_one_applies(ctx, n_q_heads, n_kv_heads)) {
+    e = tq::launch_attn_one(ctx, q, batch, n_q_heads, q_stride_batch, planes, norms, n_kv_heads,
+                            keys_stride_head, seq_start, seq_len, max_seq_len, scale, logits,
+                            logits_stride_head, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tq_attn_logits_noalloc: launch");
+    return ok();
+  }
+  // otherwise the two launches, with the prepared queries in the static scratch
   const size_t need = tq::attn_workspace_bytes(ctx, batch, n_q_heads, n_kv_heads);
   if (need > (size_t)TQ_NOALLOC_SCRATCH_BYTES)
     return fail(TQ_ERR_INVALID_ARG,
@@ -749,7 +767,7 @@ TQ_API tq_status tq_attn_logits_noalloc(const tq_ctx* ctx, const float* q, int32
                 "use tq_attn_logits with a workspace", fn, need,
                 (size_t)TQ_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  hipError_t e = tq::noalloc_scratch(ctx->device, &ws);
+  e = tq::noalloc_scratch(ctx->device, &ws);
   if (e != hipSuccess) return hip_fail(e, "tq_attn_logits_noalloc: scratch symbol");
   e = tq::launch_attn_prepare(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, ws,
                               tq::logits_fold(ctx, n_q_heads, n_kv_heads), (hipStream_t)stream);

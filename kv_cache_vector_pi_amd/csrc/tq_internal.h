@@ -114,6 +114,16 @@ hipError_t launch_attn_prepare(const tq_ctx* ctx, const float* q, int32_t batch,
 // whether tq_attn_logits' stream reads a folded preparation (d <= 64 on the
 // resident kernel)
 bool logits_fold(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads);
+// The whole logit call in one launch (query preparation inside the stream
+// kernel, no workspace), where attn_one_applies: the resident stream with
+// d <= 128 and at most 4 query heads per kv head.
+bool attn_one_applies(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads);
+hipError_t launch_attn_one(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,
+                           int64_t q_stride_batch, const uint32_t* planes, const uint16_t* norms,
+                           int32_t n_kv_heads, int64_t keys_stride_head,
+                           const int64_t* seq_start, const int32_t* seq_len,
+                           int32_t max_seq_len, float scale, float* logits,
+                           int64_t logits_stride_head, hipStream_t stream);
 hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t batch,
                               int32_t n_q_heads, const uint32_t* planes, const uint16_t* norms,
                               int32_t n_kv_heads, int64_t keys_stride_head,

@@ -204,8 +204,13 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // shifts 4 (g >> 1) .. +3), so one MFMA covers all 64 coordinates and each
 // Walsh subset (and the sign plane) takes one call instead of two; the query
 // operands are prepared in the same folded layout.
+// The stream of one wave: tokens [t_begin, t_begin + chunk) of sequence bi
+// against kv head h, with the prepared operands of the first record set in
+// Asm (LDS, NC x 64 lanes, then those of set2) and the per-head constants of
+// lane group g in cst / cst2.
 template <int NB, bool MSE, int U, int NB2, bool FOLD>
-__global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
+__device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, float4 cst,
+                                           float4 cst2, int h, int bi, int t_begin, int chunk) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
   constexpr bool SPLIT = NB2 > 0;
   constexpr int HALVES = FOLD ? 1 : 2;                 // MFMA calls per bit set
@@ -217,24 +222,9 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   constexpr int NV2 = 1 << (CP2 - 1);
   constexpr int NC2 = SPLIT ? HALVES * (NV2 + (MSE ? 0 : 1)) : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int g = lane >> 4, n = lane & 15;
-  const int h = blockIdx.y, bi = blockIdx.z;
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
-  const int chunk = a.tiles_per_wave * kTile;
-  const size_t rbb = (size_t)NC * 64 * 16 + 64;
-  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
-  const size_t rbb2 = (size_t)NC2 * 64 * 16 + 64;
-  const char* wsb2 = a.set2.ws + ((size_t)bi * a.n_kv + h) * rbb2;
-  // the 4 waves share (sequence, kv head): the prepared operands are read
-  // from memory once per workgroup
-  __shared__ v4i Asm[(NC + (SPLIT ? NC2 : 0)) * 64];
-  for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
-  if constexpr (SPLIT)
-    for (int i = threadIdx.x; i < NC2 * 64; i += 256) Asm[NC * 64 + i] = ((const v4i*)wsb2)[i];
-  __syncthreads();
-  const int t_begin = (blockIdx.x * kWaves + wave) * chunk;
   if (t_begin >= len) return;
   const int t_end = min(len, t_begin + chunk);
   const int n_tok = t_end - t_begin;
@@ -288,12 +278,11 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   }
   // per-head constants with the logit scale and the QJL factor folded in:
   // logit = nu * (vm X + Z + gamma (vq Y + W))
-  const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
   const float cX = a.scale * cst.x, cZ = a.scale * cst.z;
   const float cY = a.scale * a.alpha * cst.y, cW = a.scale * a.alpha * cst.w;
   float cX2 = 0.f, cZ2 = 0.f, cY2 = 0.f, cW2 = 0.f;
   if constexpr (SPLIT) {
-    const float4 c2 = ((const float4*)(wsb2 + (size_t)NC2 * 64 * 16))[g];
+    const float4 c2 = cst2;
     cX2 = a.scale * c2.x;
     cZ2 = a.scale * c2.z;
     cY2 = a.scale * a.set2.alpha * c2.y;
@@ -404,6 +393,196 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
     load(g0, tl + 2 * kTile * U);
     compute(g1, tl + kTile * U);
   }
+}
+
+// Stream over operands prepared beforehand in the workspace.  grid = (token
+// chunks, kv heads, batch); the 4 waves of a workgroup share (sequence, kv
+// head), so the prepared operands are read from memory once per workgroup.
+template <int NB, bool MSE, int U, int NB2, bool FOLD>
+__global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
+  constexpr bool SPLIT = NB2 > 0;
+  constexpr int HALVES = FOLD ? 1 : 2;
+  constexpr int CP = MSE ? NB : NB - 1;
+  constexpr int NC = HALVES * ((1 << (CP - 1)) + (MSE ? 0 : 1));
+  constexpr int NBs = SPLIT ? NB2 : NB;
+  constexpr int CP2 = MSE ? NBs : NBs - 1;
+  constexpr int NC2 = SPLIT ? HALVES * ((1 << (CP2 - 1)) + (MSE ? 0 : 1)) : 1;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const size_t rbb = (size_t)NC * 64 * 16 + 64;
+  const char* wsb = a.ws + ((size_t)bi * a.n_kv + h) * rbb;
+  const size_t rbb2 = (size_t)NC2 * 64 * 16 + 64;
+  const char* wsb2 = a.set2.ws + ((size_t)bi * a.n_kv + h) * rbb2;
+  __shared__ v4i Asm[(NC + (SPLIT ? NC2 : 0)) * 64];
+  for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
+  if constexpr (SPLIT)
+    for (int i = threadIdx.x; i < NC2 * 64; i += 256) Asm[NC * 64 + i] = ((const v4i*)wsb2)[i];
+  __syncthreads();
+  const int g = (threadIdx.x & 63) >> 4;
+  const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
+  float4 cst2 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (SPLIT) cst2 = ((const float4*)(wsb2 + (size_t)NC2 * 64 * 16))[g];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+  const int chunk = a.tiles_per_wave * kTile;
+  res_stream<NB, MSE, U, NB2, FOLD>(a, Asm, cst, cst2, h, bi,
+                                    (blockIdx.x * kWaves + wave) * chunk, chunk);
+}
+
+// One launch for a whole call: each workgroup of 16 waves first prepares the
+// query operands of its (sequence, kv head) into LDS -- the work and the
+// arithmetic of attn_prep_kernel (prep_block), so the operands are bit for
+// bit those of the two-launch form -- then its waves stream their tiles.
+// Waves 0-3 prepare the code part, waves 4-7 the sign part (two-stage
+// records); the rest only meet the barriers.  No workspace, and no wait on
+// another workgroup: the preparation is repeated by every workgroup of a
+// (sequence, kv head), so the grid is sized to one workgroup per CU.
+constexpr int kOneWaves = 16;
+template <int NB, bool MSE, bool FOLD>
+__global__ void __launch_bounds__(64 * kOneWaves) attn_logits_one_kernel(AttnArgs a, PrepArgs p) {
+  constexpr int HALVES = FOLD ? 1 : 2;
+  constexpr int CP = MSE ? NB : NB - 1;
+  constexpr int NC = HALVES * ((1 << (CP - 1)) + (MSE ? 0 : 1));
+  constexpr int kD = 128;                      // d <= 128 (W <= 4) on this path
+  __shared__ float qv[4 * kD];                 // coordinate j of slot hh at 4j + hh
+  __shared__ float outp[2][4 * kD];            // per part: [slot][Dp]
+  __shared__ float red[2][64 * 32];            // per part: [4 waves][16][nq], nq <= 32
+  __shared__ int qfix_e[2][4];
+  __shared__ __align__(16) char abuf[NC * 64 * 16 + 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const int part = tid >> 8, ptid = tid & 255, pwave = ptid >> 6;
+  const bool act = part < p.n_parts;           // uniform per wave
+  const int d = p.d, Dp = 32 * p.W, nq = p.nq, nj = 256 / nq;
+  const float* tab = part ? p.st : p.pit;
+  float* out = outp[part & 1];
+  float* rd = red[part & 1];
+
+  // Dp <= 4 nq: one chunk of outputs, as prep_block at these sizes; a
+  // thread's table rows (at most 16: jl = 16 at d = 128) are all requested
+  // before the queries are staged, so the two memory round trips overlap
+  const int quad = ptid & (nq - 1), jg = ptid / nq;
+  const int jl = (d + nj - 1) / nj;
+  const int ja = min(d, jg * jl), jb = min(d, ja + jl);
+  const int r = 4 * quad;
+  const bool rows = act && r < d;
+  float4 t[16];
+  if (rows) {
+    const float* tr = tab + r;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (ja + u < jb) t[u] = *(const float4*)(tr + (int64_t)(ja + u) * d);
+  }
+  for (int it = tid; it < 4 * d; it += 64 * kOneWaves) {
+    const int hh = it / d, j = it - hh * d;
+    qv[4 * j + hh] = hh < p.G
+        ? p.q[(int64_t)bi * p.q_stride_batch + (int64_t)(h * p.G + hh) * p.q_stride_head + j]
+        : 0.f;
+  }
+  __syncthreads();
+  if (act) {
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+    if (rows) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (ja + u < jb) {
+          const float4 qq = *(const float4*)&qv[4 * (ja + u)];
+          const float tv[4] = {t[u].x, t[u].y, t[u].z, t[u].w}, qs[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(tv[e], qs[i], acc[i][e]);
+        }
+      }
+    }
+    for (int off = nq; off < 64; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
+    if (lane < nq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rd[(pwave * 16 + 4 * i + e) * nq + quad] = acc[i][e];
+  }
+  __syncthreads();
+  if (act) {
+    for (int it = ptid; it < 16 * nq; it += 256) {
+      const int k = it / nq, qd = it - k * nq;
+      const float v = (rd[k * nq + qd] + rd[(16 + k) * nq + qd]) +
+                      (rd[(32 + k) * nq + qd] + rd[(48 + k) * nq + qd]);
+      const int o = 4 * qd + (k & 3);
+      if (o < Dp) out[(k >> 2) * Dp + o] = v;
+    }
+  }
+  __syncthreads();
+  float* cdst_base = (float*)(abuf + (size_t)NC * 64 * 16);
+  if (act) {
+    const float* r1 = out + pwave * Dp;
+    float m1 = 0.f, t1 = 0.f;
+    for (int j = lane; j < Dp; j += 64) {
+      m1 = fmaxf(m1, fabsf(r1[j]));
+      t1 += r1[j];
+    }
+    m1 = wave_max(m1);
+    t1 = wave_sum(t1);
+    if (lane == 0) {
+      float wmax = 2.f;
+      if (part == 0) {
+        wmax = 0.f;
+        for (int v = 0; v < p.nv; ++v) wmax = fmaxf(wmax, fabsf(p.wm2[v]));
+      }
+      const float vmax = wmax * m1;
+      int e = 0;
+      if (vmax > 0.f) { int ex; frexpf(vmax, &ex); e = min(30 - ex, 120); }
+      qfix_e[part][pwave] = e;
+      float* cdst = cdst_base + 4 * pwave;
+      if (part == 0) {
+        cdst[0] = ldexpf(1.f, -e);
+        cdst[2] = p.c0 * t1;
+        if (p.n_parts == 1) {
+          cdst[1] = 0.f;
+          cdst[3] = 0.f;
+        }
+      } else {
+        cdst[1] = ldexpf(1.f, -e);
+        cdst[3] = -t1;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    // the operands of both parts, spread over all 16 waves
+    const int code_calls = p.fold ? p.nv : 2 * p.nv;
+    const int sign_calls = p.nc - code_calls;
+    const int items0 = 4 * code_calls * 4, items = items0 + (p.n_parts > 1 ? 4 * sign_calls * 4 : 0);
+    for (int it = tid; it < items; it += 64 * kOneWaves) {
+      const int pt = it >= items0;
+      const int n_c = pt ? sign_calls : code_calls;
+      const int i = it - (pt ? items0 : 0);
+      const int g = i & 3, rest = i >> 2;
+      const int cl = rest % n_c, hh = rest / n_c;
+      const int c = (pt ? code_calls : 0) + cl;
+      const int w = p.fold ? (g & 1) : g;
+      const int kbase = p.fold ? 4 * (g >> 1) : (pt ? 4 * cl : 4 * (c % 2));
+      const float wv = pt ? 2.f : p.wm2[p.fold ? c : c / 2];
+      uint4 o[4];
+      limb_operands(outp[pt] + hh * Dp, qfix_e[pt][hh], wv, w, p.W, d, kbase, o);
+      uint4* dst = (uint4*)(abuf + ((size_t)c * 64 + 16 * g + 4 * hh) * 16);
+#pragma unroll
+      for (int L = 0; L < 4; ++L) dst[L] = o[L];
+    }
+  }
+  __syncthreads();
+  const int g = lane >> 4;
+  const float4 cst = ((const float4*)cdst_base)[g];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = a.tiles_per_wave * kTile;
+  res_stream<NB, MSE, 4, 0, FOLD>(a, (const v4i*)abuf, cst, make_float4(0.f, 0.f, 0.f, 0.f), h,
+                                  bi, (blockIdx.x * kOneWaves + wave) * chunk, chunk);
 }
 
 template <typename K>
@@ -565,6 +744,67 @@ hipError_t launch_attn_stream(const tq_ctx* ctx, const void* workspace, int32_t 
     default: TQ_LOGITS(4, false);
   }
 #undef TQ_LOGITS
+}
+
+namespace {
+
+template <int NB, bool MSE, bool FOLD>
+hipError_t launch_one(const AttnArgs& a, const PrepArgs& p, int n_cu, int32_t batch,
+                      int32_t n_kv_heads, int32_t max_seq_len, hipStream_t stream) {
+  // one workgroup per CU: the tiles per wave that cover every tile in one
+  // round (at most 256, beyond which further rounds repeat the preparation)
+  AttnArgs b = a;
+  const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
+  const int64_t tiles_total = (int64_t)batch * n_kv_heads * tiles_seq;
+  const int64_t waves = (int64_t)n_cu * kOneWaves;
+  const int64_t tpw = std::max<int64_t>(1, std::min<int64_t>(256, (tiles_total + waves - 1) / waves));
+  b.tiles_per_wave = (int)tpw;
+  const int64_t tok_per_block = (int64_t)kOneWaves * tpw * kTile;
+  const dim3 grid((unsigned)((max_seq_len + tok_per_block - 1) / tok_per_block), n_kv_heads,
+                  batch);
+  hipLaunchKernelGGL((attn_logits_one_kernel<NB, MSE, FOLD>), grid, dim3(64 * kOneWaves), 0,
+                     stream, b, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_one_applies(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads) {
+  return ctx->d <= 128 && resident_ok(ctx, (n_q_heads / n_kv_heads + 3) / 4);
+}
+
+hipError_t launch_attn_one(const tq_ctx* ctx, const float* q, int32_t batch, int32_t n_q_heads,
+                           int64_t q_stride_batch, const uint32_t* planes, const uint16_t* norms,
+                           int32_t n_kv_heads, int64_t keys_stride_head,
+                           const int64_t* seq_start, const int32_t* seq_len,
+                           int32_t max_seq_len, float scale, float* logits,
+                           int64_t logits_stride_head, hipStream_t stream) {
+  if (!attn_one_applies(ctx, n_q_heads, n_kv_heads)) return hipErrorInvalidValue;
+  const bool fold = ctx->W <= 2;
+  PrepArgs p;
+  size_t shm;
+  dim3 pgrid;
+  prep_args(ctx, q, batch, n_q_heads, q_stride_batch, n_kv_heads, nullptr, p, shm, pgrid, fold);
+  const AttnArgs a = stream_args(ctx, nullptr, n_q_heads, planes, norms, n_kv_heads,
+                                 keys_stride_head, seq_start, seq_len, scale, logits,
+                                 logits_stride_head);
+  const int n_cu = ctx->n_cu;
+#define TQ_ONE(NB, MSE)                                                                        \
+  return fold ? launch_one<NB, MSE, true>(a, p, n_cu, batch, n_kv_heads, max_seq_len, stream) \
+              : launch_one<NB, MSE, false>(a, p, n_cu, batch, n_kv_heads, max_seq_len, stream)
+  if (ctx->mse) {
+    switch (ctx->b) {
+      case 1: TQ_ONE(1, true);
+      case 2: TQ_ONE(2, true);
+      default: TQ_ONE(3, true);
+    }
+  }
+  switch (ctx->b) {
+    case 2: TQ_ONE(2, false);
+    case 3: TQ_ONE(3, false);
+    default: TQ_ONE(4, false);
+  }
+#undef TQ_ONE
 }
 
 bool logits_fold(const tq_ctx* ctx, int32_t n_q_heads, int32_t n_kv_heads) {

@@ -41,6 +41,45 @@ __device__ inline float wave_max(float v) {
 }
 
 
+// The A operands of one (slot hh, word step wsi, call c, lane group g): 16
+// bytes for each of the four lanes 16 g + 4 hh + L, L the limb.  For shift
+// k = kbase + sidx (sidx < 4) and byte el of the word, the weight of a bit is
+// A' = round(Q / 2^k) (negated for k = 7, where the byte reads -128), Q the
+// fixed-point weight round(2^e wv src[j]) of coordinate j = 32 w + 8 el + k
+// (0 beyond d); limb L is the balanced base-256 digit
+// ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that byte ^ 0x80.
+// Each A' is formed once; the four values of a shift (el = 0..3) carry
+// their limbs in bytes 0..3 (x_el = biased A' ^ 0x80808080), and a 4 x 4 byte
+// transpose (8 v_perm_b32) gives limb L's word: byte el = byte L of x_el.
+__device__ inline void limb_operands(const float* src, int e, float wv, int w, int W, int d,
+                                     int kbase, uint4 (&o)[4]) {
+  uint32_t word[4][4];
+#pragma unroll
+  for (int sidx = 0; sidx < 4; ++sidx) {
+    const int k = kbase + sidx;
+    uint32_t x[4];
+#pragma unroll
+    for (int el = 0; el < 4; ++el) {
+      const int j = 32 * w + 8 * el + k;
+      const int Q = (w < W && j < d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
+      const int Ap = (k < 7) ? dev::shift_round(Q, k) : -dev::shift_round(Q, 7);
+      x[el] = ((uint32_t)Ap + 0x80808080u) ^ 0x80808080u;
+    }
+    // v_perm_b32 (s0, s1, sel): result byte i = byte sel_i of {s0 (bytes
+    // 4..7), s1 (bytes 0..3)}
+    const uint32_t t0 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);   // x0.0 x1.0 x0.1 x1.1
+    const uint32_t t1 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);   // x0.2 x1.2 x0.3 x1.3
+    const uint32_t t2 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);   // x2.0 x3.0 x2.1 x3.1
+    const uint32_t t3 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);   // x2.2 x3.2 x2.3 x3.3
+    word[0][sidx] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);           // x0.0 x1.0 x2.0 x3.0
+    word[1][sidx] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);           // x0.1 x1.1 x2.1 x3.1
+    word[2][sidx] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);           // x0.2 x1.2 x2.2 x3.2
+    word[3][sidx] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);           // x0.3 x1.3 x2.3 x3.3
+  }
+#pragma unroll
+  for (int L = 0; L < 4; ++L) o[L] = make_uint4(word[L][0], word[L][1], word[L][2], word[L][3]);
+}
+
 // Query preparation: one block per (row block of 4 q heads and part, kv
 // head, batch).  Part 0 computes Pi q and the A operands of the code calls,
 // part 1 (two-stage records only) S q and those of the sign calls.  Outputs
@@ -197,16 +236,13 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
   // when folded), then the sign calls
   const int code_calls = a.fold ? a.nv : 2 * a.nv;
   const int c_begin = part ? code_calls : 0, n_c = part ? a.nc - code_calls : code_calls;
-  // items: (slot hh, ws, call, lane group g, limb L) -> 16 bytes of lane
-  // (16g + 4hh + L).  The weight of a bit at shift k is A' = round(Q / 2^k)
-  // (negated for k = 7, where the byte reads -128), Q the fixed-point weight
-  // (-2 w_vec Pi q, or 2 S q for the sign plane); its balanced base-256
-  // digit L is ((A' + 0x80808080) >> 8L) & 255, minus 128 -- stored as that
-  // byte ^ 0x80.
-  const int items = 4 * nws * n_c * 16;
+  // items: (slot hh, ws, call, lane group g) -> the 16 bytes of each lane
+  // (16g + 4hh + L), L < 4 (limb_operands); Q is -2 w_vec Pi q, or 2 S q for
+  // the sign plane
+  const int items = 4 * nws * n_c * 4;
   for (int it = tid; it < items; it += 256) {
-    const int L = it & 3, g = (it >> 2) & 3;
-    const int rest = it >> 4;
+    const int g = it & 3;
+    const int rest = it >> 2;
     const int cl = rest % n_c, wsi = (rest / n_c) % nws, hh = rest / (n_c * nws);
     const int c = c_begin + cl;
     // word and shift base of lane group g: unfolded, word 4 wsi + g and the
@@ -214,26 +250,11 @@ __device__ __forceinline__ void prep_block(const PrepArgs& a, int bx, int by, in
     const int w = a.fold ? (g & 1) : 4 * wsi + g;
     const int kbase = a.fold ? 4 * (g >> 1) : (part ? 4 * cl : 4 * (c % 2));
     const float wv = part ? 2.f : a.wm2[a.fold ? c : c / 2];
-    const float* src = out + hh * Dp;
-    const int e = qfix_e[hh];
-    uint32_t outw[4];
+    uint4 o[4];
+    limb_operands(out + hh * Dp, qfix_e[hh], wv, w, a.W, a.d, kbase, o);
+    uint4* dst = (uint4*)(rbase + (((size_t)wsi * a.nc + c) * 64 + 16 * g + 4 * hh) * 16);
 #pragma unroll
-    for (int sidx = 0; sidx < 4; ++sidx) {
-      const int k = kbase + sidx;
-      uint32_t word = 0;
-#pragma unroll
-      for (int el = 0; el < 4; ++el) {
-        const int j = 32 * w + 8 * el + k;
-        const int Q = (w < a.W && j < a.d) ? (int)rintf(ldexpf(wv * src[j], e)) : 0;
-        const int Ap = (k < 7) ? dev::shift_round(Q, k) : -dev::shift_round(Q, 7);
-        const uint32_t digit = (((uint32_t)Ap + 0x80808080u) >> (8 * L)) & 255u;
-        word |= (digit ^ 0x80u) << (8 * el);
-      }
-      outw[sidx] = word;
-    }
-    const int lanei = 16 * g + 4 * hh + L;
-    uint4* dst = (uint4*)(rbase + (((size_t)wsi * a.nc + c) * 64 + lanei) * 16);
-    *dst = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+    for (int L = 0; L < 4; ++L) dst[L] = o[L];
   }
 }
 

@@ -50,6 +50,14 @@ hipError_t launch_attn_prepare(const tq_ctx*, const float*, int32_t, int32_t, in
   return hipErrorNotSupported;
 }
 bool logits_fold(const tq_ctx*, int32_t, int32_t) { return false; }
+// the one-launch logit path is never taken here, so the two-launch path's
+// validation and launches are what the driver reaches
+bool attn_one_applies(const tq_ctx*, int32_t, int32_t) { return false; }
+hipError_t launch_attn_one(const tq_ctx*, const float*, int32_t, int32_t, int64_t,
+                           const uint32_t*, const uint16_t*, int32_t, int64_t, const int64_t*,
+                           const int32_t*, int32_t, float, float*, int64_t, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_attn_stream(const tq_ctx*, const void*, int32_t, int32_t, const uint32_t*,
                               const uint16_t*, int32_t, int64_t, const int64_t*, const int32_t*,
                               int32_t, float, float*, int64_t, hipStream_t) {

@@ -42,15 +42,18 @@ def _both(ctx, lens, n_q, n_kv, seed, scale):
     return got, ref, (P, N, q)
 
 
-@pytest.mark.parametrize("d,b", [(128, 4), (64, 3)])
-def test_noalloc_matches_workspace_form(orc, d, b):
+# (d, b, q heads per kv head): d = 128 with G = 8 and d = 200 take the two
+# launches through the static scratch; d = 64, G = 4 is the one-launch path
+@pytest.mark.parametrize("d,b,G", [(128, 4, 8), (200, 3, 4), (64, 3, 4)])
+def test_noalloc_matches_workspace_form(orc, d, b, G):
     pi, s, c = oracle_tables(orc, d, b)
     ctx = tq.TqContext(d, b, pi, s, c)
-    # first call: 32 "layers" x 32 q heads x 8 KV heads (the decode bench's
-    # preparation size), second call smaller: 3 ragged sequences, G = 4
-    g1, r1, _ = _both(ctx, [512] * 32, 32, 8, 41, 0.125)
+    # first call: 16 sequences x 8 KV heads x G q heads each (2.6 MB of
+    # prepared queries at d = 128, G = 8), second call smaller: 3 ragged
+    # sequences, 4 KV heads
+    g1, r1, _ = _both(ctx, [512] * 16, 8 * G, 8, 41, 0.125)
     assert torch.equal(g1, r1)
-    g2, r2, (P, N, q) = _both(ctx, [300, 77, 1000], 16, 4, 42, 0.5)
+    g2, r2, (P, N, q) = _both(ctx, [300, 77, 1000], 4 * G, 4, 42, 0.5)
     assert torch.equal(g2, r2)
     # and against the oracle, one head
     est = orc.estimate(d, b, pi, s, c, q[0, :4].double().cpu().numpy(),
