@@ -29,6 +29,11 @@ Other workloads (each prints its own JSON line; the default is the one above):
   --workload search   1e6 unit vectors at d = 1536 or 200 (--search-d), b in
                       {2, 4} (--bits): quantize the database, then score 1000
                       queries against all of it and keep the top 10
+  --workload stream_ceiling  the references the kernels are measured against
+                      (libtq_ceiling.so): a plain stream with the logit
+                      kernel's read/write mix over the default workload's
+                      8.39 M records, a 1 GiB device copy, and int8 / bf16
+                      matrix-core loops
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -58,7 +63,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "long", "batched", "search", "attn_out", "decode_fused",
-                             "split", "dequant"])
+                             "split", "dequant", "stream_ceiling"])
     ap.add_argument("--search-d", type=int, default=1536)
     ap.add_argument("--bits", type=int, default=0, help="search / long: one b (default all)")
     ap.add_argument("--mse", action="store_true",
@@ -124,7 +129,8 @@ def main():
     if args.workload != "decode":
         out = {"long": run_long, "batched": run_batched, "search": run_search,
                "attn_out": run_attn_out, "decode_fused": run_decode_fused,
-               "split": run_split, "dequant": run_dequant}[args.workload](args)
+               "split": run_split, "dequant": run_dequant,
+               "stream_ceiling": run_stream_ceiling}[args.workload](args)
         print(json.dumps(out), flush=True)
         return
     dev = "cuda"
@@ -368,6 +374,74 @@ def _line(args, metric, value, unit, workload, extra):
     if getattr(args, "mse", False):
         out["config"] = dict(out["config"], records="MSE-only: b code bits, no QJL stage")
     return out
+
+
+def run_stream_ceiling(args):
+    """Ceilings: the logit stream's byte mix as a plain stream, a plain copy,
+    and matrix-core loops (include/tq_ceiling.h)."""
+    import ctypes
+    import torch
+    import kv_cache_vector_pi_amd as tq
+    dev = "cuda"
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(tq.LIB_PATH), "libtq_ceiling.so"))
+    P = ctypes.c_void_p
+    lib.tq_ceiling_logit_mix.argtypes = [P, P, ctypes.c_int64, P, ctypes.c_int64, P]
+    lib.tq_ceiling_copy.argtypes = [P, P, ctypes.c_int64, P]
+    lib.tq_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+    reps = max(5, min(args.steps, 50))
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"ceiling kernel failed: hipError {rc}")
+
+    # the default workload's logit launch: 32 layers x 8 KV heads x 32768
+    # records of 64 + 4 bytes in, 4 logits (16 bytes) out per record
+    n = LAYERS * N_KV * N_TOK
+    planes = torch.randint(-2**31, 2**31 - 1, (n, 16), dtype=torch.int32, device=dev)
+    norms = torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, device=dev)
+    out = torch.empty((4, n), dtype=torch.float32, device=dev)
+    mix = lambda: ok(lib.tq_ceiling_logit_mix(P(planes.data_ptr()), P(norms.data_ptr()), n,
+                                              P(out.data_ptr()), n, sp))
+    for _ in range(args.warmup):
+        mix()
+    mix_ms, mix_med = _timed(mix, reps, stream)
+    mix_bytes = n * (64 + 4 + 16)
+    del planes, norms, out
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    cp = lambda: ok(lib.tq_ceiling_copy(P(src.data_ptr()), P(dst.data_ptr()), nb, sp))
+    for _ in range(args.warmup):
+        cp()
+    cp_ms, cp_med = _timed(cp, reps, stream)
+    del src, dst
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 8 * n_cu, 2000
+    sink = torch.empty(256 * blocks, dtype=torch.float32, device=dev)
+    mf = {}
+    for kind, name, ops in ((0, "i8_16x16x64", 2 * 16 * 16 * 64), (1, "bf16_32x32x16",
+                                                                   2 * 32 * 32 * 16)):
+        fn = lambda k=kind: ok(lib.tq_ceiling_mfma(k, blocks, iters, P(sink.data_ptr()), sp))
+        for _ in range(2):
+            fn()
+        ms, _ = _timed(fn, 5, stream)
+        mf[name] = blocks * 4 * iters * 8 * ops / (ms * 1e-3) / 1e12
+    mix_gbs = mix_bytes / (mix_ms * 1e-3) / 1e9
+    return _line(args, "plain-stream ceiling with the logit kernel's byte mix", mix_gbs, "GB/s",
+                 {"workload": "stream ceiling: 8,388,608 records (64 B planes + 4 B norm read, "
+                              "4 x 4 B written each) as a plain stream; 1 GiB copy; matrix-core "
+                              "loops of 8 workgroups x 4 waves per CU"},
+                 {"dtype": "u32 stream", "peak_GB_per_s": HBM_PEAK_GBS,
+                  "logit_mix": {"ms_mean": mix_ms, "ms_median": mix_med, "GB_per_s": mix_gbs,
+                                "frac": mix_gbs / HBM_PEAK_GBS, "bytes": mix_bytes},
+                  "copy_1GiB": {"ms_mean": cp_ms, "ms_median": cp_med,
+                                "GB_per_s": 2 * nb / (cp_ms * 1e-3) / 1e9,
+                                "frac": 2 * nb / (cp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                  "mfma_TOPS": mf,
+                  "mfma_peak_TOPS": {"i8_16x16x64": 5000.0, "bf16_32x32x16": 2500.0}})
 
 
 def run_dequant(args):

@@ -1,4 +1,6 @@
-"""Build libtq.so (HIP, gfx950) in-tree with hipcc.
+"""Build libtq.so (HIP, gfx950) in-tree with hipcc, and beside it
+libtq_ceiling.so (the HBM-stream and matrix-core ceiling kernels of
+include/tq_ceiling.h, used only for measurement).
 
 ``python kv_cache_vector_pi_amd/build.py`` (run as a file: importing the
 package would load the library being rebuilt) or ``build()``.  Every call
@@ -12,6 +14,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
+CEIL_LIB = os.path.join(HERE, "libtq_ceiling.so")
+CEIL_SRC = os.path.join(HERE, "ceiling", "ceiling.hip")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["tq_host.cpp", "tq_logits.hip", "tq_quantize.hip", "tq_quantize128.hip",
@@ -45,10 +49,22 @@ def _compile(src):
     return obj, warn
 
 
+def _build_ceiling():
+    tmp = CEIL_LIB + ".tmp"
+    cmd = [HIPCC] + COMMON + ["-shared", CEIL_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceiling.hip:\n{r.stderr}")
+    os.replace(tmp, CEIL_LIB)
+    return CEIL_LIB, ""
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        ceil = ex.submit(_build_ceiling)
         results = list(ex.map(_compile, SOURCES))
+        ceil.result()
     objs = [o for o, _ in results]
     if verbose:
         for (o, w) in results:

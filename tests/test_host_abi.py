@@ -36,6 +36,32 @@ def test_library_exports_every_symbol(tq):
         assert hasattr(tq.lib(), name)
 
 
+def test_ceiling_library_exports_its_header(tq):
+    """libtq_ceiling.so (measurement kernels) loads and exports every function
+    include/tq_ceiling.h declares; its host checks reject bad sizes before any
+    launch (hipErrorInvalidValue = 1)."""
+    src = open(os.path.join(ROOT, "include", "tq_ceiling.h")).read()
+    names = sorted(set(re.findall(r"^int\s+(tq_ceiling_\w+)\s*\(", src, re.M)))
+    assert names == ["tq_ceiling_copy", "tq_ceiling_logit_mix", "tq_ceiling_mfma"]
+    path = os.path.join(os.path.dirname(tq.LIB_PATH), "libtq_ceiling.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= exported
+    lib = ctypes.CDLL(path)
+    lib.tq_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]
+    lib.tq_ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
+    lib.tq_ceiling_logit_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert lib.tq_ceiling_copy(None, None, 17, None) == 1          # not a multiple of 16
+    assert lib.tq_ceiling_copy(None, None, 0, None) == 0           # empty: no-op
+    assert lib.tq_ceiling_mfma(2, 1, 1, None, None) == 1           # unknown kind
+    assert lib.tq_ceiling_logit_mix(None, None, 8, None, 4, None) == 1   # out_stride < n
+    assert lib.tq_ceiling_logit_mix(None, None, 8, None, 8, None) == 1   # NULL with work
+
+
 def test_status_strings(tq):
     assert tq.tq_status_string(0) == "TQ_OK"
     assert tq.tq_status_string(tq.TQ_ERR_NOT_CONVERGED) == "TQ_ERR_NOT_CONVERGED"
