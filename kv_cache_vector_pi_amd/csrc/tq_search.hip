@@ -10,9 +10,10 @@
 //
 // Search: records are decoded once per 128-record tile and 32-coordinate word
 // into fp16 LDS operands -- centroid hi and lo parts and gamma * s (gamma is
-// an fp16 value and s = +-1, so the product is exact) -- and the query rows,
-// split hi + lo with alpha folded into the sketch half, are staged next to
-// them.  One accumulator then takes all five passes on
+// an fp16 value and s = +-1, so the product is exact) -- and the query rows
+// of a 256-query tile, split hi + lo with alpha folded into the sketch half,
+// are staged next to them, by producer waves one word ahead of the MFMA
+// waves (search_gemm_kernel).  One accumulator then takes all five passes on
 // v_mfma_f32_32x32x16_f16:
 //   acc += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo + (alpha QP)_hi gs + (alpha QP)_lo gs,
 // and score = nu * acc.  Instead of writing every score, the epilogue keeps
@@ -42,7 +43,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kRowsTile = 64;    // dequantize: rows per workgroup
 constexpr int kRecTile = 64;     // dequantize: records per workgroup
 constexpr int kLdsRow = 40;      // halves per staged row of one word (32 + pad)
-constexpr int kQT = 128;         // search: queries per workgroup
+constexpr int kQT = 256;         // search: queries per workgroup
 constexpr int kRT = 128;         // search: records per workgroup
 constexpr int kFirst = 2048;     // search: records of the first chunk (sets the thresholds)
 constexpr int kChunk = 16384;    // search: records per later chunk = candidate capacity
@@ -442,120 +443,145 @@ struct SearchArgs {
   int* cand_i;           // [n_q][kChunk] record index within the chunk
 };
 
+// One workgroup per (128-record tile, 256-query tile), 12 waves in two roles
+// over a two-deep LDS pipeline of 32-coordinate words: in step s the four
+// producer waves stage word s's query rows (loaded into registers a step
+// ahead) and decode word s of the records into buffer s % 2, while the
+// eight MFMA waves run word s - 1's products from the other buffer; one
+// barrier per step.  So the decode (vector units) and the products (matrix
+// cores) of a compute unit overlap instead of taking turns, and two MFMA
+// waves per SIMD hide each other's operand reads.  An MFMA wave owns 64
+// queries x 64 records (2 x 2 blocks of 32 x 32).  Staged rows are 64 bytes (32 halves) per array,
+// with 16-byte chunk c of row r at position c ^ ((r >> 2) & 3), which spreads
+// an operand read of 16 consecutive rows over all 64 banks.
 template <int NB, bool MSE>
-__global__ void __launch_bounds__(256, 2) search_gemm_kernel(SearchArgs a) {
+__global__ void __launch_bounds__(768, 1) search_gemm_kernel(SearchArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;         // code planes
   // staged query arrays: QR hi, QR lo and (alpha QP) hi.  The sketch term
   // alpha gamma <QP, s> is a small part of a score, so its fp16 rounding of
   // QP (2^-12 relative) stays ~1e-4 of the scores' rms; (alpha QP) lo is not
   // used.  The code term keeps hi/lo products (2^-22).
   constexpr int NA = MSE ? 2 : 3;
-  __shared__ __align__(16) _Float16 As[NA][kQT * kLdsRow];
-  __shared__ __align__(16) _Float16 Bs[3][kRT * kLdsRow];
+  constexpr int NBS = MSE ? 2 : 3;               // decoded record arrays
+  constexpr int NAC = NA * kQT * 4 / 256;        // staged 16-byte chunks per producer thread
+  __shared__ __align__(16) _Float16 As[2][NA][kQT * 32];
+  __shared__ __align__(16) _Float16 Bs[2][NBS][kRT * 32];
   __shared__ float thr_s[kQT];
   __shared__ uint32_t ctab_s[kMaxK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
-  const int wq = wave & 1, wr = wave >> 1;       // wave tile: 64 queries x 64 records
   const int64_t r0 = (int64_t)blockIdx.x * kRT, q0 = (int64_t)blockIdx.y * kQT;
+  // halves offset of chunk c of staged row r
+  auto sw = [](int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); };
 
   if (tid < kQT) {
     const int64_t q = q0 + tid;
     thr_s[tid] = q < a.n_q ? a.thr[q] : INFINITY;   // padded rows never pass
   }
   if (tid < kMaxK) ctab_s[tid] = a.ctab[tid];
-  // decode role: record dr, coordinates 16 dh .. 16 dh + 15 of each word
-  const int dr = tid >> 1, dh = tid & 1;
-  const bool dlive = r0 + dr < a.n_rec;
-  const uint32_t* drec = a.planes + (a.rec0 + r0 + dr) * (int64_t)a.W * NB;
-  const uint16_t gbits =
-      dlive ? (uint16_t)(a.norms[a.rec0 + r0 + dr] >> 16) : (uint16_t)0;   // fp16 gamma
+  __syncthreads();
 
+  if (wave >= 8) {
+    // ======== producers: stage query rows, decode records ==================
+    const int pt = tid - 512;
+    // decode role: record dr, coordinates 16 dh .. 16 dh + 15 of each word
+    const int dr = pt >> 1, dh = pt & 1;
+    const bool dlive = r0 + dr < a.n_rec;
+    const uint32_t* drec = a.planes + (a.rec0 + r0 + dr) * (int64_t)a.W * NB;
+    const uint16_t gbits =
+        dlive ? (uint16_t)(a.norms[a.rec0 + r0 + dr] >> 16) : (uint16_t)0;   // fp16 gamma
+    // word w's query rows (NA arrays x 256 rows x 4 chunks) and record words,
+    // loaded into registers one word ahead
+    // (chunk j of a thread: array j / 4, row pt / 4 + 64 (j % 4), part pt % 4;
+    // the array index is a compile-time constant, so its pointer stays in
+    // scalar registers)
+    v8h ra[NAC];
+    uint32_t wd[NB];
+    const int prow = pt >> 2, ppart = pt & 3;
+    auto load_word = [&](int w) {
+#pragma unroll
+      for (int j = 0; j < NAC; ++j) {
+        const int row = prow + 64 * (j & 3);
+        ra[j] = *(const v8h*)(a.qa[j >> 2] + (q0 + row) * a.Dp + 32 * w + 8 * ppart);
+      }
+#pragma unroll
+      for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
+    };
+    load_word(0);
+    for (int st = 0; st <= a.W; ++st) {
+      if (st < a.W) {
+        const int buf = st & 1;
+#pragma unroll
+        for (int j = 0; j < NAC; ++j)
+          *(v8h*)(&As[buf][j >> 2][sw(prow + 64 * (j & 3), ppart)]) = ra[j];
+        v8h vh[2], vl[2], vg[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bit = 16 * dh + e;
+          uint32_t idx = 0;
+#pragma unroll
+          for (int p = 0; p < CP; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
+          const uint32_t hl = ctab_s[idx];
+          const uint16_t sgn = (MSE || ((wd[NB - 1] >> bit) & 1u)) ? (uint16_t)0 : (uint16_t)0x8000;
+          vh[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
+          vl[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
+          vg[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(gbits ^ sgn));
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int off = sw(dr, 2 * dh + h);
+          *(v8h*)(&Bs[buf][0][off]) = vh[h];
+          *(v8h*)(&Bs[buf][1][off]) = vl[h];
+          if constexpr (!MSE) *(v8h*)(&Bs[buf][2][off]) = vg[h];
+        }
+        if (st + 1 < a.W) load_word(st + 1);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ======== MFMA waves: word st - 1 from buffer (st - 1) % 2 ==================
+  const int wq = wave & 3, wr = wave >> 2;       // wave tile: 64 queries x 64 records
   v16f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
-
-  // Word w's query rows (NA arrays x 128 rows x 32 halves, 16 bytes a thread
-  // x 2 NA) and record words are loaded into registers one word ahead, so the
-  // loads are in flight while the previous word's MFMAs run.
-  v8h ra[2 * NA];
-  uint32_t wd[NB];
-  auto load_word = [&](int w) {
+  for (int st = 0; st <= a.W; ++st) {
+    if (st >= 1) {
+      const int buf = (st - 1) & 1;
 #pragma unroll
-    for (int j = 0; j < 2 * NA; ++j) {
-      const int c = tid + 256 * j;
-      const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
-      ra[j] = *(const v8h*)(a.qa[ar] + (q0 + row) * a.Dp + 32 * w + 8 * part);
-    }
+      for (int kk = 0; kk < 2; ++kk) {
+        v8h A[2][NA], B[2][3];
 #pragma unroll
-    for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
-  };
-  load_word(0);
-  for (int w = 0; w < a.W; ++w) {
-    __syncthreads();              // previous word's operands fully read
+        for (int rb = 0; rb < 2; ++rb) {
+          const int off = sw(64 * wr + 32 * rb + col, 2 * kk + hh);
 #pragma unroll
-    for (int j = 0; j < 2 * NA; ++j) {
-      const int c = tid + 256 * j;
-      const int ar = c >> 9, row = (c >> 2) & 127, part = c & 3;
-      *(v8h*)(&As[ar][row * kLdsRow + 8 * part]) = ra[j];
-    }
-    // decode word w of record dr
-    {
-      v8h vh[2], vl[2], vg[2];
+          for (int ar = 0; ar < NBS; ++ar) B[rb][ar] = *(const v8h*)(&Bs[buf][ar][off]);
+        }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int bit = 16 * dh + e;
-        uint32_t idx = 0;
+        for (int qb = 0; qb < 2; ++qb) {
+          const int off = sw(64 * wq + 32 * qb + col, 2 * kk + hh);
 #pragma unroll
-        for (int p = 0; p < CP; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
-        const uint32_t hl = ctab_s[idx];
-        const uint16_t sgn = (MSE || ((wd[NB - 1] >> bit) & 1u)) ? (uint16_t)0 : (uint16_t)0x8000;
-        vh[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
-        vl[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
-        vg[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(gbits ^ sgn));
-      }
-      const int off = dr * kLdsRow + 16 * dh;
-      *(v8h*)(&Bs[0][off]) = vh[0];
-      *(v8h*)(&Bs[0][off + 8]) = vh[1];
-      *(v8h*)(&Bs[1][off]) = vl[0];
-      *(v8h*)(&Bs[1][off + 8]) = vl[1];
-      if constexpr (!MSE) {
-        *(v8h*)(&Bs[2][off]) = vg[0];
-        *(v8h*)(&Bs[2][off + 8]) = vg[1];
+          for (int ar = 0; ar < NA; ++ar) A[qb][ar] = *(const v8h*)(&As[buf][ar][off]);
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            v16f c = acc[qb][rb];
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
+            if constexpr (!MSE)
+              c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
+            acc[qb][rb] = c;
+          }
       }
     }
     __syncthreads();
-    if (w + 1 < a.W) load_word(w + 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      v8h A[2][NA], B[2][3];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int off = (64 * wq + 32 * qb + col) * kLdsRow + 16 * kk + 8 * hh;
-#pragma unroll
-        for (int ar = 0; ar < NA; ++ar) A[qb][ar] = *(const v8h*)(&As[ar][off]);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int off = (64 * wr + 32 * rb + col) * kLdsRow + 16 * kk + 8 * hh;
-#pragma unroll
-        for (int ar = 0; ar < (MSE ? 2 : 3); ++ar) B[rb][ar] = *(const v8h*)(&Bs[ar][off]);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          v16f c = acc[qb][rb];
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
-          if constexpr (!MSE)
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
-          acc[qb][rb] = c;
-        }
-    }
   }
 
   // epilogue: element i of tile (qb, rb) is query 64wq + 32qb + 8(i/4) + 4hh + i%4
@@ -812,15 +838,15 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
       const dim3 grid((unsigned)((len + kRT - 1) / kRT), (unsigned)(L.rows_pad / kQT));
       if (ctx->mse) {
         switch (ctx->b) {
-          case 1: hipLaunchKernelGGL((search_gemm_kernel<1, true>), grid, dim3(256), 0, stream, g); break;
-          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, true>), grid, dim3(256), 0, stream, g); break;
-          default: hipLaunchKernelGGL((search_gemm_kernel<3, true>), grid, dim3(256), 0, stream, g); break;
+          case 1: hipLaunchKernelGGL((search_gemm_kernel<1, true>), grid, dim3(768), 0, stream, g); break;
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, true>), grid, dim3(768), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<3, true>), grid, dim3(768), 0, stream, g); break;
         }
       } else {
         switch (ctx->b) {
-          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, false>), grid, dim3(256), 0, stream, g); break;
-          case 3: hipLaunchKernelGGL((search_gemm_kernel<3, false>), grid, dim3(256), 0, stream, g); break;
-          default: hipLaunchKernelGGL((search_gemm_kernel<4, false>), grid, dim3(256), 0, stream, g); break;
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, false>), grid, dim3(768), 0, stream, g); break;
+          case 3: hipLaunchKernelGGL((search_gemm_kernel<3, false>), grid, dim3(768), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<4, false>), grid, dim3(768), 0, stream, g); break;
         }
       }
       e = hipGetLastError();
