@@ -32,8 +32,8 @@ Other workloads (each prints its own JSON line; the default is the one above):
   --workload stream_ceiling  the references the kernels are measured against
                       (libtq_ceiling.so): a plain stream with the logit
                       kernel's read/write mix over the default workload's
-                      8.39 M records, a 1 GiB device copy, and int8 / bf16
-                      matrix-core loops
+                      8.39 M records, a 1 GiB device copy, int8 / bf16
+                      matrix-core loops, and MFMA / vector-ALU co-issue
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 Prints one JSON line.
@@ -429,6 +429,19 @@ def run_stream_ceiling(args):
             fn()
         ms, _ = _timed(fn, 5, stream)
         mf[name] = blocks * 4 * iters * 8 * ops / (ms * 1e-3) / 1e12
+    lib.tq_ceiling_overlap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       P, P]
+    ov = {}
+    osink = torch.empty(512 * n_cu, dtype=torch.float32, device=dev)
+    for kind, name in ((0, "fma"), (1, "compare_select")):
+        t = []
+        for mode in (0, 1, 2):
+            fn = lambda m=mode, k=kind: ok(lib.tq_ceiling_overlap(m, k, n_cu, 2000,
+                                                                  P(osink.data_ptr()), sp))
+            fn()
+            t.append(_timed(fn, 5, stream)[0])
+        ov[name] = {"mfma_ms": t[0], "valu_ms": t[1], "both_ms": t[2],
+                    "both_over_max": t[2] / max(t[0], t[1]), "both_over_sum": t[2] / (t[0] + t[1])}
     mix_gbs = mix_bytes / (mix_ms * 1e-3) / 1e9
     return _line(args, "plain-stream ceiling with the logit kernel's byte mix", mix_gbs, "GB/s",
                  {"workload": "stream ceiling: 8,388,608 records (64 B planes + 4 B norm read, "
@@ -441,6 +454,7 @@ def run_stream_ceiling(args):
                                 "GB_per_s": 2 * nb / (cp_ms * 1e-3) / 1e9,
                                 "frac": 2 * nb / (cp_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
                   "mfma_TOPS": mf,
+                  "mfma_valu_overlap": ov,
                   "mfma_peak_TOPS": {"i8_16x16x64": 5000.0, "bf16_32x32x16": 2500.0}})
 
 

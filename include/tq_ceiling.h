@@ -39,6 +39,14 @@ int tq_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);
  * blocks x 4 x iters x 8 x (2 x 16 x 16 x 64 | 2 x 32 x 32 x 16). */
 int tq_ceiling_mfma(int kind, int blocks, int iters, float* out, void* stream);
 
+/* MFMA / vector-ALU co-issue: `blocks` workgroups of 8 waves (one per CU at
+ * the sizes bench.py uses); waves 4-7 run v_mfma_f32_32x32x16_bf16 loops
+ * (mode 0 or 2), waves 0-3 run vector work (mode 1 or 2): FMA chains
+ * (kind 0) or compare / select / shift-in sequences like the quantizer's
+ * code decisions (kind 1).  The time of mode 2 against modes 0 and 1 says
+ * how far the two pipes overlap on one SIMD.  out: 512 x blocks floats. */
+int tq_ceiling_overlap(int mode, int kind, int blocks, int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

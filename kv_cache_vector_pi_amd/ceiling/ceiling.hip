@@ -96,6 +96,70 @@ __global__ void __launch_bounds__(256) mfma_kernel(int iters, float* out) {
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// MFMA / VALU co-issue on one SIMD: a workgroup of 8 waves, waves 4-7 issue
+// v_mfma_f32_32x32x16_bf16 on two accumulators (if MFMA_ON), waves 0-3 issue
+// VALU work (if VALU_ON): FMA chains (VK = 0) or compare / select /
+// add-with-carry sequences like the quantizer's code decisions (VK = 1).
+template <bool MFMA_ON, bool VALU_ON, int VK>
+__global__ void __launch_bounds__(512, 1) overlap_kernel(int iters, float* out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float s = 0.f;
+  if (wave >= 4) {
+    if constexpr (MFMA_ON) {
+      v8bf a, b;
+      for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(1e-3f * (lane + i));
+        b[i] = (__bf16)(1e-3f * (i - lane));
+      }
+      v16f c0 = {}, c1 = {};
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+        }
+      }
+      for (int i = 0; i < 16; ++i) s += c0[i] + c1[i];
+    }
+  } else if constexpr (VALU_ON) {
+    if constexpr (VK == 0) {
+      float v[8];
+      for (int i = 0; i < 8; ++i) v[i] = 1e-3f * (lane + i);
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], 1.0001f, v[(i + 3) & 7]);
+      }
+      for (int i = 0; i < 8; ++i) s += v[i];
+    } else {
+      float y[8];
+      uint32_t acc[4] = {0u, 0u, 0u, 0u};
+      for (int i = 0; i < 8; ++i) y[i] = 1e-3f * (lane - 20 + 5 * i);
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float ay = fabsf(y[i]);
+            const bool g0 = ay > 0.01f, g1 = ay > 0.02f, g2 = ay > 0.04f, p = y[i] > 0.f;
+            float c = g0 ? 0.3f : 0.1f;
+            c = g1 ? 0.5f : c;
+            c = g2 ? 0.7f : c;
+            y[i] = p ? y[i] - c * 1e-3f : y[i] + c * 1e-3f;
+            acc[0] = 2u * acc[0] + (uint32_t)g0;
+            acc[1] = 2u * acc[1] + (uint32_t)g1;
+            acc[2] = 2u * acc[2] + (uint32_t)g2;
+            acc[3] = 2u * acc[3] + (uint32_t)p;
+          }
+      }
+      for (int i = 0; i < 8; ++i) s += y[i];
+      s += (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+    }
+  }
+  out[blockIdx.x * 512 + threadIdx.x] = s;
+}
+
 int n_cu() {
   static const int cus = [] {
     int dev = 0, v = 0;
@@ -150,5 +214,25 @@ extern "C" __attribute__((visibility("default"))) int tq_ceiling_mfma(int kind, 
     hipLaunchKernelGGL(mfma_kernel<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
   else
     hipLaunchKernelGGL(mfma_kernel<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  return (int)hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("default"))) int tq_ceiling_overlap(int mode, int kind,
+                                                                         int blocks, int iters,
+                                                                         float* out,
+                                                                         void* stream) {
+  if (blocks < 0 || iters < 0 || mode < 0 || mode > 2 || (kind != 0 && kind != 1))
+    return (int)hipErrorInvalidValue;
+  if (blocks == 0) return 0;
+  if (!out) return (int)hipErrorInvalidValue;
+  const hipStream_t st = (hipStream_t)stream;
+#define TQ_OV(M, V, K) \
+  hipLaunchKernelGGL((overlap_kernel<M, V, K>), dim3(blocks), dim3(512), 0, st, iters, out)
+  if (kind == 0) {
+    if (mode == 0) TQ_OV(true, false, 0); else if (mode == 1) TQ_OV(false, true, 0); else TQ_OV(true, true, 0);
+  } else {
+    if (mode == 0) TQ_OV(true, false, 1); else if (mode == 1) TQ_OV(false, true, 1); else TQ_OV(true, true, 1);
+  }
+#undef TQ_OV
   return (int)hipGetLastError();
 }
