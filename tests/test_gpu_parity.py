@@ -612,7 +612,10 @@ def topk_ok(gi, gs, ref_scores, k, tol=TOL):
 
 @pytest.mark.parametrize("d,b,n_db,n_q,k", [(128, 4, 5000, 70, 10), (200, 2, 40000, 5, 10),
                                             (200, 4, 3000, 3, 1), (1536, 2, 2000, 4, 10),
-                                            (128, 3, 100, 2, 64)])
+                                            (128, 3, 100, 2, 64),
+                                            # two query tiles of 256 (the second ragged),
+                                            # two record chunks with a ragged last tile
+                                            (128, 3, 20000, 300, 10)])
 def test_search_parity(orc, d, b, n_db, n_q, k):
     say("search", d, b, n_db, n_q, k)
     ctx, pi, s, c = ctx_for(orc, d, b)
