@@ -40,6 +40,7 @@
 //    instructions and the wait for a copy in flight can name its exact
 //    count.
 #pragma once
+#include "tq_dma.h"
 #include "tq_q128.h"
 
 namespace tq {
@@ -73,48 +74,6 @@ struct Q128SArgs {
 __device__ inline uint32_t head_of(uint32_t n, const Q128SArgs& a) {
   const uint32_t t = __umulhi(n, a.div_m);
   return (t + ((n - t) >> a.div_s1)) >> a.div_s2;
-}
-
-// LDS byte address of a shared-memory object
-__device__ inline uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from global memory into LDS at m0_base + 16 * lane
-// (one wave writes 1 KB).  M0 is saved and restored around the copy.
-__device__ inline void copy16_to_lds(const void* gaddr, uint32_t m0_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gaddr), "s"(m0_base)
-      : "memory");
-}
-
-// s_waitcnt vmcnt(n) for a uniform n in 0..15 (expcnt and lgkmcnt untouched)
-__device__ inline void wait_vmcnt(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
-  }
 }
 
 template <int NB, bool MSE>
@@ -235,19 +194,19 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
       Pm[ks] = *(const v8bf*)(a.pib_mid + off);
     }
     // Y(j): 16 MFMAs on block j's raw rows (chunk c of row r at slot c ^ (r & 7)),
-    // hi and mid products in two accumulators (two independent MFMA
-    // chains), the operand read of step ks + 1 issued before the MFMAs of
-    // step ks
+    // hi and mid products in one accumulator (back-to-back MFMAs on the same
+    // accumulator issue without a stall), the operand read of step ks + 1
+    // issued before the MFMAs of step ks
     auto y_block = [&](v16f& acc, int j) {
       const uint16_t* xr = &xb[j % kSD][col * 128];
-      v16f a1 = {}, a2 = {};
+      acc = v16f{};
       v8bf xf = *(const v8bf*)(xr + 8 * (hh ^ (col & 7)));
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         v8bf xn = xf;
         if (ks < 7) xn = *(const v8bf*)(xr + 8 * ((2 * ks + 2 + hh) ^ (col & 7)));
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph[ks], xf, a1, 0, 0, 0);
-        a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pm[ks], xf, a2, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph[ks], xf, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pm[ks], xf, acc, 0, 0, 0);
         xf = xn;
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -257,7 +216,6 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      acc = a1 + a2;
     };
     // Codes of block j from acc = Y(j).  Element i of a lane is coordinate
     // 32 grp + 8 (i/4) + 4 hh + i%4 of vector col.  acc = Pi x' with x' = x 2^k
@@ -332,6 +290,7 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
     __syncthreads();            // Y(0) has read buffer 0, which step 0 refills
     for (int j = 0; j <= nb; ++j) {
       codes(ya, j);             // block nb: stale buffers, results unused
+      __builtin_amdgcn_sched_barrier(0);
       y_block(ya, j + 1);
       __syncthreads();
     }

@@ -31,6 +31,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "tq_dma.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -44,11 +45,17 @@ constexpr int kRowsTile = 64;    // dequantize: rows per workgroup
 constexpr int kRecTile = 64;     // dequantize: records per workgroup
 constexpr int kLdsRow = 40;      // halves per staged row of one word (32 + pad)
 constexpr int kQT = 256;         // search: queries per workgroup
-constexpr int kRT = 128;         // search: records per workgroup
+constexpr int kRT = 256;         // search: records per workgroup
 constexpr int kFirst = 2048;     // search: records of the first chunk (sets the thresholds)
 constexpr int kChunk = 16384;    // search: records per later chunk = candidate capacity
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Position, within its 32-coordinate word, of coordinate c in the staged query
+// rows: K-slot 4g + t holds coordinate g + 8t.  Slots 4g .. 4g + 3 are then the
+// bits at positions g, g + 8, g + 16, g + 24 of a plane word, which one AND with
+// 0x01010101 << g spreads over four bytes.
+__host__ __device__ inline int kslot_of(int c) { return 4 * (c & 7) + (c >> 3); }
 
 // ---- row preparation: Pi q and S q, split into hi/lo fp16 -----------------
 // Block (row group of kPrepRows queries, chunk of 256 outputs): each thread
@@ -119,14 +126,15 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
   if (o >= 2 * a.Dp) return;
   __half* hi = sk ? a.qp_hi : a.qr_hi;
   __half* lo = sk ? a.qp_lo : a.qr_lo;
+  const int pos = (r & ~31) + kslot_of(r & 31);    // K-slot order within the word
 #pragma unroll
   for (int i = 0; i < kPrepRows; ++i) {
     const int64_t row = row0 + i;
     if (row < a.n_pad) {
       const float v = live ? (sk ? a.pscale * acc[i] : acc[i]) : 0.f;
       const __half vh = __float2half(v);
-      hi[row * a.Dp + r] = vh;
-      lo[row * a.Dp + r] = __float2half(v - __half2float(vh));
+      hi[row * a.Dp + pos] = vh;
+      lo[row * a.Dp + pos] = __float2half(v - __half2float(vh));
     }
   }
 }
@@ -430,176 +438,281 @@ __global__ void __launch_bounds__(256, 2) dequant128_kernel(GemmArgs a) {
 
 // ---- search GEMM with threshold-filter epilogue -------------------------------
 struct SearchArgs {
-  const __half* qa[4];   // QR hi, QR lo, (alpha QP) hi, (alpha QP) lo: [rows_pad][Dp]
+  const __half* qa[4];   // QR hi, QR lo, (alpha QP) hi, (alpha QP) lo: [rows_pad][Dp],
+                         // coordinates of each 32-word in K-slot order (below)
+  int64_t qa_step;       // qa[i] = qa[0] + i * qa_step (halves)
   int64_t n_q;
   const uint32_t* planes;
   const uint32_t* norms;
   int64_t rec0, n_rec;   // records rec0 .. rec0 + n_rec - 1 of this chunk
   int W, Dp;
-  uint32_t ctab[kMaxK];  // centroid k: fp16 hi | fp16 lo << 16
+  uint32_t tb[8];        // byte tables of the codebook for v_perm: bytes of centroid k's
+                         // fp16 hi part (low byte: tb[0] k < 4, tb[1] k >= 4; high byte:
+                         // tb[2], tb[3]) and lo part (tb[4] .. tb[7])
   const float* thr;      // [n_q] running k-th best score (-inf: fewer than k yet)
   int* cnt;              // [n_q] candidates of this chunk
   float* cand_s;         // [n_q][kChunk]
   int* cand_i;           // [n_q][kChunk] record index within the chunk
 };
 
-// One workgroup per (128-record tile, 256-query tile), 12 waves in two roles
-// over a two-deep LDS pipeline of 32-coordinate words: in step s the four
-// producer waves stage word s's query rows (loaded into registers a step
-// ahead) and decode word s of the records into buffer s % 2, while the
-// eight MFMA waves run word s - 1's products from the other buffer; one
-// barrier per step.  So the decode (vector units) and the products (matrix
-// cores) of a compute unit overlap instead of taking turns, and two MFMA
-// waves per SIMD hide each other's operand reads.  An MFMA wave owns 64
-// queries x 64 records (2 x 2 blocks of 32 x 32).  Staged rows are 64 bytes (32 halves) per array,
-// with 16-byte chunk c of row r at position c ^ ((r >> 2) & 3), which spreads
-// an operand read of 16 consecutive rows over all 64 banks.
+// One workgroup per (256-record tile, 256-query tile), 8 waves, each owning
+// 128 queries x 64 records (4 x 2 blocks of 32 x 32).  Per 32-coordinate word:
+//  * the word's query rows (NA arrays x 256 rows x 64 bytes) and the tile's
+//    plane words go from memory straight into LDS (global_load_lds, two words
+//    ahead, three buffers); 16-byte chunk c of query row r lands at position
+//    c ^ ((r >> 2) & 3), so an operand read of 16 consecutive rows covers all
+//    64 banks;
+//  * every wave reads the plane words of its own 64 records and turns them into
+//    the fp16 B operands in registers: the code index of four coordinates as
+//    four bytes (an AND-OR of the shifted planes), then v_perm_b32 lookups in
+//    the codebook's byte tables (centroid hi and lo parts) and in a per-record
+//    table of gamma's bytes (gamma * s, exact in fp16), with no per-coordinate
+//    table reads;
+//  * one barrier per word.
+// The MFMAs per word and 32 x 32 block are those of the decoded product:
+//   acc += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo + (alpha QP)_hi gamma s.
 template <int NB, bool MSE>
-__global__ void __launch_bounds__(768, 1) search_gemm_kernel(SearchArgs a) {
+__global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;         // code planes
   // staged query arrays: QR hi, QR lo and (alpha QP) hi.  The sketch term
   // alpha gamma <QP, s> is a small part of a score, so its fp16 rounding of
   // QP (2^-12 relative) stays ~1e-4 of the scores' rms; (alpha QP) lo is not
   // used.  The code term keeps hi/lo products (2^-22).
   constexpr int NA = MSE ? 2 : 3;
-  constexpr int NBS = MSE ? 2 : 3;               // decoded record arrays
-  constexpr int NAC = NA * kQT * 4 / 256;        // staged 16-byte chunks per producer thread
-  __shared__ __align__(16) _Float16 As[2][NA][kQT * 32];
-  __shared__ __align__(16) _Float16 Bs[2][NBS][kRT * 32];
-  __shared__ float thr_s[kQT];
-  __shared__ uint32_t ctab_s[kMaxK];
+  constexpr int NRC = 4 * NB;                    // record copies (256 lanes x 4 B) per word
+  __shared__ __align__(16) _Float16 As[3][NA][kQT * 32];
+  __shared__ __align__(16) uint32_t Rs[4][kRT * NB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
+  const int wq = wave & 1, wr = wave >> 1;       // queries 128 wq .., records 64 wr ..
   const int64_t r0 = (int64_t)blockIdx.x * kRT, q0 = (int64_t)blockIdx.y * kQT;
   // halves offset of chunk c of staged row r
   auto sw = [](int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); };
 
+  // Copies of one word, in items a wave issues one at a time (spread over the
+  // products, so that the address units work beside the matrix cores instead
+  // of stalling every wave at the start of a step).
+  // Query rows of word s into buffer s % 3, items 0 .. 2 NA - 1: wave w copies
+  // rows 32w .. 32w + 31 of every array, 16 rows (1 KB) per copy; lane l
+  // fills slot l % 4 of row 16 i + l / 4 with chunk slot ^ ((row >> 2) & 3).
+  auto stage_q = [&](int s, int item) {
+    const int buf = s % 3, ar = item >> 1;
+    const int rbase = 32 * wave + 16 * (item & 1);
+    const int row = rbase + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    const int sw_ = s < a.W ? s : a.W - 1;          // past the last word: a harmless copy
+    const __half* src = a.qa[0] + (int64_t)ar * a.qa_step + (q0 + row) * a.Dp + 32 * sw_ + 8 * chunk;
+    copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(&As[buf][ar][rbase * 32])));
+  };
+  // Plane words of word s into buffer s % 4, items 0 .. NRI - 1: copy j = w +
+  // 8 item (if j < NRC) moves dwords 64 j .. 64 j + 63 of the tile's
+  // [record][plane] block (a record past the chunk's end reads the last one;
+  // its scores are dropped).
+  constexpr int NRI = (NRC + 7) / 8;
+  const int n_rc = wave < NRC ? (NRC - 1 - wave) / 8 + 1 : 0;   // copies per wave
+  auto stage_r = [&](int s, int item) {
+    const int j = wave + 8 * item;
+    if (NRC % 8 == 0 || j < NRC) {
+      const int buf = s & 3;
+      const int e = 64 * j + lane, r = e / NB, p = e - r * NB;
+      const int64_t rl = r0 + r;
+      const int64_t rc = a.rec0 + (rl < a.n_rec ? rl : a.n_rec - 1);
+      const int sw_ = s < a.W ? s : a.W - 1;
+      const uint32_t* src = a.planes + rc * (int64_t)(a.W * NB) + sw_ * NB + p;
+      copy4_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(&Rs[buf][64 * j])));
+    }
+  };
+  // item i of step st: rows of word st + 2, then planes of word st + 3.  Every
+  // step issues all of them (no branch splits the step's schedule): past the
+  // last word they refill a buffer that no later step reads with a valid word.
+  auto stage_item = [&](int st, int i) {
+    if (i < 2 * NA)
+      stage_q(st + 2, i);
+    else if (i < 2 * NA + NRI)
+      stage_r(st + 3, i - 2 * NA);
+  };
+
+  // this lane's records 64 wr + 32 rb + col
+  uint32_t tg[2];            // bytes: gamma_hi ^ 0x80, gamma_hi, gamma_lo
+  float nu_r[2];
+  bool rlive[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t rl = r0 + 64 * wr + 32 * rb + col;
+    rlive[rb] = rl < a.n_rec;
+    const int64_t rc = a.rec0 + (rlive[rb] ? rl : a.n_rec - 1);
+    const uint32_t nn = a.norms[rc];
+    nu_r[rb] = __half2float(__ushort_as_half((unsigned short)(nn & 0xffffu)));
+    const uint32_t g = nn >> 16, glo = g & 0xffu, ghi = (g >> 8) & 0xffu;
+    tg[rb] = (ghi ^ 0x80u) | (ghi << 8) | (glo << 16);
+  }
+  uint32_t tb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) tb[i] = a.tb[i];
+
+  // B operands of one 32 x 32 block for K-slots 16 kk + 8 hh .. + 7, i.e. byte
+  // groups g = 4 kk + 2 hh and g + 1; w holds the plane words shifted right by
+  // 2 hh, so group g + j's bits are at 4 kk + j for every lane.  Dwords of an
+  // operand: (slots 0,1), (2,3) of group g, then of group g + 1.  One call
+  // fills the two dwords of group g + j in each array.
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  auto decode_group = [&](const uint32_t (&w)[NB], uint32_t tgr, int kk, int j, u4v (&B)[3]) {
+    const int k = 4 * kk + j;
+    uint32_t v = w[0] & (0x01010101u << k);
+    if constexpr (CP >= 2) v |= (w[1] << 1) & (0x02020202u << k);
+    if constexpr (CP >= 3) v |= (w[2] << 2) & (0x04040404u << k);
+    const uint32_t sel = v >> k;                     // code index per byte
+    const uint32_t hl = __builtin_amdgcn_perm(tb[1], tb[0], sel);
+    const uint32_t hh8 = __builtin_amdgcn_perm(tb[3], tb[2], sel);
+    B[0][2 * j] = __builtin_amdgcn_perm(hh8, hl, 0x05010400u);
+    B[0][2 * j + 1] = __builtin_amdgcn_perm(hh8, hl, 0x07030602u);
+    const uint32_t ll = __builtin_amdgcn_perm(tb[5], tb[4], sel);
+    const uint32_t lh = __builtin_amdgcn_perm(tb[7], tb[6], sel);
+    B[1][2 * j] = __builtin_amdgcn_perm(lh, ll, 0x05010400u);
+    B[1][2 * j + 1] = __builtin_amdgcn_perm(lh, ll, 0x07030602u);
+    if constexpr (!MSE) {
+      const uint32_t sb = (w[NB - 1] >> k) & 0x01010101u;     // sign bits per byte
+      // selectors (2, b0, 2, b1) and (2, b2, 2, b3) into tgr
+      const uint32_t sa = __builtin_amdgcn_perm(0x02020202u, sb, 0x01040004u);
+      const uint32_t sc = __builtin_amdgcn_perm(0x02020202u, sb, 0x03040204u);
+      B[2][2 * j] = __builtin_amdgcn_perm(0u, tgr, sa);
+      B[2][2 * j + 1] = __builtin_amdgcn_perm(0u, tgr, sc);
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
+  // this lane's plane words of word s (records 64 wr + 32 rb + col), shifted
+  // right by 2 hh
+  auto rec_words = [&](int s, uint32_t (&w)[2][NB]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const uint32_t* rw = &Rs[s & 3][(64 * wr + 32 * rb + col) * NB];
+      if constexpr (NB == 4) {
+        const uint4 v = *(const uint4*)rw;
+        w[rb][0] = v.x; w[rb][1] = v.y; w[rb][2] = v.z; w[rb][3] = v.w;
+      } else {
+#pragma unroll
+        for (int p = 0; p < NB; ++p) w[rb][p] = rw[p];
+      }
+#pragma unroll
+      for (int p = 0; p < NB; ++p) w[rb][p] >>= 2 * hh;
+    }
+  };
+  // MFMAs of K-slice kk of word s (query rows from buffer s % 3) on the
+  // operands Bc, with the decode of the next K-slice's operands Bd (group j of
+  // record block rb per 32-query block) interleaved: per query block, its three
+  // operand reads, then each MFMA followed by two vector instructions
+  auto products = [&](int s, int kk, const u4v (&Bc)[2][3], const uint32_t (&wd)[2][NB],
+                      int kkd, u4v (&Bd)[2][3]) {
+    const int buf = s % 3;
+    static_assert(2 * NA + NRI <= 8, "one copy per query block and K-slice");
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int off = sw(128 * wq + 32 * qb + col, 2 * kk + hh);
+      v8h A[NA];
+#pragma unroll
+      for (int ar = 0; ar < NA; ++ar) A[ar] = *(const v8h*)(&As[buf][ar][off]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        v16f c = acc[qb][rb];
+        const v8h b0 = __builtin_bit_cast(v8h, Bc[rb][0]);
+        const v8h b1 = __builtin_bit_cast(v8h, Bc[rb][1]);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[1], b0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], b1, c, 0, 0, 0);
+        if constexpr (!MSE)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[2], __builtin_bit_cast(v8h, Bc[rb][2]), c,
+                                                     0, 0, 0);
+        acc[qb][rb] = c;
+      }
+      decode_group(wd[qb >> 1], tg[qb >> 1], kkd, qb & 1, Bd[qb >> 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);
+#pragma unroll
+      for (int m = 0; m < (MSE ? 6 : 8); ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      stage_item(s, 4 * kk + qb);
+    }
+  };
+
+  // Copies run ahead of the products: query rows two words, plane words
+  // three.  Step s - 2 issues the rows of word s and the planes of word
+  // s + 1, so a step can decode the first K-slice of the next word during its
+  // second half and start on products right after the barrier.
+  auto stage_r_all = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < NRI; ++i) stage_r(s, i);
+  };
+  auto stage_q_all = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 2 * NA; ++i) stage_q(s, i);
+  };
+  stage_r_all(0);
+  stage_q_all(0);
+  if (a.W > 1) stage_r_all(1);
+  if (a.W > 1) stage_q_all(1);
+  if (a.W > 2) stage_r_all(2);
+  wait_vmcnt((a.W > 1 ? 2 * NA : 0) + (a.W > 2 ? n_rc : 0));   // rows of word 0, planes of 0 and 1
+  __syncthreads();
+  u4v Bn[2][3], Bk[2][3];    // K-slice 0 of the current word (decoded one step early), slice 1
+  {
+    uint32_t w[2][NB];
+    rec_words(0, w);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      decode_group(w[rb], tg[rb], 0, 0, Bn[rb]);
+      decode_group(w[rb], tg[rb], 0, 1, Bn[rb]);
+    }
+  }
+  for (int st = 0; st < a.W; ++st) {
+    if (st > 0) {
+        // rows of word st and planes of word st + 1 landed (the copies of
+      // step st - 1 may still be in flight), then for every wave
+      wait_vmcnt(2 * NA + n_rc);
+      __syncthreads();
+    }
+    // the products issue the copies of rows st + 2 and planes st + 3:
+    // buffers (st + 2) % 3 and (st + 3) % 4 were last read in step st - 1
+    // (after the last word, the "next" plane words are a stale buffer:
+    // decoded, never used)
+    uint32_t w[2][NB], wn[2][NB];
+    rec_words(st, w);
+    rec_words(st + 1, wn);
+    products(st, 0, Bn, w, 1, Bk);
+    products(st, 1, Bk, wn, 0, Bn);
+  }
+
+  // thresholds of the tile's queries, in the (now free) query-row buffers;
+  // no copy may still be writing LDS
+  wait_vmcnt(0);
+  float* thr_s = (float*)&As[0][0][0];
+  __syncthreads();
   if (tid < kQT) {
     const int64_t q = q0 + tid;
     thr_s[tid] = q < a.n_q ? a.thr[q] : INFINITY;   // padded rows never pass
   }
-  if (tid < kMaxK) ctab_s[tid] = a.ctab[tid];
   __syncthreads();
 
-  if (wave >= 8) {
-    // ======== producers: stage query rows, decode records ==================
-    const int pt = tid - 512;
-    // decode role: record dr, coordinates 16 dh .. 16 dh + 15 of each word
-    const int dr = pt >> 1, dh = pt & 1;
-    const bool dlive = r0 + dr < a.n_rec;
-    const uint32_t* drec = a.planes + (a.rec0 + r0 + dr) * (int64_t)a.W * NB;
-    const uint16_t gbits =
-        dlive ? (uint16_t)(a.norms[a.rec0 + r0 + dr] >> 16) : (uint16_t)0;   // fp16 gamma
-    // word w's query rows (NA arrays x 256 rows x 4 chunks) and record words,
-    // loaded into registers one word ahead
-    // (chunk j of a thread: array j / 4, row pt / 4 + 64 (j % 4), part pt % 4;
-    // the array index is a compile-time constant, so its pointer stays in
-    // scalar registers)
-    v8h ra[NAC];
-    uint32_t wd[NB];
-    const int prow = pt >> 2, ppart = pt & 3;
-    auto load_word = [&](int w) {
-#pragma unroll
-      for (int j = 0; j < NAC; ++j) {
-        const int row = prow + 64 * (j & 3);
-        ra[j] = *(const v8h*)(a.qa[j >> 2] + (q0 + row) * a.Dp + 32 * w + 8 * ppart);
-      }
-#pragma unroll
-      for (int p = 0; p < NB; ++p) wd[p] = dlive ? drec[w * NB + p] : 0u;
-    };
-    load_word(0);
-    for (int st = 0; st <= a.W; ++st) {
-      if (st < a.W) {
-        const int buf = st & 1;
-#pragma unroll
-        for (int j = 0; j < NAC; ++j)
-          *(v8h*)(&As[buf][j >> 2][sw(prow + 64 * (j & 3), ppart)]) = ra[j];
-        v8h vh[2], vl[2], vg[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int bit = 16 * dh + e;
-          uint32_t idx = 0;
-#pragma unroll
-          for (int p = 0; p < CP; ++p) idx |= ((wd[p] >> bit) & 1u) << p;
-          const uint32_t hl = ctab_s[idx];
-          const uint16_t sgn = (MSE || ((wd[NB - 1] >> bit) & 1u)) ? (uint16_t)0 : (uint16_t)0x8000;
-          vh[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl & 0xffffu));
-          vl[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(hl >> 16));
-          vg[e >> 3][e & 7] = __builtin_bit_cast(_Float16, (uint16_t)(gbits ^ sgn));
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int off = sw(dr, 2 * dh + h);
-          *(v8h*)(&Bs[buf][0][off]) = vh[h];
-          *(v8h*)(&Bs[buf][1][off]) = vl[h];
-          if constexpr (!MSE) *(v8h*)(&Bs[buf][2][off]) = vg[h];
-        }
-        if (st + 1 < a.W) load_word(st + 1);
-      }
-      __syncthreads();
-    }
-    return;
-  }
-
-  // ======== MFMA waves: word st - 1 from buffer (st - 1) % 2 ==================
-  const int wq = wave & 3, wr = wave >> 2;       // wave tile: 64 queries x 64 records
-  v16f acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
-  for (int st = 0; st <= a.W; ++st) {
-    if (st >= 1) {
-      const int buf = (st - 1) & 1;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        v8h A[2][NA], B[2][3];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int off = sw(64 * wr + 32 * rb + col, 2 * kk + hh);
-#pragma unroll
-          for (int ar = 0; ar < NBS; ++ar) B[rb][ar] = *(const v8h*)(&Bs[buf][ar][off]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const int off = sw(64 * wq + 32 * qb + col, 2 * kk + hh);
-#pragma unroll
-          for (int ar = 0; ar < NA; ++ar) A[qb][ar] = *(const v8h*)(&As[buf][ar][off]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) {
-            v16f c = acc[qb][rb];
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][0], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][1], B[rb][0], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][0], B[rb][1], c, 0, 0, 0);
-            if constexpr (!MSE)
-              c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[qb][2], B[rb][2], c, 0, 0, 0);
-            acc[qb][rb] = c;
-          }
-      }
-    }
-    __syncthreads();
-  }
-
-  // epilogue: element i of tile (qb, rb) is query 64wq + 32qb + 8(i/4) + 4hh + i%4
-  // and record 64wr + 32rb + col; keep scores above the query's threshold
+  // epilogue: element i of block (qb, rb) is query 128 wq + 32 qb + 8 (i / 4) +
+  // 4 hh + i % 4 and record 64 wr + 32 rb + col; keep scores above the
+  // query's threshold
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int64_t rl = r0 + 64 * wr + 32 * rb + col;
-    const bool rlive = rl < a.n_rec;
-    const float nu =
-        rlive ? __half2float(__ushort_as_half((unsigned short)(a.norms[a.rec0 + rl] & 0xffffu)))
-              : 0.f;
+    const float nu = nu_r[rb];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int ql = 64 * wq + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int ql = 128 * wq + 32 * qb + 8 * (i >> 2) + 4 * hh + (i & 3);
         const float sc = nu * acc[qb][rb][i];
-        const bool pass = rlive && sc > thr_s[ql];
+        const bool pass = rlive[rb] && sc > thr_s[ql];
         const uint64_t m = __ballot(pass);
         if (m) {
           // lanes 0..31 share one query row, lanes 32..63 another
@@ -794,17 +907,25 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
 
   SearchArgs g{};
   for (int i = 0; i < 4; ++i) g.qa[i] = (const __half*)(ws + L.qa[i]);
+  g.qa_step = (int64_t)(L.qa[1] - L.qa[0]) / (int64_t)sizeof(__half);
   g.n_q = n_queries;
   g.planes = planes;
   g.norms = (const uint32_t*)norms;
   g.W = ctx->W;
   g.Dp = ctx->Dp;
+  // codebook byte tables: byte k % 4 of tb[part * 4 + half * 2 + (k >= 4)] is
+  // byte `half` of the fp16 `part` (0: hi, 1: lo) of centroid k
+  for (int i = 0; i < 8; ++i) g.tb[i] = 0u;
   for (int j = 0; j < kMaxK; ++j) {
     const float c = j < ctx->K ? ctx->cent[j] : 0.f;
     const _Float16 h = (_Float16)c;
     const _Float16 l = (_Float16)(c - (float)h);
-    g.ctab[j] = (uint32_t)__builtin_bit_cast(uint16_t, h) |
-                ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+    const uint32_t hb = __builtin_bit_cast(uint16_t, h), lb = __builtin_bit_cast(uint16_t, l);
+    const int sh = 8 * (j & 3), up = j >> 2;
+    g.tb[0 + up] |= (hb & 0xffu) << sh;
+    g.tb[2 + up] |= (hb >> 8) << sh;
+    g.tb[4 + up] |= (lb & 0xffu) << sh;
+    g.tb[6 + up] |= (lb >> 8) << sh;
   }
   g.thr = (float*)(ws + L.thr);
   g.cnt = (int*)(ws + L.cnt);
@@ -838,15 +959,15 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
       const dim3 grid((unsigned)((len + kRT - 1) / kRT), (unsigned)(L.rows_pad / kQT));
       if (ctx->mse) {
         switch (ctx->b) {
-          case 1: hipLaunchKernelGGL((search_gemm_kernel<1, true>), grid, dim3(768), 0, stream, g); break;
-          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, true>), grid, dim3(768), 0, stream, g); break;
-          default: hipLaunchKernelGGL((search_gemm_kernel<3, true>), grid, dim3(768), 0, stream, g); break;
+          case 1: hipLaunchKernelGGL((search_gemm_kernel<1, true>), grid, dim3(512), 0, stream, g); break;
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, true>), grid, dim3(512), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<3, true>), grid, dim3(512), 0, stream, g); break;
         }
       } else {
         switch (ctx->b) {
-          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, false>), grid, dim3(768), 0, stream, g); break;
-          case 3: hipLaunchKernelGGL((search_gemm_kernel<3, false>), grid, dim3(768), 0, stream, g); break;
-          default: hipLaunchKernelGGL((search_gemm_kernel<4, false>), grid, dim3(768), 0, stream, g); break;
+          case 2: hipLaunchKernelGGL((search_gemm_kernel<2, false>), grid, dim3(512), 0, stream, g); break;
+          case 3: hipLaunchKernelGGL((search_gemm_kernel<3, false>), grid, dim3(512), 0, stream, g); break;
+          default: hipLaunchKernelGGL((search_gemm_kernel<4, false>), grid, dim3(512), 0, stream, g); break;
         }
       }
       e = hipGetLastError();
