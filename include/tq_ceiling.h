@@ -27,6 +27,16 @@ extern "C" {
 int tq_ceiling_logit_mix(const uint32_t* planes, const uint32_t* norms, int64_t n, float* out,
                          int64_t out_stride, void* stream);
 
+/* The same bytes per record (64 bytes of planes and the norm word read, 4
+ * floats written) in one-shot workgroups of per_block records each (a grid of
+ * ceil(n / per_block) workgroups of 256 threads; thread (record t / 4, part
+ * t % 4) moves 16 bytes of planes and part's float).  Small blocks keep the
+ * workgroups in flight on one tight, contiguous window of memory, which is
+ * the fastest mixed stream measured on this GPU (128 records per block).
+ * planes 16-byte aligned, out_stride >= n, per_block >= 1. */
+int tq_ceiling_logit_mix_blocks(const uint32_t* planes, const uint32_t* norms, int64_t n,
+                                float* out, int64_t out_stride, int per_block, void* stream);
+
 /* Plain device copy of `bytes` bytes (a multiple of 16; both pointers
  * 16-byte aligned), 16 bytes per lane per step. */
 int tq_ceiling_copy(const void* src, void* dst, int64_t bytes, void* stream);

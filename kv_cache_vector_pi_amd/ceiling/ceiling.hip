@@ -51,6 +51,31 @@ __global__ void __launch_bounds__(256) logit_mix_kernel(const uint32_t* __restri
   }
 }
 
+// the same bytes per record in one-shot workgroups of `per` records: thread
+// (record tid / 4, part tid % 4) loads 16 bytes of planes and the norm word,
+// stores part's float; rounds of 64 records
+__global__ void __launch_bounds__(256) logit_mix_blocks_kernel(const u4v* __restrict__ planes,
+                                                               const uint32_t* __restrict__ norms,
+                                                               int64_t n, float* __restrict__ out,
+                                                               int64_t out_stride, int per) {
+  const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
+  const int64_t b0 = (int64_t)blockIdx.x * per, b1 = std::min<int64_t>(n, b0 + per);
+  for (int64_t base = b0; base < b1; base += 128) {
+    const int64_t i0 = base + r, i1 = base + 64 + r;
+    uint32_t x0 = 0u, x1 = 0u;
+    if (i0 < b1) {
+      const u4v w = __builtin_nontemporal_load(planes + 4 * i0 + part);
+      x0 = w[0] ^ w[1] ^ w[2] ^ w[3] ^ __builtin_nontemporal_load(norms + i0);
+    }
+    if (i1 < b1) {
+      const u4v w = __builtin_nontemporal_load(planes + 4 * i1 + part);
+      x1 = w[0] ^ w[1] ^ w[2] ^ w[3] ^ __builtin_nontemporal_load(norms + i1);
+    }
+    if (i0 < b1) __builtin_nontemporal_store((float)x0, &out[part * out_stride + i0]);
+    if (i1 < b1) __builtin_nontemporal_store((float)x1, &out[part * out_stride + i1]);
+  }
+}
+
 __global__ void __launch_bounds__(256) copy_kernel(const u4v* __restrict__ src,
                                                    u4v* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -188,6 +213,19 @@ extern "C" __attribute__((visibility("default"))) int tq_ceiling_logit_mix(
   const int64_t blocks = (tiles + 4 * tpw - 1) / (4 * tpw);
   hipLaunchKernelGGL(logit_mix_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      planes, norms, n, out, out_stride, (int)tpw);
+  return (int)hipGetLastError();
+}
+
+extern "C" __attribute__((visibility("default"))) int tq_ceiling_logit_mix_blocks(
+    const uint32_t* planes, const uint32_t* norms, int64_t n, float* out, int64_t out_stride,
+    int per_block, void* stream) {
+  if (n < 0 || out_stride < n || per_block < 1) return (int)hipErrorInvalidValue;
+  if (n == 0) return 0;
+  if (!planes || !norms || !out) return (int)hipErrorInvalidValue;
+  const int64_t blocks = (n + per_block - 1) / per_block;
+  if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(logit_mix_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, (const u4v*)planes, norms, n, out, out_stride, per_block);
   return (int)hipGetLastError();
 }
 

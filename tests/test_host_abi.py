@@ -42,8 +42,8 @@ def test_ceiling_library_exports_its_header(tq):
     launch (hipErrorInvalidValue = 1)."""
     src = open(os.path.join(ROOT, "include", "tq_ceiling.h")).read()
     names = sorted(set(re.findall(r"^int\s+(tq_ceiling_\w+)\s*\(", src, re.M)))
-    assert names == ["tq_ceiling_copy", "tq_ceiling_logit_mix", "tq_ceiling_mfma",
-                     "tq_ceiling_overlap"]
+    assert names == ["tq_ceiling_copy", "tq_ceiling_logit_mix", "tq_ceiling_logit_mix_blocks",
+                     "tq_ceiling_mfma", "tq_ceiling_overlap"]
     path = os.path.join(os.path.dirname(tq.LIB_PATH), "libtq_ceiling.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
@@ -63,6 +63,13 @@ def test_ceiling_library_exports_its_header(tq):
                                        ctypes.c_void_p, ctypes.c_void_p]
     assert lib.tq_ceiling_overlap(3, 0, 1, 1, None, None) == 1     # unknown mode
     assert lib.tq_ceiling_overlap(2, 0, 0, 1, None, None) == 0     # no blocks: no-op
+    lib.tq_ceiling_logit_mix_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                                ctypes.c_int, ctypes.c_void_p]
+    assert lib.tq_ceiling_logit_mix_blocks(None, None, 8, None, 8, 0, None) == 1   # per_block < 1
+    assert lib.tq_ceiling_logit_mix_blocks(None, None, 8, None, 4, 128, None) == 1  # out_stride < n
+    assert lib.tq_ceiling_logit_mix_blocks(None, None, 8, None, 8, 128, None) == 1  # NULL with work
+    assert lib.tq_ceiling_logit_mix_blocks(None, None, 0, None, 0, 128, None) == 0  # empty: no-op
     assert lib.tq_ceiling_logit_mix(None, None, 8, None, 4, None) == 1   # out_stride < n
     assert lib.tq_ceiling_logit_mix(None, None, 8, None, 8, None) == 1   # NULL with work
 
