@@ -40,6 +40,7 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kRowsTile = 64;    // dequantize: rows per workgroup
 constexpr int kRecTile = 64;     // dequantize: records per workgroup
@@ -57,6 +58,35 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // 0x01010101 << g spreads over four bytes.
 __host__ __device__ inline int kslot_of(int c) { return 4 * (c & 7) + (c >> 3); }
 
+// float -> fp8 e4m3 (OCP: exponent bias 7, largest finite 448, no infinity),
+// round to nearest even; saturates at 448.  Host and device share it (the
+// codebook's tables are built on the host, the query rows on the device).
+__host__ __device__ inline uint8_t to_e4m3(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sg = (u >> 24) & 0x80u, a = u & 0x7fffffffu;
+  if (a >= 0x43E80000u) return (uint8_t)(sg | 0x7Eu);          // >= 464, inf, nan: 448
+  if (a < 0x3C800000u) {                                        // below 2^-6: steps of 2^-9
+    const float y = __builtin_bit_cast(float, a) * 512.0f;      // exact, < 8
+    uint32_t q = (uint32_t)y;
+    const float r = y - (float)q;
+    if (r > 0.5f || (r == 0.5f && (q & 1u))) ++q;
+    return (uint8_t)(sg | q);                                   // q == 8: 2^-6
+  }
+  uint32_t q = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);    // exponent field 1 .. 15
+  const uint32_t rem = a & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;    // carries into the exponent
+  return (uint8_t)(sg | (q > 0x7Eu ? 0x7Eu : q));
+}
+
+// Byte of K-slot kappa (0 .. 31) in a lane half's fp8 operand: lane half hh
+// holds the byte groups g (kappa = 4 g + t) with (g >> 1) & 1 == hh, in the
+// order g = 2 hh, 2 hh + 1, 4 + 2 hh, 5 + 2 hh, i.e. the groups its decode of
+// the two 16-slot halves of a word produces.  Returns 16 hh + 4 gi + t.
+__host__ __device__ inline int fp8_byte_of(int kappa) {
+  const int g = kappa >> 2, t = kappa & 3;
+  return 16 * ((g >> 1) & 1) + 4 * ((g & 1) + 2 * (g >> 2)) + t;
+}
+
 // ---- row preparation: Pi q and S q, split into hi/lo fp16 -----------------
 // Block (row group of kPrepRows queries, chunk of 256 outputs): each thread
 // owns one output row of Pi or S, reads that row as a contiguous column of
@@ -70,9 +100,9 @@ struct RowPrepArgs {
   const float* pit;      // [d][d] Pi^T
   const float* st;       // [d][d] S^T
   __half* qr_hi;         // [n_pad][Dp]
-  __half* qr_lo;
+  uint8_t* q8;           // [n_pad][Dp / 32][64]: per word, fp8 (QR lo) 2^e_lo then (QR hi) 2^e_hi
   __half* qp_hi;
-  __half* qp_lo;
+  uint32_t* q8scale;     // [n_pad]: E8M0 codes of 2^-e_lo (byte 0) and 2^-e_hi (byte 1)
   float pscale;          // factor on S q (alpha for search)
   int d, Dp;
   int64_t n, n_pad;
@@ -80,7 +110,9 @@ struct RowPrepArgs {
 
 __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
   __shared__ __align__(16) float qv[kPrepJ][kPrepRows];
+  __shared__ float qn2[kPrepRows];
   const int tid = threadIdx.x;
+  float ssq = 0.f;       // this thread's part of ||q||^2 of row tid / 16
   const int64_t row0 = (int64_t)blockIdx.x * kPrepRows;
   const int o = blockIdx.y * 256 + tid;          // output index over [Pi rows | S rows]
   const bool sk = o >= a.Dp;
@@ -99,6 +131,11 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
       qv[j][i] = (row < a.n && j < nj) ? a.q[row * a.d + j0 + j] : 0.f;
     }
     __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < kPrepJ / 16; ++jj) {
+      const float v = qv[16 * (tid & 15) + jj][tid >> 4];
+      ssq = fmaf(v, v, ssq);
+    }
     if (live) {
       auto step = [&](const float t, const int j) {
         const float4* qq = (const float4*)&qv[j][0];
@@ -123,18 +160,37 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
       for (; j < nj; ++j) step(col[(int64_t)(j0 + j) * a.d], j);
     }
   }
+  // ||q||^2 per row: the 16 threads of a row are 16 consecutive lanes
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) ssq += __shfl_xor(ssq, m, 16);
+  if ((tid & 15) == 0) qn2[tid >> 4] = ssq;
+  __syncthreads();
   if (o >= 2 * a.Dp) return;
-  __half* hi = sk ? a.qp_hi : a.qr_hi;
-  __half* lo = sk ? a.qp_lo : a.qr_lo;
-  const int pos = (r & ~31) + kslot_of(r & 31);    // K-slot order within the word
+  const int kappa = kslot_of(r & 31);
+  const int pos = (r & ~31) + kappa;                // K-slot order within the word
+  const int64_t b8 = (int64_t)(r >> 5) * 64 + fp8_byte_of(kappa);
 #pragma unroll
   for (int i = 0; i < kPrepRows; ++i) {
     const int64_t row = row0 + i;
     if (row < a.n_pad) {
       const float v = live ? (sk ? a.pscale * acc[i] : acc[i]) : 0.f;
       const __half vh = __float2half(v);
-      hi[row * a.Dp + pos] = vh;
-      lo[row * a.Dp + pos] = __float2half(v - __half2float(vh));
+      if (sk) {
+        a.qp_hi[row * a.Dp + pos] = vh;
+      } else {
+        a.qr_hi[row * a.Dp + pos] = vh;
+        // fp8 copies of the hi and lo parts for the correction products,
+        // scaled by powers of two: |Pi q|_j <= ||q|| < 2^e puts (QR hi) 2^(8-e)
+        // below 256, and |QR lo| <= 2^-11 |QR| (fp16 rounding) the lo part too
+        int e = 0;
+        frexpf(sqrtf(qn2[i]), &e);
+        const int ehi = min(100, max(-100, 8 - e)), elo = ehi + 11;
+        const float vl = v - __half2float(vh);
+        uint8_t* q8 = a.q8 + row * (int64_t)(2 * a.Dp) + b8;
+        q8[0] = to_e4m3(ldexpf(vl, elo));
+        q8[32] = to_e4m3(ldexpf(__half2float(vh), ehi));
+        if (o == 0) a.q8scale[row] = (uint32_t)(127 - elo) | ((uint32_t)(127 - ehi) << 8);
+      }
     }
   }
 }
@@ -438,8 +494,9 @@ __global__ void __launch_bounds__(256, 2) dequant128_kernel(GemmArgs a) {
 
 // ---- search GEMM with threshold-filter epilogue -------------------------------
 struct SearchArgs {
-  const __half* qa[4];   // QR hi, QR lo, (alpha QP) hi, (alpha QP) lo: [rows_pad][Dp],
-                         // coordinates of each 32-word in K-slot order (below)
+  const __half* qa[4];   // [rows_pad][Dp] halves each, coordinates of each 32-word in K-slot
+                         // order (below): QR hi; the fp8 correction rows (64 bytes per
+                         // word, row preparation); (alpha QP) hi; qa[3] holds q8scale
   int64_t qa_step;       // qa[i] = qa[0] + i * qa_step (halves)
   int64_t n_q;
   const uint32_t* planes;
@@ -448,7 +505,10 @@ struct SearchArgs {
   int W, Dp;
   uint32_t tb[8];        // byte tables of the codebook for v_perm: bytes of centroid k's
                          // fp16 hi part (low byte: tb[0] k < 4, tb[1] k >= 4; high byte:
-                         // tb[2], tb[3]) and lo part (tb[4] .. tb[7])
+                         // tb[2], tb[3]); fp8 (c hi) 2^e_chi (tb[4], tb[5]) and fp8
+                         // (c lo) 2^e_clo (tb[6], tb[7])
+  uint32_t bscale;       // E8M0 codes of 2^-e_chi (byte 0) and 2^-e_clo (byte 1)
+  const uint32_t* q8scale;   // [rows_pad]: the query rows' fp8 scale codes (row preparation)
   const float* thr;      // [n_q] running k-th best score (-inf: fewer than k yet)
   int* cnt;              // [n_q] candidates of this chunk
   float* cand_s;         // [n_q][kChunk]
@@ -470,14 +530,21 @@ struct SearchArgs {
 //    table reads;
 //  * one barrier per word.
 // The MFMAs per word and 32 x 32 block are those of the decoded product:
-//   acc += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo + (alpha QP)_hi gamma s.
+//   acc += QR_hi c_hi + (alpha QP)_hi gamma s       (fp16, two per K-slice)
+//        + QR_lo c_hi + QR_hi c_lo                  (one scaled fp8 MFMA per word).
+// The two correction terms are each about 2^-11 of the code term, so fp8
+// (3 mantissa bits, about 2^-4 relative per factor) leaves them an error near
+// 2^-14 of the code term, while the per-block power-of-two scales of
+// v_mfma_scale_f32_32x32x64_f8f6f4 keep both products inside fp8's range.  The
+// fp8 MFMA covers 64 K-slots (both terms of a word) in the time of two fp16 ones,
+// so the matrix cores do three quarters of the work of four fp16 passes.
 template <int NB, bool MSE>
 __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   constexpr int CP = MSE ? NB : NB - 1;         // code planes
-  // staged query arrays: QR hi, QR lo and (alpha QP) hi.  The sketch term
-  // alpha gamma <QP, s> is a small part of a score, so its fp16 rounding of
-  // QP (2^-12 relative) stays ~1e-4 of the scores' rms; (alpha QP) lo is not
-  // used.  The code term keeps hi/lo products (2^-22).
+  // staged query arrays: QR hi, the fp8 correction rows and (alpha QP) hi.
+  // The sketch term alpha gamma <QP, s> is a small part of a score, so its
+  // fp16 rounding of QP (2^-12 relative) stays ~1e-4 of the scores' rms;
+  // (alpha QP) lo is not used.
   constexpr int NA = MSE ? 2 : 3;
   constexpr int NRC = 4 * NB;                    // record copies (256 lanes x 4 B) per word
   __shared__ __align__(16) _Float16 As[3][NA][kQT * 32];
@@ -554,10 +621,13 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   // B operands of one 32 x 32 block for K-slots 16 kk + 8 hh .. + 7, i.e. byte
   // groups g = 4 kk + 2 hh and g + 1; w holds the plane words shifted right by
   // 2 hh, so group g + j's bits are at 4 kk + j for every lane.  Dwords of an
-  // operand: (slots 0,1), (2,3) of group g, then of group g + 1.  One call
-  // fills the two dwords of group g + j in each array.
+  // fp16 operand: (slots 0,1), (2,3) of group g, then of group g + 1.  One call
+  // fills the two dwords of group g + j in B[0] (centroid hi) and B[1]
+  // (gamma s), and dword 2 kk + j (fp8 centroid hi) and 4 + 2 kk + j (fp8
+  // centroid lo) of the lane's fp8 operand B8 for the word's correction product.
   typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-  auto decode_group = [&](const uint32_t (&w)[NB], uint32_t tgr, int kk, int j, u4v (&B)[3]) {
+  auto decode_group = [&](const uint32_t (&w)[NB], uint32_t tgr, int kk, int j, u4v (&B)[2],
+                          v8i& B8) {
     const int k = 4 * kk + j;
     uint32_t v = w[0] & (0x01010101u << k);
     if constexpr (CP >= 2) v |= (w[1] << 1) & (0x02020202u << k);
@@ -567,17 +637,15 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
     const uint32_t hh8 = __builtin_amdgcn_perm(tb[3], tb[2], sel);
     B[0][2 * j] = __builtin_amdgcn_perm(hh8, hl, 0x05010400u);
     B[0][2 * j + 1] = __builtin_amdgcn_perm(hh8, hl, 0x07030602u);
-    const uint32_t ll = __builtin_amdgcn_perm(tb[5], tb[4], sel);
-    const uint32_t lh = __builtin_amdgcn_perm(tb[7], tb[6], sel);
-    B[1][2 * j] = __builtin_amdgcn_perm(lh, ll, 0x05010400u);
-    B[1][2 * j + 1] = __builtin_amdgcn_perm(lh, ll, 0x07030602u);
+    B8[2 * kk + j] = (int)__builtin_amdgcn_perm(tb[5], tb[4], sel);
+    B8[4 + 2 * kk + j] = (int)__builtin_amdgcn_perm(tb[7], tb[6], sel);
     if constexpr (!MSE) {
       const uint32_t sb = (w[NB - 1] >> k) & 0x01010101u;     // sign bits per byte
       // selectors (2, b0, 2, b1) and (2, b2, 2, b3) into tgr
       const uint32_t sa = __builtin_amdgcn_perm(0x02020202u, sb, 0x01040004u);
       const uint32_t sc = __builtin_amdgcn_perm(0x02020202u, sb, 0x03040204u);
-      B[2][2 * j] = __builtin_amdgcn_perm(0u, tgr, sa);
-      B[2][2 * j + 1] = __builtin_amdgcn_perm(0u, tgr, sc);
+      B[1][2 * j] = __builtin_amdgcn_perm(0u, tgr, sa);
+      B[1][2 * j + 1] = __builtin_amdgcn_perm(0u, tgr, sc);
     }
   };
 
@@ -586,6 +654,7 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (v16f){};
+  v8i B8[2];                 // per record block: the word's fp8 correction operand
   // this lane's plane words of word s (records 64 wr + 32 rb + col), shifted
   // right by 2 hh
   auto rec_words = [&](int s, uint32_t (&w)[2][NB]) {
@@ -603,41 +672,68 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
       for (int p = 0; p < NB; ++p) w[rb][p] >>= 2 * hh;
     }
   };
-  // MFMAs of K-slice kk of word s (query rows from buffer s % 3) on the
-  // operands Bc, with the decode of the next K-slice's operands Bd (group j of
-  // record block rb per 32-query block) interleaved: per query block, its three
-  // operand reads, then each MFMA followed by two vector instructions
-  auto products = [&](int s, int kk, const u4v (&Bc)[2][3], const uint32_t (&wd)[2][NB],
-                      int kkd, u4v (&Bd)[2][3]) {
+  // scales of the fp8 correction product: lane (row, hh) gives the code of its
+  // row's block hh (A: 2^-e_lo for the lo part, 2^-e_hi for the hi part),
+  // lane (record, hh) that of its column's block hh (B: 2^-e_chi, 2^-e_clo)
+  int sa8[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+    sa8[qb] = (int)((a.q8scale[q0 + 128 * wq + 32 * qb + col] >> (8 * hh)) & 0xffu);
+  const int sb8 = (int)((a.bscale >> (8 * hh)) & 0xffu);
+
+  // fp16 MFMAs of K-slice kk of word s (query rows from buffer s % 3) on the
+  // operands Bc: QR hi x centroid hi and (alpha QP) hi x gamma s.  The decode
+  // of the next K-slice's operands Bd / B8 (group j of record block rb per
+  // 32-query block) is interleaved: per query block, its operand reads, then
+  // each MFMA followed by vector instructions.
+  constexpr int NF = MSE ? 1 : 2;                // fp16 MFMAs per block and K-slice
+  auto products = [&](int s, int kk, const u4v (&Bc)[2][2], const uint32_t (&wd)[2][NB],
+                      int kkd, u4v (&Bd)[2][2]) {
     const int buf = s % 3;
     static_assert(2 * NA + NRI <= 8, "one copy per query block and K-slice");
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int off = sw(128 * wq + 32 * qb + col, 2 * kk + hh);
-      v8h A[NA];
-#pragma unroll
-      for (int ar = 0; ar < NA; ++ar) A[ar] = *(const v8h*)(&As[buf][ar][off]);
+      const v8h A0 = *(const v8h*)(&As[buf][0][off]);
+      v8h A2 = A0;
+      if constexpr (!MSE) A2 = *(const v8h*)(&As[buf][2][off]);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         v16f c = acc[qb][rb];
-        const v8h b0 = __builtin_bit_cast(v8h, Bc[rb][0]);
-        const v8h b1 = __builtin_bit_cast(v8h, Bc[rb][1]);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], b0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[1], b0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[0], b1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A0, __builtin_bit_cast(v8h, Bc[rb][0]), c, 0,
+                                                   0, 0);
         if constexpr (!MSE)
-          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[2], __builtin_bit_cast(v8h, Bc[rb][2]), c,
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A2, __builtin_bit_cast(v8h, Bc[rb][1]), c,
                                                      0, 0, 0);
         acc[qb][rb] = c;
       }
-      decode_group(wd[qb >> 1], tg[qb >> 1], kkd, qb & 1, Bd[qb >> 1]);
-      __builtin_amdgcn_sched_group_barrier(0x100, NA, 0);
+      decode_group(wd[qb >> 1], tg[qb >> 1], kkd, qb & 1, Bd[qb >> 1], B8[qb >> 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
 #pragma unroll
-      for (int m = 0; m < (MSE ? 6 : 8); ++m) {
+      for (int m = 0; m < 2 * NF; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
       stage_item(s, 4 * kk + qb);
+    }
+  };
+  // the word's correction products, one scaled fp8 MFMA per 32 x 32 block:
+  // K block 0 = (QR lo) 2^e_lo x (c hi) 2^e_chi, block 1 = (QR hi) 2^e_hi x
+  // (c lo) 2^e_clo, over the lane's 16 K-slots of each (query rows from
+  // buffer s % 3, array 1: the lo part in chunks 0-1, the hi part in 2-3)
+  auto corrections = [&](int s) {
+    const int buf = s % 3;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int row = 128 * wq + 32 * qb + col;
+      const uint4 lo = *(const uint4*)(&As[buf][1][sw(row, hh)]);
+      const uint4 hi = *(const uint4*)(&As[buf][1][sw(row, 2 + hh)]);
+      const v8i A8 = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        acc[qb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A8, B8[rb], acc[qb][rb], 0,
+                                                                      0, 0, sa8[qb], 0, sb8);
     }
   };
 
@@ -660,14 +756,14 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   if (a.W > 2) stage_r_all(2);
   wait_vmcnt((a.W > 1 ? 2 * NA : 0) + (a.W > 2 ? n_rc : 0));   // rows of word 0, planes of 0 and 1
   __syncthreads();
-  u4v Bn[2][3], Bk[2][3];    // K-slice 0 of the current word (decoded one step early), slice 1
+  u4v Bn[2][2], Bk[2][2];    // K-slice 0 of the current word (decoded one step early), slice 1
   {
     uint32_t w[2][NB];
     rec_words(0, w);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      decode_group(w[rb], tg[rb], 0, 0, Bn[rb]);
-      decode_group(w[rb], tg[rb], 0, 1, Bn[rb]);
+      decode_group(w[rb], tg[rb], 0, 0, Bn[rb], B8[rb]);
+      decode_group(w[rb], tg[rb], 0, 1, Bn[rb], B8[rb]);
     }
   }
   for (int st = 0; st < a.W; ++st) {
@@ -685,6 +781,7 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
     rec_words(st, w);
     rec_words(st + 1, wn);
     products(st, 0, Bn, w, 1, Bk);
+    corrections(st);           // B8 complete: slice 0 (a step early) and slice 1
     products(st, 1, Bk, wn, 0, Bn);
   }
 
@@ -888,9 +985,9 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   p.pit = ctx->t.pit32;
   p.st = ctx->t.st32;
   p.qr_hi = (__half*)(ws + L.qa[0]);
-  p.qr_lo = (__half*)(ws + L.qa[1]);
+  p.q8 = (uint8_t*)(ws + L.qa[1]);               // 64 bytes per row and word: as large as QR lo
   p.qp_hi = (__half*)(ws + L.qa[2]);
-  p.qp_lo = (__half*)(ws + L.qa[3]);
+  p.q8scale = (uint32_t*)(ws + L.qa[3]);
   p.pscale = alpha;
   p.d = ctx->d;
   p.Dp = ctx->Dp;
@@ -913,20 +1010,29 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   g.norms = (const uint32_t*)norms;
   g.W = ctx->W;
   g.Dp = ctx->Dp;
-  // codebook byte tables: byte k % 4 of tb[part * 4 + half * 2 + (k >= 4)] is
-  // byte `half` of the fp16 `part` (0: hi, 1: lo) of centroid k
+  // codebook byte tables: byte k % 4 of tb[half * 2 + (k >= 4)] is byte
+  // `half` of centroid k's fp16 hi part; of tb[4 + (k >= 4)] its fp8 hi part
+  // (c_hi 2^e_chi), of tb[6 + (k >= 4)] its fp8 lo part (c_lo 2^e_clo).
+  // |c| < 2^e puts c_hi 2^(8-e) below 256, and |c_lo| <= 2^-11 |c| the lo part.
+  float cmax = 0.f;
+  for (int j = 0; j < ctx->K; ++j) cmax = std::max(cmax, std::fabs(ctx->cent[j]));
+  int ce = 0;
+  std::frexp(cmax, &ce);
+  const int echi = std::min(100, std::max(-100, 8 - ce)), eclo = echi + 11;
+  g.bscale = (uint32_t)(127 - echi) | ((uint32_t)(127 - eclo) << 8);
   for (int i = 0; i < 8; ++i) g.tb[i] = 0u;
   for (int j = 0; j < kMaxK; ++j) {
     const float c = j < ctx->K ? ctx->cent[j] : 0.f;
     const _Float16 h = (_Float16)c;
-    const _Float16 l = (_Float16)(c - (float)h);
-    const uint32_t hb = __builtin_bit_cast(uint16_t, h), lb = __builtin_bit_cast(uint16_t, l);
+    const float l = c - (float)h;
+    const uint32_t hb = __builtin_bit_cast(uint16_t, h);
     const int sh = 8 * (j & 3), up = j >> 2;
     g.tb[0 + up] |= (hb & 0xffu) << sh;
     g.tb[2 + up] |= (hb >> 8) << sh;
-    g.tb[4 + up] |= (lb & 0xffu) << sh;
-    g.tb[6 + up] |= (lb >> 8) << sh;
+    g.tb[4 + up] |= (uint32_t)to_e4m3(std::ldexp((float)h, echi)) << sh;
+    g.tb[6 + up] |= (uint32_t)to_e4m3(std::ldexp(l, eclo)) << sh;
   }
+  g.q8scale = (const uint32_t*)(ws + L.qa[3]);
   g.thr = (float*)(ws + L.thr);
   g.cnt = (int*)(ws + L.cnt);
   g.cand_s = (float*)(ws + L.cand_s);
