@@ -47,6 +47,34 @@ __device__ inline void copy4_to_lds(const void* gaddr, uint32_t m0_base) {
       : "memory");
 }
 
+// The same copies with a scalar base: lane l reads base + voff (voff a 32-bit
+// byte offset), so a loop whose lanes keep fixed offsets from a moving base
+// spends no vector instructions on addresses.
+__device__ inline void copy16_to_lds_s(uint32_t voff, const void* sbase, uint32_t m0_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m0_base)
+      : "memory");
+}
+__device__ inline void copy4_to_lds_s(uint32_t voff, const void* sbase, uint32_t m0_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m0_base)
+      : "memory");
+}
+
 // s_waitcnt vmcnt(n) for a uniform n in 0..15 (expcnt and lgkmcnt untouched)
 __device__ inline void wait_vmcnt(int n) {
   switch (n) {

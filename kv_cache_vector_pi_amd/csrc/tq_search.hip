@@ -559,18 +559,25 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
 
   // Copies of one word, in items a wave issues one at a time (spread over the
   // products, so that the address units work beside the matrix cores instead
-  // of stalling every wave at the start of a step).
+  // of stalling every wave at the start of a step).  A lane's byte offsets are
+  // fixed for the whole loop; only the scalar bases move with the word.
   // Query rows of word s into buffer s % 3, items 0 .. 2 NA - 1: wave w copies
   // rows 32w .. 32w + 31 of every array, 16 rows (1 KB) per copy; lane l
   // fills slot l % 4 of row 16 i + l / 4 with chunk slot ^ ((row >> 2) & 3).
+  uint32_t qoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 32 * wave + 16 * i + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    qoff[i] = (uint32_t)((row * a.Dp + 8 * chunk) * 2);
+  }
+  const char* qbase = (const char*)(a.qa[0] + q0 * a.Dp);
   auto stage_q = [&](int s, int item) {
     const int buf = s % 3, ar = item >> 1;
     const int rbase = 32 * wave + 16 * (item & 1);
-    const int row = rbase + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     const int sw_ = s < a.W ? s : a.W - 1;          // past the last word: a harmless copy
-    const __half* src = a.qa[0] + (int64_t)ar * a.qa_step + (q0 + row) * a.Dp + 32 * sw_ + 8 * chunk;
-    copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(&As[buf][ar][rbase * 32])));
+    copy16_to_lds_s(qoff[item & 1], qbase + ((int64_t)ar * a.qa_step + 32 * sw_) * 2,
+                    __builtin_amdgcn_readfirstlane(lds_addr(&As[buf][ar][rbase * 32])));
   };
   // Plane words of word s into buffer s % 4, items 0 .. NRI - 1: copy j = w +
   // 8 item (if j < NRC) moves dwords 64 j .. 64 j + 63 of the tile's
@@ -578,16 +585,21 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   // its scores are dropped).
   constexpr int NRI = (NRC + 7) / 8;
   const int n_rc = wave < NRC ? (NRC - 1 - wave) / 8 + 1 : 0;   // copies per wave
+  uint32_t roff[NRI];
+#pragma unroll
+  for (int i = 0; i < NRI; ++i) {
+    const int e = 64 * (wave + 8 * i) + lane, r = e / NB, p = e - r * NB;
+    const int64_t rl = r0 + r;
+    roff[i] = (uint32_t)(((rl < a.n_rec ? rl : a.n_rec - 1) * (int64_t)(a.W * NB) + p) * 4);
+  }
+  const char* rbase_p = (const char*)(a.planes + a.rec0 * (int64_t)(a.W * NB));
   auto stage_r = [&](int s, int item) {
     const int j = wave + 8 * item;
     if (NRC % 8 == 0 || j < NRC) {
       const int buf = s & 3;
-      const int e = 64 * j + lane, r = e / NB, p = e - r * NB;
-      const int64_t rl = r0 + r;
-      const int64_t rc = a.rec0 + (rl < a.n_rec ? rl : a.n_rec - 1);
       const int sw_ = s < a.W ? s : a.W - 1;
-      const uint32_t* src = a.planes + rc * (int64_t)(a.W * NB) + sw_ * NB + p;
-      copy4_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(&Rs[buf][64 * j])));
+      copy4_to_lds_s(roff[item], rbase_p + (int64_t)sw_ * NB * 4,
+                     __builtin_amdgcn_readfirstlane(lds_addr(&Rs[buf][64 * j])));
     }
   };
   // item i of step st: rows of word st + 2, then planes of word st + 3.  Every
@@ -687,16 +699,28 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   // 32-query block) is interleaved: per query block, its operand reads, then
   // each MFMA followed by vector instructions.
   constexpr int NF = MSE ? 1 : 2;                // fp16 MFMAs per block and K-slice
+  // Operand reads: row 128 wq + 32 qb + col, chunk c sits at halves
+  // (row * 32) + ((c ^ ((row >> 2) & 3)) << 3), and (row >> 2) & 3 is the same
+  // for every qb, so a lane reads chunk c of all its rows, arrays and buffers
+  // at fixed distances from one address per chunk (immediate offsets).
+  typedef const __attribute__((address_space(3))) char* lds_cp;
+  const uint32_t rsw = (uint32_t)(col >> 2) & 3u;
+  const uint32_t as0 = lds_addr(&As[0][0][0]);
+  auto a_addr = [&](int buf, int c) -> lds_cp {
+    const uint32_t off = (((uint32_t)(128 * wq + col) * 32u + ((((uint32_t)c) ^ rsw) << 3)) * 2u) & 0xffffu;
+    return (lds_cp)(uintptr_t)(as0 + (uint32_t)buf * (uint32_t)(NA * kQT * 64) + off);
+  };
+  constexpr int kArr = kQT * 32 * 2;             // bytes per staged array
   auto products = [&](int s, int kk, const u4v (&Bc)[2][2], const uint32_t (&wd)[2][NB],
                       int kkd, u4v (&Bd)[2][2]) {
-    const int buf = s % 3;
+    const lds_cp ab = a_addr(s % 3, 2 * kk + hh);
     static_assert(2 * NA + NRI <= 8, "one copy per query block and K-slice");
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int off = sw(128 * wq + 32 * qb + col, 2 * kk + hh);
-      const v8h A0 = *(const v8h*)(&As[buf][0][off]);
+      const v8h A0 = *(const __attribute__((address_space(3))) v8h*)(ab + qb * 2048);
       v8h A2 = A0;
-      if constexpr (!MSE) A2 = *(const v8h*)(&As[buf][2][off]);
+      if constexpr (!MSE)
+        A2 = *(const __attribute__((address_space(3))) v8h*)(ab + 2 * kArr + qb * 2048);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         v16f c = acc[qb][rb];
@@ -722,14 +746,14 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   // (c lo) 2^e_clo, over the lane's 16 K-slots of each (query rows from
   // buffer s % 3, array 1: the lo part in chunks 0-1, the hi part in 2-3)
   auto corrections = [&](int s) {
-    const int buf = s % 3;
+    const lds_cp al = a_addr(s % 3, hh) + kArr;
+    const lds_cp ah = a_addr(s % 3, 2 + hh) + kArr;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
-      const int row = 128 * wq + 32 * qb + col;
-      const uint4 lo = *(const uint4*)(&As[buf][1][sw(row, hh)]);
-      const uint4 hi = *(const uint4*)(&As[buf][1][sw(row, 2 + hh)]);
-      const v8i A8 = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const u4v lo = *(const __attribute__((address_space(3))) u4v*)(al + qb * 2048);
+      const u4v hi = *(const __attribute__((address_space(3))) u4v*)(ah + qb * 2048);
+      const v8i A8 = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
         acc[qb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A8, B8[rb], acc[qb][rb], 0,
