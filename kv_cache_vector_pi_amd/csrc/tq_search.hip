@@ -554,8 +554,6 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   const int col = lane & 31, hh = lane >> 5;
   const int wq = wave & 1, wr = wave >> 1;       // queries 128 wq .., records 64 wr ..
   const int64_t r0 = (int64_t)blockIdx.x * kRT, q0 = (int64_t)blockIdx.y * kQT;
-  // halves offset of chunk c of staged row r
-  auto sw = [](int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); };
 
   // Copies of one word, in items a wave issues one at a time (spread over the
   // products, so that the address units work beside the matrix cores instead
