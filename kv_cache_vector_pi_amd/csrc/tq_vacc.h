@@ -144,7 +144,6 @@ __device__ void vacc_mfma(const uint32_t* planes, int nt, int W, const float* wt
   v4i* aops = (v4i*)lds;                      // [block][part][half][64 lanes]
   uint32_t* wordsT = (uint32_t*)(lds + kVAopsBytes);   // [4 words][NB planes][kVChunk]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int RW = W * NB;
 
   // 1. scale and sum per (part, head): wave w takes combos 2w, 2w + 1
 #pragma unroll
