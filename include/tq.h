@@ -409,7 +409,9 @@ TQ_API tq_status tq_attn_decode(const tq_ctx* ctx, const float* q, int32_t batch
                                 int64_t out_stride_batch, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
-/* Workspace for tq_search_topk, in bytes. */
+/* Workspace for tq_search_topk, in bytes: the prepared query rows (about
+ * 8 x d bytes per query) and per-query candidate lists of one chunk of
+ * records (8 bytes x 65536 per query, or x 16384 where that would pass 1 GiB). */
 TQ_API size_t tq_search_workspace_bytes(const tq_ctx* ctx, int64_t n_queries, int64_t n_db,
                                         int32_t k);
 

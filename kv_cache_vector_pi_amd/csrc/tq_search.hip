@@ -48,7 +48,14 @@ constexpr int kLdsRow = 40;      // halves per staged row of one word (32 + pad)
 constexpr int kQT = 256;         // search: queries per workgroup
 constexpr int kRT = 256;         // search: records per workgroup
 constexpr int kFirst = 2048;     // search: records of the first chunk (sets the thresholds)
-constexpr int kChunk = 16384;    // search: records per later chunk = candidate capacity
+constexpr int kChunk = 65536;    // search: records per later chunk = candidate capacity ...
+constexpr int kChunkSmall = 16384;   // ... unless n_q x kChunk candidates exceed kCandCap bytes
+constexpr int64_t kCandCap = (int64_t)1 << 30;
+
+// records per chunk after the first: the candidate lists hold a chunk's worth
+inline int search_chunk(int64_t n_queries) {
+  return n_queries * (int64_t)kChunk * 8 <= kCandCap ? kChunk : kChunkSmall;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -511,8 +518,9 @@ struct SearchArgs {
   const uint32_t* q8scale;   // [rows_pad]: the query rows' fp8 scale codes (row preparation)
   const float* thr;      // [n_q] running k-th best score (-inf: fewer than k yet)
   int* cnt;              // [n_q] candidates of this chunk
-  float* cand_s;         // [n_q][kChunk]
-  int* cand_i;           // [n_q][kChunk] record index within the chunk
+  float* cand_s;         // [n_q][chunk]
+  int* cand_i;           // [n_q][chunk] record index within the chunk
+  int64_t chunk;         // candidate capacity per query (records per chunk)
 };
 
 // One workgroup per (256-record tile, 256-query tile), 8 waves, each owning
@@ -840,7 +848,7 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
           if (col == 0 && mh) base = atomicAdd(&a.cnt[q0 + ql], __popc(mh));
           base = __shfl(base, 32 * hh);
           if (pass) {
-            const int64_t slot = (q0 + ql) * (int64_t)kChunk + base + __popc(mh & ((1u << col) - 1u));
+            const int64_t slot = (q0 + ql) * a.chunk + base + __popc(mh & ((1u << col) - 1u));
             a.cand_s[slot] = sc;
             a.cand_i[slot] = (int)rl;
           }
@@ -857,6 +865,7 @@ struct MergeArgs {
   int* cnt;
   const float* cand_s;
   const int* cand_i;
+  int64_t chunk;         // candidate capacity per query
   float* run_score;      // [n_q][k]
   int64_t* run_idx;
   int first, last;
@@ -882,8 +891,8 @@ __global__ void __launch_bounds__(256) cand_merge_kernel(MergeArgs a) {
   float ts = __shfl(sv, k - 1);
   int64_t ti = __shfl(iv, k - 1);
   const int n = a.cnt[q];
-  const float* cs = a.cand_s + q * (int64_t)kChunk;
-  const int* ci = a.cand_i + q * (int64_t)kChunk;
+  const float* cs = a.cand_s + q * a.chunk;
+  const int* ci = a.cand_i + q * a.chunk;
   for (int b0 = 0; b0 < n; b0 += 64) {
     const bool in = b0 + lane < n;
     const float v = in ? cs[b0 + lane] : -INFINITY;
@@ -980,8 +989,9 @@ SearchLayout search_layout(const tq_ctx* ctx, int64_t n_queries, int32_t k) {
   }
   L.thr = off; off += align256((size_t)n_queries * sizeof(float));
   L.cnt = off; off += align256((size_t)n_queries * sizeof(int));
-  L.cand_s = off; off += align256((size_t)n_queries * kChunk * sizeof(float));
-  L.cand_i = off; off += align256((size_t)n_queries * kChunk * sizeof(int));
+  const size_t chunk = (size_t)search_chunk(n_queries);
+  L.cand_s = off; off += align256((size_t)n_queries * chunk * sizeof(float));
+  L.cand_i = off; off += align256((size_t)n_queries * chunk * sizeof(int));
   L.run_s = off; off += align256((size_t)n_queries * k * sizeof(float));
   L.run_i = off; off += align256((size_t)n_queries * k * sizeof(int64_t));
   L.total = off;
@@ -1059,6 +1069,7 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   g.cnt = (int*)(ws + L.cnt);
   g.cand_s = (float*)(ws + L.cand_s);
   g.cand_i = (int*)(ws + L.cand_i);
+  g.chunk = search_chunk(n_queries);
 
   MergeArgs m{};
   m.n_q = n_queries;
@@ -1067,6 +1078,7 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   m.cnt = g.cnt;
   m.cand_s = g.cand_s;
   m.cand_i = g.cand_i;
+  m.chunk = g.chunk;
   m.run_score = (float*)(ws + L.run_s);
   m.run_idx = (int64_t*)(ws + L.run_i);
   m.out_score = out_score;
@@ -1076,11 +1088,11 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
                      stream, m.thr, m.cnt, n_queries);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // chunks: a small first one sets the thresholds, then kChunk records each
+  // chunks: a small first one sets the thresholds, then g.chunk records each
   int64_t base = 0;
   bool first = true;
   do {
-    const int64_t len = std::min<int64_t>(n_db - base, first ? kFirst : kChunk);
+    const int64_t len = std::min<int64_t>(n_db - base, first ? kFirst : g.chunk);
     if (len > 0) {
       g.rec0 = base;
       g.n_rec = len;
