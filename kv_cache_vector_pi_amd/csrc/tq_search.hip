@@ -787,14 +787,12 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
   wait_vmcnt((a.W > 1 ? 2 * NA : 0) + (a.W > 2 ? n_rc : 0));   // rows of word 0, planes of 0 and 1
   __syncthreads();
   u4v Bn[2][2], Bk[2][2];    // K-slice 0 of the current word (decoded one step early), slice 1
-  {
-    uint32_t w[2][NB];
-    rec_words(0, w);
+  uint32_t w[2][NB];         // the current word's plane words (read one step early)
+  rec_words(0, w);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      decode_group(w[rb], tg[rb], 0, 0, Bn[rb], B8[rb]);
-      decode_group(w[rb], tg[rb], 0, 1, Bn[rb], B8[rb]);
-    }
+  for (int rb = 0; rb < 2; ++rb) {
+    decode_group(w[rb], tg[rb], 0, 0, Bn[rb], B8[rb]);
+    decode_group(w[rb], tg[rb], 0, 1, Bn[rb], B8[rb]);
   }
   for (int st = 0; st < a.W; ++st) {
     if (st > 0) {
@@ -807,12 +805,15 @@ __global__ void __launch_bounds__(512, 2) search_gemm_kernel(SearchArgs a) {
     // buffers (st + 2) % 3 and (st + 3) % 4 were last read in step st - 1
     // (after the last word, the "next" plane words are a stale buffer:
     // decoded, never used)
-    uint32_t w[2][NB], wn[2][NB];
-    rec_words(st, w);
-    rec_words(st + 1, wn);
     products(st, 0, Bn, w, 1, Bk);
     corrections(st);           // B8 complete: slice 0 (a step early) and slice 1
+    uint32_t wn[2][NB];        // planes of word st + 1 landed before this step's barrier
+    rec_words(st + 1, wn);
     products(st, 1, Bk, wn, 0, Bn);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int p = 0; p < NB; ++p) w[rb][p] = wn[rb][p];
   }
 
   // thresholds of the tile's queries, in the (now free) query-row buffers;
