@@ -95,12 +95,15 @@ __host__ __device__ inline int fp8_byte_of(int kappa) {
 }
 
 // ---- row preparation: Pi q and S q, split into hi/lo fp16 -----------------
-// Block (row group of kPrepRows queries, chunk of 256 outputs): each thread
-// owns one output row of Pi or S, reads that row as a contiguous column of
-// Pi^T / S^T (coalesced across the wave) and accumulates it against the
-// group's queries, which are staged through LDS 256 coordinates at a time.
-constexpr int kPrepRows = 16;
-constexpr int kPrepJ = 256;
+// On the fp32 matrix cores: a workgroup computes 32 query rows x 128 outputs
+// of [Pi rows | S rows] (4 waves, 32 outputs each) with
+// v_mfma_f32_32x32x2_f32 over the d coordinates, two per instruction.  Lane
+// l supplies q[row0 + l % 32][j + l / 32] (A) and coordinate j + l / 32 of
+// output row o = o0 + l % 32 of Pi or S, read as Pi^T[j + l / 32][o] (B,
+// coalesced across the wave).  The sum of squares of the A values gives
+// ||q|| per row for the fp8 scales.
+constexpr int kPrepRows = 32;
+constexpr int kPrepOut = 128;
 
 struct RowPrepArgs {
   const float* q;        // [n][d]
@@ -112,73 +115,70 @@ struct RowPrepArgs {
   uint32_t* q8scale;     // [n_pad]: E8M0 codes of 2^-e_lo (byte 0) and 2^-e_hi (byte 1)
   float pscale;          // factor on S q (alpha for search)
   int d, Dp;
-  int64_t n, n_pad;
+  int64_t n, n_pad;      // n_pad: a multiple of kPrepRows
 };
 
 __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
-  __shared__ __align__(16) float qv[kPrepJ][kPrepRows];
   __shared__ float qn2[kPrepRows];
-  const int tid = threadIdx.x;
-  float ssq = 0.f;       // this thread's part of ||q||^2 of row tid / 16
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
   const int64_t row0 = (int64_t)blockIdx.x * kPrepRows;
-  const int o = blockIdx.y * 256 + tid;          // output index over [Pi rows | S rows]
+  const int o = blockIdx.y * kPrepOut + 32 * wave + col;   // output column of this lane
   const bool sk = o >= a.Dp;
   const int r = sk ? o - a.Dp : o;
   const bool live = o < 2 * a.Dp && r < a.d;
-  const float* col = (sk ? a.st : a.pit) + (live ? r : 0);
-  float acc[kPrepRows];
+  const float* tc = (sk ? a.st : a.pit) + (live ? r : 0);  // Pi^T / S^T column r
+  const bool qlive = row0 + col < a.n;
+  const float* qp = a.q + (qlive ? row0 + col : 0) * (int64_t)a.d;
+  v16f acc = {};
+  float ssq = 0.f;
+  int j = 0;
+  // batches of 8 coordinates as 4 MFMAs: lane half hh takes coordinates
+  // j + 4 hh .. + 3, one per MFMA, so its query values are one 16-byte load
+  // (the contraction order within a batch is free: A and B agree on it)
+  if (a.d % 4 == 0 && ((uintptr_t)a.q & 15) == 0) {
+    constexpr int U = 8;                         // batches in flight
+    for (; j + 8 * U <= a.d; j += 8 * U) {
+      float4 av[U];
+      float bv[U][4];
 #pragma unroll
-  for (int i = 0; i < kPrepRows; ++i) acc[i] = 0.f;
-  for (int j0 = 0; j0 < a.d; j0 += kPrepJ) {
-    const int nj = min(kPrepJ, a.d - j0);
-    __syncthreads();
-    for (int it = tid; it < kPrepJ * kPrepRows; it += 256) {
-      const int i = it / kPrepJ, j = it % kPrepJ;
-      const int64_t row = row0 + i;
-      qv[j][i] = (row < a.n && j < nj) ? a.q[row * a.d + j0 + j] : 0.f;
-    }
-    __syncthreads();
+      for (int u = 0; u < U; ++u) {
+        const int jb = j + 8 * u + 4 * hh;
+        av[u] = qlive ? *(const float4*)(qp + jb) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int jj = 0; jj < kPrepJ / 16; ++jj) {
-      const float v = qv[16 * (tid & 15) + jj][tid >> 4];
-      ssq = fmaf(v, v, ssq);
-    }
-    if (live) {
-      auto step = [&](const float t, const int j) {
-        const float4* qq = (const float4*)&qv[j][0];
-#pragma unroll
-        for (int i4 = 0; i4 < kPrepRows / 4; ++i4) {
-          const float4 v = qq[i4];
-          acc[4 * i4 + 0] = fmaf(t, v.x, acc[4 * i4 + 0]);
-          acc[4 * i4 + 1] = fmaf(t, v.y, acc[4 * i4 + 1]);
-          acc[4 * i4 + 2] = fmaf(t, v.z, acc[4 * i4 + 2]);
-          acc[4 * i4 + 3] = fmaf(t, v.w, acc[4 * i4 + 3]);
-        }
-      };
-      int j = 0;
-      // batches of 16 independent column loads in flight
-      for (; j + 16 <= nj; j += 16) {
-        float t[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = col[(int64_t)(j0 + j + u) * a.d];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) step(t[u], j + u);
+        for (int c = 0; c < 4; ++c) bv[u][c] = live ? tc[(int64_t)(jb + c) * a.d] : 0.f;
       }
-      for (; j < nj; ++j) step(col[(int64_t)(j0 + j) * a.d], j);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float aq[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          ssq = fmaf(aq[c], aq[c], ssq);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(aq[c], bv[u][c], acc, 0, 0, 0);
+        }
+      }
     }
   }
-  // ||q||^2 per row: the 16 threads of a row are 16 consecutive lanes
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) ssq += __shfl_xor(ssq, m, 16);
-  if ((tid & 15) == 0) qn2[tid >> 4] = ssq;
+  for (; j < a.d; j += 2) {
+    const int jj = j + hh;
+    const float av = (qlive && jj < a.d) ? qp[jj] : 0.f;
+    const float bv = (live && jj < a.d) ? tc[(int64_t)jj * a.d] : 0.f;
+    ssq = fmaf(av, av, ssq);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+  }
+  // ||q||^2 of row col: the two lane halves hold the two halves of its coordinates
+  ssq += __shfl_xor(ssq, 32);
+  if (wave == 0 && hh == 0) qn2[col] = ssq;
   __syncthreads();
   if (o >= 2 * a.Dp) return;
   const int kappa = kslot_of(r & 31);
   const int pos = (r & ~31) + kappa;                // K-slot order within the word
   const int64_t b8 = (int64_t)(r >> 5) * 64 + fp8_byte_of(kappa);
+  // element i: query row 8 (i / 4) + 4 hh + i % 4 of the tile, output o
 #pragma unroll
-  for (int i = 0; i < kPrepRows; ++i) {
-    const int64_t row = row0 + i;
+  for (int i = 0; i < 16; ++i) {
+    const int rl = 8 * (i >> 2) + 4 * hh + (i & 3);
+    const int64_t row = row0 + rl;
     if (row < a.n_pad) {
       const float v = live ? (sk ? a.pscale * acc[i] : acc[i]) : 0.f;
       const __half vh = __float2half(v);
@@ -190,7 +190,7 @@ __global__ void __launch_bounds__(256) row_prep_kernel(RowPrepArgs a) {
         // scaled by powers of two: |Pi q|_j <= ||q|| < 2^e puts (QR hi) 2^(8-e)
         // below 256, and |QR lo| <= 2^-11 |QR| (fp16 rounding) the lo part too
         int e = 0;
-        frexpf(sqrtf(qn2[i]), &e);
+        frexpf(sqrtf(qn2[rl]), &e);
         const int ehi = min(100, max(-100, 8 - e)), elo = ehi + 11;
         const float vl = v - __half2float(vh);
         uint8_t* q8 = a.q8 + row * (int64_t)(2 * a.Dp) + b8;
@@ -1030,7 +1030,7 @@ hipError_t launch_search_topk(const tq_ctx* ctx, const float* queries, int64_t n
   const int prep_out = ctx->mse ? ctx->Dp : 2 * ctx->Dp;
   hipLaunchKernelGGL(row_prep_kernel,
                      dim3((unsigned)((L.rows_pad + kPrepRows - 1) / kPrepRows),
-                          (unsigned)((prep_out + 255) / 256)),
+                          (unsigned)((prep_out + kPrepOut - 1) / kPrepOut)),
                      dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
