@@ -8,19 +8,22 @@
 // the rows are the unit vectors e_j, i.e. QR = Pi^T and QP = S^T, so the
 // "score" of row j is coordinate j of nu (Pi^T c[idx] + alpha gamma S^T s).
 //
-// Search: records are decoded once per 128-record tile and 32-coordinate word
-// into fp16 LDS operands -- centroid hi and lo parts and gamma * s (gamma is
-// an fp16 value and s = +-1, so the product is exact) -- and the query rows
-// of a 256-query tile, split hi + lo with alpha folded into the sketch half,
-// are staged next to them, by producer waves one word ahead of the MFMA
-// waves (search_gemm_kernel).  One accumulator then takes all five passes on
-// v_mfma_f32_32x32x16_f16:
-//   acc += QR_hi c_hi + QR_lo c_hi + QR_hi c_lo + (alpha QP)_hi gs + (alpha QP)_lo gs,
-// and score = nu * acc.  Instead of writing every score, the epilogue keeps
-// only those above the query's running k-th best score (candidates appended
-// with one atomic per wave and query row), and a one-wave-per-query merge
-// after each chunk of records folds them into the running top-k (score
-// descending, index ascending) and raises the threshold.
+// Search: the query rows (Pi q, S q; row_prep_kernel on the fp32 matrix
+// cores) are split into fp16 hi parts plus fp8 copies for the correction
+// products, with alpha folded into the sketch half, and stored in K-slot
+// order.  search_gemm_kernel copies a 256-query tile's rows and a 256-record
+// tile's plane words into LDS two words ahead, and each MFMA wave decodes its
+// own records' words into its B operands in registers (v_perm_b32 lookups in
+// byte tables of the codebook and of each record's gamma).  Per 32-coordinate
+// word and 32 x 32 block one accumulator takes
+//   acc += QR_hi c_hi + (alpha QP)_hi gamma s        (v_mfma_f32_32x32x16_f16)
+//        + QR_lo c_hi + QR_hi c_lo                   (v_mfma_scale_f32_32x32x64_f8f6f4)
+// (gamma s is exact in fp16: gamma is an fp16 value and s = +-1), and score
+// = nu * acc.  Instead of writing every score, the epilogue keeps only those
+// above the query's running k-th best score (candidates appended with one
+// atomic per wave and query row), and a one-wave-per-query merge after each
+// chunk of records folds them into the running top-k (score descending,
+// index ascending) and raises the threshold.
 //
 // Dequantization has two kernels, picked by tq_dequantize: at d = 128 with
 // at least 64 records per compute unit, dequant128_kernel keeps each wave's
