@@ -615,7 +615,10 @@ def topk_ok(gi, gs, ref_scores, k, tol=TOL):
                                             (128, 3, 100, 2, 64),
                                             # two query tiles of 256 (the second ragged),
                                             # two record chunks with a ragged last tile
-                                            (128, 3, 20000, 300, 10)])
+                                            (128, 3, 20000, 300, 10),
+                                            # above 2048 queries the later chunks hold
+                                            # 16384 records: three chunks, nine query tiles
+                                            (128, 4, 23432, 2100, 10)])
 def test_search_parity(orc, d, b, n_db, n_q, k):
     say("search", d, b, n_db, n_q, k)
     ctx, pi, s, c = ctx_for(orc, d, b)
