@@ -76,9 +76,13 @@ def parse():
 
 
 PROFILE_LOGITS = os.path.join(ROOT, "profiles", "attn_logits_llama8b_decode_32layers.md")
+PROFILE_DEQUANT = os.path.join(ROOT, "profiles", "dequantize_llama_layer.md")
 # sources of the logit kernel (hashed together, in this order)
 LOGIT_SOURCES = [os.path.join(ROOT, "kv_cache_vector_pi_amd", "csrc", f)
                  for f in ("tq_logits.hip", "tq_dev.h")]
+
+
+DEQUANT_SOURCES = [os.path.join(ROOT, "kv_cache_vector_pi_amd", "csrc", "tq_search.hip")]
 
 
 def profiled_traffic(profile, sources):
@@ -553,7 +557,8 @@ def run_dequant(args):
                  {"dtype": "fp16-mfma/fp32", "per_config": res,
                   "roofline": {"bound": "hbm", "kernel": big["kernel"],
                                "achieved": big["GB_per_s"], "peak": 8000.0, "unit": "GB/s",
-                               "frac": big["GB_per_s"] / 8000.0, "traffic": None,
+                               "frac": big["GB_per_s"] / 8000.0,
+                               "traffic": profiled_traffic(PROFILE_DEQUANT, DEQUANT_SOURCES),
                                "mfma_TFLOP_per_s_algorithmic": big["TFLOP_per_s"],
                                "mfma_frac_algorithmic": big["TFLOP_per_s"] / 2500.0}})
 
