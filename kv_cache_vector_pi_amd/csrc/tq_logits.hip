@@ -190,9 +190,14 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // Resident variant (d <= 128, at most 4 query heads per KV head): the A
 // operands and constants stay in registers, and key records are streamed in
 // groups of U tiles with double buffering, so every wave keeps 2U tiles of
-// loads in flight while its MFMAs run.  Records and norms are read through
-// buffer resources bounded to the wave's token range, so loads past the end
-// of the sequence (and of word groups beyond d) return zeros without branches.
+// loads in flight while its MFMAs run.  The nw waves on one (sequence, kv
+// head) take its groups in turn (wave gw: groups gw, gw + nw, ...), so at any
+// moment they read one compact window of the records rather than nw places
+// far apart; with many such streams open at once, the compact window measured
+// faster than contiguous per-wave chunks (the one-shot-block ceiling).
+// Records and norms are read through buffer resources bounded to the group's
+// tokens, so loads past the end of the sequence (and of word groups beyond d)
+// return zeros without branches.
 //
 // NB2 > 0: channel-split records (fractional bit widths, two instances over
 // the first and the remaining channels).  A second record set (a.set2, NB2
@@ -204,13 +209,19 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // shifts 4 (g >> 1) .. +3), so one MFMA covers all 64 coordinates and each
 // Walsh subset (and the sign plane) takes one call instead of two; the query
 // operands are prepared in the same folded layout.
-// The stream of one wave: tokens [t_begin, t_begin + chunk) of sequence bi
-// against kv head h, with the prepared operands of the first record set in
-// Asm (LDS, NC x 64 lanes, then those of set2) and the per-head constants of
-// lane group g in cst / cst2.
-template <int NB, bool MSE, int U, int NB2, bool FOLD>
-__device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, float4 cst,
-                                           float4 cst2, int h, int bi, int t_begin, int chunk) {
+// The stream of one wave: groups gw, gw + nw, gw + 2 nw, ... of U tiles of
+// sequence bi against kv head h, with the prepared operands of the first
+// record set in Asm (LDS, NC x 64 lanes, then those of set2) and the per-head
+// constants of lane group g at cstp[g] / cstp2[g].  pre() runs once on every
+// wave after its first PRIME (1 or 2) groups' loads are issued and before
+// Asm and the constants are read (the kernels fill Asm there), so the first
+// records are on their way from memory while the operands are fetched or
+// prepared.  (The one-call kernel primes one group: a second would not fit
+// its registers beside the preparation's.)
+template <int NB, bool MSE, int U, int NB2, bool FOLD, int PRIME, typename Pre>
+__device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, const float4* cstp,
+                                           const float4* cstp2, int h, int bi, int gw, int nw,
+                                           Pre&& pre) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
   constexpr bool SPLIT = NB2 > 0;
   constexpr int HALVES = FOLD ? 1 : 2;                 // MFMA calls per bit set
@@ -223,27 +234,18 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
   constexpr int NC2 = SPLIT ? HALVES * (NV2 + (MSE ? 0 : 1)) : 1;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
+  constexpr int GT = kTile * U;                        // tokens per group
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
-  if (t_begin >= len) return;
-  const int t_end = min(len, t_begin + chunk);
-  const int n_tok = t_end - t_begin;
-  const int64_t rec_first = (int64_t)h * a.keys_stride_head + start + t_begin;
+  const int64_t rec_seq = (int64_t)h * a.keys_stride_head + start;
   const uint32_t rec_bytes = (uint32_t)(a.W * NB * 4);
-  const rsrc_t rp = make_rsrc(a.planes + rec_first * a.W * NB, (uint32_t)n_tok * rec_bytes);
-  const rsrc_t rn = make_rsrc(a.norms + rec_first, (uint32_t)n_tok * 4u);
   // word group of this lane's token (g, or g & 1 folded); groups beyond d read
   // out of range (0)
   const int wg = FOLD ? (g & 1) : g;
   const uint32_t goff = wg < a.W ? (uint32_t)(wg * NB * 4) : 0x80000000u;
   const uint32_t rec_bytes2 = SPLIT ? (uint32_t)(a.set2.W * NB2 * 4) : 0u;
-  rsrc_t rp2 = rp, rn2 = rn;
   uint32_t goff2 = 0u;
-  if constexpr (SPLIT) {
-    rp2 = make_rsrc(a.set2.planes + rec_first * a.set2.W * NB2, (uint32_t)n_tok * rec_bytes2);
-    rn2 = make_rsrc(a.set2.norms + rec_first, (uint32_t)n_tok * 4u);
-    goff2 = wg < a.set2.W ? (uint32_t)(wg * NB2 * 4) : 0x80000000u;
-  }
+  if constexpr (SPLIT) goff2 = wg < a.set2.W ? (uint32_t)(wg * NB2 * 4) : 0x80000000u;
   // folded bit masks: shifts 4 (g >> 1) + i of every byte
   uint32_t fmk[4];
 #pragma unroll
@@ -269,6 +271,54 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
   // source lanes (head g, token n) of the values this lane stores
   const int src_a = 16 * hf + (ts & 15), src_b = 32 + src_a;
 
+  struct Grp {
+    uint32_t wd[U][NB];
+    uint32_t nr[U];
+    uint32_t wd2[U][NBs];
+    uint32_t nr2[U];
+  };
+  // load(gr, tl): the group whose first token is tl (wave-uniform).  Every
+  // buffer resource covers only tokens that exist.  One plane resource per
+  // tile keeps the lane's plane offset the same for every tile of every
+  // group, so it stays in one register.  The clamps go through readfirstlane:
+  // as vector med3 results they would put the resources in vector registers
+  // and every load in a waterfall loop.
+  const uint32_t voff = (uint32_t)n * rec_bytes + goff;
+  const uint32_t voff2 = (uint32_t)n * rec_bytes2 + goff2;
+  auto load = [&](Grp& gr, int tl) {
+    const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(GT, len - tl)));
+    const int64_t rec = rec_seq + tl;
+    const rsrc_t rn = make_rsrc(a.norms + rec, nt * 4u);
+    rsrc_t rn2 = rn;
+    if constexpr (SPLIT) rn2 = make_rsrc(a.set2.norms + rec, nt * 4u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t ntu = (uint32_t)__builtin_amdgcn_readfirstlane(
+          max(0, min(kTile, (int)nt - kTile * u)));
+      const int64_t ru = rec + kTile * u;
+      buf_group<NB>(make_rsrc(a.planes + ru * a.W * NB, ntu * rec_bytes), voff, gr.wd[u]);
+      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
+      if constexpr (SPLIT) {
+        buf_group<NB2>(make_rsrc(a.set2.planes + ru * a.set2.W * NB2, ntu * rec_bytes2), voff2,
+                       gr.wd2[u]);
+        gr.nr2[u] =
+            __builtin_amdgcn_raw_buffer_load_b32(rn2, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
+      }
+    }
+  };
+  Grp g0, g1;
+  const int step = nw * GT;
+  int tl = gw * GT;
+  const bool any = tl < len;                  // wave-uniform
+  if (any) {
+    load(g0, tl);
+    if constexpr (PRIME > 1) load(g1, tl + step);
+  }
+  pre();
+  if constexpr (PRIME < 2)
+    if (any) load(g1, tl + step);
+  if (!any) return;
+
   v4i A[NC], A2[NC2];
 #pragma unroll
   for (int c = 0; c < NC; ++c) A[c] = Asm[c * 64 + lane];
@@ -278,36 +328,17 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
   }
   // per-head constants with the logit scale and the QJL factor folded in:
   // logit = nu * (vm X + Z + gamma (vq Y + W))
+  const float4 cst = cstp[g];
   const float cX = a.scale * cst.x, cZ = a.scale * cst.z;
   const float cY = a.scale * a.alpha * cst.y, cW = a.scale * a.alpha * cst.w;
   float cX2 = 0.f, cZ2 = 0.f, cY2 = 0.f, cW2 = 0.f;
   if constexpr (SPLIT) {
-    const float4 c2 = cst2;
+    const float4 c2 = cstp2[g];
     cX2 = a.scale * c2.x;
     cZ2 = a.scale * c2.z;
     cY2 = a.scale * a.set2.alpha * c2.y;
     cW2 = a.scale * a.set2.alpha * c2.w;
   }
-
-  struct Grp {
-    uint32_t wd[U][NB];
-    uint32_t nr[U];
-    uint32_t wd2[U][NBs];
-    uint32_t nr2[U];
-  };
-  // tl: local index (from t_begin) of the group's first token
-  auto load = [&](Grp& gr, int tl) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t t = (uint32_t)(tl + kTile * u + n);
-      buf_group<NB>(rp, t * rec_bytes + goff, gr.wd[u]);
-      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4u, 0, kNT);
-      if constexpr (SPLIT) {
-        buf_group<NB2>(rp2, t * rec_bytes2 + goff2, gr.wd2[u]);
-        gr.nr2[u] = __builtin_amdgcn_raw_buffer_load_b32(rn2, t * 4u, 0, kNT);
-      }
-    }
-  };
   // limbs -> float: |limb accumulators| < 2^21.1 (at most 16 NV K-slots per
   // shift, |A| <= 128, |B| <= 2^k), so limb pairs combine exactly in int32
   auto limbs = [](v4i c) {
@@ -328,10 +359,10 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
   auto finish2 = [&](float v0, float v1, int tl) {
     const float a0 = __shfl(v0, src_a), a1 = __shfl(v1, src_a);
     const float b0 = __shfl(v0, src_b), b1 = __shfl(v1, src_b);
-    const int tloc = tl + ts;
-    if (tloc < n_tok) {
-      if (head_a) __builtin_nontemporal_store(ts < 16 ? a0 : a1, &out_a[t_begin + tloc]);
-      if (head_b) __builtin_nontemporal_store(ts < 16 ? b0 : b1, &out_b[t_begin + tloc]);
+    const int tok = tl + ts;
+    if (tok < len) {
+      if (head_a) __builtin_nontemporal_store(ts < 16 ? a0 : a1, &out_a[tok]);
+      if (head_b) __builtin_nontemporal_store(ts < 16 ? b0 : b1, &out_b[tok]);
     }
   };
   // the MFMA chains of one record set (B words per group) for a tile pair,
@@ -370,7 +401,7 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
   auto compute = [&](const Grp& gr, int tl) {
 #pragma unroll
     for (int u = 0; u < U; u += 2) {
-      if (tl + kTile * u >= n_tok) break;
+      if (tl + kTile * u >= len) break;
       v4i am0 = {0, 0, 0, 0}, aq0 = {0, 0, 0, 0}, am1 = {0, 0, 0, 0}, aq1 = {0, 0, 0, 0};
       dots(std::integral_constant<int, NB>{}, A, gr.wd[u], gr.wd[u + 1], am0, aq0, am1, aq1);
       float v0 = logit(am0, aq0, gr.nr[u], cX, cZ, cY, cW);
@@ -385,13 +416,11 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, fl
       finish2(v0, v1, tl + kTile * u);
     }
   };
-  Grp g0, g1;
-  load(g0, 0);
-  for (int tl = 0; tl < n_tok; tl += 2 * kTile * U) {
-    load(g1, tl + kTile * U);
+  for (; tl < len; tl += 2 * step) {
     compute(g0, tl);
-    load(g0, tl + 2 * kTile * U);
-    compute(g1, tl + kTile * U);
+    load(g0, tl + 2 * step);
+    compute(g1, tl + step);
+    load(g1, tl + 3 * step);
   }
 }
 
@@ -413,18 +442,17 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const size_t rbb2 = (size_t)NC2 * 64 * 16 + 64;
   const char* wsb2 = a.set2.ws + ((size_t)bi * a.n_kv + h) * rbb2;
   __shared__ v4i Asm[(NC + (SPLIT ? NC2 : 0)) * 64];
-  for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
-  if constexpr (SPLIT)
-    for (int i = threadIdx.x; i < NC2 * 64; i += 256) Asm[NC * 64 + i] = ((const v4i*)wsb2)[i];
-  __syncthreads();
-  const int g = (threadIdx.x & 63) >> 4;
-  const float4 cst = ((const float4*)(wsb + (size_t)NC * 64 * 16))[g];
-  float4 cst2 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if constexpr (SPLIT) cst2 = ((const float4*)(wsb2 + (size_t)NC2 * 64 * 16))[g];
+  // the operands are copied to LDS once the first records are requested
+  auto pre = [&]() {
+    for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
+    if constexpr (SPLIT)
+      for (int i = threadIdx.x; i < NC2 * 64; i += 256) Asm[NC * 64 + i] = ((const v4i*)wsb2)[i];
+    __syncthreads();
+  };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-  const int chunk = a.tiles_per_wave * kTile;
-  res_stream<NB, MSE, U, NB2, FOLD>(a, Asm, cst, cst2, h, bi,
-                                    (blockIdx.x * kWaves + wave) * chunk, chunk);
+  res_stream<NB, MSE, U, NB2, FOLD, (NB2 > 0 ? 1 : 2)>(a, Asm, (const float4*)(wsb + (size_t)NC * 64 * 16),
+                                    (const float4*)(wsb2 + (size_t)NC2 * 64 * 16), h, bi,
+                                    blockIdx.x * kWaves + wave, gridDim.x * kWaves, pre);
 }
 
 // One launch for a whole call: each workgroup of 16 waves first prepares the
@@ -456,133 +484,135 @@ __global__ void __launch_bounds__(64 * kOneWaves) attn_logits_one_kernel(AttnArg
   float* out = outp[part & 1];
   float* rd = red[part & 1];
 
-  // Dp <= 4 nq: one chunk of outputs, as prep_block at these sizes; a
-  // thread's table rows (at most 16: jl = 16 at d = 128) are all requested
-  // before the queries are staged, so the two memory round trips overlap
-  const int quad = ptid & (nq - 1), jg = ptid / nq;
-  const int jl = (d + nj - 1) / nj;
-  const int ja = min(d, jg * jl), jb = min(d, ja + jl);
-  const int r = 4 * quad;
-  const bool rows = act && r < d;
-  float4 t[16];
-  if (rows) {
-    const float* tr = tab + r;
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (ja + u < jb) t[u] = *(const float4*)(tr + (int64_t)(ja + u) * d);
-  }
-  for (int it = tid; it < 4 * d; it += 64 * kOneWaves) {
-    const int hh = it / d, j = it - hh * d;
-    qv[4 * j + hh] = hh < p.G
-        ? p.q[(int64_t)bi * p.q_stride_batch + (int64_t)(h * p.G + hh) * p.q_stride_head + j]
-        : 0.f;
-  }
-  __syncthreads();
-  if (act) {
-    float acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
-    if (rows) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (ja + u < jb) {
-          const float4 qq = *(const float4*)&qv[4 * (ja + u)];
-          const float tv[4] = {t[u].x, t[u].y, t[u].z, t[u].w}, qs[4] = {qq.x, qq.y, qq.z, qq.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(tv[e], qs[i], acc[i][e]);
-        }
-      }
-    }
-    for (int off = nq; off < 64; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
-    if (lane < nq)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rd[(pwave * 16 + 4 * i + e) * nq + quad] = acc[i][e];
-  }
-  __syncthreads();
-  if (act) {
-    for (int it = ptid; it < 16 * nq; it += 256) {
-      const int k = it / nq, qd = it - k * nq;
-      const float v = (rd[k * nq + qd] + rd[(16 + k) * nq + qd]) +
-                      (rd[(32 + k) * nq + qd] + rd[(48 + k) * nq + qd]);
-      const int o = 4 * qd + (k & 3);
-      if (o < Dp) out[(k >> 2) * Dp + o] = v;
-    }
-  }
-  __syncthreads();
   float* cdst_base = (float*)(abuf + (size_t)NC * 64 * 16);
-  if (act) {
-    const float* r1 = out + pwave * Dp;
-    float m1 = 0.f, t1 = 0.f;
-    for (int j = lane; j < Dp; j += 64) {
-      m1 = fmaxf(m1, fabsf(r1[j]));
-      t1 += r1[j];
-    }
-    m1 = wave_max(m1);
-    t1 = wave_sum(t1);
-    if (lane == 0) {
-      float wmax = 2.f;
-      if (part == 0) {
-        wmax = 0.f;
-        for (int v = 0; v < p.nv; ++v) wmax = fmaxf(wmax, fabsf(p.wm2[v]));
-      }
-      const float vmax = wmax * m1;
-      int e = 0;
-      if (vmax > 0.f) { int ex; frexpf(vmax, &ex); e = min(30 - ex, 120); }
-      qfix_e[part][pwave] = e;
-      float* cdst = cdst_base + 4 * pwave;
-      if (part == 0) {
-        cdst[0] = ldexpf(1.f, -e);
-        cdst[2] = p.c0 * t1;
-        if (p.n_parts == 1) {
-          cdst[1] = 0.f;
-          cdst[3] = 0.f;
-        }
-      } else {
-        cdst[1] = ldexpf(1.f, -e);
-        cdst[3] = -t1;
-      }
-    }
-  }
-  __syncthreads();
-  {
-    // the operands of both parts, spread over all 16 waves
-    const int code_calls = p.fold ? p.nv : 2 * p.nv;
-    const int sign_calls = p.nc - code_calls;
-    const int items0 = 4 * code_calls * 4, items = items0 + (p.n_parts > 1 ? 4 * sign_calls * 4 : 0);
-    for (int it = tid; it < items; it += 64 * kOneWaves) {
-      const int pt = it >= items0;
-      const int n_c = pt ? sign_calls : code_calls;
-      const int i = it - (pt ? items0 : 0);
-      const int g = i & 3, rest = i >> 2;
-      const int cl = rest % n_c, hh = rest / n_c;
-      const int c = (pt ? code_calls : 0) + cl;
-      const int w = p.fold ? (g & 1) : g;
-      const int kbase = p.fold ? 4 * (g >> 1) : (pt ? 4 * cl : 4 * (c % 2));
-      const float wv = pt ? 2.f : p.wm2[p.fold ? c : c / 2];
-      uint4 o[4];
-      limb_operands(outp[pt] + hh * Dp, qfix_e[pt][hh], wv, w, p.W, d, kbase, o);
-      uint4* dst = (uint4*)(abuf + ((size_t)c * 64 + 16 * g + 4 * hh) * 16);
+
+  // the preparation: every wave runs it once its first records are requested
+  auto pre = [&]() {
+    // Dp <= 4 nq: one chunk of outputs, as prep_block at these sizes; a
+    // thread's table rows (at most 16: jl = 16 at d = 128) are all requested
+    // before the queries are staged, so the two memory round trips overlap
+    const int quad = ptid & (nq - 1), jg = ptid / nq;
+    const int jl = (d + nj - 1) / nj;
+    const int ja = min(d, jg * jl), jb = min(d, ja + jl);
+    const int r = 4 * quad;
+    const bool rows = act && r < d;
+    float4 t[16];
+    if (rows) {
+      const float* tr = tab + r;
 #pragma unroll
-      for (int L = 0; L < 4; ++L) dst[L] = o[L];
+      for (int u = 0; u < 16; ++u)
+        if (ja + u < jb) t[u] = *(const float4*)(tr + (int64_t)(ja + u) * d);
     }
-  }
-  __syncthreads();
-  const int g = lane >> 4;
-  const float4 cst = ((const float4*)cdst_base)[g];
+    for (int it = tid; it < 4 * d; it += 64 * kOneWaves) {
+      const int hh = it / d, j = it - hh * d;
+      qv[4 * j + hh] = hh < p.G
+          ? p.q[(int64_t)bi * p.q_stride_batch + (int64_t)(h * p.G + hh) * p.q_stride_head + j]
+          : 0.f;
+    }
+    __syncthreads();
+    if (act) {
+      float acc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = 0.f;
+      if (rows) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (ja + u < jb) {
+            const float4 qq = *(const float4*)&qv[4 * (ja + u)];
+            const float tv[4] = {t[u].x, t[u].y, t[u].z, t[u].w}, qs[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(tv[e], qs[i], acc[i][e]);
+          }
+        }
+      }
+      for (int off = nq; off < 64; off <<= 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] += __shfl_xor(acc[i][e], off);
+      if (lane < nq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rd[(pwave * 16 + 4 * i + e) * nq + quad] = acc[i][e];
+    }
+    __syncthreads();
+    if (act) {
+      for (int it = ptid; it < 16 * nq; it += 256) {
+        const int k = it / nq, qd = it - k * nq;
+        const float v = (rd[k * nq + qd] + rd[(16 + k) * nq + qd]) +
+                        (rd[(32 + k) * nq + qd] + rd[(48 + k) * nq + qd]);
+        const int o = 4 * qd + (k & 3);
+        if (o < Dp) out[(k >> 2) * Dp + o] = v;
+      }
+    }
+    __syncthreads();
+    if (act) {
+      const float* r1 = out + pwave * Dp;
+      float m1 = 0.f, t1 = 0.f;
+      for (int j = lane; j < Dp; j += 64) {
+        m1 = fmaxf(m1, fabsf(r1[j]));
+        t1 += r1[j];
+      }
+      m1 = wave_max(m1);
+      t1 = wave_sum(t1);
+      if (lane == 0) {
+        float wmax = 2.f;
+        if (part == 0) {
+          wmax = 0.f;
+          for (int v = 0; v < p.nv; ++v) wmax = fmaxf(wmax, fabsf(p.wm2[v]));
+        }
+        const float vmax = wmax * m1;
+        int e = 0;
+        if (vmax > 0.f) { int ex; frexpf(vmax, &ex); e = min(30 - ex, 120); }
+        qfix_e[part][pwave] = e;
+        float* cdst = cdst_base + 4 * pwave;
+        if (part == 0) {
+          cdst[0] = ldexpf(1.f, -e);
+          cdst[2] = p.c0 * t1;
+          if (p.n_parts == 1) {
+            cdst[1] = 0.f;
+            cdst[3] = 0.f;
+          }
+        } else {
+          cdst[1] = ldexpf(1.f, -e);
+          cdst[3] = -t1;
+        }
+      }
+    }
+    __syncthreads();
+    {
+      // the operands of both parts, spread over all 16 waves
+      const int code_calls = p.fold ? p.nv : 2 * p.nv;
+      const int sign_calls = p.nc - code_calls;
+      const int items0 = 4 * code_calls * 4, items = items0 + (p.n_parts > 1 ? 4 * sign_calls * 4 : 0);
+      for (int it = tid; it < items; it += 64 * kOneWaves) {
+        const int pt = it >= items0;
+        const int n_c = pt ? sign_calls : code_calls;
+        const int i = it - (pt ? items0 : 0);
+        const int g = i & 3, rest = i >> 2;
+        const int cl = rest % n_c, hh = rest / n_c;
+        const int c = (pt ? code_calls : 0) + cl;
+        const int w = p.fold ? (g & 1) : g;
+        const int kbase = p.fold ? 4 * (g >> 1) : (pt ? 4 * cl : 4 * (c % 2));
+        const float wv = pt ? 2.f : p.wm2[p.fold ? c : c / 2];
+        uint4 o[4];
+        limb_operands(outp[pt] + hh * Dp, qfix_e[pt][hh], wv, w, p.W, d, kbase, o);
+        uint4* dst = (uint4*)(abuf + ((size_t)c * 64 + 16 * g + 4 * hh) * 16);
+#pragma unroll
+        for (int L = 0; L < 4; ++L) dst[L] = o[L];
+      }
+    }
+    __syncthreads();
+  };
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chunk = a.tiles_per_wave * kTile;
-  res_stream<NB, MSE, 4, 0, FOLD>(a, (const v4i*)abuf, cst, make_float4(0.f, 0.f, 0.f, 0.f), h,
-                                  bi, (blockIdx.x * kOneWaves + wave) * chunk, chunk);
+  res_stream<NB, MSE, 4, 0, FOLD, 1>(a, (const v4i*)abuf, (const float4*)cdst_base,
+                                  (const float4*)cdst_base, h, bi, blockIdx.x * kOneWaves + wave,
+                                  gridDim.x * kOneWaves, pre);
 }
 
 template <typename K>
@@ -653,12 +683,9 @@ bool resident_ok(const tq_ctx* ctx, int n_rb) {
   return ctx->W <= 4 && n_rb == 1 && masks_ok;
 }
 
-// Grid of a stream with nb resident blocks per CU: one round of resident
-// waves over all tiles (each wave takes a contiguous chunk of one sequence),
-// so no partial second round is left.  Short chunks (about 8 rounds of
-// resident waves) keep many independent read/write streams in flight, which
-// measured best on the mixed record-read / logit-write traffic; at least 8
-// tiles per wave.
+// Grid of a stream with nb resident blocks per CU: about 8 rounds of resident
+// workgroups over all tiles, at least 8 tiles per wave (the resident kernels
+// hand a sequence's tile groups to its waves in turn).
 dim3 stream_grid(int n_cu, int nb, int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
                  int& tiles_per_wave) {
   const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
