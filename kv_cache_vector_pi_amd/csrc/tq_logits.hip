@@ -190,14 +190,9 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // Resident variant (d <= 128, at most 4 query heads per KV head): the A
 // operands and constants stay in registers, and key records are streamed in
 // groups of U tiles with double buffering, so every wave keeps 2U tiles of
-// loads in flight while its MFMAs run.  The nw waves on one (sequence, kv
-// head) take its groups in turn (wave gw: groups gw, gw + nw, ...), so at any
-// moment they read one compact window of the records rather than nw places
-// far apart; with many such streams open at once, the compact window measured
-// faster than contiguous per-wave chunks (the one-shot-block ceiling).
-// Records and norms are read through buffer resources bounded to the group's
-// tokens, so loads past the end of the sequence (and of word groups beyond d)
-// return zeros without branches.
+// loads in flight while its MFMAs run.  Records and norms are read through
+// buffer resources bounded to the wave's tokens, so loads past them (and of
+// word groups beyond d) return zeros without branches or traffic.
 //
 // NB2 > 0: channel-split records (fractional bit widths, two instances over
 // the first and the remaining channels).  A second record set (a.set2, NB2
@@ -209,19 +204,24 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // shifts 4 (g >> 1) .. +3), so one MFMA covers all 64 coordinates and each
 // Walsh subset (and the sign plane) takes one call instead of two; the query
 // operands are prepared in the same folded layout.
-// The stream of one wave: groups gw, gw + nw, gw + 2 nw, ... of U tiles of
-// sequence bi against kv head h, with the prepared operands of the first
-// record set in Asm (LDS, NC x 64 lanes, then those of set2) and the per-head
-// constants of lane group g at cstp[g] / cstp2[g].  pre() runs once on every
-// wave after its first PRIME (1 or 2) groups' loads are issued and before
-// Asm and the constants are read (the kernels fill Asm there), so the first
-// records are on their way from memory while the operands are fetched or
-// prepared.  (The one-call kernel primes one group: a second would not fit
-// its registers beside the preparation's.)
-template <int NB, bool MSE, int U, int NB2, bool FOLD, int PRIME, typename Pre>
+// The stream of one wave, wave wi of the wn on sequence bi against kv head h,
+// with the prepared operands of the first record set in Asm (LDS, NC x 64
+// lanes, then those of set2) and the per-head constants of lane group g at
+// cstp[g] / cstp2[g].  The tokens come in groups of U tiles:
+//  * IL false: the wave's own contiguous chunk [wi chunk, wi chunk + chunk);
+//  * IL true: the sequence's groups in turn (wave wi: groups wi, wi + wn,
+//    ...), so the waves of a sequence read one compact window together.
+// pre() runs once on every wave (the kernels fill Asm there).  PRIME = 0:
+// the first loads follow it; PRIME = 1: the first group's loads are issued
+// before it, so they are in flight while the operands are prepared.  On the
+// one-call kernel at b >= 3 the interleaved order with one primed group
+// measured 2-7% faster than the contiguous order; on the prepared-operand
+// stream, and at b = 2, the contiguous order without priming was faster
+// (2-3% on the 32-layer stream).
+template <int NB, bool MSE, int U, int NB2, bool FOLD, bool IL, int PRIME, typename Pre>
 __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, const float4* cstp,
-                                           const float4* cstp2, int h, int bi, int gw, int nw,
-                                           Pre&& pre) {
+                                           const float4* cstp2, int h, int bi, int wi, int wn,
+                                           int chunk, Pre&& pre) {
   static_assert(U % 2 == 0, "tiles are processed in pairs");
   constexpr bool SPLIT = NB2 > 0;
   constexpr int HALVES = FOLD ? 1 : 2;                 // MFMA calls per bit set
@@ -237,6 +237,9 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, co
   constexpr int GT = kTile * U;                        // tokens per group
   const int len = a.seq_len[bi];
   const int64_t start = a.seq_start[bi];
+  const int t_begin = IL ? wi * GT : wi * chunk;       // first group's first token
+  const int t_end = IL ? len : min(len, t_begin + chunk);   // the wave's tokens end here
+  const int step = IL ? wn * GT : GT;                  // from one group to the next
   const int64_t rec_seq = (int64_t)h * a.keys_stride_head + start;
   const uint32_t rec_bytes = (uint32_t)(a.W * NB * 4);
   // word group of this lane's token (g, or g & 1 folded); groups beyond d read
@@ -277,46 +280,65 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, co
     uint32_t wd2[U][NBs];
     uint32_t nr2[U];
   };
-  // load(gr, tl): the group whose first token is tl (wave-uniform).  Every
-  // buffer resource covers only tokens that exist.  One plane resource per
-  // tile keeps the lane's plane offset the same for every tile of every
-  // group, so it stays in one register.  The clamps go through readfirstlane:
-  // as vector med3 results they would put the resources in vector registers
-  // and every load in a waterfall loop.
+  // load(gr, tl): the group whose first token is tl (wave-uniform).
+  //  * IL: one plane resource per tile (its tokens that exist) keeps a lane's
+  //    plane offset the same for every tile of every group, in one register.
+  //    The clamps go through readfirstlane: as vector med3 results they would
+  //    put the resources in vector registers and every load in a waterfall
+  //    loop.
+  //  * contiguous: one resource per wave over its chunk.
   const uint32_t voff = (uint32_t)n * rec_bytes + goff;
   const uint32_t voff2 = (uint32_t)n * rec_bytes2 + goff2;
+  const int64_t rec_first = rec_seq + t_begin;
+  const uint32_t n_tok = (uint32_t)max(0, t_end - t_begin);
+  const rsrc_t rp_w = make_rsrc(a.planes + rec_first * a.W * NB, n_tok * rec_bytes);
+  const rsrc_t rn_w = make_rsrc(a.norms + rec_first, n_tok * 4u);
+  rsrc_t rp2_w = rp_w, rn2_w = rn_w;
+  if constexpr (SPLIT) {
+    rp2_w = make_rsrc(a.set2.planes + rec_first * a.set2.W * NB2, n_tok * rec_bytes2);
+    rn2_w = make_rsrc(a.set2.norms + rec_first, n_tok * 4u);
+  }
   auto load = [&](Grp& gr, int tl) {
-    const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(GT, len - tl)));
-    const int64_t rec = rec_seq + tl;
-    const rsrc_t rn = make_rsrc(a.norms + rec, nt * 4u);
-    rsrc_t rn2 = rn;
-    if constexpr (SPLIT) rn2 = make_rsrc(a.set2.norms + rec, nt * 4u);
+    if constexpr (IL) {
+      const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(GT, t_end - tl)));
+      const int64_t rec = rec_seq + tl;
+      const rsrc_t rn = make_rsrc(a.norms + rec, nt * 4u);
+      rsrc_t rn2 = rn;
+      if constexpr (SPLIT) rn2 = make_rsrc(a.set2.norms + rec, nt * 4u);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t ntu = (uint32_t)__builtin_amdgcn_readfirstlane(
-          max(0, min(kTile, (int)nt - kTile * u)));
-      const int64_t ru = rec + kTile * u;
-      buf_group<NB>(make_rsrc(a.planes + ru * a.W * NB, ntu * rec_bytes), voff, gr.wd[u]);
-      gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
-      if constexpr (SPLIT) {
-        buf_group<NB2>(make_rsrc(a.set2.planes + ru * a.set2.W * NB2, ntu * rec_bytes2), voff2,
-                       gr.wd2[u]);
-        gr.nr2[u] =
-            __builtin_amdgcn_raw_buffer_load_b32(rn2, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
+      for (int u = 0; u < U; ++u) {
+        const uint32_t ntu = (uint32_t)__builtin_amdgcn_readfirstlane(
+            max(0, min(kTile, (int)nt - kTile * u)));
+        const int64_t ru = rec + kTile * u;
+        buf_group<NB>(make_rsrc(a.planes + ru * a.W * NB, ntu * rec_bytes), voff, gr.wd[u]);
+        gr.nr[u] =
+            __builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
+        if constexpr (SPLIT) {
+          buf_group<NB2>(make_rsrc(a.set2.planes + ru * a.set2.W * NB2, ntu * rec_bytes2), voff2,
+                         gr.wd2[u]);
+          gr.nr2[u] =
+              __builtin_amdgcn_raw_buffer_load_b32(rn2, (uint32_t)(kTile * u + n) * 4u, 0, kNT);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t t = (uint32_t)(tl - t_begin + kTile * u + n);
+        buf_group<NB>(rp_w, t * rec_bytes + goff, gr.wd[u]);
+        gr.nr[u] = __builtin_amdgcn_raw_buffer_load_b32(rn_w, t * 4u, 0, kNT);
+        if constexpr (SPLIT) {
+          buf_group<NB2>(rp2_w, t * rec_bytes2 + goff2, gr.wd2[u]);
+          gr.nr2[u] = __builtin_amdgcn_raw_buffer_load_b32(rn2_w, t * 4u, 0, kNT);
+        }
       }
     }
   };
   Grp g0, g1;
-  const int step = nw * GT;
-  int tl = gw * GT;
-  const bool any = tl < len;                  // wave-uniform
-  if (any) {
-    load(g0, tl);
-    if constexpr (PRIME > 1) load(g1, tl + step);
-  }
+  int tl = t_begin;
+  const bool any = tl < t_end;                // wave-uniform
+  if constexpr (PRIME > 0)
+    if (any) load(g0, tl);
   pre();
-  if constexpr (PRIME < 2)
-    if (any) load(g1, tl + step);
   if (!any) return;
 
   v4i A[NC], A2[NC2];
@@ -360,7 +382,7 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, co
     const float a0 = __shfl(v0, src_a), a1 = __shfl(v1, src_a);
     const float b0 = __shfl(v0, src_b), b1 = __shfl(v1, src_b);
     const int tok = tl + ts;
-    if (tok < len) {
+    if (tok < t_end) {
       if (head_a) __builtin_nontemporal_store(ts < 16 ? a0 : a1, &out_a[tok]);
       if (head_b) __builtin_nontemporal_store(ts < 16 ? b0 : b1, &out_b[tok]);
     }
@@ -401,7 +423,7 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, co
   auto compute = [&](const Grp& gr, int tl) {
 #pragma unroll
     for (int u = 0; u < U; u += 2) {
-      if (tl + kTile * u >= len) break;
+      if (tl + kTile * u >= t_end) break;
       v4i am0 = {0, 0, 0, 0}, aq0 = {0, 0, 0, 0}, am1 = {0, 0, 0, 0}, aq1 = {0, 0, 0, 0};
       dots(std::integral_constant<int, NB>{}, A, gr.wd[u], gr.wd[u + 1], am0, aq0, am1, aq1);
       float v0 = logit(am0, aq0, gr.nr[u], cX, cZ, cY, cW);
@@ -416,11 +438,12 @@ __device__ __forceinline__ void res_stream(const AttnArgs& a, const v4i* Asm, co
       finish2(v0, v1, tl + kTile * u);
     }
   };
-  for (; tl < len; tl += 2 * step) {
+  if constexpr (PRIME == 0) load(g0, tl);
+  for (; tl < t_end; tl += 2 * step) {
+    load(g1, tl + step);
     compute(g0, tl);
     load(g0, tl + 2 * step);
     compute(g1, tl + step);
-    load(g1, tl + 3 * step);
   }
 }
 
@@ -442,7 +465,6 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
   const size_t rbb2 = (size_t)NC2 * 64 * 16 + 64;
   const char* wsb2 = a.set2.ws + ((size_t)bi * a.n_kv + h) * rbb2;
   __shared__ v4i Asm[(NC + (SPLIT ? NC2 : 0)) * 64];
-  // the operands are copied to LDS once the first records are requested
   auto pre = [&]() {
     for (int i = threadIdx.x; i < NC * 64; i += 256) Asm[i] = ((const v4i*)wsb)[i];
     if constexpr (SPLIT)
@@ -450,9 +472,10 @@ __global__ void __launch_bounds__(256) attn_logits_res_kernel(AttnArgs a) {
     __syncthreads();
   };
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-  res_stream<NB, MSE, U, NB2, FOLD, (NB2 > 0 ? 1 : 2)>(a, Asm, (const float4*)(wsb + (size_t)NC * 64 * 16),
-                                    (const float4*)(wsb2 + (size_t)NC2 * 64 * 16), h, bi,
-                                    blockIdx.x * kWaves + wave, gridDim.x * kWaves, pre);
+  res_stream<NB, MSE, U, NB2, FOLD, false, 0>(a, Asm, (const float4*)(wsb + (size_t)NC * 64 * 16),
+                                              (const float4*)(wsb2 + (size_t)NC2 * 64 * 16), h,
+                                              bi, blockIdx.x * kWaves + wave, gridDim.x * kWaves,
+                                              a.tiles_per_wave * kTile, pre);
 }
 
 // One launch for a whole call: each workgroup of 16 waves first prepares the
@@ -486,7 +509,8 @@ __global__ void __launch_bounds__(64 * kOneWaves) attn_logits_one_kernel(AttnArg
 
   float* cdst_base = (float*)(abuf + (size_t)NC * 64 * 16);
 
-  // the preparation: every wave runs it once its first records are requested
+  // the preparation (every wave runs it, in the stream after its first loads
+  // are issued where the stream primes them)
   auto pre = [&]() {
     // Dp <= 4 nq: one chunk of outputs, as prep_block at these sizes; a
     // thread's table rows (at most 16: jl = 16 at d = 128) are all requested
@@ -610,9 +634,12 @@ __global__ void __launch_bounds__(64 * kOneWaves) attn_logits_one_kernel(AttnArg
     __syncthreads();
   };
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  res_stream<NB, MSE, 4, 0, FOLD, 1>(a, (const v4i*)abuf, (const float4*)cdst_base,
-                                  (const float4*)cdst_base, h, bi, blockIdx.x * kOneWaves + wave,
-                                  gridDim.x * kOneWaves, pre);
+  constexpr bool IL = NB >= 3;                 // (measured: see res_stream)
+  res_stream<NB, MSE, 4, 0, FOLD, IL, IL ? 1 : 0>(a, (const v4i*)abuf, (const float4*)cdst_base,
+                                                  (const float4*)cdst_base, h, bi,
+                                                  blockIdx.x * kOneWaves + wave,
+                                                  gridDim.x * kOneWaves,
+                                                  a.tiles_per_wave * kTile, pre);
 }
 
 template <typename K>
@@ -683,9 +710,12 @@ bool resident_ok(const tq_ctx* ctx, int n_rb) {
   return ctx->W <= 4 && n_rb == 1 && masks_ok;
 }
 
-// Grid of a stream with nb resident blocks per CU: about 8 rounds of resident
-// workgroups over all tiles, at least 8 tiles per wave (the resident kernels
-// hand a sequence's tile groups to its waves in turn).
+// Grid of a stream with nb resident blocks per CU: one round of resident
+// waves over all tiles (each wave takes a contiguous chunk of one sequence),
+// so no partial second round is left.  Short chunks (about 8 rounds of
+// resident waves) keep many independent read/write streams in flight, which
+// measured best on the mixed record-read / logit-write traffic; at least 8
+// tiles per wave.
 dim3 stream_grid(int n_cu, int nb, int32_t batch, int32_t n_kv_heads, int32_t max_seq_len,
                  int& tiles_per_wave) {
   const int64_t tiles_seq = (max_seq_len + kTile - 1) / kTile;
