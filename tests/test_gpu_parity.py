@@ -291,6 +291,49 @@ def test_prepared_queries_match_one_call(orc, d, b):
         tq.tq_attn_logits_prepared(ctx, ws2[:64], 1, 8, P, N, 2, n, ss, sl, n, 0.5, two, n)
 
 
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_one_call_long_ragged_matches_prepared(orc, b):
+    """At lengths where every wave of the one-call kernel streams several tile
+    groups (b >= 3: the groups of a sequence taken by its waves in turn; b = 2:
+    contiguous chunks) and the sequences end inside a group, the one-call
+    logits equal the prepared form's bit for bit, and nothing outside the
+    sequences' logit ranges is written."""
+    d, n_q, n_kv = 128, 32, 8
+    ctx, pi, s, c = ctx_for(orc, d, b)
+    lens = [150001, 70003]
+    total = sum(lens)
+    starts = [0, lens[0]]
+    stride_head = total + 5
+    P, N = workloads.random_records(n_kv * total, tq.tq_record_words(d, b), 21 + b, DEV)
+    q = workloads.normal((2, n_q, d), 21 + b, 12, DEV)
+    ss = torch.as_tensor(starts, dtype=torch.int64, device=DEV)
+    sl = torch.as_tensor(lens, dtype=torch.int32, device=DEV)
+    one = torch.full((n_q, stride_head), float("nan"), device=DEV)
+    ws = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 2, n_q, n_kv))
+    tq.tq_attn_logits(ctx, q, 2, n_q, n_q * d, P, N, n_kv, total, ss, sl, max(lens), 0.125,
+                      one, stride_head, ws)
+    ws2 = tq.workspace(tq.tq_attn_logits_workspace_bytes(ctx, 2, n_q, n_kv))
+    tq.tq_attn_prepare(ctx, q, 2, n_q, n_q * d, n_kv, ws2)
+    two = torch.full((n_q, stride_head), float("nan"), device=DEV)
+    tq.tq_attn_logits_prepared(ctx, ws2, 2, n_q, P, N, n_kv, total, ss, sl, max(lens), 0.125,
+                               two, stride_head)
+    torch.cuda.synchronize()
+    assert torch.equal(one[:, :total], two[:, :total])
+    assert bool(torch.isfinite(one[:, :total]).all())
+    assert bool(torch.isnan(one[:, total:]).all()) and bool(torch.isnan(two[:, total:]).all())
+    # a few tokens of each sequence against the oracle (first, last, a group edge)
+    G = n_q // n_kv
+    for bi, (st, ln) in enumerate(zip(starts, lens)):
+        for h in (0, n_kv - 1):
+            for t in (0, 63, 64, ln - 1):
+                rec = h * total + st + t
+                ref = orc.estimate(d, b, pi, s, c, q[bi, h * G:(h + 1) * G].double().cpu().numpy(),
+                                   P[rec:rec + 1].cpu().numpy().view(np.uint32),
+                                   N[rec:rec + 1].cpu().numpy().view(np.uint16), scale=0.125)
+                got = one[h * G:(h + 1) * G, st + t:st + t + 1].cpu().numpy()
+                assert np.abs(got - ref).max() <= 1e-3 * max(1.0, np.abs(ref).max()), (bi, h, t)
+
+
 def _step_case(orc, d, b, mse, dtype, n_heads, n_tok, L, n_q, n_kv):
     if mse:
         pi = orc.make_rotation(d, 0)[2]
