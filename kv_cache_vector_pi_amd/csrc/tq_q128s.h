@@ -344,10 +344,13 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
     auto finish = [&](const v16f& z, int j) {
       uint32_t sw = 0u;
       if constexpr (!MSE) {
-        uint32_t sb = 0u;
+        // sign bits of z shifted in from i = 15 down (v_alignbit: one vector op
+        // per coordinate), then inverted: bit set <=> z >= 0 (z is never -0:
+        // the accumulators start at +0)
+        uint32_t sn = 0u;
 #pragma unroll
-        for (int i = 15; i >= 0; --i) sb = shift_in(sb, __builtin_amdgcn_ballot_w64(z[i] >= 0.f));
-        sw = halves_or(spread16(sb, hh));
+        for (int i = 15; i >= 0; --i) sn = __builtin_amdgcn_alignbit(sn, __float_as_uint(z[i]), 31);
+        sw = halves_or(spread16(~sn, hh));
       }
       const uint32_t blk = g + (uint32_t)j * G;
       const uint32_t h = head_of(blk, a);
