@@ -30,7 +30,7 @@
 //    outside [2^-120, 2^120] is rescaled in LDS by a power of two before its
 //    Y, so the products (and the norm) stay inside fp32's normal range.
 //  * x rows land in LDS 256 bytes apart with their 16-byte chunks permuted
-//    (chunk c of row r at slot c ^ (r & 7)), so the MFMA operand reads of 8
+//    (chunk c of row r at slot c ^ (r & 15)), so the MFMA operand reads of 16
 //    rows at one chunk hit distinct banks.
 //  * Code wave w and sketch wave 4 + w own output coordinates 32w..32w+31;
 //    their slices of Pi (bf16 hi, mid) and of M (fp16 hi, lo) stay in
@@ -102,7 +102,7 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
   // ---- copy of local block j into LDS buffer j % kSD (sketch waves) -------
   // sketch wave grp copies rows 8 grp .. 8 grp + 7 as two 1 KB pieces (4 rows
   // each); lane l of piece i fills slot l % 16 of row 8 grp + 4i + l / 16
-  // with the row's chunk (slot ^ (row & 7))
+  // with the row's chunk (slot ^ (row & 15))
   auto copy_block = [&](int j) {
     const uint32_t blk = g + (uint32_t)j * G;
     const uint32_t h = head_of(blk, a);
@@ -112,7 +112,7 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = 8 * grp + 4 * i + (lane >> 4);
-      const int chunk = (lane & 15) ^ (row & 7);
+      const int chunk = (lane & 15) ^ (row & 15);
       const uint16_t* src = base + (int64_t)row * a.x_stride_token + 8 * chunk;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(
           lds_addr(&xb[buf][(8 * grp + 4 * i) * 128]));
@@ -127,8 +127,8 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
     const int v = 8 * grp + (lane >> 3);
     const int q = lane & 7;
     uint16_t* rowp = &xb[buf][v * 128];
-    uint4* p0 = (uint4*)(rowp + 8 * ((2 * q) ^ (v & 7)));
-    uint4* p1 = (uint4*)(rowp + 8 * ((2 * q + 1) ^ (v & 7)));
+    uint4* p0 = (uint4*)(rowp + 8 * ((2 * q) ^ (v & 15)));
+    uint4* p1 = (uint4*)(rowp + 8 * ((2 * q + 1) ^ (v & 15)));
     uint4 u0 = *p0, u1 = *p1;
     const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     float ss = 0.f;
@@ -193,18 +193,18 @@ __device__ __forceinline__ void q128s_body(const Q128SArgs& a) {
       Ph[ks] = *(const v8bf*)(a.pib_hi + off);
       Pm[ks] = *(const v8bf*)(a.pib_mid + off);
     }
-    // Y(j): 16 MFMAs on block j's raw rows (chunk c of row r at slot c ^ (r & 7)),
+    // Y(j): 16 MFMAs on block j's raw rows (chunk c of row r at slot c ^ (r & 15)),
     // hi and mid products in one accumulator (back-to-back MFMAs on the same
     // accumulator issue without a stall), the operand read of step ks + 1
     // issued before the MFMAs of step ks
     auto y_block = [&](v16f& acc, int j) {
       const uint16_t* xr = &xb[j % kSD][col * 128];
       acc = v16f{};
-      v8bf xf = *(const v8bf*)(xr + 8 * (hh ^ (col & 7)));
+      v8bf xf = *(const v8bf*)(xr + 8 * (hh ^ (col & 15)));
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         v8bf xn = xf;
-        if (ks < 7) xn = *(const v8bf*)(xr + 8 * ((2 * ks + 2 + hh) ^ (col & 7)));
+        if (ks < 7) xn = *(const v8bf*)(xr + 8 * ((2 * ks + 2 + hh) ^ (col & 15)));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ph[ks], xf, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Pm[ks], xf, acc, 0, 0, 0);
         xf = xn;
