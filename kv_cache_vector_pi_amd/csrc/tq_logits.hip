@@ -215,7 +215,7 @@ __device__ inline void buf_group(rsrc_t r, uint32_t off, uint32_t (&w)[NB]) {
 // the first loads follow it; PRIME = 1: the first group's loads are issued
 // before it, so they are in flight while the operands are prepared.  On the
 // one-call kernel at b >= 3 the interleaved order with one primed group
-// measured 2-7% faster than the contiguous order; on the prepared-operand
+// measured 2-5% faster than the contiguous order; on the prepared-operand
 // stream, and at b = 2, the contiguous order without priming was faster
 // (2-3% on the 32-layer stream).
 template <int NB, bool MSE, int U, int NB2, bool FOLD, bool IL, int PRIME, typename Pre>
